@@ -1,0 +1,199 @@
+"""Plain CPU oracle for the MoE dispatch / combine layout transformation.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the CPU-baseline leg
+of the benchmark are the only code that may import this package.  The product
+path (the HIP library and its Python binding) never touches it, and the two
+share no code.
+
+The arithmetic lives in ``oracle.c`` (plain sequential C, compiled with gcc,
+no fast-math, no FP contraction); this module only marshals numpy arrays to it
+through ctypes.  Every function returns numpy arrays and raises
+``OracleError`` with the oracle's status code on rejected input.
+
+Sources: "GPU microarchitecture: DeepEP first principles" (sections 1.1, 1.2,
+6.1, 6.2, 7.1) and "Deep Dive - DeepEP" (sections "Dispatch: layout, move, and
+epilogue", "Combine: reverse routing plus reduction", "Precision: FP8 on the
+wire, BF16 for the reduction", "A runnable routing ledger").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+OK, BAD_ARG, BAD_ROUTE, NO_CAPACITY = 0, 1, 2, 3
+
+GCC_FLAGS = ["-O2", "-std=c11", "-Wall", "-Wextra", "-ffp-contract=off",
+             "-fno-fast-math", "-fPIC", "-shared"]
+
+
+class OracleError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"oracle {what} rejected its input (status {code})")
+        self.code = code
+
+
+def build_library() -> str:
+    """Compile oracle.c into liboracle.so with gcc (always recompiles)."""
+    tmp = _LIB + ".tmp"
+    subprocess.run(["gcc", *GCC_FLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build_library()
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    lib.oracle_bf16_round.restype = ctypes.c_uint16
+    lib.oracle_bf16_round.argtypes = [ctypes.c_float]
+    lib.oracle_bf16_to_float.restype = ctypes.c_float
+    lib.oracle_bf16_to_float.argtypes = [ctypes.c_uint16]
+    lib.oracle_e4m3_value.restype = ctypes.c_double
+    lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+    lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+    for name in ("oracle_bf16_round_array", "oracle_e4m3_encode_array",
+                 "oracle_e4m3_value_array"):
+        getattr(lib, name).restype = None
+        getattr(lib, name).argtypes = [i64, P, P]
+    lib.oracle_layout.restype = ctypes.c_int
+    lib.oracle_layout.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P]
+    lib.oracle_dispatch.restype = ctypes.c_int
+    lib.oracle_dispatch.argtypes = [i32, i32, i32, i32, i32, i32, i32, P, P, P,
+                                    i64, P, P, P, P, P]
+    lib.oracle_combine.restype = ctypes.c_int
+    lib.oracle_combine.argtypes = [i32, i32, i32, i64, P, P, P, P, P]
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# --------------------------------------------------------------------------
+# conversions
+# --------------------------------------------------------------------------
+
+def bf16_round(v) -> np.ndarray:
+    """fp32 values -> bf16 bit patterns (uint16), round to nearest even."""
+    v = _c(v, np.float32)
+    out = np.empty(v.shape, np.uint16)
+    _load().oracle_bf16_round_array(v.size, _ptr(v), _ptr(out))
+    return out
+
+
+def bf16_to_float(bits) -> np.ndarray:
+    """bf16 bit patterns -> fp32 values (exact)."""
+    bits = _c(bits, np.uint16)
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """fp32 values -> OCP E4M3FN codes (uint8), RNE, saturating."""
+    v = _c(v, np.float32)
+    out = np.empty(v.shape, np.uint8)
+    _load().oracle_e4m3_encode_array(v.size, _ptr(v), _ptr(out))
+    return out
+
+
+def e4m3_value(codes) -> np.ndarray:
+    """E4M3FN codes -> float64 values (NaN for 0x7F / 0xFF)."""
+    codes = _c(codes, np.uint8)
+    out = np.empty(codes.shape, np.float64)
+    _load().oracle_e4m3_value_array(codes.size, _ptr(codes), _ptr(out))
+    return out
+
+
+# --------------------------------------------------------------------------
+# the path
+# --------------------------------------------------------------------------
+
+def layout(topk_idx, num_experts: int, num_ranks: int, alignment: int = 1) -> dict:
+    idx = _c(topk_idx, np.int32)
+    T, k = idx.shape
+    E, R = num_experts, num_ranks
+    out = dict(
+        num_tokens_per_rank=np.zeros(R, np.int32),
+        num_tokens_per_expert=np.zeros(E, np.int32),
+        is_token_in_rank=np.zeros((T, R), np.uint8),
+        expert_offsets=np.zeros(E + 1, np.int32),
+        rank_offsets=np.zeros(R + 1, np.int32),
+    )
+    rc = _load().oracle_layout(T, k, E, R, alignment, _ptr(idx),
+                               _ptr(out["num_tokens_per_rank"]),
+                               _ptr(out["num_tokens_per_expert"]),
+                               _ptr(out["is_token_in_rank"]),
+                               _ptr(out["expert_offsets"]),
+                               _ptr(out["rank_offsets"]))
+    if rc:
+        raise OracleError(rc, "layout")
+    return out
+
+
+def dispatch(x_bits, topk_idx, topk_weights, num_experts: int, num_ranks: int,
+             alignment: int = 1, fp8: bool = False, capacity: int | None = None,
+             fill_recv: int = 0) -> dict:
+    """Returns recv_x (uint16 [cap,H] or uint8 [cap,H]), recv_scales
+    (fp32 [cap,H/128] or None), recv_weights, tok_slot_row, row_src.
+    Rows past expert_offsets[E] keep the fill value ``fill_recv``."""
+    x = _c(x_bits, np.uint16)
+    idx = _c(topk_idx, np.int32)
+    T, H = x.shape
+    k = idx.shape[1]
+    w = None if topk_weights is None else _c(topk_weights, np.float32)
+    if capacity is None:
+        capacity = T * k + num_experts * (alignment - 1)
+    if fp8:
+        recv_x = np.full((capacity, H), fill_recv & 0xFF, np.uint8)
+        recv_scales = np.zeros((capacity, H // 128 if H % 128 == 0 else 1), np.float32)
+    else:
+        recv_x = np.full((capacity, H), fill_recv & 0xFFFF, np.uint16)
+        recv_scales = None
+    recv_weights = np.zeros(capacity, np.float32) if w is not None else None
+    tok_slot_row = np.zeros((T, k), np.int32)
+    row_src = np.full(capacity, -2, np.int32)
+    rc = _load().oracle_dispatch(T, H, k, num_experts, num_ranks, alignment,
+                                 1 if fp8 else 0, _ptr(x), _ptr(idx), _ptr(w),
+                                 capacity, _ptr(recv_x), _ptr(recv_scales),
+                                 _ptr(recv_weights), _ptr(tok_slot_row),
+                                 _ptr(row_src))
+    if rc:
+        raise OracleError(rc, "dispatch")
+    return dict(recv_x=recv_x, recv_scales=recv_scales, recv_weights=recv_weights,
+                tok_slot_row=tok_slot_row, row_src=row_src)
+
+
+def combine(y_bits, tok_slot_row, topk_weights) -> tuple[np.ndarray, np.ndarray]:
+    """Returns (out bf16 bits uint16 [T,H], fp32 accumulator [T,H])."""
+    y = _c(y_bits, np.uint16)
+    tsr = _c(tok_slot_row, np.int32)
+    cap, H = y.shape
+    T, k = tsr.shape
+    w = None if topk_weights is None else _c(topk_weights, np.float32)
+    out = np.empty((T, H), np.uint16)
+    acc = np.empty((T, H), np.float32)
+    rc = _load().oracle_combine(T, H, k, cap, _ptr(y), _ptr(tsr), _ptr(w),
+                                _ptr(out), _ptr(acc))
+    if rc:
+        raise OracleError(rc, "combine")
+    return out, acc

@@ -1,0 +1,89 @@
+/*
+ * Plain, sequential CPU oracle for the MoE expert-parallel dispatch / combine
+ * layout transformation.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link,
+ * load or call this code: only the tests, the smoke check and the CPU-baseline
+ * leg of the benchmark do.  It shares no code, header, table or constant with
+ * the HIP implementation.
+ *
+ * Sources (the pages are cited by title and section):
+ *   [P2]  "GPU microarchitecture: DeepEP first principles" (backyes.github.io),
+ *         sections 1.1-1.2 (dispatch / combine as layout transformation),
+ *         "6.1 Layout Metadata", "6.2 Identity Metadata", "7.1 Does Sort Exist?".
+ *   [P3]  "Deep Dive - DeepEP" (leetllm.com), sections "Why expert parallelism
+ *         needs a communication layer", "Dispatch: layout, move, and epilogue",
+ *         "Combine: reverse routing plus reduction", "Precision: FP8 on the
+ *         wire, BF16 for the reduction", "A runnable routing ledger".
+ *
+ * Conventions: T tokens, H hidden, k top-k, E experts, R logical ranks
+ * (E % R == 0, E/R experts per rank, expert e lives on rank e / (E/R)),
+ * A expert alignment.  topk_idx is int32 [T,k] row-major, -1 = unused slot.
+ * Hidden rows are bf16 bit patterns (uint16).  All functions return
+ * ORACLE_OK or one of the error codes below and write nothing on error.
+ */
+#ifndef EP_ORACLE_H
+#define EP_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARG 1      /* sizes / dtype / non-finite hidden values */
+#define ORACLE_BAD_ROUTE 2    /* expert id outside [-1, E) or repeated in a row */
+#define ORACLE_NO_CAPACITY 3  /* receive buffer has fewer rows than needed */
+
+/* bf16 <-> fp32 (round to nearest even, the bit procedure of [P3] "Combine"). */
+uint16_t oracle_bf16_round(float v);
+float oracle_bf16_to_float(uint16_t b);
+
+/* OCP FP8 E4M3 "FN" code <-> value.  Decode returns NaN for 0x7F / 0xFF.
+ * Encode is round-to-nearest, ties to the even code, saturating at 448,
+ * sign kept on zero results. */
+double oracle_e4m3_value(uint8_t code);
+uint8_t oracle_e4m3_encode(float v);
+
+/* Element-wise array forms of the conversions above. */
+void oracle_bf16_round_array(int64_t n, const float *in, uint16_t *out);
+void oracle_e4m3_encode_array(int64_t n, const float *in, uint8_t *out);
+void oracle_e4m3_value_array(int64_t n, const uint8_t *in, double *out);
+
+/* Layout: per-expert counts, per-rank distinct-token counts, token-in-rank
+ * mask [T,R] (0/1 bytes), aligned expert offsets [E+1], rank offsets [R+1]. */
+int oracle_layout(int32_t T, int32_t k, int32_t E, int32_t R, int32_t A,
+                  const int32_t *topk_idx,
+                  int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
+                  uint8_t *is_token_in_rank, int32_t *expert_offsets,
+                  int32_t *rank_offsets);
+
+/* Dispatch: stable counting-sort placement of every valid (t, j) selection
+ * into expert-major receive rows, plus the handle.
+ *   fp8 == 0: recv_x is bf16 [capacity, H]; recv_scales unused (may be NULL).
+ *   fp8 != 0: recv_x is e4m3 bytes [capacity, H]; recv_scales fp32
+ *             [capacity, H/128]; requires H % 128 == 0.
+ * topk_weights and recv_weights may be NULL (then no weights are copied).
+ * Rows [0, expert_offsets[E]) are written; rows past it are left untouched. */
+int oracle_dispatch(int32_t T, int32_t H, int32_t k, int32_t E, int32_t R,
+                    int32_t A, int32_t fp8, const uint16_t *x,
+                    const int32_t *topk_idx, const float *topk_weights,
+                    int64_t capacity, void *recv_x, float *recv_scales,
+                    float *recv_weights, int32_t *tok_slot_row,
+                    int32_t *row_src);
+
+/* Combine: out[t,c] = bf16(sum over valid j, in slot order j = 0..k-1, of
+ * w[t,j] * y[tok_slot_row[t,j], c]) accumulated in fp32 with one fused
+ * multiply-add per term.  topk_weights == NULL means y is already weighted
+ * and the terms are plain fp32 additions.  acc_out (nullable) receives the
+ * fp32 accumulator before the bf16 rounding. */
+int oracle_combine(int32_t T, int32_t H, int32_t k, int64_t capacity,
+                   const uint16_t *y, const int32_t *tok_slot_row,
+                   const float *topk_weights, uint16_t *out, float *acc_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_ORACLE_H */
