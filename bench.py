@@ -1,0 +1,224 @@
+"""Benchmark: one step = layout + dispatch + combine over one batch.
+
+Workload (default): Prefill, 4096 tokens x 7168 hidden bf16, top-8 of 256
+experts on 8 logical ranks, FP8 E4M3 dispatch with per-128 fp32 scales, bf16
+combine of a synthetic expert output [T*k, 7168].  Inputs are resident in
+HBM before timing starts.  The receive buffer is sized for the worst case
+(T*k rows) and no count is read back, so a step makes no host round trip.
+
+Throughput is algorithmic bytes per second (decimal GB), the bytes the
+method must move:
+  layout    T*k*4 (topk_idx) + T*R (rank mask) + 4*(E+R) (counts) + 4*(E+R+2) (offsets)
+  dispatch  T*H*2 (x once) + T*k*8 (idx, gates) + M*row (row = 2H bf16, or
+            H + 4H/128 FP8) + M*8 (row_src, recv gate) + T*k*4 (tok_slot_row)
+  combine   M*2H (gathered rows) + T*k*8 (tok_slot_row, gates) + T*2H (out)
+with M valid selections.  Workspace traffic is overhead and not counted.
+
+Prints one JSON line.  --gpus above 1 exits: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
+METRIC = "dispatch+combine HBM GB/s and % of peak; tokens/s at 4096x7168 top-8"
+KERNEL_SOURCES = [os.path.join(ROOT, "combine_get_dispatch_amd", "csrc", f)
+                  for f in ("ep_kernels.hip", "ep_internal.h")]
+
+
+def algorithmic_bytes(w, M: int) -> dict:
+    T, H, k, E, R = w.num_tokens, w.hidden, w.num_topk, w.num_experts, w.num_ranks
+    row = (H + 4 * (H // 128)) if w.fp8 else 2 * H
+    layout = T * k * 4 + T * R + 4 * (E + R) + 4 * (E + R + 2)
+    dispatch = T * H * 2 + T * k * 8 + M * row + M * 8 + T * k * 4
+    combine = M * 2 * H + T * k * 8 + T * 2 * H
+    return dict(layout=layout, dispatch=dispatch, combine=combine,
+                total=layout + dispatch + combine)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, inp, budget_s: float):
+    """The CPU oracle as it stands (single-threaded C), timed on this host on
+    whole steps of the same batch, repeated until about budget_s seconds."""
+    import oracle
+
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        lay = oracle.layout(inp["topk_idx"], w.num_experts, w.num_ranks, w.alignment)
+        d = oracle.dispatch(inp["x"], inp["topk_idx"], inp["topk_weights"], w.num_experts,
+                            w.num_ranks, w.alignment, fp8=w.fp8)
+        oracle.combine(inp["y"], d["tok_slot_row"], inp["topk_weights"])
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 8:
+            break
+    M = int(lay["expert_offsets"][-1])
+    b = algorithmic_bytes(w, M)["total"]
+    return dict(value=round(b * reps / el / 1e9, 3), unit="GB/s", cores=1, kind="oracle",
+                sample=f"{reps} full {w.name} step(s) (layout+dispatch+combine, "
+                       f"{w.num_tokens} tokens) in {el:.1f} s, single-threaded C",
+                tokens_per_s=round(w.num_tokens * reps / el, 1))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter scale)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import combine_get_dispatch_amd as ep
+    import ep_workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    print(f"bench: generating {w.name} inputs", file=sys.stderr, flush=True)
+    inp = W.generate(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = torch.from_numpy(inp["x"].view(np.int16)).view(torch.bfloat16).to(dev)
+    idx = torch.from_numpy(inp["topk_idx"]).to(dev)
+    wts = torch.from_numpy(inp["topk_weights"]).to(dev)
+    y = torch.from_numpy(inp["y"].view(np.int16)).view(torch.bfloat16).to(dev)
+    b = ep.EpBuffers(w.num_tokens, w.hidden, w.num_topk, w.num_experts, w.num_ranks,
+                     w.alignment, fp8=w.fp8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        b.layout(idx)
+        b.dispatch(x, idx, wts)
+        b.combine(y, wts)
+
+    print(f"bench: warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    b.check_status()
+    M = int(b.expert_offsets[-1].item())
+
+    # whole steps
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    print(f"bench: {args.steps} steps, {ms_per_step * 1e3:.1f} us/step", file=sys.stderr,
+          flush=True)
+
+    # per call, events on the launch stream
+    names = ("layout", "dispatch", "combine")
+    ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)] for n in names}
+    for i in range(args.steps):
+        for n, fn in zip(names, (lambda: b.layout(idx), lambda: b.dispatch(x, idx, wts),
+                                 lambda: b.combine(y, wts))):
+            ev[n][i][0].record(stream)
+            fn()
+            ev[n][i][1].record(stream)
+    torch.cuda.synchronize()
+    b.check_status()
+    per_us = {n: float(np.mean([a.elapsed_time(c) for a, c in ev[n]])) * 1e3 for n in names}
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    by = algorithmic_bytes(w, M)
+    step_s = ms_per_step / 1e3
+    gbps = by["total"] / step_s / 1e9
+    dom = max(("dispatch", "combine"), key=lambda n: per_us[n])
+    achieved = by[dom] / (per_us[dom] / 1e6) / 1e9
+    traffic = load_traffic(w.name, dom)
+    rec = {
+        "metric": METRIC,
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.num_tokens} tokens x {w.hidden} hidden, "
+                               f"top-{w.num_topk} of {w.num_experts} experts on "
+                               f"{w.num_ranks} logical ranks, "
+                               f"{'FP8 E4M3' if w.fp8 else 'bf16'} dispatch, bf16 combine",
+                   "tokens": w.num_tokens, "hidden": w.hidden, "topk": w.num_topk,
+                   "experts": w.num_experts, "logical_ranks": w.num_ranks,
+                   "dispatch_payload": "fp8_e4m3" if w.fp8 else "bf16",
+                   "valid_selections": M},
+        "pct_of_peak": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
+        "tokens_per_s": round(w.num_tokens / step_s, 1),
+        "algorithmic_bytes_per_step": by,
+        "kernel_us": {n: round(v, 2) for n, v in per_us.items()},
+        "host_wall_s": round(wall, 4),
+        "roofline": {
+            "kernel": dom,
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("bench: CPU oracle baseline", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,285 @@
+"""Python binding of libep.so: MoE expert-parallel dispatch / combine on one
+MI355X (gfx950).
+
+Argument marshalling only.  Every step of the path (layout, dispatch,
+combine) runs in the HIP kernels of libep.so; torch provides device memory
+and the current stream.  The raw functions below carry the C names of
+include/ep.h and take preallocated torch tensors; ``EpBuffers`` allocates
+the tensors for one configuration and chains the three calls.
+
+There is no fallback: if libep.so is missing or cannot be loaded, every call
+raises.  Build it with ``python -m combine_get_dispatch_amd._build`` (or
+``__graft_entry__.build()``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libep.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "ep.h")
+
+EP_OK, EP_ERR_INVALID_ARG, EP_ERR_INVALID_ROUTE, EP_ERR_CAPACITY, EP_ERR_WORKSPACE, EP_ERR_HIP = range(6)
+EP_DTYPE_BF16, EP_DTYPE_FP8_E4M3 = 0, 1
+
+
+class EpError(RuntimeError):
+    """A libep call returned a non-OK status."""
+
+    def __init__(self, status: int, func: str, message: str):
+        super().__init__(f"{func}: status {status}: {message}")
+        self.status = status
+
+
+class ep_config_t(ctypes.Structure):
+    _fields_ = [("num_tokens", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("num_topk", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+                ("num_ranks", ctypes.c_int32), ("expert_alignment", ctypes.c_int32)]
+
+
+class ep_handle_t(ctypes.Structure):
+    _fields_ = [("config", ep_config_t), ("capacity", ctypes.c_int64),
+                ("tok_slot_row", ctypes.c_void_p), ("row_src", ctypes.c_void_p),
+                ("expert_offsets", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libep.so (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run `python -m combine_get_dispatch_amd._build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, S, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64
+    cfgp = ctypes.POINTER(ep_config_t)
+    L.ep_status_string.restype = ctypes.c_char_p
+    L.ep_status_string.argtypes = [ctypes.c_int]
+    L.ep_last_error.restype = ctypes.c_char_p
+    L.ep_last_error.argtypes = []
+    L.ep_layout_workspace_bytes.argtypes = [cfgp, ctypes.POINTER(S)]
+    L.ep_recv_capacity_rows.argtypes = [cfgp, ctypes.POINTER(i64)]
+    L.ep_get_dispatch_layout.argtypes = [cfgp, P, P, P, P, P, P, P, S, P,
+                                         ctypes.POINTER(ctypes.c_int32), P]
+    L.ep_dispatch.argtypes = [cfgp, ctypes.c_int, P, P, P, P, P, S, i64, P, P, P, P, P, P,
+                              ctypes.POINTER(ep_handle_t), P]
+    L.ep_combine.argtypes = [ctypes.POINTER(ep_handle_t), P, P, P, P]
+    L.ep_read_status.argtypes = [P, P]
+    for f in ("ep_layout_workspace_bytes", "ep_recv_capacity_rows", "ep_get_dispatch_layout",
+              "ep_dispatch", "ep_combine", "ep_read_status"):
+        getattr(L, f).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/ep.h declares."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"\b(ep_[a-z_]+)\s*\(", text)
+
+
+def _check(status: int, func: str):
+    if status != EP_OK:
+        msg = lib().ep_last_error().decode()
+        raise EpError(status, func, msg)
+
+
+def _cfg(T, H, k, E, R, A) -> ep_config_t:
+    return ep_config_t(T, H, k, E, R, A)
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream)
+    import torch
+
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t, dtype=None, shape=None, name="tensor"):
+    """Device pointer of a contiguous CUDA tensor (None passes NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+# --------------------------------------------------------------------------
+# C entry points, same names as include/ep.h
+# --------------------------------------------------------------------------
+
+def ep_layout_workspace_bytes(cfg: ep_config_t) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().ep_layout_workspace_bytes(ctypes.byref(cfg), ctypes.byref(n)),
+           "ep_layout_workspace_bytes")
+    return n.value
+
+
+def ep_recv_capacity_rows(cfg: ep_config_t) -> int:
+    n = ctypes.c_int64()
+    _check(lib().ep_recv_capacity_rows(ctypes.byref(cfg), ctypes.byref(n)), "ep_recv_capacity_rows")
+    return n.value
+
+
+def ep_get_dispatch_layout(cfg, topk_idx, num_tokens_per_rank, num_tokens_per_expert,
+                           is_token_in_rank, expert_offsets, rank_offsets, workspace, status,
+                           sync: bool = False, stream=None):
+    """Enqueue the layout.  With sync=True, wait and return the rows used
+    (raises on a device-detected error)."""
+    import torch
+
+    T, k, E, R = cfg.num_tokens, cfg.num_topk, cfg.num_experts, cfg.num_ranks
+    rows = ctypes.c_int32(-1)
+    st = lib().ep_get_dispatch_layout(
+        ctypes.byref(cfg), _ptr(topk_idx, torch.int32, (T, k), "topk_idx"),
+        _ptr(num_tokens_per_rank, torch.int32, (R,), "num_tokens_per_rank"),
+        _ptr(num_tokens_per_expert, torch.int32, (E,), "num_tokens_per_expert"),
+        _ptr(is_token_in_rank, torch.uint8, (T, R), "is_token_in_rank"),
+        _ptr(expert_offsets, torch.int32, (E + 1,), "expert_offsets"),
+        _ptr(rank_offsets, torch.int32, (R + 1,), "rank_offsets"),
+        _ptr(workspace, torch.uint8, name="workspace"),
+        workspace.numel(), _ptr(status, torch.int32, (1,), "status"),
+        ctypes.byref(rows) if sync else None, _stream(stream))
+    _check(st, "ep_get_dispatch_layout")
+    return rows.value if sync else None
+
+
+def ep_dispatch(cfg, recv_dtype, x, topk_idx, topk_weights, expert_offsets, workspace,
+                capacity, recv_x, recv_scales, recv_weights, tok_slot_row, row_src, status,
+                stream=None) -> ep_handle_t:
+    import torch
+
+    T, H, k, E = cfg.num_tokens, cfg.hidden, cfg.num_topk, cfg.num_experts
+    cap = int(capacity)
+    fp8 = int(recv_dtype) == EP_DTYPE_FP8_E4M3
+    handle = ep_handle_t()
+    st = lib().ep_dispatch(
+        ctypes.byref(cfg), int(recv_dtype), _ptr(x, torch.bfloat16, (T, H), "x"),
+        _ptr(topk_idx, torch.int32, (T, k), "topk_idx"),
+        _ptr(topk_weights, torch.float32, (T, k), "topk_weights"),
+        _ptr(expert_offsets, torch.int32, (E + 1,), "expert_offsets"),
+        _ptr(workspace, torch.uint8, name="workspace"), workspace.numel(), cap,
+        _ptr(recv_x, torch.uint8 if fp8 else torch.bfloat16, (cap, H), "recv_x"),
+        _ptr(recv_scales, torch.float32, (cap, H // 128), "recv_scales") if fp8 else None,
+        _ptr(recv_weights, torch.float32, (cap,), "recv_weights"),
+        _ptr(tok_slot_row, torch.int32, (T, k), "tok_slot_row"),
+        _ptr(row_src, torch.int32, (cap,), "row_src"),
+        _ptr(status, torch.int32, (1,), "status"), ctypes.byref(handle), _stream(stream))
+    _check(st, "ep_dispatch")
+    return handle
+
+
+def ep_combine(handle: ep_handle_t, expert_out, topk_weights, out, stream=None):
+    import torch
+
+    c = handle.config
+    T, H, k, cap = c.num_tokens, c.hidden, c.num_topk, handle.capacity
+    if expert_out is None or expert_out.dim() != 2 or expert_out.shape[1] != H \
+            or expert_out.shape[0] < cap:
+        raise ValueError(f"expert_out must be bf16 [>= {cap}, {H}]")
+    if expert_out.shape[0] > 0:
+        _ptr(expert_out, torch.bfloat16, name="expert_out")
+    st = lib().ep_combine(ctypes.byref(handle),
+                          ctypes.c_void_p(expert_out.data_ptr()) if expert_out.numel() else None,
+                          _ptr(topk_weights, torch.float32, (T, k), "topk_weights"),
+                          _ptr(out, torch.bfloat16, (T, H), "out"), _stream(stream))
+    _check(st, "ep_combine")
+
+
+def make_handle(num_tokens, hidden, num_topk, capacity, tok_slot_row, row_src=None,
+                expert_offsets=None, num_experts=None, num_ranks=1, expert_alignment=1):
+    """Build an ep_handle_t around existing device arrays (combine only reads
+    the config, the capacity and tok_slot_row)."""
+    import torch
+
+    E = num_topk if num_experts is None else num_experts
+    h = ep_handle_t()
+    h.config = _cfg(num_tokens, hidden, num_topk, E, num_ranks, expert_alignment)
+    h.capacity = int(capacity)
+    p = _ptr(tok_slot_row, torch.int32, (num_tokens, num_topk), "tok_slot_row")
+    h.tok_slot_row = p.value if p is not None else None
+    h.row_src = row_src.data_ptr() if row_src is not None else None
+    h.expert_offsets = expert_offsets.data_ptr() if expert_offsets is not None else None
+    return h
+
+
+def ep_read_status(status, stream=None):
+    import torch
+
+    _check(lib().ep_read_status(_ptr(status, torch.int32), _stream(stream)), "ep_read_status")
+
+
+# --------------------------------------------------------------------------
+# Buffers for one configuration
+# --------------------------------------------------------------------------
+
+class EpBuffers:
+    """Device tensors for one (T, H, k, E, R, A, dtype) configuration, and
+    the three calls on them.  Tensors are allocated once with torch and
+    reused; outputs are views into them."""
+
+    def __init__(self, num_tokens, hidden, num_topk, num_experts, num_ranks,
+                 expert_alignment=1, fp8=False, capacity=None, device="cuda"):
+        import torch
+
+        self.cfg = _cfg(num_tokens, hidden, num_topk, num_experts, num_ranks, expert_alignment)
+        self.fp8 = bool(fp8)
+        self.capacity = ep_recv_capacity_rows(self.cfg) if capacity is None else int(capacity)
+        T, H, k, E, R = num_tokens, hidden, num_topk, num_experts, num_ranks
+        dev = torch.device(device)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.workspace = torch.empty(ep_layout_workspace_bytes(self.cfg), dtype=torch.uint8, device=dev)
+        self.status = torch.zeros(1, **i32)
+        self.num_tokens_per_rank = torch.empty(R, **i32)
+        self.num_tokens_per_expert = torch.empty(E, **i32)
+        self.is_token_in_rank = torch.empty((T, R), dtype=torch.uint8, device=dev)
+        self.expert_offsets = torch.empty(E + 1, **i32)
+        self.rank_offsets = torch.empty(R + 1, **i32)
+        cap = self.capacity
+        if self.fp8:
+            self.recv_x = torch.empty((cap, H), dtype=torch.uint8, device=dev)
+            self.recv_scales = torch.empty((cap, H // 128 if H % 128 == 0 else 1),
+                                           dtype=torch.float32, device=dev)
+        else:
+            self.recv_x = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
+            self.recv_scales = None
+        self.recv_weights = torch.empty(cap, dtype=torch.float32, device=dev)
+        self.tok_slot_row = torch.empty((T, k), **i32)
+        self.row_src = torch.empty(cap, **i32)
+        self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        self.handle = None
+
+    def layout(self, topk_idx, sync=False, stream=None):
+        return ep_get_dispatch_layout(self.cfg, topk_idx, self.num_tokens_per_rank,
+                                      self.num_tokens_per_expert, self.is_token_in_rank,
+                                      self.expert_offsets, self.rank_offsets, self.workspace,
+                                      self.status, sync=sync, stream=stream)
+
+    def dispatch(self, x, topk_idx, topk_weights, stream=None):
+        self.handle = ep_dispatch(self.cfg, EP_DTYPE_FP8_E4M3 if self.fp8 else EP_DTYPE_BF16,
+                                  x, topk_idx, topk_weights, self.expert_offsets, self.workspace,
+                                  self.capacity, self.recv_x, self.recv_scales,
+                                  self.recv_weights if topk_weights is not None else None,
+                                  self.tok_slot_row, self.row_src, self.status, stream=stream)
+        return self.handle
+
+    def combine(self, expert_out, topk_weights, out=None, stream=None):
+        out = self.out if out is None else out
+        ep_combine(self.handle, expert_out, topk_weights, out, stream=stream)
+        return out
+
+    def check_status(self, stream=None):
+        ep_read_status(self.status, stream=stream)

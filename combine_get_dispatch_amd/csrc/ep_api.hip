@@ -1,0 +1,220 @@
+// Host side of the libep.so C ABI: argument validation, workspace sizing,
+// kernel launches and status read-back.  Declarations and contracts are in
+// include/ep.h.  Every check below runs before any HIP call, so a rejected
+// call enqueues nothing and touches no device state.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "ep.h"
+#include "ep_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+ep_status_t fail(ep_status_t st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+ep_status_t hip_fail(hipError_t err, const char *what) {
+  return fail(EP_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+}
+
+ep_status_t check_config(const ep_config_t *c) {
+  if (c == nullptr) return fail(EP_ERR_INVALID_ARG, "config is NULL");
+  if (c->num_tokens < 0) return fail(EP_ERR_INVALID_ARG, "num_tokens %d < 0", c->num_tokens);
+  if (c->hidden < 8 || c->hidden % 8 != 0)
+    return fail(EP_ERR_INVALID_ARG, "hidden %d must be a positive multiple of 8", c->hidden);
+  if (c->num_experts < 1 || c->num_experts > EP_MAX_EXPERTS)
+    return fail(EP_ERR_INVALID_ARG, "num_experts %d outside [1, %d]", c->num_experts,
+                EP_MAX_EXPERTS);
+  if (c->num_topk < 1 || c->num_topk > EP_MAX_TOPK || c->num_topk > c->num_experts)
+    return fail(EP_ERR_INVALID_ARG, "num_topk %d outside [1, min(num_experts, %d)]",
+                c->num_topk, EP_MAX_TOPK);
+  if (c->num_ranks < 1 || c->num_ranks > EP_MAX_RANKS || c->num_experts % c->num_ranks != 0)
+    return fail(EP_ERR_INVALID_ARG,
+                "num_ranks %d must be in [1, %d] and divide num_experts %d", c->num_ranks,
+                EP_MAX_RANKS, c->num_experts);
+  if (c->expert_alignment < 1)
+    return fail(EP_ERR_INVALID_ARG, "expert_alignment %d < 1", c->expert_alignment);
+  const int64_t rows = (int64_t)c->num_tokens * c->num_topk +
+                       (int64_t)c->num_experts * (c->expert_alignment - 1);
+  if (rows >= INT32_MAX)
+    return fail(EP_ERR_INVALID_ARG, "T*k + E*(A-1) = %lld does not fit int32 row indices",
+                (long long)rows);
+  const int64_t chunks = (c->hidden + ep::kChunkCols - 1) / ep::kChunkCols;
+  if ((int64_t)c->num_tokens * chunks >= INT32_MAX)
+    return fail(EP_ERR_INVALID_ARG, "num_tokens x hidden too large");
+  return EP_OK;
+}
+
+ep::Dims dims_of(const ep_config_t *c) {
+  return ep::Dims{c->num_tokens, c->hidden, c->num_topk,
+                  c->num_experts, c->num_ranks, c->expert_alignment};
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char *ep_status_string(ep_status_t status) {
+  switch (status) {
+    case EP_OK: return "ok";
+    case EP_ERR_INVALID_ARG: return "invalid argument";
+    case EP_ERR_INVALID_ROUTE: return "invalid route (expert id out of range or repeated)";
+    case EP_ERR_CAPACITY: return "receive buffer too small";
+    case EP_ERR_WORKSPACE: return "workspace not written by a layout of this configuration";
+    case EP_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char *ep_last_error(void) { return g_last_error; }
+
+ep_status_t ep_layout_workspace_bytes(const ep_config_t *cfg, size_t *bytes_host) {
+  ep_status_t st = check_config(cfg);
+  if (st != EP_OK) return st;
+  if (bytes_host == nullptr) return fail(EP_ERR_INVALID_ARG, "bytes_host is NULL");
+  *bytes_host = ep::workspace_layout(cfg->num_tokens, cfg->num_topk, cfg->num_experts,
+                                     cfg->num_ranks)
+                    .total;
+  return EP_OK;
+}
+
+ep_status_t ep_recv_capacity_rows(const ep_config_t *cfg, int64_t *rows_host) {
+  ep_status_t st = check_config(cfg);
+  if (st != EP_OK) return st;
+  if (rows_host == nullptr) return fail(EP_ERR_INVALID_ARG, "rows_host is NULL");
+  *rows_host = (int64_t)cfg->num_tokens * cfg->num_topk +
+               (int64_t)cfg->num_experts * (cfg->expert_alignment - 1);
+  return EP_OK;
+}
+
+ep_status_t ep_read_status(const int32_t *status, hipStream_t stream) {
+  if (status == nullptr) return fail(EP_ERR_INVALID_ARG, "status is NULL");
+  int32_t host = 0;
+  hipError_t err = hipMemcpyAsync(&host, status, sizeof host, hipMemcpyDeviceToHost, stream);
+  if (err != hipSuccess) return hip_fail(err, "reading the status word");
+  err = hipStreamSynchronize(stream);
+  if (err != hipSuccess) return hip_fail(err, "synchronising the stream");
+  if (host & EP_STATUS_BIT_ROUTE)
+    return fail(EP_ERR_INVALID_ROUTE, "an expert id is outside [-1, E) or repeated in a token");
+  if (host & EP_STATUS_BIT_CAPACITY)
+    return fail(EP_ERR_CAPACITY, "a selection did not fit in the receive rows");
+  if (host & EP_STATUS_BIT_WORKSPACE)
+    return fail(EP_ERR_WORKSPACE, "dispatch workspace does not match its configuration");
+  return EP_OK;
+}
+
+ep_status_t ep_get_dispatch_layout(const ep_config_t *cfg, const int32_t *topk_idx,
+                                   int32_t *num_tokens_per_rank,
+                                   int32_t *num_tokens_per_expert,
+                                   uint8_t *is_token_in_rank, int32_t *expert_offsets,
+                                   int32_t *rank_offsets, void *workspace,
+                                   size_t workspace_bytes, int32_t *status,
+                                   int32_t *num_recv_rows_host, hipStream_t stream) {
+  ep_status_t st = check_config(cfg);
+  if (st != EP_OK) return st;
+  const bool empty = cfg->num_tokens == 0;
+  if ((!empty && (topk_idx == nullptr || is_token_in_rank == nullptr)) ||
+      num_tokens_per_rank == nullptr || num_tokens_per_expert == nullptr ||
+      expert_offsets == nullptr || rank_offsets == nullptr || workspace == nullptr ||
+      status == nullptr)
+    return fail(EP_ERR_INVALID_ARG, "a required pointer is NULL");
+  const size_t need =
+      ep::workspace_layout(cfg->num_tokens, cfg->num_topk, cfg->num_experts, cfg->num_ranks)
+          .total;
+  if (workspace_bytes < need)
+    return fail(EP_ERR_INVALID_ARG, "workspace has %zu bytes, layout needs %zu",
+                workspace_bytes, need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(EP_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  hipError_t err = ep::launch_layout(dims_of(cfg), topk_idx, num_tokens_per_rank,
+                                     num_tokens_per_expert, is_token_in_rank, expert_offsets,
+                                     rank_offsets, static_cast<char *>(workspace), status,
+                                     stream);
+  if (err != hipSuccess) return hip_fail(err, "layout launch");
+  if (num_recv_rows_host != nullptr) {
+    err = hipMemcpyAsync(num_recv_rows_host, expert_offsets + cfg->num_experts, sizeof(int32_t),
+                         hipMemcpyDeviceToHost, stream);
+    if (err != hipSuccess) return hip_fail(err, "reading the row count");
+    return ep_read_status(status, stream);
+  }
+  return EP_OK;
+}
+
+ep_status_t ep_dispatch(const ep_config_t *cfg, ep_dtype_t recv_dtype, const uint16_t *x,
+                        const int32_t *topk_idx, const float *topk_weights,
+                        const int32_t *expert_offsets, const void *workspace,
+                        size_t workspace_bytes, int64_t capacity, void *recv_x,
+                        float *recv_scales, float *recv_weights, int32_t *tok_slot_row,
+                        int32_t *row_src, int32_t *status, ep_handle_t *handle_host,
+                        hipStream_t stream) {
+  ep_status_t st = check_config(cfg);
+  if (st != EP_OK) return st;
+  if (recv_dtype != EP_DTYPE_BF16 && recv_dtype != EP_DTYPE_FP8_E4M3)
+    return fail(EP_ERR_INVALID_ARG, "unknown recv_dtype %d", (int)recv_dtype);
+  const bool fp8 = recv_dtype == EP_DTYPE_FP8_E4M3;
+  if (fp8 && cfg->hidden % 128 != 0)
+    return fail(EP_ERR_INVALID_ARG, "FP8 dispatch needs hidden %% 128 == 0 (hidden %d)",
+                cfg->hidden);
+  if (capacity < 0 || capacity >= INT32_MAX)
+    return fail(EP_ERR_INVALID_ARG, "capacity %lld outside [0, 2^31 - 1)", (long long)capacity);
+  const bool empty = cfg->num_tokens == 0;
+  if ((!empty && (x == nullptr || topk_idx == nullptr || tok_slot_row == nullptr)) ||
+      expert_offsets == nullptr || workspace == nullptr || status == nullptr ||
+      (capacity > 0 && (recv_x == nullptr || row_src == nullptr)) ||
+      (fp8 && capacity > 0 && recv_scales == nullptr))
+    return fail(EP_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(x) || !aligned16(recv_x))
+    return fail(EP_ERR_INVALID_ARG, "x and recv_x must be 16-byte aligned");
+  const size_t need =
+      ep::workspace_layout(cfg->num_tokens, cfg->num_topk, cfg->num_experts, cfg->num_ranks)
+          .total;
+  if (workspace_bytes < need)
+    return fail(EP_ERR_INVALID_ARG, "workspace has %zu bytes, dispatch needs %zu",
+                workspace_bytes, need);
+  hipError_t err = ep::launch_dispatch(dims_of(cfg), fp8, x, topk_idx, topk_weights,
+                                       expert_offsets, static_cast<const char *>(workspace),
+                                       capacity, recv_x, recv_scales, recv_weights, tok_slot_row,
+                                       row_src, status, stream);
+  if (err != hipSuccess) return hip_fail(err, "dispatch launch");
+  if (handle_host != nullptr) {
+    handle_host->config = *cfg;
+    handle_host->capacity = capacity;
+    handle_host->tok_slot_row = tok_slot_row;
+    handle_host->row_src = row_src;
+    handle_host->expert_offsets = expert_offsets;
+  }
+  return EP_OK;
+}
+
+ep_status_t ep_combine(const ep_handle_t *handle, const uint16_t *expert_out,
+                       const float *topk_weights, uint16_t *out, hipStream_t stream) {
+  if (handle == nullptr) return fail(EP_ERR_INVALID_ARG, "handle is NULL");
+  ep_status_t st = check_config(&handle->config);
+  if (st != EP_OK) return st;
+  if (handle->capacity < 0 || handle->capacity >= INT32_MAX)
+    return fail(EP_ERR_INVALID_ARG, "handle capacity %lld invalid",
+                (long long)handle->capacity);
+  if (handle->config.num_tokens > 0 &&
+      (handle->tok_slot_row == nullptr || out == nullptr ||
+       (handle->capacity > 0 && expert_out == nullptr)))
+    return fail(EP_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(expert_out) || !aligned16(out))
+    return fail(EP_ERR_INVALID_ARG, "expert_out and out must be 16-byte aligned");
+  hipError_t err = ep::launch_combine(dims_of(&handle->config), handle->capacity, expert_out,
+                                      handle->tok_slot_row, topk_weights, out, stream);
+  if (err != hipSuccess) return hip_fail(err, "combine launch");
+  return EP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// Internal declarations shared by the host API (ep_api.hip) and the kernels
+// (ep_kernels.hip) of libep.so.  Not installed; callers use include/ep.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ep {
+
+// A layout tile is one 256-thread workgroup with one token per lane, so a
+// tile holds four wave64s' worth of tokens.
+constexpr int kTileTokens = 256;
+constexpr int kWave = 64;
+constexpr int kBlock = 256;
+constexpr int kWavesPerBlock = kBlock / kWave;
+
+// Columns one wave moves per work item: 64 lanes x 8 bf16 (16 bytes) x 2.
+constexpr int kChunkCols = 1024;
+
+constexpr int32_t kWorkspaceMagic = 0x45504C59;  // "EPLY"
+constexpr int kHeaderInts = 16;
+
+// Byte offsets of the workspace sections for one configuration.
+struct WorkspaceLayout {
+  int32_t ntiles;
+  size_t tile_cnt;       // int32 [ntiles, E]: tile histogram, then tile base
+  size_t tile_rank_cnt;  // int32 [ntiles, R]: distinct tokens per rank per tile
+  size_t cnt;            // int32 [E]: unaligned count per expert
+  size_t slot_rank;      // int32 [T, k]: rank of (t, j) inside its tile's run of e
+  size_t total;
+};
+
+WorkspaceLayout workspace_layout(int32_t T, int32_t k, int32_t E, int32_t R);
+
+struct Dims {
+  int32_t T, H, k, E, R, A;
+};
+
+hipError_t launch_layout(const Dims &d, const int32_t *topk_idx, int32_t *num_tokens_per_rank,
+                         int32_t *num_tokens_per_expert, uint8_t *is_token_in_rank,
+                         int32_t *expert_offsets, int32_t *rank_offsets, char *ws,
+                         int32_t *status, hipStream_t stream);
+
+hipError_t launch_dispatch(const Dims &d, bool fp8, const uint16_t *x, const int32_t *topk_idx,
+                           const float *topk_weights, const int32_t *expert_offsets,
+                           const char *ws, int64_t capacity, void *recv_x, float *recv_scales,
+                           float *recv_weights, int32_t *tok_slot_row, int32_t *row_src,
+                           int32_t *status, hipStream_t stream);
+
+hipError_t launch_combine(const Dims &d, int64_t capacity, const uint16_t *expert_out,
+                          const int32_t *tok_slot_row, const float *topk_weights,
+                          uint16_t *out, hipStream_t stream);
+
+}  // namespace ep

@@ -1,0 +1,588 @@
+// HIP kernels of libep.so for gfx950 (CDNA4, wave64).
+//
+// Pages cited: "GPU microarchitecture: DeepEP first principles"
+// (backyes.github.io) and "Deep Dive - DeepEP" (leetllm.com), by section.
+//
+// The path is pure data movement (no dense contraction, so no MFMA):
+//   layout_count_kernel   one workgroup per 256-token tile: per-wave expert
+//                         bitmasks in LDS (64-bit OR per selection), their
+//                         popcounts give the tile histogram and each
+//                         selection's stable rank inside the tile; ballots
+//                         give distinct tokens per rank.
+//   layout_scan_kernel    one workgroup: per expert, exclusive scan over
+//                         tiles (tile bases); over experts, exclusive scan of
+//                         the aligned counts (segment starts).
+//   dispatch_*_kernel     one wave per (token, 1024-column chunk): reads the
+//                         x chunk once with 16-byte loads, optionally
+//                         quantises it to E4M3 in registers, and stores it to
+//                         each of the token's receive rows.
+//   combine_kernel        one wave per (token, 1024-column chunk): k gathered
+//                         16-byte loads per lane, fp32 FMAs in slot order,
+//                         one bf16 rounding, one 16-byte store.
+// Output positions never depend on atomics or scheduling, so every result
+// is deterministic.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ep.h"
+#include "ep_internal.h"
+
+namespace ep {
+
+namespace {
+
+__device__ __forceinline__ void flag(int32_t *status, int32_t bit) { atomicOr(status, bit); }
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ int32_t lane_value(int32_t v, int lane) {
+  return __builtin_amdgcn_readlane(v, lane);
+}
+
+__device__ __forceinline__ float lane_value_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// bf16 bits -> fp32 (exact), for the low and high halves of a 32-bit word.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even: add 0x7FFF plus the lowest kept
+// bit and keep the upper half ("Deep Dive - DeepEP", "Combine: reverse
+// routing plus reduction").  NaN keeps its sign and upper payload with the
+// quiet bit set.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t b = __float_as_uint(f);
+  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return (b >> 16) | 0x40u;
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return bf16_rne(lo) | (bf16_rne(hi) << 16);
+}
+
+// Workspace header check shared by the dispatch kernels: the workspace must
+// have been written by a layout of exactly this configuration.
+__device__ __forceinline__ bool workspace_ok(const int32_t *hdr, const Dims &d) {
+  return hdr[0] == kWorkspaceMagic && hdr[1] == d.T && hdr[2] == d.k && hdr[3] == d.E &&
+         hdr[4] == d.R && hdr[5] == d.A;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Layout (count, then prefix sum: "GPU microarchitecture: DeepEP first
+// principles", "7.1 Does Sort Exist?")
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kBlock) void layout_count_kernel(
+    const int32_t *__restrict__ topk_idx, Dims d, int32_t experts_per_rank,
+    int32_t *__restrict__ tile_cnt, int32_t *__restrict__ tile_rank_cnt,
+    int32_t *__restrict__ slot_rank, uint8_t *__restrict__ is_token_in_rank,
+    int32_t *__restrict__ status) {
+  extern __shared__ unsigned long long masks[];  // [kWavesPerBlock][E]
+  __shared__ int32_t rank_cnt[EP_MAX_RANKS];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int tile = blockIdx.x;
+  const int64_t t = (int64_t)tile * kTileTokens + tid;
+  const int E = d.E, k = d.k, R = d.R;
+
+  for (int i = tid; i < kWavesPerBlock * E; i += kBlock) masks[i] = 0ull;
+  for (int i = tid; i < R; i += kBlock) rank_cnt[i] = 0;
+  __syncthreads();
+
+  // Mark this token in its wave's bitmask of every expert it selected.  The
+  // OR returns the previous mask, which exposes a repeated expert.
+  const unsigned long long me = 1ull << lane;
+  bool bad = false;
+  unsigned long long rmask = 0ull;
+  if (t < d.T) {
+    const int32_t *row = topk_idx + t * k;
+    for (int j = 0; j < k; ++j) {
+      const int32_t e = row[j];
+      if (e < -1 || e >= E) {
+        bad = true;
+        continue;
+      }
+      if (e < 0) continue;
+      const unsigned long long old = atomicOr(&masks[wave * E + e], me);
+      if (old & me) bad = true;
+      rmask |= 1ull << (e / experts_per_rank);
+    }
+    uint8_t *dst = is_token_in_rank + t * R;
+    for (int r = 0; r < R; ++r) dst[r] = (uint8_t)((rmask >> r) & 1ull);
+  }
+  if (bad) flag(status, EP_STATUS_BIT_ROUTE);
+
+  // Distinct tokens per rank in this tile.
+  for (int r = 0; r < R; ++r) {
+    const unsigned long long b = __ballot((rmask >> r) & 1ull);
+    if (lane == 0 && b) atomicAdd(&rank_cnt[r], (int32_t)__popcll(b));
+  }
+  __syncthreads();
+
+  for (int e = tid; e < E; e += kBlock) {
+    int32_t c = 0;
+    for (int w = 0; w < kWavesPerBlock; ++w) c += __popcll(masks[w * E + e]);
+    tile_cnt[(int64_t)tile * E + e] = c;
+  }
+  for (int r = tid; r < R; r += kBlock) tile_rank_cnt[(int64_t)tile * R + r] = rank_cnt[r];
+
+  // Stable rank of (t, e) inside the tile: tokens of earlier waves that chose
+  // e, plus lanes below this one in its own wave that chose e.
+  if (t < d.T) {
+    const int32_t *row = topk_idx + t * k;
+    const unsigned long long below = me - 1ull;
+    for (int j = 0; j < k; ++j) {
+      const int32_t e = row[j];
+      int32_t rank = -1;
+      if (e >= 0 && e < E) {
+        rank = __popcll(masks[wave * E + e] & below);
+        for (int w = 0; w < wave; ++w) rank += __popcll(masks[w * E + e]);
+      }
+      slot_rank[t * k + j] = rank;
+    }
+  }
+}
+
+__global__ __launch_bounds__(1024) void layout_scan_kernel(
+    Dims d, int32_t ntiles, int32_t experts_per_rank, int32_t *__restrict__ tile_cnt,
+    const int32_t *__restrict__ tile_rank_cnt, int32_t *__restrict__ cnt_ws,
+    int32_t *__restrict__ num_tokens_per_expert, int32_t *__restrict__ num_tokens_per_rank,
+    int32_t *__restrict__ expert_offsets, int32_t *__restrict__ rank_offsets,
+    int32_t *__restrict__ header) {
+  __shared__ int32_t wave_sum[1024 / kWave];
+  __shared__ int32_t offsets[EP_MAX_EXPERTS + 1];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int E = d.E;
+
+  // Per expert: tile histogram -> exclusive tile bases (in place) and total.
+  int32_t padded = 0;
+  if (tid < E) {
+    int32_t run = 0;
+    for (int tile = 0; tile < ntiles; ++tile) {
+      const int64_t i = (int64_t)tile * E + tid;
+      const int32_t c = tile_cnt[i];
+      tile_cnt[i] = run;
+      run += c;
+    }
+    cnt_ws[tid] = run;
+    num_tokens_per_expert[tid] = run;
+    padded = (run + d.A - 1) / d.A * d.A;
+  }
+
+  // Exclusive scan of the aligned counts over experts (wave scan + wave sums).
+  int32_t incl = padded;
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int32_t v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
+  }
+  if (lane == kWave - 1) wave_sum[wave] = incl;
+  __syncthreads();
+  if (tid == 0) {
+    int32_t run = 0;
+    for (int w = 0; w < 1024 / kWave; ++w) {
+      const int32_t s = wave_sum[w];
+      wave_sum[w] = run;
+      run += s;
+    }
+  }
+  __syncthreads();
+  const int32_t excl = incl - padded + wave_sum[wave];
+  if (tid < E) {
+    offsets[tid] = excl;
+    expert_offsets[tid] = excl;
+    if (tid == E - 1) {
+      offsets[E] = excl + padded;
+      expert_offsets[E] = excl + padded;
+    }
+  }
+  __syncthreads();
+
+  if (tid < d.R) {
+    int32_t n = 0;
+    for (int tile = 0; tile < ntiles; ++tile) n += tile_rank_cnt[(int64_t)tile * d.R + tid];
+    num_tokens_per_rank[tid] = n;
+  }
+  if (tid <= d.R) rank_offsets[tid] = offsets[tid * experts_per_rank];
+  if (tid == 0) {
+    header[1] = d.T;
+    header[2] = d.k;
+    header[3] = d.E;
+    header[4] = d.R;
+    header[5] = d.A;
+    header[6] = ntiles;
+    header[0] = kWorkspaceMagic;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch ("GPU microarchitecture: DeepEP first principles", 1.1 and 6.1;
+// "Deep Dive - DeepEP", "Dispatch: layout, move, and epilogue")
+// ---------------------------------------------------------------------------
+
+// Receive row of selection (t, lane) for lanes below k, -1 otherwise.  The
+// row is the expert's segment start, plus the selections of e in earlier
+// tiles, plus the rank inside this tile: the stable counting-sort position.
+// Wave-uniform t.  The first chunk's wave also writes the handle.
+__device__ __forceinline__ int32_t selection_row(const Dims &d, int64_t t, int lane,
+                                                 bool write_handle,
+                                                 const int32_t *__restrict__ topk_idx,
+                                                 const float *__restrict__ topk_weights,
+                                                 const int32_t *__restrict__ expert_offsets,
+                                                 const int32_t *__restrict__ tile_base,
+                                                 const int32_t *__restrict__ slot_rank,
+                                                 int64_t capacity, float *__restrict__ recv_weights,
+                                                 int32_t *__restrict__ tok_slot_row,
+                                                 int32_t *__restrict__ row_src,
+                                                 int32_t *__restrict__ status) {
+  int32_t row = -1;
+  if (lane < d.k) {
+    const int64_t s = t * d.k + lane;
+    const int32_t e = topk_idx[s];
+    if (e >= 0 && e < d.E) {
+      const int32_t rank = slot_rank[s];
+      if (rank >= 0) {
+        const int64_t r = (int64_t)expert_offsets[e] +
+                          tile_base[(t / kTileTokens) * d.E + e] + rank;
+        if (r >= 0 && r < capacity)
+          row = (int32_t)r;
+        else
+          flag(status, EP_STATUS_BIT_CAPACITY);
+      }
+    }
+    if (write_handle) {
+      tok_slot_row[s] = row;
+      if (row >= 0) {
+        row_src[row] = (int32_t)s;
+        if (recv_weights != nullptr && topk_weights != nullptr)
+          recv_weights[row] = topk_weights[s];
+      }
+    }
+  }
+  return row;
+}
+
+// bf16 rows: a bit copy of the x chunk into each receive row.
+__global__ __launch_bounds__(kBlock) void dispatch_bf16_kernel(
+    Dims d, int32_t nchunks, const uint16_t *__restrict__ x, const int32_t *__restrict__ topk_idx,
+    const float *__restrict__ topk_weights, const int32_t *__restrict__ expert_offsets,
+    const int32_t *__restrict__ header, const int32_t *__restrict__ tile_base,
+    const int32_t *__restrict__ slot_rank, int64_t capacity, uint16_t *__restrict__ recv_x,
+    float *__restrict__ recv_weights, int32_t *__restrict__ tok_slot_row,
+    int32_t *__restrict__ row_src, int32_t *__restrict__ status) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int item = uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
+  if (item >= d.T * nchunks) return;
+  if (!workspace_ok(header, d)) {
+    if (lane == 0) flag(status, EP_STATUS_BIT_WORKSPACE);
+    return;
+  }
+  const int64_t t = item / nchunks;
+  const int chunk = item - (int)t * nchunks;
+  const int32_t row = selection_row(d, t, lane, chunk == 0, topk_idx, topk_weights,
+                                    expert_offsets, tile_base, slot_rank, capacity,
+                                    recv_weights, tok_slot_row, row_src, status);
+
+  constexpr int U = kChunkCols / (kWave * 8);
+  const int64_t H = d.H;
+  uint4 v[U];
+  int col[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    col[u] = chunk * kChunkCols + u * (kWave * 8) + lane * 8;
+    if (col[u] < H) v[u] = *reinterpret_cast<const uint4 *>(x + t * H + col[u]);
+  }
+  for (int j = 0; j < d.k; ++j) {
+    const int32_t r = lane_value(row, j);
+    if (r < 0) continue;
+    uint16_t *dst = recv_x + (int64_t)r * H;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (col[u] < H) *reinterpret_cast<uint4 *>(dst + col[u]) = v[u];
+  }
+}
+
+// FP8 rows: per token and 128-value block (16 lanes x 8 values), amax over
+// the block, scale = amax / 448 and codes = E4M3(x / scale), both rounded to
+// nearest even ("Deep Dive - DeepEP", "Precision: FP8 on the wire, BF16 for
+// the reduction").  An all-zero block gets scale 0 and zero codes.
+__global__ __launch_bounds__(kBlock) void dispatch_fp8_kernel(
+    Dims d, int32_t nchunks, const uint16_t *__restrict__ x, const int32_t *__restrict__ topk_idx,
+    const float *__restrict__ topk_weights, const int32_t *__restrict__ expert_offsets,
+    const int32_t *__restrict__ header, const int32_t *__restrict__ tile_base,
+    const int32_t *__restrict__ slot_rank, int64_t capacity, uint8_t *__restrict__ recv_x,
+    float *__restrict__ recv_scales, float *__restrict__ recv_weights,
+    int32_t *__restrict__ tok_slot_row, int32_t *__restrict__ row_src,
+    int32_t *__restrict__ status) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int item = uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
+  if (item >= d.T * nchunks) return;
+  if (!workspace_ok(header, d)) {
+    if (lane == 0) flag(status, EP_STATUS_BIT_WORKSPACE);
+    return;
+  }
+  const int64_t t = item / nchunks;
+  const int chunk = item - (int)t * nchunks;
+  const int32_t row = selection_row(d, t, lane, chunk == 0, topk_idx, topk_weights,
+                                    expert_offsets, tile_base, slot_rank, capacity,
+                                    recv_weights, tok_slot_row, row_src, status);
+
+  constexpr int U = kChunkCols / (kWave * 8);
+  const int64_t H = d.H;
+  const int64_t nblk = H / 128;
+  uint2 q[U];
+  float scale[U];
+  int col[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    col[u] = chunk * kChunkCols + u * (kWave * 8) + lane * 8;
+    // H % 128 == 0, so the 16 lanes of a block are all in range or all out.
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (col[u] < H) v = *reinterpret_cast<const uint4 *>(x + t * H + col[u]);
+    float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                  bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+    const float s = amax / 448.0f;
+    scale[u] = s;
+    int lo = 0, hi = 0;
+    if (s > 0.0f) {
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0] / s, f[1] / s, lo, false);
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2] / s, f[3] / s, lo, true);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4] / s, f[5] / s, hi, false);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6] / s, f[7] / s, hi, true);
+    }
+    q[u] = make_uint2((uint32_t)lo, (uint32_t)hi);
+  }
+  for (int j = 0; j < d.k; ++j) {
+    const int32_t r = lane_value(row, j);
+    if (r < 0) continue;
+    uint8_t *dst = recv_x + (int64_t)r * H;
+    float *sdst = recv_scales + (int64_t)r * nblk;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (col[u] < H) {
+        *reinterpret_cast<uint2 *>(dst + col[u]) = q[u];
+        if ((lane & 15) == 0) sdst[col[u] / 128] = scale[u];
+      }
+    }
+  }
+}
+
+// Alignment padding rows of expert e (one workgroup per expert): zero
+// payload, zero scale, zero gate, no source ("Deep Dive - DeepEP",
+// "Dispatch: layout, move, and epilogue": padding is not a token).
+__global__ __launch_bounds__(kBlock) void pad_fill_kernel(
+    Dims d, bool fp8, const int32_t *__restrict__ expert_offsets, const int32_t *__restrict__ cnt,
+    int64_t capacity, void *__restrict__ recv_x, float *__restrict__ recv_scales,
+    float *__restrict__ recv_weights, int32_t *__restrict__ row_src) {
+  const int e = blockIdx.x;
+  const int64_t first = (int64_t)expert_offsets[e] + cnt[e];
+  int64_t last = expert_offsets[e + 1];
+  if (last > capacity) last = capacity;
+  const int64_t row_bytes = fp8 ? (int64_t)d.H : (int64_t)d.H * 2;
+  const int64_t nblk = d.H / 128;
+  for (int64_t r = first; r < last; ++r) {
+    uint4 *dst = reinterpret_cast<uint4 *>(static_cast<char *>(recv_x) + r * row_bytes);
+    for (int64_t i = threadIdx.x; i < row_bytes / 16; i += kBlock) dst[i] = make_uint4(0, 0, 0, 0);
+    if (fp8)
+      for (int64_t i = threadIdx.x; i < nblk; i += kBlock) recv_scales[r * nblk + i] = 0.0f;
+    if (threadIdx.x == 0) {
+      row_src[r] = -1;
+      if (recv_weights != nullptr) recv_weights[r] = 0.0f;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Combine ("GPU microarchitecture: DeepEP first principles", 1.2; "Deep Dive
+// - DeepEP", "Combine: reverse routing plus reduction")
+// ---------------------------------------------------------------------------
+
+// Rows are gathered in batches of KB slots so that KB x U 16-byte loads per
+// lane are in flight before the FMAs, which then run in slot order.
+template <bool kWeighted, int KB>
+__global__ __launch_bounds__(kBlock) void combine_kernel(
+    Dims d, int32_t nchunks, int64_t capacity, const uint16_t *__restrict__ y,
+    const int32_t *__restrict__ tok_slot_row, const float *__restrict__ topk_weights,
+    uint16_t *__restrict__ out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int item = uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
+  if (item >= d.T * nchunks) return;
+  const int64_t t = item / nchunks;
+  const int chunk = item - (int)t * nchunks;
+
+  int32_t row = -1;
+  float gate = 0.0f;
+  if (lane < d.k) {
+    const int32_t r = tok_slot_row[t * d.k + lane];
+    if (r >= 0 && r < capacity) {
+      row = r;
+      if (kWeighted) gate = topk_weights[t * d.k + lane];
+    }
+  }
+
+  constexpr int U = kChunkCols / (kWave * 8);
+  const int64_t H = d.H;
+  int col[U];
+  float acc[U][8];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    col[u] = chunk * kChunkCols + u * (kWave * 8) + lane * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[u][i] = 0.0f;
+  }
+
+  for (int jb = 0; jb < d.k; jb += KB) {
+    uint4 v[KB][U];
+    int32_t r[KB];
+#pragma unroll
+    for (int jj = 0; jj < KB; ++jj) {
+      r[jj] = (jb + jj < d.k) ? lane_value(row, jb + jj) : -1;
+      if (r[jj] >= 0) {
+        const uint16_t *src = y + (int64_t)r[jj] * H;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (col[u] < H) v[jj][u] = *reinterpret_cast<const uint4 *>(src + col[u]);
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < KB; ++jj) {
+      if (r[jj] < 0) continue;
+      const float g = kWeighted ? lane_value_f(gate, jb + jj) : 1.0f;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t w4[4] = {v[jj][u].x, v[jj][u].y, v[jj][u].z, v[jj][u].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (kWeighted) {
+            acc[u][2 * i] = __builtin_fmaf(g, bf16_lo(w4[i]), acc[u][2 * i]);
+            acc[u][2 * i + 1] = __builtin_fmaf(g, bf16_hi(w4[i]), acc[u][2 * i + 1]);
+          } else {
+            acc[u][2 * i] = acc[u][2 * i] + bf16_lo(w4[i]);
+            acc[u][2 * i + 1] = acc[u][2 * i + 1] + bf16_hi(w4[i]);
+          }
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (col[u] < H) {
+      uint4 o;
+      o.x = pack_bf16(acc[u][0], acc[u][1]);
+      o.y = pack_bf16(acc[u][2], acc[u][3]);
+      o.z = pack_bf16(acc[u][4], acc[u][5]);
+      o.w = pack_bf16(acc[u][6], acc[u][7]);
+      *reinterpret_cast<uint4 *>(out + t * H + col[u]) = o;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+
+static size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+WorkspaceLayout workspace_layout(int32_t T, int32_t k, int32_t E, int32_t R) {
+  WorkspaceLayout w;
+  w.ntiles = (T + kTileTokens - 1) / kTileTokens;
+  size_t off = align256(sizeof(int32_t) * kHeaderInts);
+  w.tile_cnt = off;
+  off += align256(sizeof(int32_t) * (size_t)w.ntiles * E);
+  w.tile_rank_cnt = off;
+  off += align256(sizeof(int32_t) * (size_t)w.ntiles * R);
+  w.cnt = off;
+  off += align256(sizeof(int32_t) * (size_t)E);
+  w.slot_rank = off;
+  off += align256(sizeof(int32_t) * (size_t)T * k);
+  w.total = off;
+  return w;
+}
+
+hipError_t launch_layout(const Dims &d, const int32_t *topk_idx, int32_t *num_tokens_per_rank,
+                         int32_t *num_tokens_per_expert, uint8_t *is_token_in_rank,
+                         int32_t *expert_offsets, int32_t *rank_offsets, char *ws,
+                         int32_t *status, hipStream_t stream) {
+  const WorkspaceLayout w = workspace_layout(d.T, d.k, d.E, d.R);
+  const int32_t epr = d.E / d.R;
+  int32_t *tile_cnt = reinterpret_cast<int32_t *>(ws + w.tile_cnt);
+  int32_t *tile_rank_cnt = reinterpret_cast<int32_t *>(ws + w.tile_rank_cnt);
+  if (w.ntiles > 0) {
+    const size_t lds = sizeof(unsigned long long) * kWavesPerBlock * (size_t)d.E;
+    hipLaunchKernelGGL(layout_count_kernel, dim3(w.ntiles), dim3(kBlock), lds, stream, topk_idx,
+                       d, epr, tile_cnt, tile_rank_cnt,
+                       reinterpret_cast<int32_t *>(ws + w.slot_rank), is_token_in_rank, status);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(1024), 0, stream, d, w.ntiles, epr,
+                     tile_cnt, tile_rank_cnt, reinterpret_cast<int32_t *>(ws + w.cnt),
+                     num_tokens_per_expert, num_tokens_per_rank, expert_offsets, rank_offsets,
+                     reinterpret_cast<int32_t *>(ws));
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch(const Dims &d, bool fp8, const uint16_t *x, const int32_t *topk_idx,
+                           const float *topk_weights, const int32_t *expert_offsets,
+                           const char *ws, int64_t capacity, void *recv_x, float *recv_scales,
+                           float *recv_weights, int32_t *tok_slot_row, int32_t *row_src,
+                           int32_t *status, hipStream_t stream) {
+  const WorkspaceLayout w = workspace_layout(d.T, d.k, d.E, d.R);
+  const int32_t *header = reinterpret_cast<const int32_t *>(ws);
+  const int32_t *tile_base = reinterpret_cast<const int32_t *>(ws + w.tile_cnt);
+  const int32_t *slot_rank = reinterpret_cast<const int32_t *>(ws + w.slot_rank);
+  const int32_t nchunks = (d.H + kChunkCols - 1) / kChunkCols;
+  if (d.T > 0) {
+    const int64_t items = (int64_t)d.T * nchunks;
+    const dim3 grid((unsigned)((items + kWavesPerBlock - 1) / kWavesPerBlock));
+    if (fp8)
+      hipLaunchKernelGGL(dispatch_fp8_kernel, grid, dim3(kBlock), 0, stream, d, nchunks, x,
+                         topk_idx, topk_weights, expert_offsets, header, tile_base, slot_rank,
+                         capacity, static_cast<uint8_t *>(recv_x), recv_scales, recv_weights,
+                         tok_slot_row, row_src, status);
+    else
+      hipLaunchKernelGGL(dispatch_bf16_kernel, grid, dim3(kBlock), 0, stream, d, nchunks, x,
+                         topk_idx, topk_weights, expert_offsets, header, tile_base, slot_rank,
+                         capacity, static_cast<uint16_t *>(recv_x), recv_weights, tok_slot_row,
+                         row_src, status);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (d.A > 1) {
+    hipLaunchKernelGGL(pad_fill_kernel, dim3(d.E), dim3(kBlock), 0, stream, d, fp8,
+                       expert_offsets, reinterpret_cast<const int32_t *>(ws + w.cnt), capacity,
+                       recv_x, recv_scales, topk_weights != nullptr ? recv_weights : nullptr,
+                       row_src);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_combine(const Dims &d, int64_t capacity, const uint16_t *expert_out,
+                          const int32_t *tok_slot_row, const float *topk_weights,
+                          uint16_t *out, hipStream_t stream) {
+  if (d.T == 0) return hipSuccess;
+  const int32_t nchunks = (d.H + kChunkCols - 1) / kChunkCols;
+  const int64_t items = (int64_t)d.T * nchunks;
+  const dim3 grid((unsigned)((items + kWavesPerBlock - 1) / kWavesPerBlock));
+  if (topk_weights != nullptr)
+    hipLaunchKernelGGL((combine_kernel<true, 8>), grid, dim3(kBlock), 0, stream, d, nchunks,
+                       capacity, expert_out, tok_slot_row, topk_weights, out);
+  else
+    hipLaunchKernelGGL((combine_kernel<false, 8>), grid, dim3(kBlock), 0, stream, d, nchunks,
+                       capacity, expert_out, tok_slot_row, topk_weights, out);
+  return hipGetLastError();
+}
+
+}  // namespace ep

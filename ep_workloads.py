@@ -75,6 +75,29 @@ def to_bf16_bits(v: np.ndarray) -> np.ndarray:
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
+_CHUNK = 1 << 22
+
+
+def normal_bf16(rng, shape, sigma: float = 1.0) -> np.ndarray:
+    """bf16 bits of standard-normal fp32 draws times sigma (in fp32), drawn
+    in fixed-size pieces straight into the output.  The stream is the one a
+    single ``rng.standard_normal(shape, dtype=float32)`` call would draw."""
+    import torch
+
+    out = np.empty(shape, np.uint16)
+    flat = out.reshape(-1)
+    buf = np.empty(min(_CHUNK, flat.size), np.float32)
+    tout = torch.from_numpy(flat.view(np.int16))
+    for lo in range(0, flat.size, _CHUNK):
+        n = min(_CHUNK, flat.size - lo)
+        piece = buf[:n]
+        rng.standard_normal(n, dtype=np.float32, out=piece)
+        if sigma != 1.0:
+            piece *= np.float32(sigma)
+        tout[lo:lo + n] = torch.from_numpy(piece).to(torch.bfloat16).view(torch.int16)
+    return out
+
+
 def _softmax64(logits: np.ndarray) -> np.ndarray:
     z = logits.astype(np.float64)
     z = z - z.max(axis=1, keepdims=True)
@@ -119,7 +142,7 @@ def generate(w: Workload, with_y: bool = True) -> dict:
     (float32 [T,k]) and, with ``with_y``, y (uint16 bf16 bits [capacity,H])."""
     rng = np.random.default_rng(w.seed)
     T, H, k, E = w.num_tokens, w.hidden, w.num_topk, w.num_experts
-    x = to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32) * np.float32(w.sigma))
+    x = normal_bf16(rng, (T, H), w.sigma)
     if w.routing == "uniform":
         idx = _uniform_routes(rng, T, E, k)
         logits = rng.standard_normal((T, k), dtype=np.float32)
@@ -139,7 +162,7 @@ def generate(w: Workload, with_y: bool = True) -> dict:
     out = dict(x=x, topk_idx=np.ascontiguousarray(idx, np.int32),
                topk_weights=np.ascontiguousarray(weights, np.float32))
     if with_y:
-        out["y"] = to_bf16_bits(rng.standard_normal((w.capacity, H), dtype=np.float32))
+        out["y"] = normal_bf16(rng, (w.capacity, H))
     return out
 
 

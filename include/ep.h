@@ -1,0 +1,220 @@
+/*
+ * ep.h - C ABI of libep.so: MoE expert-parallel dispatch / combine layout
+ * transformation on one AMD Instinct MI355X (gfx950).
+ *
+ * The expert-parallel group is emulated on one GPU as R logical ranks, each a
+ * partition of one receive buffer in HBM, so the hop between ranks is an
+ * in-HBM copy.  Three calls make up the path:
+ *
+ *   ep_get_dispatch_layout  counts and prefix offsets per expert and rank
+ *   ep_dispatch             token-major rows -> rank partitions -> expert
+ *                           segments (bf16 copy, or FP8 E4M3 + fp32 scales),
+ *                           plus the source-index handle
+ *   ep_combine              expert-major rows -> token-major, gate applied
+ *                           once, fixed-order fp32 sum, bf16 result
+ *
+ * Pages cited: "GPU microarchitecture: DeepEP first principles"
+ * (backyes.github.io) and "Deep Dive - DeepEP" (leetllm.com), by section.
+ *
+ * Conventions for every call
+ *   - Sizes: T tokens, H hidden, k top-k, E experts, R logical ranks with
+ *     E % R == 0 (expert e lives on rank e / (E/R)), A expert alignment.
+ *   - Pointers named *_host are host memory; every other pointer is device
+ *     memory owned by the caller.  The library allocates nothing, keeps no
+ *     state between calls and may be called from several threads on
+ *     different streams at once, as long as their buffers do not overlap.
+ *   - Every call enqueues work on `stream` and returns without waiting,
+ *     except where a *_host output is requested (then it synchronises that
+ *     stream).  Waiting on the stream orders later work after the results;
+ *     it is a stream dependency, not a host barrier ("Deep Dive - DeepEP",
+ *     "EventOverlap: a stream contract").
+ *   - Errors never cross the ABI as exceptions.  Bad sizes, pointers or
+ *     dtypes are rejected synchronously with EP_ERR_INVALID_ARG before any
+ *     work is enqueued ("Deep Dive - DeepEP", "Combine: reverse routing plus
+ *     reduction": fail at the contract boundary, not after a silent
+ *     reinterpretation).  Problems only the GPU can see (a bad route, too
+ *     few receive rows, a workspace that does not belong to this
+ *     configuration) are OR-ed as bits into the caller's device status word
+ *     and surface through ep_read_status.  HIP launch failures return
+ *     EP_ERR_HIP.  ep_last_error() describes the last failure of the
+ *     calling thread.
+ */
+#ifndef EP_H
+#define EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ep_status {
+  EP_OK = 0,
+  EP_ERR_INVALID_ARG = 1,   /* sizes, pointers, dtype, alignment (synchronous) */
+  EP_ERR_INVALID_ROUTE = 2, /* expert id outside [-1, E) or repeated in a token */
+  EP_ERR_CAPACITY = 3,      /* receive buffer has fewer rows than the layout needs */
+  EP_ERR_WORKSPACE = 4,     /* workspace not written by a layout of this config */
+  EP_ERR_HIP = 5            /* a HIP runtime call failed */
+} ep_status_t;
+
+/* Bits the kernels OR into the device status word. */
+#define EP_STATUS_BIT_ROUTE 0x1
+#define EP_STATUS_BIT_CAPACITY 0x2
+#define EP_STATUS_BIT_WORKSPACE 0x4
+
+typedef enum ep_dtype {
+  EP_DTYPE_BF16 = 0,     /* rows are bf16, copied bit for bit */
+  EP_DTYPE_FP8_E4M3 = 1  /* OCP E4M3 ("FN", max 448) codes + one fp32 scale per 128 values */
+} ep_dtype_t;
+
+/* Limits of this implementation (checked; EP_ERR_INVALID_ARG beyond them). */
+#define EP_MAX_EXPERTS 1024
+#define EP_MAX_TOPK 32
+#define EP_MAX_RANKS 64
+
+typedef struct ep_config {
+  int32_t num_tokens;       /* T >= 0 */
+  int32_t hidden;           /* H >= 8, H % 8 == 0 (H % 128 == 0 for FP8) */
+  int32_t num_topk;         /* 1 <= k <= min(E, EP_MAX_TOPK) */
+  int32_t num_experts;      /* 1 <= E <= EP_MAX_EXPERTS */
+  int32_t num_ranks;        /* 1 <= R <= EP_MAX_RANKS, E % R == 0 */
+  int32_t expert_alignment; /* A >= 1; T*k + E*(A-1) < 2^31 */
+} ep_config_t;
+
+/*
+ * The handle ep_dispatch returns and ep_combine consumes: route and
+ * reverse-slot metadata, never gate values ("Deep Dive - DeepEP", sections
+ * "A four-token routing ledger" and "EPHandle: route metadata with a
+ * lifetime").  It is a plain host struct that borrows the caller's device
+ * arrays; it stays valid while they live and only for the route it was
+ * built from.
+ */
+typedef struct ep_handle {
+  ep_config_t config;
+  int64_t capacity;              /* rows of the receive / expert-output buffers */
+  const int32_t *tok_slot_row;   /* [T, k]: receive row of selection (t, j), -1 if unused */
+  const int32_t *row_src;        /* [capacity]: t*k + j of the row's source, -1 for padding */
+  const int32_t *expert_offsets; /* [E + 1]: aligned start of each expert segment */
+} ep_handle_t;
+
+/* Static description of a status code (never NULL). */
+const char *ep_status_string(ep_status_t status);
+
+/* Message for the last failing call on this thread ("" if none). */
+const char *ep_last_error(void);
+
+/* Host only.  Bytes of device workspace that ep_get_dispatch_layout fills
+ * and ep_dispatch reads for this configuration. */
+ep_status_t ep_layout_workspace_bytes(const ep_config_t *cfg, size_t *bytes_host);
+
+/* Host only.  Receive rows that always suffice without reading counts back:
+ * T*k + E*(A-1) (every slot valid, every expert segment padded). */
+ep_status_t ep_recv_capacity_rows(const ep_config_t *cfg, int64_t *rows_host);
+
+/*
+ * Layout: "count, prefix sum" of the counting sort ("GPU microarchitecture:
+ * DeepEP first principles", sections "6.1 Layout Metadata" and "7.1 Does
+ * Sort Exist?"), with per-rank counts of distinct tokens (a token goes to a
+ * rank once however many of its experts live there: "Deep Dive - DeepEP",
+ * "Why expert parallelism needs a communication layer") and aligned expert
+ * segment starts ("Deep Dive - DeepEP", "Dispatch: layout, move, and
+ * epilogue").
+ *
+ *   topk_idx             [T, k] int32, row-major; -1 = unused selection
+ *   num_tokens_per_rank  [R] int32 out: distinct tokens with an expert on rank r
+ *   num_tokens_per_expert[E] int32 out: selections of expert e
+ *   is_token_in_rank     [T, R] uint8 out: 1 if token t has an expert on rank r
+ *   expert_offsets       [E + 1] int32 out: offsets[0] = 0, offsets[e+1] =
+ *                        offsets[e] + ceil(count[e] / A) * A.  The valid rows of
+ *                        expert e are [offsets[e], offsets[e] + count[e]).
+ *   rank_offsets         [R + 1] int32 out: rank r's receive partition is
+ *                        rows [rank_offsets[r], rank_offsets[r+1])
+ *   workspace            device scratch of ep_layout_workspace_bytes() bytes,
+ *                        read later by ep_dispatch (keep it until then)
+ *   status               device int32 the kernels OR EP_STATUS_BIT_* into;
+ *                        the caller zeroes it before a new route
+ *   num_recv_rows_host   optional: if not NULL, the call synchronises the
+ *                        stream and stores offsets[E] (rows used) here, and
+ *                        returns the device status (the CPU-sync variant)
+ */
+ep_status_t ep_get_dispatch_layout(const ep_config_t *cfg, const int32_t *topk_idx,
+                                   int32_t *num_tokens_per_rank,
+                                   int32_t *num_tokens_per_expert,
+                                   uint8_t *is_token_in_rank, int32_t *expert_offsets,
+                                   int32_t *rank_offsets, void *workspace,
+                                   size_t workspace_bytes, int32_t *status,
+                                   int32_t *num_recv_rows_host, hipStream_t stream);
+
+/*
+ * Dispatch: token-major -> destination-major -> expert-major in one pass
+ * ("GPU microarchitecture: DeepEP first principles", section 1.1).  Each
+ * valid selection (t, j) with expert e gets the receive row
+ *     expert_offsets[e] + #{t' < t : token t' also selected e}
+ * (the stable placement dst = prefix[expert]++ of section "6.1 Layout
+ * Metadata"; rows of a segment are in ascending token order, the order the
+ * deterministic mode of "Deep Dive - DeepEP", "EPHandle", sorts by).
+ *
+ *   recv_dtype    EP_DTYPE_BF16: recv_x is bf16 [capacity, H], a bit copy of x.
+ *                 EP_DTYPE_FP8_E4M3: recv_x is uint8 [capacity, H] and
+ *                 recv_scales fp32 [capacity, H/128]; per token and 128-value
+ *                 block, scale = amax/448 (fp32, round to nearest even) and
+ *                 code = E4M3(x / scale) rounded to nearest even, with scale 0
+ *                 and zero codes for an all-zero block ("Deep Dive - DeepEP",
+ *                 "Precision: FP8 on the wire, BF16 for the reduction").
+ *   x             [T, H] bf16 hidden states (finite)
+ *   topk_idx      [T, k] int32, the same array given to the layout
+ *   topk_weights  [T, k] fp32 gates or NULL
+ *   expert_offsets[E + 1] from ep_get_dispatch_layout
+ *   workspace     the workspace that layout filled for this route
+ *   capacity      rows of recv_x / recv_scales / recv_weights / row_src; a
+ *                 selection whose row would be >= capacity is dropped and
+ *                 EP_STATUS_BIT_CAPACITY is set (ep_recv_capacity_rows() or
+ *                 the synchronised row count always suffices)
+ *   recv_weights  [capacity] fp32 out or NULL: the gate of each row
+ *   tok_slot_row  [T, k] int32 out: row of (t, j), -1 if unused
+ *   row_src       [capacity] int32 out: t*k + j of each row, -1 for padding
+ *   handle_host   optional: filled with the handle for ep_combine
+ * Rows in [offsets[e] + count[e], offsets[e+1]) are alignment padding: zero
+ * payload, zero scale, zero weight, row_src -1.  Rows at or past
+ * expert_offsets[E] are not written.
+ */
+ep_status_t ep_dispatch(const ep_config_t *cfg, ep_dtype_t recv_dtype, const uint16_t *x,
+                        const int32_t *topk_idx, const float *topk_weights,
+                        const int32_t *expert_offsets, const void *workspace,
+                        size_t workspace_bytes, int64_t capacity, void *recv_x,
+                        float *recv_scales, float *recv_weights, int32_t *tok_slot_row,
+                        int32_t *row_src, int32_t *status, ep_handle_t *handle_host,
+                        hipStream_t stream);
+
+/*
+ * Combine: expert-major rows back to token-major ("GPU microarchitecture:
+ * DeepEP first principles", section 1.2), each gate applied exactly once
+ * ("Deep Dive - DeepEP", "Combine: reverse routing plus reduction"):
+ *     out[t, c] = bf16( sum_{j = 0..k-1, row_j >= 0} w[t, j] * y[row_j, c] )
+ * with row_j = tok_slot_row[t, j], accumulated in fp32 in slot order j = 0, 1,
+ * ..., one fused multiply-add per term starting from +0, then rounded once to
+ * bf16 (nearest even).  Unused slots contribute nothing and their gates are
+ * never read; remaining gates are not renormalised.
+ *
+ *   handle        from ep_dispatch (config, capacity, tok_slot_row)
+ *   expert_out    [capacity, H] bf16 expert outputs, row p = expert output of
+ *                 receive row p
+ *   topk_weights  [T, k] fp32 gates, or NULL when the caller already
+ *                 weighted the rows (then the terms are plain fp32 adds)
+ *   out           [T, H] bf16 out
+ */
+ep_status_t ep_combine(const ep_handle_t *handle, const uint16_t *expert_out,
+                       const float *topk_weights, uint16_t *out, hipStream_t stream);
+
+/* Synchronises `stream`, reads the device status word and returns the
+ * first error it holds (route, then capacity, then workspace) or EP_OK. */
+ep_status_t ep_read_status(const int32_t *status, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_H */

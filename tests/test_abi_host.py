@@ -1,0 +1,104 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, every
+function include/ep.h declares is exported, host-only queries return the
+documented sizes, and bad arguments are rejected before anything is enqueued
+(these calls return before any HIP call, so they run without a device)."""
+import ctypes
+
+import pytest
+
+import combine_get_dispatch_amd as ep
+
+
+def test_library_exports_every_declared_function():
+    names = ep.header_functions()
+    assert set(names) >= {"ep_get_dispatch_layout", "ep_dispatch", "ep_combine"}
+    L = ep.lib()
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in ep.h but not exported"
+
+
+def test_status_strings():
+    L = ep.lib()
+    for code in range(6):
+        assert L.ep_status_string(code)
+    assert L.ep_status_string(99) == b"unknown status"
+
+
+def test_capacity_and_workspace_queries():
+    cfg = ep.ep_config_t(4096, 7168, 8, 256, 8, 1)
+    assert ep.ep_recv_capacity_rows(cfg) == 4096 * 8
+    cfg4 = ep.ep_config_t(4, 8, 2, 4, 2, 4)
+    assert ep.ep_recv_capacity_rows(cfg4) == 4 * 2 + 4 * 3
+    n = ep.ep_layout_workspace_bytes(cfg)
+    # header + tile histogram + tile rank counts + counts + in-tile ranks
+    assert n >= 4 * (16 * 256 + 16 * 8 + 256 + 4096 * 8) and n % 256 == 0
+
+
+@pytest.mark.parametrize("bad", [
+    (4, 8, 2, 6, 4, 1),     # E % R != 0
+    (4, 12, 2, 4, 2, 1),    # H % 8 != 0
+    (4, 8, 5, 4, 2, 1),     # k > E
+    (4, 8, 33, 64, 2, 1),   # k > EP_MAX_TOPK
+    (4, 8, 2, 2048, 2, 1),  # E > EP_MAX_EXPERTS
+    (4, 8, 2, 128, 128, 1), # R > EP_MAX_RANKS
+    (4, 8, 2, 4, 2, 0),     # A < 1
+    (-1, 8, 2, 4, 2, 1),    # T < 0
+    (1 << 28, 8, 8, 4, 2, 1),  # T*k overflows int32 rows
+])
+def test_bad_config_rejected(bad):
+    with pytest.raises(ep.EpError) as e:
+        ep.ep_recv_capacity_rows(ep.ep_config_t(*bad))
+    assert e.value.status == ep.EP_ERR_INVALID_ARG
+    assert ep.lib().ep_last_error()
+
+
+def _fake(n):
+    return ctypes.c_void_p(0x100000 * n)  # never dereferenced: rejected first
+
+
+def test_dispatch_rejections_happen_before_launch():
+    L = ep.lib()
+    cfg = ep.ep_config_t(16, 200, 2, 4, 2, 1)  # H % 128 != 0
+    h = ep.ep_handle_t()
+    st = L.ep_dispatch(ctypes.byref(cfg), ep.EP_DTYPE_FP8_E4M3, _fake(1), _fake(2), None,
+                       _fake(3), _fake(4), 1 << 20, 32, _fake(5), _fake(6), None, _fake(7),
+                       _fake(8), _fake(9), ctypes.byref(h), None)
+    assert st == ep.EP_ERR_INVALID_ARG and b"128" in L.ep_last_error()
+    cfg = ep.ep_config_t(16, 256, 2, 4, 2, 1)
+    st = L.ep_dispatch(ctypes.byref(cfg), 7, _fake(1), _fake(2), None, _fake(3), _fake(4),
+                       1 << 20, 32, _fake(5), _fake(6), None, _fake(7), _fake(8), _fake(9),
+                       None, None)
+    assert st == ep.EP_ERR_INVALID_ARG  # unknown dtype
+    st = L.ep_dispatch(ctypes.byref(cfg), ep.EP_DTYPE_BF16, _fake(1), _fake(2), None,
+                       _fake(3), _fake(4), 16, 32, _fake(5), None, None, _fake(7), _fake(8),
+                       _fake(9), None, None)
+    assert st == ep.EP_ERR_INVALID_ARG and b"workspace" in L.ep_last_error()
+    st = L.ep_dispatch(ctypes.byref(cfg), ep.EP_DTYPE_BF16, None, _fake(2), None,
+                       _fake(3), _fake(4), 1 << 20, 32, _fake(5), None, None, _fake(7),
+                       _fake(8), _fake(9), None, None)
+    assert st == ep.EP_ERR_INVALID_ARG  # NULL x
+    st = L.ep_dispatch(ctypes.byref(cfg), ep.EP_DTYPE_BF16, ctypes.c_void_p(0x100008),
+                       _fake(2), None, _fake(3), _fake(4), 1 << 20, 32, _fake(5), None, None,
+                       _fake(7), _fake(8), _fake(9), None, None)
+    assert st == ep.EP_ERR_INVALID_ARG and b"aligned" in L.ep_last_error()
+
+
+def test_layout_and_combine_rejections():
+    L = ep.lib()
+    cfg = ep.ep_config_t(16, 256, 2, 4, 2, 1)
+    st = L.ep_get_dispatch_layout(ctypes.byref(cfg), _fake(1), _fake(2), _fake(3), _fake(4),
+                                  _fake(5), _fake(6), _fake(7), 8, _fake(8), None, None)
+    assert st == ep.EP_ERR_INVALID_ARG and b"workspace" in L.ep_last_error()
+    st = L.ep_get_dispatch_layout(ctypes.byref(cfg), _fake(1), _fake(2), _fake(3), _fake(4),
+                                  _fake(5), _fake(6), ctypes.c_void_p(0x100010), 1 << 20,
+                                  _fake(8), None, None)
+    assert st == ep.EP_ERR_INVALID_ARG and b"aligned" in L.ep_last_error()
+    assert L.ep_combine(None, _fake(1), None, _fake(2), None) == ep.EP_ERR_INVALID_ARG
+    h = ep.ep_handle_t()
+    h.config = ep.ep_config_t(16, 256, 2, 4, 2, 1)
+    h.capacity = -1
+    assert L.ep_combine(ctypes.byref(h), _fake(1), None, _fake(2), None) == ep.EP_ERR_INVALID_ARG
+    h.capacity = 32
+    h.tok_slot_row = None
+    assert L.ep_combine(ctypes.byref(h), _fake(1), None, _fake(2), None) == ep.EP_ERR_INVALID_ARG
+    assert L.ep_read_status(None, None) == ep.EP_ERR_INVALID_ARG

@@ -1,0 +1,254 @@
+"""GPU edge cases: the FP8 encoder over every bf16 value it can see at unit
+scale, empty and degenerate inputs, the implementation limits, device-side
+error reporting, alignment padding, rank-count independence and
+determinism.  Each case is compared with the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+import combine_get_dispatch_amd as ep  # noqa: E402
+import ep_workloads as W  # noqa: E402
+import oracle  # noqa: E402
+from tests.ep_cases import bits_to_f32  # noqa: E402
+from tests.gpu_backend import GpuBackend, dev, dev_bf16, host_bf16, say  # noqa: E402
+
+GPU = GpuBackend()
+
+
+def test_fp8_encoder_every_bf16_value_at_unit_scale():
+    """Blocks whose largest magnitude is 448 get scale exactly 1, so the codes
+    are the E4M3 rounding of the bf16 values themselves: every finite bf16
+    value with |v| <= 448 (ties, subnormal codes, signed zeros included)."""
+    allbits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    vals = bits_to_f32(allbits)
+    keep = np.isfinite(vals) & (np.abs(vals) <= 448)
+    pool = allbits[keep]
+    per = 127
+    nblk = -(-len(pool) // per)
+    blocks = np.zeros((nblk, 128), np.uint16)
+    flat = np.concatenate([pool, np.zeros(nblk * per - len(pool), np.uint16)])
+    blocks[:, :per] = flat.reshape(nblk, per)
+    blocks[:, per] = np.where(np.arange(nblk) % 2 == 0, 0x43E0, 0xC3E0)  # +-448
+    H = 1024
+    T = -(-nblk // 8)
+    x = np.zeros((T * 8, 128), np.uint16)
+    x[:nblk] = blocks
+    x[nblk:, 0] = 0x43E0
+    x = x.reshape(T, H)
+    idx = np.zeros((T, 1), np.int32)
+    dg = GPU.dispatch(x, idx, None, 1, 1, 1, True, T)
+    do = oracle.dispatch(x, idx, None, 1, 1, fp8=True, capacity=T)
+    assert np.all(do["recv_scales"] == 1.0)
+    assert np.array_equal(dg["recv_scales"], do["recv_scales"])
+    assert np.array_equal(dg["recv_x"], do["recv_x"])
+
+
+def test_fp8_zero_and_tiny_blocks():
+    H = 512
+    x = np.zeros((3, H), np.uint16)
+    x[0, 128:256] = 0x8000                       # -0 only: amax 0 -> scale 0, codes 0
+    x[1, :128] = 0x0001                          # bf16 subnormal block
+    x[1, 128] = 0x8001
+    x[2] = W.normal_bf16(np.random.default_rng(3), (1, H), 1e-30)
+    idx = np.array([[0, 1]] * 3, np.int32)
+    dg = GPU.dispatch(x, idx, None, 2, 1, 1, True, 6)
+    do = oracle.dispatch(x, idx, None, 2, 1, fp8=True, capacity=6)
+    assert np.array_equal(dg["recv_x"], do["recv_x"])
+    assert np.array_equal(dg["recv_scales"].view(np.uint32), do["recv_scales"].view(np.uint32))
+
+
+def test_empty_batch():
+    E, R, k, H = 8, 2, 2, 256
+    b = ep.EpBuffers(0, H, k, E, R, 1, fp8=True)
+    idx = torch.zeros((0, k), dtype=torch.int32, device="cuda")
+    say("empty batch")
+    assert b.layout(idx, sync=True) == 0
+    assert torch.all(b.expert_offsets == 0) and torch.all(b.num_tokens_per_rank == 0)
+    b.dispatch(torch.zeros((0, H), dtype=torch.bfloat16, device="cuda"), idx,
+               torch.zeros((0, k), dtype=torch.float32, device="cuda"))
+    out = b.combine(torch.zeros((0, H), dtype=torch.bfloat16, device="cuda"),
+                    torch.zeros((0, k), dtype=torch.float32, device="cuda"))
+    b.check_status()
+    assert out.shape == (0, H)
+
+
+def test_all_masked_and_nan_gates():
+    rng = np.random.default_rng(4)
+    T, H, k, E, R = 70, 136, 3, 6, 3
+    idx = W.random_routes(rng, T, E, k)
+    idx[::3] = -1                                   # tokens with no expert at all
+    idx[1::3, 1] = -1
+    w = rng.random((T, k)).astype(np.float32)
+    w[idx < 0] = np.nan                             # must never be read
+    x = W.normal_bf16(rng, (T, H))
+    dg = GPU.dispatch(x, idx, w, E, R, 1, False, T * k)
+    do = oracle.dispatch(x, idx, w, E, R, 1, capacity=T * k)
+    assert np.array_equal(dg["tok_slot_row"], do["tok_slot_row"])
+    y = W.normal_bf16(rng, (T * k, H))
+    og = GPU.combine(y, do["tok_slot_row"], w)
+    oo, _ = oracle.combine(y, do["tok_slot_row"], w)
+    assert np.array_equal(og, oo)
+    assert np.all(og[::3] == 0)                     # +0, not -0, not NaN
+
+
+def test_hot_expert():
+    """Every token picks expert 0 (plus others): one segment holds all T
+    rows, in token order."""
+    rng = np.random.default_rng(5)
+    T, H, k, E, R = 3000, 264, 4, 16, 4
+    idx = np.concatenate([np.zeros((T, 1), np.int32),
+                          1 + W.random_routes(rng, T, E - 1, k - 1)], axis=1)
+    x = W.normal_bf16(rng, (T, H))
+    w = rng.random((T, k)).astype(np.float32)
+    lg, lo = GPU.layout(idx, E, R, 1), oracle.layout(idx, E, R, 1)
+    assert lg["num_tokens_per_expert"][0] == T
+    for key in lo:
+        assert np.array_equal(lg[key], lo[key])
+    dg = GPU.dispatch(x, idx, w, E, R, 1, False, T * k)
+    do = oracle.dispatch(x, idx, w, E, R, 1, capacity=T * k)
+    assert np.array_equal(dg["tok_slot_row"], do["tok_slot_row"])
+    assert np.array_equal(dg["recv_x"], do["recv_x"])
+
+
+@pytest.mark.parametrize("case", ["max_experts", "max_topk", "max_ranks"])
+def test_implementation_limits(case):
+    rng = np.random.default_rng(6)
+    T, H = 777, 128
+    E, R, k = {"max_experts": (1024, 8, 8), "max_topk": (64, 8, 32),
+               "max_ranks": (128, 64, 8)}[case]
+    idx = W.random_routes(rng, T, E, k, mask_prob=0.05)
+    x = W.normal_bf16(rng, (T, H))
+    w = rng.random((T, k)).astype(np.float32)
+    lg, lo = GPU.layout(idx, E, R, 2), oracle.layout(idx, E, R, 2)
+    for key in lo:
+        assert np.array_equal(lg[key], lo[key]), key
+    cap = T * k + E
+    for fp8 in (False, True):
+        dg = GPU.dispatch(x, idx, w, E, R, 2, fp8, cap)
+        do = oracle.dispatch(x, idx, w, E, R, 2, fp8=fp8, capacity=cap)
+        used = int(lo["expert_offsets"][-1])
+        assert np.array_equal(dg["tok_slot_row"], do["tok_slot_row"])
+        assert np.array_equal(dg["recv_x"][:used], do["recv_x"][:used])
+        assert np.array_equal(dg["row_src"][:used], do["row_src"][:used])
+    y = W.normal_bf16(rng, (cap, H))
+    assert np.array_equal(GPU.combine(y, do["tok_slot_row"], w),
+                          oracle.combine(y, do["tok_slot_row"], w)[0])
+
+
+def _raw_run(T, H, k, E, R, idx, capacity=None, x=None):
+    b = ep.EpBuffers(T, H, k, E, R, 1, capacity=capacity)
+    b.status.zero_()
+    idx_d = dev(idx)
+    b.layout(idx_d)
+    xs = dev_bf16(np.zeros((T, H), np.uint16) if x is None else x)
+    b.dispatch(xs, idx_d, None)
+    return b
+
+
+def test_invalid_routes_reported():
+    T, H, k, E, R = 40, 64, 2, 8, 2
+    for bad in ("duplicate", "too_large", "below_minus_one"):
+        say(f"invalid route: {bad}")
+        idx = np.tile(np.array([[0, 1]], np.int32), (T, 1))
+        if bad == "duplicate":
+            idx[7] = [3, 3]
+        elif bad == "too_large":
+            idx[9, 1] = E
+        else:
+            idx[11, 0] = -5
+        b = _raw_run(T, H, k, E, R, idx)
+        with pytest.raises(ep.EpError) as e:
+            b.check_status()
+        assert e.value.status == ep.EP_ERR_INVALID_ROUTE
+
+
+def test_capacity_too_small_reported_and_bounded():
+    T, H, k, E, R = 50, 64, 2, 4, 2
+    idx = np.tile(np.array([[0, 3]], np.int32), (T, 1))
+    x = W.normal_bf16(np.random.default_rng(7), (T, H))
+    say("capacity too small")
+    b = _raw_run(T, H, k, E, R, idx, capacity=60, x=x)
+    with pytest.raises(ep.EpError) as e:
+        b.check_status()
+    assert e.value.status == ep.EP_ERR_CAPACITY
+    tsr = b.tok_slot_row.cpu().numpy()
+    assert tsr.max() < 60
+    # the rows that fit are still right
+    do = oracle.dispatch(x, idx, None, E, R, capacity=T * k)
+    fit = do["tok_slot_row"] < 60
+    assert np.array_equal(tsr[fit], do["tok_slot_row"][fit])
+    assert np.all(tsr[~fit] == -1)
+
+
+def test_workspace_from_other_config_rejected():
+    T, H, k, E, R = 64, 64, 2, 8, 2
+    idx = np.tile(np.array([[0, 5]], np.int32), (T, 1))
+    b = ep.EpBuffers(T, H, k, E, R, 1)
+    b.status.zero_()
+    b.layout(dev(idx))
+    say("workspace mismatch")
+    other = ep.ep_config_t(T // 2, H, k, E, R, 1)
+    ep.ep_dispatch(other, ep.EP_DTYPE_BF16, dev_bf16(np.zeros((T // 2, H), np.uint16)),
+                   dev(idx[: T // 2]), None, b.expert_offsets, b.workspace, b.capacity,
+                   b.recv_x, None, None, b.tok_slot_row[: T // 2].contiguous(), b.row_src,
+                   b.status)
+    with pytest.raises(ep.EpError) as e:
+        b.check_status()
+    assert e.value.status == ep.EP_ERR_WORKSPACE
+
+
+def test_rank_count_moves_partitions_not_rows():
+    """Same routes on R = 1, 2, 8 logical ranks: expert-major rows are
+    identical, rank partitions and distinct-token counts change."""
+    rng = np.random.default_rng(8)
+    T, H, k, E = 500, 256, 4, 32
+    idx = W.random_routes(rng, T, E, k)
+    x = W.normal_bf16(rng, (T, H))
+    base = None
+    for R in (1, 2, 8):
+        d = GPU.dispatch(x, idx, None, E, R, 1, False, T * k)
+        lay = GPU.layout(idx, E, R, 1)
+        lo = oracle.layout(idx, E, R, 1)
+        assert np.array_equal(lay["rank_offsets"], lo["rank_offsets"])
+        assert np.array_equal(lay["num_tokens_per_rank"], lo["num_tokens_per_rank"])
+        if base is None:
+            base = d["recv_x"]
+        assert np.array_equal(d["recv_x"], base)
+
+
+def test_deterministic_repeat():
+    w = W.WORKLOADS["skewed"]
+    inp = W.generate(w)
+    outs = []
+    for rep in range(2):
+        say(f"determinism repeat {rep}")
+        b = ep.EpBuffers(w.num_tokens, w.hidden, w.num_topk, w.num_experts, w.num_ranks)
+        idx, wts = dev(inp["topk_idx"]), dev(inp["topk_weights"])
+        b.layout(idx)
+        b.dispatch(dev_bf16(inp["x"]), idx, wts)
+        out = b.combine(dev_bf16(inp["y"]), wts)
+        b.check_status()
+        used = int(b.expert_offsets[-1].item())
+        outs.append((host_bf16(b.recv_x[:used]), b.row_src[:used].cpu().numpy(),
+                     b.tok_slot_row.cpu().numpy(), host_bf16(out)))
+    for a, c in zip(*outs):
+        assert np.array_equal(a, c)
+
+
+def test_identity_round_trip_gpu():
+    """bf16 dispatch, identity experts, combine with gates summing to one:
+    the input comes back (as values)."""
+    w = W.WORKLOADS["decode"]
+    inp = W.generate(w, with_y=False)
+    idx = inp["topk_idx"]
+    g64 = inp["topk_weights"].astype(np.float64)
+    g = (g64 / g64.sum(axis=1, keepdims=True)).astype(np.float32)
+    b = ep.EpBuffers(w.num_tokens, w.hidden, w.num_topk, w.num_experts, w.num_ranks)
+    idx_d, g_d = dev(idx), dev(g)
+    b.layout(idx_d)
+    b.dispatch(dev_bf16(inp["x"]), idx_d, g_d)
+    out = b.combine(b.recv_x, g_d)
+    b.check_status()
+    assert np.array_equal(bits_to_f32(host_bf16(out)), bits_to_f32(inp["x"]))
