@@ -70,8 +70,9 @@ def lib() -> ctypes.CDLL:
                               ctypes.POINTER(ep_handle_t), P]
     L.ep_combine.argtypes = [ctypes.POINTER(ep_handle_t), P, P, P, P]
     L.ep_read_status.argtypes = [P, P]
+    L.ep_workspace_init.argtypes = [P, S, P]
     for f in ("ep_layout_workspace_bytes", "ep_recv_capacity_rows", "ep_get_dispatch_layout",
-              "ep_dispatch", "ep_combine", "ep_read_status"):
+              "ep_dispatch", "ep_combine", "ep_read_status", "ep_workspace_init"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -126,6 +127,13 @@ def ep_layout_workspace_bytes(cfg: ep_config_t) -> int:
     _check(lib().ep_layout_workspace_bytes(ctypes.byref(cfg), ctypes.byref(n)),
            "ep_layout_workspace_bytes")
     return n.value
+
+
+def ep_workspace_init(workspace, stream=None):
+    import torch
+
+    _check(lib().ep_workspace_init(_ptr(workspace, torch.uint8, name="workspace"),
+                                   workspace.numel(), _stream(stream)), "ep_workspace_init")
 
 
 def ep_recv_capacity_rows(cfg: ep_config_t) -> int:
@@ -242,6 +250,7 @@ class EpBuffers:
         dev = torch.device(device)
         i32 = dict(dtype=torch.int32, device=dev)
         self.workspace = torch.empty(ep_layout_workspace_bytes(self.cfg), dtype=torch.uint8, device=dev)
+        ep_workspace_init(self.workspace)
         self.status = torch.zeros(1, **i32)
         self.num_tokens_per_rank = torch.empty(R, **i32)
         self.num_tokens_per_expert = torch.empty(E, **i32)

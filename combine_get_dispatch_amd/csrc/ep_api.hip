@@ -98,6 +98,18 @@ ep_status_t ep_recv_capacity_rows(const ep_config_t *cfg, int64_t *rows_host) {
   return EP_OK;
 }
 
+ep_status_t ep_workspace_init(void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (workspace == nullptr) return fail(EP_ERR_INVALID_ARG, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(EP_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (workspace_bytes < 256)
+    return fail(EP_ERR_INVALID_ARG, "workspace has %zu bytes, needs at least 256",
+                workspace_bytes);
+  hipError_t err = ep::launch_workspace_init(static_cast<char *>(workspace), stream);
+  if (err != hipSuccess) return hip_fail(err, "workspace init launch");
+  return EP_OK;
+}
+
 ep_status_t ep_read_status(const int32_t *status, hipStream_t stream) {
   if (status == nullptr) return fail(EP_ERR_INVALID_ARG, "status is NULL");
   int32_t host = 0;

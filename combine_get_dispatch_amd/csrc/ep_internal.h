@@ -17,8 +17,11 @@ constexpr int kWavesPerBlock = kBlock / kWave;
 // Columns one wave moves per work item: 64 lanes x 8 bf16 (16 bytes) x 2.
 constexpr int kChunkCols = 1024;
 
+// Workspace header (int32 words): [0] magic once a layout has completed,
+// [1..5] T, k, E, R, A of that layout, [6] tiles, [8] layout ticket.
 constexpr int32_t kWorkspaceMagic = 0x45504C59;  // "EPLY"
 constexpr int kHeaderInts = 16;
+constexpr int kHeaderTicket = 8;
 
 // Byte offsets of the workspace sections for one configuration.
 struct WorkspaceLayout {
@@ -40,6 +43,8 @@ hipError_t launch_layout(const Dims &d, const int32_t *topk_idx, int32_t *num_to
                          int32_t *num_tokens_per_expert, uint8_t *is_token_in_rank,
                          int32_t *expert_offsets, int32_t *rank_offsets, char *ws,
                          int32_t *status, hipStream_t stream);
+
+hipError_t launch_workspace_init(char *ws, hipStream_t stream);
 
 hipError_t launch_dispatch(const Dims &d, bool fp8, const uint16_t *x, const int32_t *topk_idx,
                            const float *topk_weights, const int32_t *expert_offsets,

@@ -4,14 +4,13 @@
 // (backyes.github.io) and "Deep Dive - DeepEP" (leetllm.com), by section.
 //
 // The path is pure data movement (no dense contraction, so no MFMA):
-//   layout_count_kernel   one workgroup per 256-token tile: per-wave expert
+//   layout_kernel         one workgroup per 256-token tile: per-wave expert
 //                         bitmasks in LDS (64-bit OR per selection), their
 //                         popcounts give the tile histogram and each
 //                         selection's stable rank inside the tile; ballots
-//                         give distinct tokens per rank.
-//   layout_scan_kernel    one workgroup: per expert, exclusive scan over
-//                         tiles (tile bases); over experts, exclusive scan of
-//                         the aligned counts (segment starts).
+//                         give distinct tokens per rank.  The last
+//                         workgroup to finish scans: per expert over tiles
+//                         (tile bases), then over experts (segment starts).
 //   dispatch_*_kernel     one wave per (token, 1024-column chunk): reads the
 //                         x chunk once with 16-byte loads, optionally
 //                         quantises it to E4M3 in registers, and stores it to
@@ -43,6 +42,23 @@ __device__ __forceinline__ float lane_value_f(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
+// Streaming (non-temporal) 16-byte accesses for data touched exactly once per
+// pass: the receive rows written by dispatch, the expert outputs read and the
+// rows written by combine.  Written lines drain to HBM during the kernel that
+// wrote them instead of being evicted during the next one.  (x is read with
+// plain loads: streaming loads measured slower for it.)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load_stream(const void *p) {
+  const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4 *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void store_stream(void *p, uint4 v) {
+  const u32x4 q = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(q, static_cast<u32x4 *>(p));
+}
+
 // bf16 bits -> fp32 (exact), for the low and high halves of a 32-bit word.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -72,38 +88,61 @@ __device__ __forceinline__ bool workspace_ok(const int32_t *hdr, const Dims &d) 
 
 // ---------------------------------------------------------------------------
 // Layout (count, then prefix sum: "GPU microarchitecture: DeepEP first
-// principles", "7.1 Does Sort Exist?")
+// principles", "7.1 Does Sort Exist?"), in one launch.  Every workgroup
+// counts one 256-token tile.  The last workgroup to finish (it draws the
+// last ticket from a device-scope counter after a release fence) then scans
+// all tile histograms.  The ticket lives in the workspace header; it starts
+// at zero (ep_workspace_init) and the scanning workgroup resets it, so
+// consecutive layouts on one stream can reuse the workspace.
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(kBlock) void layout_count_kernel(
-    const int32_t *__restrict__ topk_idx, Dims d, int32_t experts_per_rank,
+// K is a compile-time bound on k (k <= K) so that a token's expert ids stay
+// in registers between the marking pass and the ranking pass.
+template <int K>
+__global__ __launch_bounds__(kBlock) void layout_kernel(
+    const int32_t *__restrict__ topk_idx, Dims d, int32_t ntiles, int32_t experts_per_rank,
     int32_t *__restrict__ tile_cnt, int32_t *__restrict__ tile_rank_cnt,
     int32_t *__restrict__ slot_rank, uint8_t *__restrict__ is_token_in_rank,
+    int32_t *__restrict__ cnt_ws, int32_t *__restrict__ num_tokens_per_expert,
+    int32_t *__restrict__ num_tokens_per_rank, int32_t *__restrict__ expert_offsets,
+    int32_t *__restrict__ rank_offsets, int32_t *__restrict__ header,
     int32_t *__restrict__ status) {
-  extern __shared__ unsigned long long masks[];  // [kWavesPerBlock][E]
+  // [kWavesPerBlock][E] expert bitmasks while counting; the scan reuses the
+  // same bytes for E + 1 aligned counts / offsets.
+  extern __shared__ unsigned long long masks[];
   __shared__ int32_t rank_cnt[EP_MAX_RANKS];
+  __shared__ int32_t wave_total[kWavesPerBlock];
+  __shared__ int is_last;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int tile = blockIdx.x;
-  const int64_t t = (int64_t)tile * kTileTokens + tid;
   const int E = d.E, k = d.k, R = d.R;
 
-  for (int i = tid; i < kWavesPerBlock * E; i += kBlock) masks[i] = 0ull;
-  for (int i = tid; i < R; i += kBlock) rank_cnt[i] = 0;
-  __syncthreads();
+  if (tile < ntiles) {
+    const int64_t t = (int64_t)tile * kTileTokens + tid;
+    const bool live = t < d.T;
 
-  // Mark this token in its wave's bitmask of every expert it selected.  The
-  // OR returns the previous mask, which exposes a repeated expert.
-  const unsigned long long me = 1ull << lane;
-  bool bad = false;
-  unsigned long long rmask = 0ull;
-  if (t < d.T) {
-    const int32_t *row = topk_idx + t * k;
-    for (int j = 0; j < k; ++j) {
-      const int32_t e = row[j];
+    // The token's expert ids, loaded together before any LDS traffic.
+    int32_t ex[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) ex[j] = (live && j < k) ? topk_idx[t * k + j] : -1;
+
+    for (int i = tid; i < kWavesPerBlock * E; i += kBlock) masks[i] = 0ull;
+    for (int i = tid; i < R; i += kBlock) rank_cnt[i] = 0;
+    __syncthreads();
+
+    // Mark this token in its wave's bitmask of every expert it selected.
+    // The OR returns the previous mask, which exposes a repeated expert.
+    const unsigned long long me = 1ull << lane;
+    bool bad = false;
+    unsigned long long rmask = 0ull;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const int32_t e = ex[j];
       if (e < -1 || e >= E) {
         bad = true;
+        ex[j] = -1;
         continue;
       }
       if (e < 0) continue;
@@ -111,104 +150,126 @@ __global__ __launch_bounds__(kBlock) void layout_count_kernel(
       if (old & me) bad = true;
       rmask |= 1ull << (e / experts_per_rank);
     }
-    uint8_t *dst = is_token_in_rank + t * R;
-    for (int r = 0; r < R; ++r) dst[r] = (uint8_t)((rmask >> r) & 1ull);
-  }
-  if (bad) flag(status, EP_STATUS_BIT_ROUTE);
+    if (bad) flag(status, EP_STATUS_BIT_ROUTE);
+    if (live) {
+      uint8_t *dst = is_token_in_rank + t * R;
+      if ((R & 3) == 0) {
+        for (int r = 0; r < R; r += 4) {
+          const uint32_t b = (uint32_t)(rmask >> r);
+          *reinterpret_cast<uint32_t *>(dst + r) =
+              (b & 1u) | ((b >> 1) & 1u) << 8 | ((b >> 2) & 1u) << 16 | ((b >> 3) & 1u) << 24;
+        }
+      } else {
+        for (int r = 0; r < R; ++r) dst[r] = (uint8_t)((rmask >> r) & 1ull);
+      }
+    }
 
-  // Distinct tokens per rank in this tile.
-  for (int r = 0; r < R; ++r) {
-    const unsigned long long b = __ballot((rmask >> r) & 1ull);
-    if (lane == 0 && b) atomicAdd(&rank_cnt[r], (int32_t)__popcll(b));
+    // Distinct tokens per rank in this tile.
+    for (int r = 0; r < R; ++r) {
+      const unsigned long long b = __ballot((rmask >> r) & 1ull);
+      if (lane == 0 && b) atomicAdd(&rank_cnt[r], (int32_t)__popcll(b));
+    }
+    __syncthreads();
+
+    for (int e = tid; e < E; e += kBlock) {
+      int32_t c = 0;
+#pragma unroll
+      for (int w = 0; w < kWavesPerBlock; ++w) c += __popcll(masks[w * E + e]);
+      tile_cnt[(int64_t)tile * E + e] = c;
+    }
+    for (int r = tid; r < R; r += kBlock) tile_rank_cnt[(int64_t)tile * R + r] = rank_cnt[r];
+
+    // Stable rank of (t, e) inside the tile: tokens of earlier waves that
+    // chose e, plus lanes below this one in its own wave that chose e.
+    if (live) {
+      const unsigned long long below = me - 1ull;
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        const int32_t e = ex[j];
+        int32_t rank = -1;
+        if (e >= 0) {
+          rank = __popcll(masks[wave * E + e] & below);
+#pragma unroll
+          for (int w = 0; w < kWavesPerBlock - 1; ++w)
+            if (w < wave) rank += __popcll(masks[w * E + e]);
+        }
+        if (j < k) slot_rank[t * k + j] = rank;
+      }
+    }
+  }
+
+  // Ticket: the workgroup that draws the last one scans.
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) is_last = atomicAdd(&header[kHeaderTicket], 1) == (int)gridDim.x - 1;
+  __syncthreads();
+  if (!is_last) return;
+  __threadfence();
+
+  // Per expert: tile histogram -> exclusive tile bases (in place) and its
+  // total.  Tiles go in batches whose loads are all issued before any store.
+  int32_t *aligned = reinterpret_cast<int32_t *>(masks);  // [E + 1]
+  for (int e = tid; e < E; e += kBlock) {
+    constexpr int kBatch = 16;
+    int32_t run = 0;
+    for (int t0 = 0; t0 < ntiles; t0 += kBatch) {
+      int32_t c[kBatch];
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b)
+        c[b] = (t0 + b < ntiles) ? tile_cnt[(int64_t)(t0 + b) * E + e] : 0;
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        if (t0 + b < ntiles) tile_cnt[(int64_t)(t0 + b) * E + e] = run;
+        run += c[b];
+      }
+    }
+    cnt_ws[e] = run;
+    num_tokens_per_expert[e] = run;
+    aligned[e] = (run + d.A - 1) / d.A * d.A;
   }
   __syncthreads();
 
-  for (int e = tid; e < E; e += kBlock) {
-    int32_t c = 0;
-    for (int w = 0; w < kWavesPerBlock; ++w) c += __popcll(masks[w * E + e]);
-    tile_cnt[(int64_t)tile * E + e] = c;
-  }
-  for (int r = tid; r < R; r += kBlock) tile_rank_cnt[(int64_t)tile * R + r] = rank_cnt[r];
-
-  // Stable rank of (t, e) inside the tile: tokens of earlier waves that chose
-  // e, plus lanes below this one in its own wave that chose e.
-  if (t < d.T) {
-    const int32_t *row = topk_idx + t * k;
-    const unsigned long long below = me - 1ull;
-    for (int j = 0; j < k; ++j) {
-      const int32_t e = row[j];
-      int32_t rank = -1;
-      if (e >= 0 && e < E) {
-        rank = __popcll(masks[wave * E + e] & below);
-        for (int w = 0; w < wave; ++w) rank += __popcll(masks[w * E + e]);
-      }
-      slot_rank[t * k + j] = rank;
-    }
-  }
-}
-
-__global__ __launch_bounds__(1024) void layout_scan_kernel(
-    Dims d, int32_t ntiles, int32_t experts_per_rank, int32_t *__restrict__ tile_cnt,
-    const int32_t *__restrict__ tile_rank_cnt, int32_t *__restrict__ cnt_ws,
-    int32_t *__restrict__ num_tokens_per_expert, int32_t *__restrict__ num_tokens_per_rank,
-    int32_t *__restrict__ expert_offsets, int32_t *__restrict__ rank_offsets,
-    int32_t *__restrict__ header) {
-  __shared__ int32_t wave_sum[1024 / kWave];
-  __shared__ int32_t offsets[EP_MAX_EXPERTS + 1];
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-  const int E = d.E;
-
-  // Per expert: tile histogram -> exclusive tile bases (in place) and total.
-  int32_t padded = 0;
-  if (tid < E) {
-    int32_t run = 0;
-    for (int tile = 0; tile < ntiles; ++tile) {
-      const int64_t i = (int64_t)tile * E + tid;
-      const int32_t c = tile_cnt[i];
-      tile_cnt[i] = run;
-      run += c;
-    }
-    cnt_ws[tid] = run;
-    num_tokens_per_expert[tid] = run;
-    padded = (run + d.A - 1) / d.A * d.A;
-  }
-
-  // Exclusive scan of the aligned counts over experts (wave scan + wave sums).
-  int32_t incl = padded;
+  // Exclusive scan of the aligned counts over experts: each thread owns a
+  // run of G consecutive experts; runs are scanned across the wave with
+  // shuffles and across the four waves through LDS.
+  const int G = (E + kBlock - 1) / kBlock;
+  const int e0 = tid * G;
+  int32_t local = 0;
+  for (int i = 0; i < G; ++i)
+    if (e0 + i < E) local += aligned[e0 + i];
+  int32_t incl = local;
   for (int off = 1; off < kWave; off <<= 1) {
     const int32_t v = __shfl_up(incl, off);
     if (lane >= off) incl += v;
   }
-  if (lane == kWave - 1) wave_sum[wave] = incl;
+  if (lane == kWave - 1) wave_total[wave] = incl;
   __syncthreads();
-  if (tid == 0) {
-    int32_t run = 0;
-    for (int w = 0; w < 1024 / kWave; ++w) {
-      const int32_t s = wave_sum[w];
-      wave_sum[w] = run;
-      run += s;
+  int32_t base = incl - local;
+  for (int w = 0; w < wave; ++w) base += wave_total[w];
+  int32_t total = 0;
+  for (int w = 0; w < kWavesPerBlock; ++w) total += wave_total[w];
+  __syncthreads();  // every thread has read its run of aligned[] above
+  for (int i = 0; i < G; ++i) {
+    if (e0 + i < E) {
+      const int32_t a = aligned[e0 + i];
+      aligned[e0 + i] = base;
+      expert_offsets[e0 + i] = base;
+      base += a;
     }
   }
-  __syncthreads();
-  const int32_t excl = incl - padded + wave_sum[wave];
-  if (tid < E) {
-    offsets[tid] = excl;
-    expert_offsets[tid] = excl;
-    if (tid == E - 1) {
-      offsets[E] = excl + padded;
-      expert_offsets[E] = excl + padded;
-    }
+  if (tid == 0) {
+    aligned[E] = total;
+    expert_offsets[E] = total;
   }
   __syncthreads();
 
-  if (tid < d.R) {
+  if (tid < R) {
     int32_t n = 0;
-    for (int tile = 0; tile < ntiles; ++tile) n += tile_rank_cnt[(int64_t)tile * d.R + tid];
+#pragma unroll 16
+    for (int t0 = 0; t0 < ntiles; ++t0) n += tile_rank_cnt[(int64_t)t0 * R + tid];
     num_tokens_per_rank[tid] = n;
   }
-  if (tid <= d.R) rank_offsets[tid] = offsets[tid * experts_per_rank];
+  if (tid <= R) rank_offsets[tid] = aligned[tid * experts_per_rank];
   if (tid == 0) {
     header[1] = d.T;
     header[2] = d.k;
@@ -217,7 +278,13 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(
     header[5] = d.A;
     header[6] = ntiles;
     header[0] = kWorkspaceMagic;
+    atomicExch(&header[kHeaderTicket], 0);
   }
+}
+
+// Zeroes the workspace header (magic and ticket) once, before first use.
+__global__ void workspace_init_kernel(int32_t *__restrict__ header) {
+  if (threadIdx.x < kHeaderInts) header[threadIdx.x] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -303,14 +370,40 @@ __global__ __launch_bounds__(kBlock) void dispatch_bf16_kernel(
     uint16_t *dst = recv_x + (int64_t)r * H;
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (col[u] < H) *reinterpret_cast<uint4 *>(dst + col[u]) = v[u];
+      if (col[u] < H) store_stream(dst + col[u], v[u]);
   }
 }
 
-// FP8 rows: per token and 128-value block (16 lanes x 8 values), amax over
-// the block, scale = amax / 448 and codes = E4M3(x / scale), both rounded to
-// nearest even ("Deep Dive - DeepEP", "Precision: FP8 on the wire, BF16 for
-// the reduction").  An all-zero block gets scale 0 and zero codes.
+// FP8 rows: per token and 128-value block, amax over the block, scale =
+// amax / 448 and codes = E4M3(x / scale), both rounded to nearest even
+// ("Deep Dive - DeepEP", "Precision: FP8 on the wire, BF16 for the
+// reduction").  An all-zero block gets scale 0 and zero codes.  Each lane
+// owns 16 consecutive values (two 16-byte loads, one 16-byte store of
+// codes), so a block is 8 lanes and a wave covers 1024 columns.
+__device__ __forceinline__ float amax8(const uint4 v) {
+  float m = fabsf(bf16_lo(v.x));
+  m = fmaxf(m, fabsf(bf16_hi(v.x)));
+  m = fmaxf(m, fabsf(bf16_lo(v.y)));
+  m = fmaxf(m, fabsf(bf16_hi(v.y)));
+  m = fmaxf(m, fabsf(bf16_lo(v.z)));
+  m = fmaxf(m, fabsf(bf16_hi(v.z)));
+  m = fmaxf(m, fabsf(bf16_lo(v.w)));
+  return fmaxf(m, fabsf(bf16_hi(v.w)));
+}
+
+// Eight bf16 values divided by s (correctly rounded fp32 division) and
+// converted to E4M3 with round to nearest even, packed little-endian.
+__device__ __forceinline__ uint2 quantize8(const uint4 v, float s) {
+  int lo = 0, hi = 0;
+  if (s > 0.0f) {
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(v.x) / s, bf16_hi(v.x) / s, lo, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(v.y) / s, bf16_hi(v.y) / s, lo, true);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(v.z) / s, bf16_hi(v.z) / s, hi, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(v.w) / s, bf16_hi(v.w) / s, hi, true);
+  }
+  return make_uint2((uint32_t)lo, (uint32_t)hi);
+}
+
 __global__ __launch_bounds__(kBlock) void dispatch_fp8_kernel(
     Dims d, int32_t nchunks, const uint16_t *__restrict__ x, const int32_t *__restrict__ topk_idx,
     const float *__restrict__ topk_weights, const int32_t *__restrict__ expert_offsets,
@@ -332,48 +425,29 @@ __global__ __launch_bounds__(kBlock) void dispatch_fp8_kernel(
                                     expert_offsets, tile_base, slot_rank, capacity,
                                     recv_weights, tok_slot_row, row_src, status);
 
-  constexpr int U = kChunkCols / (kWave * 8);
   const int64_t H = d.H;
   const int64_t nblk = H / 128;
-  uint2 q[U];
-  float scale[U];
-  int col[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    col[u] = chunk * kChunkCols + u * (kWave * 8) + lane * 8;
-    // H % 128 == 0, so the 16 lanes of a block are all in range or all out.
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (col[u] < H) v = *reinterpret_cast<const uint4 *>(x + t * H + col[u]);
-    float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                  bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
-    const float s = amax / 448.0f;
-    scale[u] = s;
-    int lo = 0, hi = 0;
-    if (s > 0.0f) {
-      lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0] / s, f[1] / s, lo, false);
-      lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2] / s, f[3] / s, lo, true);
-      hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4] / s, f[5] / s, hi, false);
-      hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6] / s, f[7] / s, hi, true);
-    }
-    q[u] = make_uint2((uint32_t)lo, (uint32_t)hi);
+  // H % 128 == 0, so the 8 lanes of a block are all in range or all out.
+  const int col = chunk * kChunkCols + lane * 16;
+  const bool in = col < H;
+  uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
+  if (in) {
+    v0 = *reinterpret_cast<const uint4 *>(x + t * H + col);
+    v1 = *reinterpret_cast<const uint4 *>(x + t * H + col + 8);
   }
+  float amax = fmaxf(amax8(v0), amax8(v1));
+#pragma unroll
+  for (int m = 1; m < 8; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+  const float scale = amax / 448.0f;
+  const uint2 q0 = quantize8(v0, scale);
+  const uint2 q1 = quantize8(v1, scale);
+  const uint4 q = make_uint4(q0.x, q0.y, q1.x, q1.y);
+
   for (int j = 0; j < d.k; ++j) {
     const int32_t r = lane_value(row, j);
-    if (r < 0) continue;
-    uint8_t *dst = recv_x + (int64_t)r * H;
-    float *sdst = recv_scales + (int64_t)r * nblk;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (col[u] < H) {
-        *reinterpret_cast<uint2 *>(dst + col[u]) = q[u];
-        if ((lane & 15) == 0) sdst[col[u] / 128] = scale[u];
-      }
-    }
+    if (r < 0 || !in) continue;
+    store_stream(recv_x + (int64_t)r * H + col, q);
+    if ((lane & 7) == 0) recv_scales[(int64_t)r * nblk + col / 128] = scale;
   }
 }
 
@@ -451,7 +525,7 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(
         const uint16_t *src = y + (int64_t)r[jj] * H;
 #pragma unroll
         for (int u = 0; u < U; ++u)
-          if (col[u] < H) v[jj][u] = *reinterpret_cast<const uint4 *>(src + col[u]);
+          if (col[u] < H) v[jj][u] = load_stream(src + col[u]);
       }
     }
 #pragma unroll
@@ -483,7 +557,7 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(
       o.y = pack_bf16(acc[u][2], acc[u][3]);
       o.z = pack_bf16(acc[u][4], acc[u][5]);
       o.w = pack_bf16(acc[u][6], acc[u][7]);
-      *reinterpret_cast<uint4 *>(out + t * H + col[u]) = o;
+      store_stream(out + t * H + col[u], o);
     }
   }
 }
@@ -515,20 +589,22 @@ hipError_t launch_layout(const Dims &d, const int32_t *topk_idx, int32_t *num_to
                          int32_t *expert_offsets, int32_t *rank_offsets, char *ws,
                          int32_t *status, hipStream_t stream) {
   const WorkspaceLayout w = workspace_layout(d.T, d.k, d.E, d.R);
-  const int32_t epr = d.E / d.R;
-  int32_t *tile_cnt = reinterpret_cast<int32_t *>(ws + w.tile_cnt);
-  int32_t *tile_rank_cnt = reinterpret_cast<int32_t *>(ws + w.tile_rank_cnt);
-  if (w.ntiles > 0) {
-    const size_t lds = sizeof(unsigned long long) * kWavesPerBlock * (size_t)d.E;
-    hipLaunchKernelGGL(layout_count_kernel, dim3(w.ntiles), dim3(kBlock), lds, stream, topk_idx,
-                       d, epr, tile_cnt, tile_rank_cnt,
-                       reinterpret_cast<int32_t *>(ws + w.slot_rank), is_token_in_rank, status);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
-  hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(1024), 0, stream, d, w.ntiles, epr,
-                     tile_cnt, tile_rank_cnt, reinterpret_cast<int32_t *>(ws + w.cnt),
-                     num_tokens_per_expert, num_tokens_per_rank, expert_offsets, rank_offsets,
+  const size_t lds = sizeof(unsigned long long) * kWavesPerBlock * (size_t)d.E;
+  auto kernel = d.k <= 8 ? layout_kernel<8> : (d.k <= 16 ? layout_kernel<16> : layout_kernel<32>);
+  // An empty batch still needs one workgroup to write zero counts and offsets.
+  const unsigned grid = w.ntiles > 0 ? (unsigned)w.ntiles : 1u;
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kBlock), lds, stream, topk_idx, d, w.ntiles,
+                     d.E / d.R, reinterpret_cast<int32_t *>(ws + w.tile_cnt),
+                     reinterpret_cast<int32_t *>(ws + w.tile_rank_cnt),
+                     reinterpret_cast<int32_t *>(ws + w.slot_rank), is_token_in_rank,
+                     reinterpret_cast<int32_t *>(ws + w.cnt), num_tokens_per_expert,
+                     num_tokens_per_rank, expert_offsets, rank_offsets,
+                     reinterpret_cast<int32_t *>(ws), status);
+  return hipGetLastError();
+}
+
+hipError_t launch_workspace_init(char *ws, hipStream_t stream) {
+  hipLaunchKernelGGL(workspace_init_kernel, dim3(1), dim3(kWave), 0, stream,
                      reinterpret_cast<int32_t *>(ws));
   return hipGetLastError();
 }

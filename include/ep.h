@@ -110,6 +110,17 @@ const char *ep_last_error(void);
  * and ep_dispatch reads for this configuration. */
 ep_status_t ep_layout_workspace_bytes(const ep_config_t *cfg, size_t *bytes_host);
 
+/*
+ * Prepares a workspace for its first layout: clears its header (the marker
+ * that a layout completed and the counter the layout's workgroups use to
+ * elect the one that finishes the prefix sums).  Call once per allocation
+ * (a zero-filled allocation needs no call); every layout leaves the header
+ * ready for the next one.  Enqueued on `stream` as a small kernel (no
+ * memset), so it may be captured in a graph.  workspace must be 256-byte
+ * aligned with at least 256 bytes.
+ */
+ep_status_t ep_workspace_init(void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Host only.  Receive rows that always suffice without reading counts back:
  * T*k + E*(A-1) (every slot valid, every expert segment padded). */
 ep_status_t ep_recv_capacity_rows(const ep_config_t *cfg, int64_t *rows_host);
@@ -133,7 +144,10 @@ ep_status_t ep_recv_capacity_rows(const ep_config_t *cfg, int64_t *rows_host);
  *   rank_offsets         [R + 1] int32 out: rank r's receive partition is
  *                        rows [rank_offsets[r], rank_offsets[r+1])
  *   workspace            device scratch of ep_layout_workspace_bytes() bytes,
- *                        read later by ep_dispatch (keep it until then)
+ *                        256-byte aligned, prepared once by ep_workspace_init
+ *                        (or zero-filled), read later by ep_dispatch (keep it
+ *                        until then).  Two layouts must not use one workspace
+ *                        at the same time (e.g. on two streams).
  *   status               device int32 the kernels OR EP_STATUS_BIT_* into;
  *                        the caller zeroes it before a new route
  *   num_recv_rows_host   optional: if not NULL, the call synchronises the

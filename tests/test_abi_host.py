@@ -102,3 +102,6 @@ def test_layout_and_combine_rejections():
     h.tok_slot_row = None
     assert L.ep_combine(ctypes.byref(h), _fake(1), None, _fake(2), None) == ep.EP_ERR_INVALID_ARG
     assert L.ep_read_status(None, None) == ep.EP_ERR_INVALID_ARG
+    assert L.ep_workspace_init(None, 1024, None) == ep.EP_ERR_INVALID_ARG
+    assert L.ep_workspace_init(ctypes.c_void_p(0x100010), 1024, None) == ep.EP_ERR_INVALID_ARG
+    assert L.ep_workspace_init(_fake(1), 64, None) == ep.EP_ERR_INVALID_ARG

@@ -252,3 +252,27 @@ def test_identity_round_trip_gpu():
     out = b.combine(b.recv_x, g_d)
     b.check_status()
     assert np.array_equal(bits_to_f32(host_bf16(out)), bits_to_f32(inp["x"]))
+
+
+def test_workspace_reused_across_layouts():
+    """One workspace, several layouts with different routes in a row: each
+    layout's last workgroup resets the ticket for the next one."""
+    rng = np.random.default_rng(9)
+    T, H, k, E, R = 1500, 128, 6, 48, 4
+    b = ep.EpBuffers(T, H, k, E, R, 1)
+    for rep in range(5):
+        say(f"workspace reuse {rep}")
+        idx = W.random_routes(rng, T, E, k, mask_prob=0.1 * rep)
+        x = W.normal_bf16(rng, (T, H))
+        b.status.zero_()
+        idx_d = dev(idx)
+        rows = b.layout(idx_d, sync=True)
+        b.dispatch(dev_bf16(x), idx_d, None)
+        b.check_status()
+        lo = oracle.layout(idx, E, R, 1)
+        do = oracle.dispatch(x, idx, None, E, R, capacity=T * k)
+        assert rows == lo["expert_offsets"][-1]
+        assert np.array_equal(b.expert_offsets.cpu().numpy(), lo["expert_offsets"])
+        assert np.array_equal(b.num_tokens_per_rank.cpu().numpy(), lo["num_tokens_per_rank"])
+        assert np.array_equal(b.tok_slot_row.cpu().numpy(), do["tok_slot_row"])
+        assert np.array_equal(host_bf16(b.recv_x[:rows]), do["recv_x"][:rows])
