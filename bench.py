@@ -53,17 +53,99 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def _read_kv(path: str) -> dict:
+    out = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                key, _, val = line.partition("=")
+                out[key.strip()] = val.strip()
+    return out
+
+
 def load_traffic(workload: str, kernel: str):
     """HBM bytes per launch from the committed counter summary, if it was
     taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
-    with open(path) as f:
-        rec = json.load(f)
+    rec = _read_kv(path)
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return rec.get("bytes_per_launch")
+    return int(float(rec["hbm_bytes_per_launch"]))
+
+
+KERNEL_KEYS = {"layout": "layout_kernel", "dispatch": "dispatch_fp8_kernel",
+               "dispatch_bf16": "dispatch_bf16_kernel", "combine": "combine_kernel"}
+
+
+def pmc_summary(run_dir: str, workload: str, copy_mib: int, cmds: dict):
+    """Summarise rocprofv3 runs under run_dir (trace/, fetch/, write/) into
+    profiles/: per-kernel average durations, and HBM bytes per launch from
+    FETCH_SIZE / WRITE_SIZE scaled by what the counters read for a plain
+    device copy of copy_mib MiB."""
+    import csv
+    import statistics
+
+    def rows(sub, name):
+        with open(os.path.join(run_dir, sub, name)) as f:
+            return list(csv.DictReader(f))
+
+    def per_kernel(sub):
+        vals = {}
+        for r in rows(sub, "ep_counter_collection.csv"):
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    fetch, write = per_kernel("fetch"), per_kernel("write")
+    copy_kib = copy_mib * 1024.0
+
+    def copy_factor(vals):
+        cands = [max(v) for k, v in vals.items() if "copyBuffer" in k]
+        return copy_kib / max(cands)
+
+    ff, wf = copy_factor(fetch), copy_factor(write)
+    stats = {r["Name"]: r for r in rows("trace", "ep_kernel_stats.csv")}
+    src_hash = kernel_source_hash()
+    lines = ["# Kernel durations, " + workload + " workload",
+             "", "Command:", "", "    " + cmds["trace"], "",
+             "| kernel | calls | average (us) | min (us) | max (us) |", "|---|---|---|---|---|"]
+    for name, r in stats.items():
+        short = name.split("(")[0].replace("void ", "")
+        lines.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    lines += ["", f"kernel_source_hash = {src_hash}", ""]
+    with open(os.path.join(ROOT, "profiles", f"{workload}_kernel_trace.md"), "w") as f:
+        f.write("\n".join(lines))
+    for key, kname in KERNEL_KEYS.items():
+        fk = [k for k in fetch if kname in k]
+        wk = [k for k in write if kname in k]
+        if not fk or not wk:
+            continue
+        fkib = statistics.median(fetch[fk[0]])
+        wkib = statistics.median(write[wk[0]])
+        avg_ns = [float(r["AverageNs"]) for n, r in stats.items() if kname in n]
+        body = [
+            f"# HBM traffic of {kname}, {workload} workload (rocprofv3 counters)",
+            "# FETCH_SIZE and WRITE_SIZE are KiB per dispatch (median over dispatches),",
+            f"# scaled by copy_mib*1024 / (counter of a plain {copy_mib} MiB device copy).",
+            f"# trace command: {cmds['trace']}",
+            f"# fetch command: {cmds['fetch']}",
+            f"# write command: {cmds['write']}",
+            f"kernel = {fk[0].split('(')[0]}",
+            f"fetch_size_kib = {fkib:.1f}",
+            f"write_size_kib = {wkib:.1f}",
+            f"copy_fetch_factor = {ff:.4f}",
+            f"copy_write_factor = {wf:.4f}",
+            f"hbm_read_bytes_per_launch = {fkib * ff * 1024:.0f}",
+            f"hbm_write_bytes_per_launch = {wkib * wf * 1024:.0f}",
+            f"hbm_bytes_per_launch = {(fkib * ff + wkib * wf) * 1024:.0f}",
+            f"average_duration_us = {avg_ns[0] / 1e3:.2f}" if avg_ns else "average_duration_us = nan",
+            f"kernel_source_hash = {src_hash}",
+        ]
+        with open(os.path.join(ROOT, "profiles", f"{key}_{workload}_hbm_traffic.txt"), "w") as f:
+            f.write("\n".join(body) + "\n")
+    print(f"profiles written for {workload} (copy factors fetch {ff:.4f}, write {wf:.4f})")
 
 
 def cpu_baseline(w, inp, budget_s: float):
@@ -99,7 +181,22 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter scale)")
+    ap.add_argument("--pmc-summary", metavar="DIR", default=None,
+                    help="summarise rocprofv3 trace/fetch/write runs in DIR into profiles/")
     args = ap.parse_args()
+
+    if args.pmc_summary:
+        base = (f"python3 bench.py --workload {args.workload} --steps 3 --warmup 1 "
+                f"--no-cpu-baseline --copy-probe-mib 256")
+        cmds = {
+            "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace -o ep -- "
+                     f"python3 bench.py --workload {args.workload} --steps 20 --warmup 5 "
+                     "--no-cpu-baseline --copy-probe-mib 256",
+            "fetch": f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch -o ep -- {base}",
+            "write": f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write -o ep -- {base}",
+        }
+        pmc_summary(args.pmc_summary, args.workload, 256, cmds)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
