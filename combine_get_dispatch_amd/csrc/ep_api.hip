@@ -48,7 +48,7 @@ ep_status_t check_config(const ep_config_t *c) {
   if (rows >= INT32_MAX)
     return fail(EP_ERR_INVALID_ARG, "T*k + E*(A-1) = %lld does not fit int32 row indices",
                 (long long)rows);
-  const int64_t chunks = (c->hidden + ep::kChunkCols - 1) / ep::kChunkCols;
+  const int64_t chunks = (c->hidden + ep::kCombineCols - 1) / ep::kCombineCols;
   if ((int64_t)c->num_tokens * chunks >= INT32_MAX)
     return fail(EP_ERR_INVALID_ARG, "num_tokens x hidden too large");
   return EP_OK;

@@ -14,8 +14,10 @@ constexpr int kWave = 64;
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
 
-// Columns one wave moves per work item: 64 lanes x 8 bf16 (16 bytes) x 2.
+// Columns one dispatch wave moves per work item: 64 lanes x 16 values.
 constexpr int kChunkCols = 1024;
+// Columns one combine wave reduces per work item: 64 lanes x 8 bf16.
+constexpr int kCombineCols = 512;
 
 // Workspace header (int32 words): [0] magic once a layout has completed,
 // [1..5] T, k, E, R, A of that layout, [6] tiles, [8] layout ticket.

@@ -15,7 +15,7 @@
 //                         x chunk once with 16-byte loads, optionally
 //                         quantises it to E4M3 in registers, and stores it to
 //                         each of the token's receive rows.
-//   combine_kernel        one wave per (token, 1024-column chunk): k gathered
+//   combine_kernel        one wave per (token, 512-column chunk): k gathered
 //                         16-byte loads per lane, fp32 FMAs in slot order,
 //                         one bf16 rounding, one 16-byte store.
 // Output positions never depend on atomics or scheduling, so every result
@@ -63,18 +63,18 @@ __device__ __forceinline__ void store_stream(void *p, uint4 v) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// fp32 -> bf16 bits, round to nearest even: add 0x7FFF plus the lowest kept
-// bit and keep the upper half ("Deep Dive - DeepEP", "Combine: reverse
-// routing plus reduction").  NaN keeps its sign and upper payload with the
-// quiet bit set.
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t b = __float_as_uint(f);
-  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return (b >> 16) | 0x40u;
-  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
-}
+// Two fp32 -> packed bf16 with v_cvt_pk_bf16_f32 (gfx950): round to nearest
+// even, and a NaN keeps its sign and upper payload with the quiet bit set.
+// These are the results of the integer procedure of "Deep Dive - DeepEP",
+// "Combine: reverse routing plus reduction" (add 0x7FFF plus the lowest kept
+// bit, keep the upper half), which the oracle implements; the parity tests
+// compare every combined element with it.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return bf16_rne(lo) | (bf16_rne(hi) << 16);
+  const f32x2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
 // Workspace header check shared by the dispatch kernels: the workspace must
@@ -107,8 +107,8 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
     int32_t *__restrict__ num_tokens_per_rank, int32_t *__restrict__ expert_offsets,
     int32_t *__restrict__ rank_offsets, int32_t *__restrict__ header,
     int32_t *__restrict__ status) {
-  // [kWavesPerBlock][E] expert bitmasks while counting; the scan reuses the
-  // same bytes for E + 1 aligned counts / offsets.
+  // [kWavesPerBlock][E] expert bitmasks; the scanning workgroup then uses
+  // the E + 1 words after them for aligned counts / offsets.
   extern __shared__ unsigned long long masks[];
   __shared__ int32_t rank_cnt[EP_MAX_RANKS];
   __shared__ int32_t wave_total[kWavesPerBlock];
@@ -118,13 +118,15 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
   const int wave = tid / kWave;
   const int tile = blockIdx.x;
   const int E = d.E, k = d.k, R = d.R;
+  const bool has_tile = tile < ntiles;
+  const int64_t t = (int64_t)tile * kTileTokens + tid;
+  const bool live = has_tile && t < d.T;
+  const unsigned long long me = 1ull << lane;
+  unsigned long long rmask = 0ull;
+  int32_t ex[K];
 
-  if (tile < ntiles) {
-    const int64_t t = (int64_t)tile * kTileTokens + tid;
-    const bool live = t < d.T;
-
+  if (has_tile) {
     // The token's expert ids, loaded together before any LDS traffic.
-    int32_t ex[K];
 #pragma unroll
     for (int j = 0; j < K; ++j) ex[j] = (live && j < k) ? topk_idx[t * k + j] : -1;
 
@@ -132,11 +134,9 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
     for (int i = tid; i < R; i += kBlock) rank_cnt[i] = 0;
     __syncthreads();
 
-    // Mark this token in its wave's bitmask of every expert it selected.
-    // The OR returns the previous mask, which exposes a repeated expert.
-    const unsigned long long me = 1ull << lane;
+    // Mark this token in its wave's bitmask of every expert it selected;
+    // reject ids outside [-1, E) and ids repeated within the token.
     bool bad = false;
-    unsigned long long rmask = 0ull;
 #pragma unroll
     for (int j = 0; j < K; ++j) {
       const int32_t e = ex[j];
@@ -146,23 +146,12 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
         continue;
       }
       if (e < 0) continue;
-      const unsigned long long old = atomicOr(&masks[wave * E + e], me);
-      if (old & me) bad = true;
+#pragma unroll
+      for (int jj = 0; jj < j; ++jj) bad |= ex[jj] == e;
+      atomicOr(&masks[wave * E + e], me);
       rmask |= 1ull << (e / experts_per_rank);
     }
     if (bad) flag(status, EP_STATUS_BIT_ROUTE);
-    if (live) {
-      uint8_t *dst = is_token_in_rank + t * R;
-      if ((R & 3) == 0) {
-        for (int r = 0; r < R; r += 4) {
-          const uint32_t b = (uint32_t)(rmask >> r);
-          *reinterpret_cast<uint32_t *>(dst + r) =
-              (b & 1u) | ((b >> 1) & 1u) << 8 | ((b >> 2) & 1u) << 16 | ((b >> 3) & 1u) << 24;
-        }
-      } else {
-        for (int r = 0; r < R; ++r) dst[r] = (uint8_t)((rmask >> r) & 1ull);
-      }
-    }
 
     // Distinct tokens per rank in this tile.
     for (int r = 0; r < R; ++r) {
@@ -171,6 +160,7 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
     }
     __syncthreads();
 
+    // Publish the tile's counts first: only they are needed by the scan.
     for (int e = tid; e < E; e += kBlock) {
       int32_t c = 0;
 #pragma unroll
@@ -178,107 +168,123 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
       tile_cnt[(int64_t)tile * E + e] = c;
     }
     for (int r = tid; r < R; r += kBlock) tile_rank_cnt[(int64_t)tile * R + r] = rank_cnt[r];
+  }
 
-    // Stable rank of (t, e) inside the tile: tokens of earlier waves that
-    // chose e, plus lanes below this one in its own wave that chose e.
-    if (live) {
-      const unsigned long long below = me - 1ull;
+  // Ticket: the workgroup that draws the last one scans.  The release fence
+  // covers the tile counts above; the per-token outputs below are written
+  // after it and overlap the scan.  A single workgroup needs neither fence
+  // nor ticket (the barrier orders its own writes).
+  const bool many = gridDim.x > 1;
+  if (many) __threadfence();
+  __syncthreads();
+  if (tid == 0) is_last = many ? atomicAdd(&header[kHeaderTicket], 1) == (int)gridDim.x - 1 : 1;
+  __syncthreads();
+
+  if (is_last) {
+    if (many) __threadfence();
+    int32_t *aligned = reinterpret_cast<int32_t *>(masks + kWavesPerBlock * E);  // [E + 1]
+    // Per expert: tile histogram -> exclusive tile bases (in place) and its
+    // total; thread r < R also sums rank r's tile counts (R <= E, so e = r is
+    // its first expert).  Tiles go in batches whose loads are all issued
+    // before any store.
+    int32_t rank_sum = 0;
+    for (int e = tid; e < E; e += kBlock) {
+      constexpr int kBatch = 16;
+      int32_t run = 0;
+      for (int t0 = 0; t0 < ntiles; t0 += kBatch) {
+        int32_t c[kBatch], rc[kBatch];
 #pragma unroll
-      for (int j = 0; j < K; ++j) {
-        const int32_t e = ex[j];
-        int32_t rank = -1;
-        if (e >= 0) {
-          rank = __popcll(masks[wave * E + e] & below);
-#pragma unroll
-          for (int w = 0; w < kWavesPerBlock - 1; ++w)
-            if (w < wave) rank += __popcll(masks[w * E + e]);
+        for (int b = 0; b < kBatch; ++b) {
+          const bool in = t0 + b < ntiles;
+          c[b] = in ? tile_cnt[(int64_t)(t0 + b) * E + e] : 0;
+          rc[b] = (in && e < R) ? tile_rank_cnt[(int64_t)(t0 + b) * R + e] : 0;
         }
-        if (j < k) slot_rank[t * k + j] = rank;
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+          if (t0 + b < ntiles) tile_cnt[(int64_t)(t0 + b) * E + e] = run;
+          run += c[b];
+          rank_sum += rc[b];
+        }
+      }
+      cnt_ws[e] = run;
+      num_tokens_per_expert[e] = run;
+      aligned[e] = (run + d.A - 1) / d.A * d.A;
+    }
+    if (tid < R) num_tokens_per_rank[tid] = rank_sum;
+    __syncthreads();
+
+    // Exclusive scan of the aligned counts over experts: each thread owns a
+    // run of G consecutive experts; runs are scanned across the wave with
+    // shuffles and across the four waves through LDS.
+    const int G = (E + kBlock - 1) / kBlock;
+    const int e0 = tid * G;
+    int32_t local = 0;
+    for (int i = 0; i < G; ++i)
+      if (e0 + i < E) local += aligned[e0 + i];
+    int32_t incl = local;
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int32_t v = __shfl_up(incl, off);
+      if (lane >= off) incl += v;
+    }
+    if (lane == kWave - 1) wave_total[wave] = incl;
+    __syncthreads();
+    int32_t base = incl - local;
+    for (int w = 0; w < wave; ++w) base += wave_total[w];
+    int32_t total = 0;
+    for (int w = 0; w < kWavesPerBlock; ++w) total += wave_total[w];
+    for (int i = 0; i < G; ++i) {
+      if (e0 + i < E) {
+        const int32_t a = aligned[e0 + i];
+        aligned[e0 + i] = base;
+        expert_offsets[e0 + i] = base;
+        base += a;
       }
     }
+    if (tid == 0) {
+      aligned[E] = total;
+      expert_offsets[E] = total;
+    }
+    __syncthreads();
+    if (tid <= R) rank_offsets[tid] = aligned[tid * experts_per_rank];
+    if (tid == 0) {
+      header[1] = d.T;
+      header[2] = d.k;
+      header[3] = d.E;
+      header[4] = d.R;
+      header[5] = d.A;
+      header[6] = ntiles;
+      header[0] = kWorkspaceMagic;
+      if (many) atomicExch(&header[kHeaderTicket], 0);
+    }
   }
 
-  // Ticket: the workgroup that draws the last one scans.
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) is_last = atomicAdd(&header[kHeaderTicket], 1) == (int)gridDim.x - 1;
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-
-  // Per expert: tile histogram -> exclusive tile bases (in place) and its
-  // total.  Tiles go in batches whose loads are all issued before any store.
-  int32_t *aligned = reinterpret_cast<int32_t *>(masks);  // [E + 1]
-  for (int e = tid; e < E; e += kBlock) {
-    constexpr int kBatch = 16;
-    int32_t run = 0;
-    for (int t0 = 0; t0 < ntiles; t0 += kBatch) {
-      int32_t c[kBatch];
-#pragma unroll
-      for (int b = 0; b < kBatch; ++b)
-        c[b] = (t0 + b < ntiles) ? tile_cnt[(int64_t)(t0 + b) * E + e] : 0;
-#pragma unroll
-      for (int b = 0; b < kBatch; ++b) {
-        if (t0 + b < ntiles) tile_cnt[(int64_t)(t0 + b) * E + e] = run;
-        run += c[b];
+  // Per-token outputs: the rank mask and the stable rank of (t, e) inside
+  // the tile (tokens of earlier waves that chose e, plus lanes below this
+  // one in its own wave that chose e).
+  if (live) {
+    uint8_t *dst = is_token_in_rank + t * R;
+    if ((R & 3) == 0) {
+      for (int r = 0; r < R; r += 4) {
+        const uint32_t b = (uint32_t)(rmask >> r);
+        *reinterpret_cast<uint32_t *>(dst + r) =
+            (b & 1u) | ((b >> 1) & 1u) << 8 | ((b >> 2) & 1u) << 16 | ((b >> 3) & 1u) << 24;
       }
+    } else {
+      for (int r = 0; r < R; ++r) dst[r] = (uint8_t)((rmask >> r) & 1ull);
     }
-    cnt_ws[e] = run;
-    num_tokens_per_expert[e] = run;
-    aligned[e] = (run + d.A - 1) / d.A * d.A;
-  }
-  __syncthreads();
-
-  // Exclusive scan of the aligned counts over experts: each thread owns a
-  // run of G consecutive experts; runs are scanned across the wave with
-  // shuffles and across the four waves through LDS.
-  const int G = (E + kBlock - 1) / kBlock;
-  const int e0 = tid * G;
-  int32_t local = 0;
-  for (int i = 0; i < G; ++i)
-    if (e0 + i < E) local += aligned[e0 + i];
-  int32_t incl = local;
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int32_t v = __shfl_up(incl, off);
-    if (lane >= off) incl += v;
-  }
-  if (lane == kWave - 1) wave_total[wave] = incl;
-  __syncthreads();
-  int32_t base = incl - local;
-  for (int w = 0; w < wave; ++w) base += wave_total[w];
-  int32_t total = 0;
-  for (int w = 0; w < kWavesPerBlock; ++w) total += wave_total[w];
-  __syncthreads();  // every thread has read its run of aligned[] above
-  for (int i = 0; i < G; ++i) {
-    if (e0 + i < E) {
-      const int32_t a = aligned[e0 + i];
-      aligned[e0 + i] = base;
-      expert_offsets[e0 + i] = base;
-      base += a;
+    const unsigned long long below = me - 1ull;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const int32_t e = ex[j];
+      int32_t rank = -1;
+      if (e >= 0) {
+        rank = __popcll(masks[wave * E + e] & below);
+#pragma unroll
+        for (int w = 0; w < kWavesPerBlock - 1; ++w)
+          if (w < wave) rank += __popcll(masks[w * E + e]);
+      }
+      if (j < k) slot_rank[t * k + j] = rank;
     }
-  }
-  if (tid == 0) {
-    aligned[E] = total;
-    expert_offsets[E] = total;
-  }
-  __syncthreads();
-
-  if (tid < R) {
-    int32_t n = 0;
-#pragma unroll 16
-    for (int t0 = 0; t0 < ntiles; ++t0) n += tile_rank_cnt[(int64_t)t0 * R + tid];
-    num_tokens_per_rank[tid] = n;
-  }
-  if (tid <= R) rank_offsets[tid] = aligned[tid * experts_per_rank];
-  if (tid == 0) {
-    header[1] = d.T;
-    header[2] = d.k;
-    header[3] = d.E;
-    header[4] = d.R;
-    header[5] = d.A;
-    header[6] = ntiles;
-    header[0] = kWorkspaceMagic;
-    atomicExch(&header[kHeaderTicket], 0);
   }
 }
 
@@ -504,13 +510,13 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(
     }
   }
 
-  constexpr int U = kChunkCols / (kWave * 8);
+  constexpr int U = kCombineCols / (kWave * 8);
   const int64_t H = d.H;
   int col[U];
   float acc[U][8];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    col[u] = chunk * kChunkCols + u * (kWave * 8) + lane * 8;
+    col[u] = chunk * kCombineCols + u * (kWave * 8) + lane * 8;
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[u][i] = 0.0f;
   }
@@ -589,7 +595,8 @@ hipError_t launch_layout(const Dims &d, const int32_t *topk_idx, int32_t *num_to
                          int32_t *expert_offsets, int32_t *rank_offsets, char *ws,
                          int32_t *status, hipStream_t stream) {
   const WorkspaceLayout w = workspace_layout(d.T, d.k, d.E, d.R);
-  const size_t lds = sizeof(unsigned long long) * kWavesPerBlock * (size_t)d.E;
+  const size_t lds = sizeof(unsigned long long) * kWavesPerBlock * (size_t)d.E +
+                     sizeof(int32_t) * ((size_t)d.E + 1);
   auto kernel = d.k <= 8 ? layout_kernel<8> : (d.k <= 16 ? layout_kernel<16> : layout_kernel<32>);
   // An empty batch still needs one workgroup to write zero counts and offsets.
   const unsigned grid = w.ntiles > 0 ? (unsigned)w.ntiles : 1u;
@@ -649,7 +656,7 @@ hipError_t launch_combine(const Dims &d, int64_t capacity, const uint16_t *exper
                           const int32_t *tok_slot_row, const float *topk_weights,
                           uint16_t *out, hipStream_t stream) {
   if (d.T == 0) return hipSuccess;
-  const int32_t nchunks = (d.H + kChunkCols - 1) / kChunkCols;
+  const int32_t nchunks = (d.H + kCombineCols - 1) / kCombineCols;
   const int64_t items = (int64_t)d.T * nchunks;
   const dim3 grid((unsigned)((items + kWavesPerBlock - 1) / kWavesPerBlock));
   if (topk_weights != nullptr)

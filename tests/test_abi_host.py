@@ -31,7 +31,7 @@ def test_capacity_and_workspace_queries():
     assert ep.ep_recv_capacity_rows(cfg4) == 4 * 2 + 4 * 3
     n = ep.ep_layout_workspace_bytes(cfg)
     # header + tile histogram + tile rank counts + counts + in-tile ranks
-    assert n >= 4 * (16 * 256 + 16 * 8 + 256 + 4096 * 8) and n % 256 == 0
+    assert n >= 4 * (16 + 16 * 256 + 16 * 8 + 256 + 4096 * 8) and n % 256 == 0
 
 
 @pytest.mark.parametrize("bad", [

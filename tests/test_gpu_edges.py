@@ -276,3 +276,23 @@ def test_workspace_reused_across_layouts():
         assert np.array_equal(b.num_tokens_per_rank.cpu().numpy(), lo["num_tokens_per_rank"])
         assert np.array_equal(b.tok_slot_row.cpu().numpy(), do["tok_slot_row"])
         assert np.array_equal(host_bf16(b.recv_x[:rows]), do["recv_x"][:rows])
+
+
+@pytest.mark.parametrize("T,E,k", [(255, 16, 3), (256, 16, 3), (257, 16, 3), (1, 256, 8),
+                                   (2049, 256, 8), (1537, 512, 8), (1000, 1024, 4),
+                                   (70001, 32, 2)])
+def test_layout_tile_boundaries(T, E, k):
+    """Layout counts 256-token tiles in separate workgroups (one workgroup
+    skips the ticket); ranks must carry across tile boundaries."""
+    rng = np.random.default_rng(T + E)
+    R = 8 if E % 8 == 0 else 1
+    idx = W.random_routes(rng, T, E, k, mask_prob=0.03)
+    lg, lo = GPU.layout(idx, E, R, 1), oracle.layout(idx, E, R, 1)
+    for key in lo:
+        assert np.array_equal(lg[key], lo[key]), key
+    x = W.normal_bf16(rng, (T, 8))
+    dg = GPU.dispatch(x, idx, None, E, R, 1, False, T * k)
+    do = oracle.dispatch(x, idx, None, E, R, capacity=T * k)
+    assert np.array_equal(dg["tok_slot_row"], do["tok_slot_row"])
+    used = int(lo["expert_offsets"][-1])
+    assert np.array_equal(dg["row_src"][:used], do["row_src"][:used])
