@@ -300,6 +300,8 @@ def main():
         "tokens_per_s": round(w.num_tokens / step_s, 1),
         "algorithmic_bytes_per_step": by,
         "kernel_us": {n: round(v, 2) for n, v in per_us.items()},
+        "kernel_roofline_frac": {n: round(by[n] / (per_us[n] / 1e6) / 1e9 / PEAK_HBM_GBPS, 4)
+                                 for n in names},
         "host_wall_s": round(wall, 4),
         "roofline": {
             "kernel": dom,
