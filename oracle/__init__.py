@@ -78,6 +78,10 @@ def _load():
                                     i64, P, P, P, P, P]
     lib.oracle_combine.restype = ctypes.c_int
     lib.oracle_combine.argtypes = [i32, i32, i32, i64, P, P, P, P, P]
+    lib.oracle_dispatch_backward.restype = ctypes.c_int
+    lib.oracle_dispatch_backward.argtypes = [i32, i32, i32, i64, P, P, P, P]
+    lib.oracle_combine_backward.restype = ctypes.c_int
+    lib.oracle_combine_backward.argtypes = [i32, i32, i32, i64, i64, P, P, P, P, P, P, P]
     _lib = lib
     return lib
 
@@ -197,3 +201,40 @@ def combine(y_bits, tok_slot_row, topk_weights) -> tuple[np.ndarray, np.ndarray]
     if rc:
         raise OracleError(rc, "combine")
     return out, acc
+
+
+def dispatch_backward(grad_recv_bits, tok_slot_row) -> tuple[np.ndarray, np.ndarray]:
+    """Transpose of the unweighted dispatch: returns (grad_x bf16 bits
+    [T,H], fp32 accumulator [T,H])."""
+    g = _c(grad_recv_bits, np.uint16)
+    tsr = _c(tok_slot_row, np.int32)
+    cap, H = g.shape
+    T, k = tsr.shape
+    out = np.empty((T, H), np.uint16)
+    acc = np.empty((T, H), np.float32)
+    rc = _load().oracle_dispatch_backward(T, H, k, cap, _ptr(g), _ptr(tsr), _ptr(out), _ptr(acc))
+    if rc:
+        raise OracleError(rc, "dispatch_backward")
+    return out, acc
+
+
+def combine_backward(grad_out_bits, tok_slot_row, topk_weights, expert_out_bits, rows_used: int,
+                     capacity: int | None = None, fill: int = 0) -> dict:
+    """Backward of combine: grad_expert_out (bf16 bits [cap,H]; rows past
+    rows_used keep ``fill``), grad_w and grad_w_abs (fp64 [T,k]; None when
+    expert_out_bits is None)."""
+    g = _c(grad_out_bits, np.uint16)
+    tsr = _c(tok_slot_row, np.int32)
+    T, H = g.shape
+    k = tsr.shape[1]
+    w = None if topk_weights is None else _c(topk_weights, np.float32)
+    y = None if expert_out_bits is None else _c(expert_out_bits, np.uint16)
+    cap = rows_used if capacity is None else capacity
+    gy = np.full((cap, H), fill & 0xFFFF, np.uint16)
+    gw = np.zeros((T, k), np.float64) if y is not None else None
+    ga = np.zeros((T, k), np.float64) if y is not None else None
+    rc = _load().oracle_combine_backward(T, H, k, cap, rows_used, _ptr(g), _ptr(tsr), _ptr(w),
+                                         _ptr(y), _ptr(gy), _ptr(gw), _ptr(ga))
+    if rc:
+        raise OracleError(rc, "combine_backward")
+    return dict(grad_expert_out=gy, grad_w=gw, grad_w_abs=ga)

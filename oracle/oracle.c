@@ -335,3 +335,69 @@ int oracle_combine(int32_t T, int32_t H, int32_t k, int64_t capacity,
   }
   return ORACLE_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Backward                                                                  */
+/* ------------------------------------------------------------------------ */
+
+/* [DD] "Combine: reverse routing plus reduction", backward duality: the
+ * transpose of copying a token's row into each of its expert rows is
+ * summing the gradients of those rows back into the token. */
+int oracle_dispatch_backward(int32_t T, int32_t H, int32_t k, int64_t capacity,
+                             const uint16_t *grad_recv, const int32_t *tok_slot_row,
+                             uint16_t *grad_x, float *acc_out) {
+  if (T < 0 || H < 1 || k < 1 || capacity < 0) return ORACLE_BAD_ARG;
+  for (int64_t i = 0; i < (int64_t)T * k; ++i)
+    if (tok_slot_row[i] < -1 || tok_slot_row[i] >= capacity) return ORACLE_BAD_ARG;
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t c = 0; c < H; ++c) {
+      float acc = 0.0f;
+      for (int j = 0; j < k; ++j) {
+        int64_t p = tok_slot_row[t * k + j];
+        if (p < 0) continue;
+        acc = acc + oracle_bf16_to_float(grad_recv[p * H + c]);
+      }
+      grad_x[t * H + c] = oracle_bf16_round(acc);
+      if (acc_out) acc_out[t * H + c] = acc;
+    }
+  }
+  return ORACLE_OK;
+}
+
+/* Backward of out[t] = sum_j w[t,j] * y[p_j]: the gradient reaching expert
+ * row p_j is w[t,j] * grad_out[t] (the gate applied once, as in the forward
+ * pass), and the gradient of the gate is the dot product of the expert row
+ * with grad_out[t] ([DD] "Combine: reverse routing plus reduction": the
+ * autograd wrapper must still produce gate gradients). */
+int oracle_combine_backward(int32_t T, int32_t H, int32_t k, int64_t capacity,
+                            int64_t rows_used, const uint16_t *grad_out,
+                            const int32_t *tok_slot_row, const float *topk_weights,
+                            const uint16_t *expert_out, uint16_t *grad_expert_out,
+                            double *grad_w, double *grad_w_abs) {
+  if (T < 0 || H < 1 || k < 1 || capacity < 0 || rows_used < 0 || rows_used > capacity)
+    return ORACLE_BAD_ARG;
+  for (int64_t i = 0; i < (int64_t)T * k; ++i)
+    if (tok_slot_row[i] < -1 || tok_slot_row[i] >= rows_used) return ORACLE_BAD_ARG;
+  for (int64_t i = 0; i < rows_used * H; ++i) grad_expert_out[i] = 0;
+  for (int64_t t = 0; t < T; ++t) {
+    for (int j = 0; j < k; ++j) {
+      int64_t p = tok_slot_row[t * k + j];
+      double dot = 0.0, mag = 0.0;
+      if (p >= 0) {
+        float w = topk_weights ? topk_weights[t * k + j] : 1.0f;
+        for (int64_t c = 0; c < H; ++c) {
+          float g = oracle_bf16_to_float(grad_out[t * H + c]);
+          grad_expert_out[p * H + c] = oracle_bf16_round(w * g);
+          if (expert_out) {
+            double term = (double)oracle_bf16_to_float(expert_out[p * H + c]) * (double)g;
+            dot += term;
+            mag += fabs(term);
+          }
+        }
+      }
+      if (grad_w) grad_w[t * k + j] = dot;
+      if (grad_w_abs) grad_w_abs[t * k + j] = mag;
+    }
+  }
+  return ORACLE_OK;
+}

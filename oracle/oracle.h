@@ -82,6 +82,32 @@ int oracle_combine(int32_t T, int32_t H, int32_t k, int64_t capacity,
                    const uint16_t *y, const int32_t *tok_slot_row,
                    const float *topk_weights, uint16_t *out, float *acc_out);
 
+/* Backward of dispatch ([DD] "Combine: reverse routing plus reduction",
+ * backward duality: for the unweighted route, copying a row forward becomes
+ * summing its gradients backward):
+ *   grad_x[t,c] = bf16(sum over valid j, in slot order, of
+ *                      grad_recv[tok_slot_row[t,j], c])
+ * accumulated in fp32 from +0.  acc_out (nullable) gets the fp32 sums. */
+int oracle_dispatch_backward(int32_t T, int32_t H, int32_t k, int64_t capacity,
+                             const uint16_t *grad_recv, const int32_t *tok_slot_row,
+                             uint16_t *grad_x, float *acc_out);
+
+/* Backward of combine.  For each valid (t, j) with row p = tok_slot_row[t,j]:
+ *   grad_expert_out[p,c] = bf16(fp32(w[t,j] * grad_out[t,c]))   (w = 1 when
+ *                          topk_weights is NULL: a copy of grad_out[t])
+ *   grad_w[t,j]          = sum_c expert_out[p,c] * grad_out[t,c], exact
+ *                          (fp64; each product of two bf16 values is exact)
+ *   grad_w_abs[t,j]      = sum_c |expert_out[p,c] * grad_out[t,c]|
+ * Rows [0, rows_used) that no selection references (alignment padding) get
+ * zero gradients; rows at or past rows_used are left untouched.  Unused
+ * slots get grad_w = 0.  expert_out, grad_w and grad_w_abs may be NULL
+ * together (no gate gradient). */
+int oracle_combine_backward(int32_t T, int32_t H, int32_t k, int64_t capacity,
+                            int64_t rows_used, const uint16_t *grad_out,
+                            const int32_t *tok_slot_row, const float *topk_weights,
+                            const uint16_t *expert_out, uint16_t *grad_expert_out,
+                            double *grad_w, double *grad_w_abs);
+
 #ifdef __cplusplus
 }
 #endif
