@@ -45,6 +45,17 @@ def algorithmic_bytes(w, M: int) -> dict:
                 total=layout + dispatch + combine)
 
 
+def backward_bytes(w, M: int) -> dict:
+    """Algorithmic bytes of the backward pair.
+    dispatch_backward: M*2H (row gradients) + T*k*4 (tok_slot_row) + T*2H (grad_x)
+    combine_backward:  T*2H (grad_out) + T*k*8 (tok_slot_row, gates) + M*2H (expert
+                       outputs) + M*2H (row gradients) + T*k*4 (gate gradients)"""
+    T, H, k = w.num_tokens, w.hidden, w.num_topk
+    db = M * 2 * H + T * k * 4 + T * 2 * H
+    cb = T * 2 * H + T * k * 8 + 2 * M * 2 * H + T * k * 4
+    return dict(dispatch_backward=db, combine_backward=cb, total=db + cb)
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
@@ -171,6 +182,68 @@ def cpu_baseline(w, inp, budget_s: float):
                 tokens_per_s=round(w.num_tokens * reps / el, 1))
 
 
+def run_backward(args, w, b, x, idx, wts, y, inp, dev, stream):
+    """Time the backward pair over one batch: gradient w.r.t. the receive
+    rows -> grad_x (dispatch backward), and grad_out -> row and gate
+    gradients (combine backward), after one forward layout + dispatch."""
+    import numpy as np
+    import torch
+
+    import ep_workloads as W
+
+    g = W.normal_bf16(np.random.default_rng(100 + w.seed), (w.num_tokens, w.hidden))
+    g_d = torch.from_numpy(g.view(np.int16)).view(torch.bfloat16).to(dev)
+    b.layout(idx)
+    b.dispatch(x, idx, wts)
+    b.check_status()
+    M = int(b.expert_offsets[-1].item())
+    grad_x = torch.empty_like(b.out)
+    gy = torch.empty((b.capacity, w.hidden), dtype=torch.bfloat16, device=dev)
+    gw = torch.empty((w.num_tokens, w.num_topk), dtype=torch.float32, device=dev)
+
+    def step():
+        b.dispatch_backward(y, grad_x)
+        b.combine_backward(g_d, wts, y, gy, gw)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    names = ("dispatch_backward", "combine_backward")
+    ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)] for n in names}
+    for i in range(args.steps):
+        for n, fn in zip(names, (lambda: b.dispatch_backward(y, grad_x),
+                                 lambda: b.combine_backward(g_d, wts, y, gy, gw))):
+            ev[n][i][0].record(stream)
+            fn()
+            ev[n][i][1].record(stream)
+    torch.cuda.synchronize()
+    per_us = {n: float(np.mean([a.elapsed_time(c) for a, c in ev[n]])) * 1e3 for n in names}
+    by = backward_bytes(w, M)
+    gbps = by["total"] / (ms / 1e3) / 1e9
+    rec = {
+        "metric": "backward (dispatch_backward + combine_backward) HBM GB/s",
+        "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "pct_of_peak": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
+        "tokens_per_s": round(w.num_tokens / (ms / 1e3), 1),
+        "config": {"workload": w.name, "tokens": w.num_tokens, "hidden": w.hidden,
+                   "topk": w.num_topk, "experts": w.num_experts, "valid_selections": M},
+        "algorithmic_bytes_per_step": by,
+        "kernel_us": {n: round(v, 2) for n, v in per_us.items()},
+        "kernel_roofline_frac": {n: round(by[n] / (per_us[n] / 1e6) / 1e9 / PEAK_HBM_GBPS, 4)
+                                 for n in names},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -181,6 +254,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter scale)")
+    ap.add_argument("--direction", choices=("forward", "backward"), default="forward",
+                    help="backward times ep_dispatch_backward + ep_combine_backward (its own "
+                         "JSON line, not the forward metric)")
     ap.add_argument("--pmc-summary", metavar="DIR", default=None,
                     help="summarise rocprofv3 trace/fetch/write runs in DIR into profiles/")
     args = ap.parse_args()
@@ -226,6 +302,10 @@ def main():
         b.layout(idx)
         b.dispatch(x, idx, wts)
         b.combine(y, wts)
+
+    if args.direction == "backward":
+        run_backward(args, w, b, x, idx, wts, y, inp, dev, stream)
+        return
 
     print(f"bench: warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):

@@ -71,8 +71,11 @@ def lib() -> ctypes.CDLL:
     L.ep_combine.argtypes = [ctypes.POINTER(ep_handle_t), P, P, P, P]
     L.ep_read_status.argtypes = [P, P]
     L.ep_workspace_init.argtypes = [P, S, P]
+    L.ep_dispatch_backward.argtypes = [ctypes.POINTER(ep_handle_t), P, P, P]
+    L.ep_combine_backward.argtypes = [ctypes.POINTER(ep_handle_t), P, P, P, P, P, P]
     for f in ("ep_layout_workspace_bytes", "ep_recv_capacity_rows", "ep_get_dispatch_layout",
-              "ep_dispatch", "ep_combine", "ep_read_status", "ep_workspace_init"):
+              "ep_dispatch", "ep_combine", "ep_read_status", "ep_workspace_init",
+              "ep_dispatch_backward", "ep_combine_backward"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -207,6 +210,41 @@ def ep_combine(handle: ep_handle_t, expert_out, topk_weights, out, stream=None):
     _check(st, "ep_combine")
 
 
+def _rows_tensor(t, rows, H, name):
+    import torch
+
+    if t is None or t.dim() != 2 or t.shape[1] != H or t.shape[0] < rows:
+        raise ValueError(f"{name} must be bf16 [>= {rows}, {H}]")
+    if t.numel() == 0:
+        return None
+    return _ptr(t, torch.bfloat16, name=name)
+
+
+def ep_dispatch_backward(handle: ep_handle_t, grad_recv_x, grad_x, stream=None):
+    import torch
+
+    c = handle.config
+    st = lib().ep_dispatch_backward(
+        ctypes.byref(handle), _rows_tensor(grad_recv_x, handle.capacity, c.hidden, "grad_recv_x"),
+        _ptr(grad_x, torch.bfloat16, (c.num_tokens, c.hidden), "grad_x"), _stream(stream))
+    _check(st, "ep_dispatch_backward")
+
+
+def ep_combine_backward(handle: ep_handle_t, grad_out, topk_weights, expert_out, grad_expert_out,
+                        grad_weights, stream=None):
+    import torch
+
+    c = handle.config
+    T, H, k = c.num_tokens, c.hidden, c.num_topk
+    st = lib().ep_combine_backward(
+        ctypes.byref(handle), _ptr(grad_out, torch.bfloat16, (T, H), "grad_out"),
+        _ptr(topk_weights, torch.float32, (T, k), "topk_weights"),
+        None if expert_out is None else _rows_tensor(expert_out, handle.capacity, H, "expert_out"),
+        _rows_tensor(grad_expert_out, handle.capacity, H, "grad_expert_out"),
+        _ptr(grad_weights, torch.float32, (T, k), "grad_weights"), _stream(stream))
+    _check(st, "ep_combine_backward")
+
+
 def make_handle(num_tokens, hidden, num_topk, capacity, tok_slot_row, row_src=None,
                 expert_offsets=None, num_experts=None, num_ranks=1, expert_alignment=1):
     """Build an ep_handle_t around existing device arrays (combine only reads
@@ -289,6 +327,25 @@ class EpBuffers:
         out = self.out if out is None else out
         ep_combine(self.handle, expert_out, topk_weights, out, stream=stream)
         return out
+
+    def dispatch_backward(self, grad_recv_x, grad_x=None, stream=None):
+        import torch
+
+        if grad_x is None:
+            grad_x = torch.empty_like(self.out)
+        ep_dispatch_backward(self.handle, grad_recv_x, grad_x, stream=stream)
+        return grad_x
+
+    def combine_backward(self, grad_out, topk_weights, expert_out, grad_expert_out=None,
+                         grad_weights=None, stream=None):
+        import torch
+
+        if grad_expert_out is None:
+            grad_expert_out = torch.empty((self.capacity, self.cfg.hidden), dtype=torch.bfloat16,
+                                          device=grad_out.device)
+        ep_combine_backward(self.handle, grad_out, topk_weights, expert_out, grad_expert_out,
+                            grad_weights, stream=stream)
+        return grad_expert_out
 
     def check_status(self, stream=None):
         ep_read_status(self.status, stream=stream)

@@ -229,4 +229,52 @@ ep_status_t ep_combine(const ep_handle_t *handle, const uint16_t *expert_out,
   return EP_OK;
 }
 
+ep_status_t ep_dispatch_backward(const ep_handle_t *handle, const uint16_t *grad_recv_x,
+                                 uint16_t *grad_x, hipStream_t stream) {
+  if (handle == nullptr) return fail(EP_ERR_INVALID_ARG, "handle is NULL");
+  ep_status_t st = check_config(&handle->config);
+  if (st != EP_OK) return st;
+  if (handle->capacity < 0 || handle->capacity >= INT32_MAX)
+    return fail(EP_ERR_INVALID_ARG, "handle capacity %lld invalid",
+                (long long)handle->capacity);
+  if (handle->config.num_tokens > 0 &&
+      (handle->tok_slot_row == nullptr || grad_x == nullptr ||
+       (handle->capacity > 0 && grad_recv_x == nullptr)))
+    return fail(EP_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(grad_recv_x) || !aligned16(grad_x))
+    return fail(EP_ERR_INVALID_ARG, "grad_recv_x and grad_x must be 16-byte aligned");
+  hipError_t err = ep::launch_combine(dims_of(&handle->config), handle->capacity, grad_recv_x,
+                                      handle->tok_slot_row, nullptr, grad_x, stream);
+  if (err != hipSuccess) return hip_fail(err, "dispatch backward launch");
+  return EP_OK;
+}
+
+ep_status_t ep_combine_backward(const ep_handle_t *handle, const uint16_t *grad_out,
+                                const float *topk_weights, const uint16_t *expert_out,
+                                uint16_t *grad_expert_out, float *grad_weights,
+                                hipStream_t stream) {
+  if (handle == nullptr) return fail(EP_ERR_INVALID_ARG, "handle is NULL");
+  ep_status_t st = check_config(&handle->config);
+  if (st != EP_OK) return st;
+  if (handle->capacity < 0 || handle->capacity >= INT32_MAX)
+    return fail(EP_ERR_INVALID_ARG, "handle capacity %lld invalid",
+                (long long)handle->capacity);
+  const bool empty = handle->config.num_tokens == 0;
+  if ((!empty && (handle->tok_slot_row == nullptr || grad_out == nullptr)) ||
+      (handle->capacity > 0 && grad_expert_out == nullptr) ||
+      (grad_weights != nullptr && !empty && expert_out == nullptr))
+    return fail(EP_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (handle->config.expert_alignment > 1 &&
+      (handle->row_src == nullptr || handle->expert_offsets == nullptr))
+    return fail(EP_ERR_INVALID_ARG,
+                "with expert_alignment > 1 the handle needs row_src and expert_offsets");
+  if (!aligned16(grad_out) || !aligned16(expert_out) || !aligned16(grad_expert_out))
+    return fail(EP_ERR_INVALID_ARG, "grad_out, expert_out and grad_expert_out must be 16-byte aligned");
+  hipError_t err = ep::launch_combine_backward(
+      dims_of(&handle->config), handle->capacity, grad_out, handle->tok_slot_row, topk_weights,
+      expert_out, grad_expert_out, grad_weights, handle->expert_offsets, handle->row_src, stream);
+  if (err != hipSuccess) return hip_fail(err, "combine backward launch");
+  return EP_OK;
+}
+
 }  // extern "C"

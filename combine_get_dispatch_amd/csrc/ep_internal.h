@@ -58,4 +58,10 @@ hipError_t launch_combine(const Dims &d, int64_t capacity, const uint16_t *exper
                           const int32_t *tok_slot_row, const float *topk_weights,
                           uint16_t *out, hipStream_t stream);
 
+hipError_t launch_combine_backward(const Dims &d, int64_t capacity, const uint16_t *grad_out,
+                                   const int32_t *tok_slot_row, const float *topk_weights,
+                                   const uint16_t *expert_out, uint16_t *grad_expert_out,
+                                   float *grad_weights, const int32_t *expert_offsets,
+                                   const int32_t *row_src, hipStream_t stream);
+
 }  // namespace ep

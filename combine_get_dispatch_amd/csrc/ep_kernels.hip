@@ -569,6 +569,102 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Backward of combine ("Deep Dive - DeepEP", "Combine: reverse routing plus
+// reduction": backward duality, and the gate gradient the autograd wrapper
+// still owes).  One wave per token walks the whole row in 512-column steps:
+//   grad_expert_out[row_j, c] = bf16(w[t,j] * grad_out[t,c])
+//   grad_w[t,j]               = sum_c expert_out[row_j, c] * grad_out[t,c]
+// Each lane accumulates its columns' products in fp32 in a fixed order and
+// an xor butterfly adds the 64 lane sums, so every run gives the same bits.
+// ---------------------------------------------------------------------------
+
+template <int K>
+__global__ __launch_bounds__(kBlock) void combine_backward_kernel(
+    Dims d, int64_t capacity, const uint16_t *__restrict__ grad_out,
+    const int32_t *__restrict__ tok_slot_row, const float *__restrict__ topk_weights,
+    const uint16_t *__restrict__ expert_out, uint16_t *__restrict__ grad_expert_out,
+    float *__restrict__ grad_weights) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int t = uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
+  if (t >= d.T) return;
+  const int64_t H = d.H;
+  const bool want_gate = grad_weights != nullptr;
+
+  int32_t row = -1;
+  float gate = 1.0f;
+  if (lane < d.k) {
+    const int32_t r = tok_slot_row[(int64_t)t * d.k + lane];
+    if (r >= 0 && r < capacity) row = r;
+    if (topk_weights != nullptr) gate = topk_weights[(int64_t)t * d.k + lane];
+  }
+  int32_t rows[K];
+  float gates[K];
+  float dot[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    rows[j] = j < d.k ? lane_value(row, j) : -1;
+    gates[j] = j < d.k ? lane_value_f(gate, j) : 0.0f;
+    dot[j] = 0.0f;
+  }
+
+  for (int64_t col = lane * 8; col < H; col += kCombineCols) {
+    const uint4 gv = *reinterpret_cast<const uint4 *>(grad_out + (int64_t)t * H + col);
+    const float g[8] = {bf16_lo(gv.x), bf16_hi(gv.x), bf16_lo(gv.y), bf16_hi(gv.y),
+                        bf16_lo(gv.z), bf16_hi(gv.z), bf16_lo(gv.w), bf16_hi(gv.w)};
+    uint4 yv[K];
+    if (want_gate) {
+#pragma unroll
+      for (int j = 0; j < K; ++j)
+        if (rows[j] >= 0) yv[j] = load_stream(expert_out + (int64_t)rows[j] * H + col);
+    }
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      if (rows[j] < 0) continue;
+      uint4 o;
+      o.x = pack_bf16(gates[j] * g[0], gates[j] * g[1]);
+      o.y = pack_bf16(gates[j] * g[2], gates[j] * g[3]);
+      o.z = pack_bf16(gates[j] * g[4], gates[j] * g[5]);
+      o.w = pack_bf16(gates[j] * g[6], gates[j] * g[7]);
+      store_stream(grad_expert_out + (int64_t)rows[j] * H + col, o);
+      if (want_gate) {
+        const uint32_t w4[4] = {yv[j].x, yv[j].y, yv[j].z, yv[j].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          dot[j] = __builtin_fmaf(bf16_lo(w4[i]), g[2 * i], dot[j]);
+          dot[j] = __builtin_fmaf(bf16_hi(w4[i]), g[2 * i + 1], dot[j]);
+        }
+      }
+    }
+  }
+
+  if (want_gate) {
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      float v = dot[j];
+#pragma unroll
+      for (int m = kWave / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+      if (lane == 0 && j < d.k) grad_weights[(int64_t)t * d.k + j] = rows[j] >= 0 ? v : 0.0f;
+    }
+  }
+}
+
+// Alignment padding rows of a gradient w.r.t. the receive buffer get zeros
+// (one workgroup per expert; padding rows are those without a source).
+__global__ __launch_bounds__(kBlock) void zero_padding_rows_kernel(
+    Dims d, const int32_t *__restrict__ expert_offsets, const int32_t *__restrict__ row_src,
+    int64_t capacity, uint16_t *__restrict__ rows_out) {
+  const int e = blockIdx.x;
+  int64_t last = expert_offsets[e + 1];
+  if (last > capacity) last = capacity;
+  const int64_t H = d.H;
+  for (int64_t r = expert_offsets[e]; r < last; ++r) {
+    if (row_src[r] >= 0) continue;
+    uint4 *dst = reinterpret_cast<uint4 *>(rows_out + r * H);
+    for (int64_t i = threadIdx.x; i < H / 8; i += kBlock) dst[i] = make_uint4(0, 0, 0, 0);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 
@@ -666,6 +762,32 @@ hipError_t launch_combine(const Dims &d, int64_t capacity, const uint16_t *exper
     hipLaunchKernelGGL((combine_kernel<false, 8>), grid, dim3(kBlock), 0, stream, d, nchunks,
                        capacity, expert_out, tok_slot_row, topk_weights, out);
   return hipGetLastError();
+}
+
+}  // namespace ep
+
+namespace ep {
+
+hipError_t launch_combine_backward(const Dims &d, int64_t capacity, const uint16_t *grad_out,
+                                   const int32_t *tok_slot_row, const float *topk_weights,
+                                   const uint16_t *expert_out, uint16_t *grad_expert_out,
+                                   float *grad_weights, const int32_t *expert_offsets,
+                                   const int32_t *row_src, hipStream_t stream) {
+  if (d.T > 0) {
+    const dim3 grid((unsigned)((d.T + kWavesPerBlock - 1) / kWavesPerBlock));
+    auto kernel = d.k <= 8 ? combine_backward_kernel<8>
+                           : (d.k <= 16 ? combine_backward_kernel<16> : combine_backward_kernel<32>);
+    hipLaunchKernelGGL(kernel, grid, dim3(kBlock), 0, stream, d, capacity, grad_out, tok_slot_row,
+                       topk_weights, expert_out, grad_expert_out, grad_weights);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (d.A > 1) {
+    hipLaunchKernelGGL(zero_padding_rows_kernel, dim3(d.E), dim3(kBlock), 0, stream, d,
+                       expert_offsets, row_src, capacity, grad_expert_out);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 }  // namespace ep

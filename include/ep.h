@@ -223,6 +223,51 @@ ep_status_t ep_dispatch(const ep_config_t *cfg, ep_dtype_t recv_dtype, const uin
 ep_status_t ep_combine(const ep_handle_t *handle, const uint16_t *expert_out,
                        const float *topk_weights, uint16_t *out, hipStream_t stream);
 
+/*
+ * Backward of dispatch: the transpose of the unweighted dispatch ("Deep
+ * Dive - DeepEP", "Combine: reverse routing plus reduction": for the
+ * unweighted route, copying a row forward becomes summing its gradients
+ * backward).  For each token t and channel c,
+ *     grad_x[t, c] = bf16( sum_{j = 0..k-1, row_j >= 0} grad_recv_x[row_j, c] )
+ * accumulated in fp32 in slot order from +0 and rounded once (the same
+ * arithmetic as ep_combine with NULL weights).  A gate multiplied in by the
+ * caller before combine belongs to the caller's own backward.
+ *
+ *   handle       from ep_dispatch
+ *   grad_recv_x  [capacity, H] bf16: gradient w.r.t. the receive rows
+ *   grad_x       [T, H] bf16 out: gradient w.r.t. x
+ */
+ep_status_t ep_dispatch_backward(const ep_handle_t *handle, const uint16_t *grad_recv_x,
+                                 uint16_t *grad_x, hipStream_t stream);
+
+/*
+ * Backward of combine ("Deep Dive - DeepEP", "Combine: reverse routing plus
+ * reduction": backward duality, plus the gate gradient).  For each valid
+ * selection (t, j) with row p = tok_slot_row[t, j]:
+ *     grad_expert_out[p, c] = bf16( fp32(w[t, j] * grad_out[t, c]) )
+ *     grad_weights[t, j]    = sum_c expert_out[p, c] * grad_out[t, c]
+ * The row gradient applies the gate once (w = 1 when topk_weights is NULL,
+ * which makes it a copy of grad_out[t]).  The gate gradient is an fp32 sum
+ * in a fixed order (deterministic); its error against the exact sum is at
+ * most H * 2^-24 / (1 - H * 2^-24) * sum_c |expert_out[p,c] * grad_out[t,c]|.
+ * Unused slots get grad_weights 0.  Alignment padding rows of
+ * grad_expert_out are zero-filled; rows at or past expert_offsets[E] are
+ * not written.
+ *
+ *   handle           from ep_dispatch (with A > 1 it must carry row_src and
+ *                    expert_offsets)
+ *   grad_out         [T, H] bf16: gradient w.r.t. the combined rows
+ *   topk_weights     [T, k] fp32 gates used in the forward combine, or NULL
+ *   expert_out       [capacity, H] bf16 forward expert outputs (needed only
+ *                    for grad_weights)
+ *   grad_expert_out  [capacity, H] bf16 out
+ *   grad_weights     [T, k] fp32 out, or NULL to skip the gate gradient
+ */
+ep_status_t ep_combine_backward(const ep_handle_t *handle, const uint16_t *grad_out,
+                                const float *topk_weights, const uint16_t *expert_out,
+                                uint16_t *grad_expert_out, float *grad_weights,
+                                hipStream_t stream);
+
 /* Synchronises `stream`, reads the device status word and returns the
  * first error it holds (route, then capacity, then workspace) or EP_OK. */
 ep_status_t ep_read_status(const int32_t *status, hipStream_t stream);
