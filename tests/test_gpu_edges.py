@@ -296,3 +296,64 @@ def test_layout_tile_boundaries(T, E, k):
     assert np.array_equal(dg["tok_slot_row"], do["tok_slot_row"])
     used = int(lo["expert_offsets"][-1])
     assert np.array_equal(dg["row_src"][:used], do["row_src"][:used])
+
+
+def test_cached_route_replay():
+    """One layout, several dispatches of new hidden states over the same route
+    (and both payload types), each combined through its handle: the layout's
+    workspace is the cached route ("Deep Dive - DeepEP", "EPHandle")."""
+    rng = np.random.default_rng(21)
+    T, H, k, E, R = 900, 256, 4, 32, 4
+    idx = W.random_routes(rng, T, E, k, mask_prob=0.1)
+    w = rng.random((T, k)).astype(np.float32)
+    b16 = ep.EpBuffers(T, H, k, E, R, 1)
+    idx_d, w_d = dev(idx), dev(w)
+    b16.layout(idx_d)
+    b8 = ep.EpBuffers(T, H, k, E, R, 1, fp8=True)
+    b8.workspace = b16.workspace  # same route, same workspace
+    b8.expert_offsets = b16.expert_offsets
+    for rep in range(3):
+        say(f"replay {rep}")
+        x = W.normal_bf16(rng, (T, H), 1.0 + rep)
+        b16.dispatch(dev_bf16(x), idx_d, w_d)
+        b8.dispatch(dev_bf16(x), idx_d, w_d)
+        y = W.normal_bf16(rng, (T * k, H))
+        out = b16.combine(dev_bf16(y), w_d)
+        b16.check_status()
+        d16 = oracle.dispatch(x, idx, w, E, R)
+        d8 = oracle.dispatch(x, idx, w, E, R, fp8=True)
+        used = int(b16.expert_offsets[-1].item())
+        assert np.array_equal(host_bf16(b16.recv_x[:used]), d16["recv_x"][:used])
+        assert np.array_equal(b8.recv_x[:used].cpu().numpy(), d8["recv_x"][:used])
+        assert np.array_equal(b8.recv_scales[:used].cpu().numpy(), d8["recv_scales"][:used])
+        ref, _ = oracle.combine(y, d16["tok_slot_row"], w)
+        assert np.array_equal(host_bf16(out), ref)
+
+
+def test_no_sync_valid_ranges():
+    """Without reading counts back: the receive buffer is sized for the worst
+    case, and the device-side offsets and counts tell the caller which rows
+    are data ([off[e], off[e] + cnt[e])) and which are zero padding
+    ("Deep Dive - DeepEP", "Dispatch: layout, move, and epilogue")."""
+    rng = np.random.default_rng(22)
+    T, H, k, E, R, A = 700, 128, 3, 24, 4, 8
+    idx = W.random_routes(rng, T, E, k, mask_prob=0.2)
+    x = W.normal_bf16(rng, (T, H))
+    b = ep.EpBuffers(T, H, k, E, R, A)
+    b.recv_x.fill_(3.0)
+    b.row_src.fill_(-7)
+    idx_d = dev(idx)
+    b.layout(idx_d)               # no sync
+    b.dispatch(dev_bf16(x), idx_d, None)
+    b.check_status()
+    off = b.expert_offsets.cpu().numpy()
+    cnt = b.num_tokens_per_expert.cpu().numpy()
+    rs = b.row_src.cpu().numpy()
+    rx = host_bf16(b.recv_x)
+    for e in range(E):
+        data = np.arange(off[e], off[e] + cnt[e])
+        pad = np.arange(off[e] + cnt[e], off[e + 1])
+        assert np.all(rs[data] >= 0) and np.all(idx.reshape(-1)[rs[data]] == e)
+        assert np.all(rs[pad] == -1) and np.all(rx[pad] == 0)
+    assert off[-1] <= b.capacity
+    assert np.all(rs[off[-1]:] == -7)  # past the last segment nothing is written
