@@ -35,11 +35,14 @@ KERNEL_SOURCES = [os.path.join(ROOT, "combine_get_dispatch_amd", "csrc", f)
                   for f in ("ep_kernels.hip", "ep_internal.h")]
 
 
-def algorithmic_bytes(w, M: int) -> dict:
+def algorithmic_bytes(w, M: int, fp8_input: bool = False) -> dict:
+    """fp8_input: rows arrive as E4M3 codes + scales (read once: H + H/32
+    bytes per token instead of 2H)."""
     T, H, k, E, R = w.num_tokens, w.hidden, w.num_topk, w.num_experts, w.num_ranks
     row = (H + 4 * (H // 128)) if w.fp8 else 2 * H
     layout = T * k * 4 + T * R + 4 * (E + R) + 4 * (E + R + 2)
-    dispatch = T * H * 2 + T * k * 8 + M * row + M * 8 + T * k * 4
+    x_bytes = T * (H + 4 * (H // 128)) if fp8_input else T * H * 2
+    dispatch = x_bytes + T * k * 8 + M * row + M * 8 + T * k * 4
     combine = M * 2 * H + T * k * 8 + T * 2 * H
     return dict(layout=layout, dispatch=dispatch, combine=combine,
                 total=layout + dispatch + combine)
@@ -254,6 +257,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter scale)")
+    ap.add_argument("--fp8-input", action="store_true",
+                    help="dispatch pre-quantised rows (E4M3 codes + scales) instead of bf16")
     ap.add_argument("--direction", choices=("forward", "backward"), default="forward",
                     help="backward times ep_dispatch_backward + ep_combine_backward (its own "
                          "JSON line, not the forward metric)")
@@ -297,10 +302,24 @@ def main():
     b = ep.EpBuffers(w.num_tokens, w.hidden, w.num_topk, w.num_experts, w.num_ranks,
                      w.alignment, fp8=w.fp8, device=dev)
     stream = torch.cuda.current_stream()
+    if args.fp8_input and not w.fp8:
+        raise SystemExit("--fp8-input needs an FP8 workload (prefill or large)")
+    if args.fp8_input:
+        rng = np.random.default_rng(500 + w.seed)
+        codes = torch.from_numpy(rng.integers(0, 256, (w.num_tokens, w.hidden),
+                                              dtype=np.uint8)).to(dev)
+        scales = torch.from_numpy(rng.random((w.num_tokens, w.hidden // 128))
+                                  .astype(np.float32)).to(dev)
+
+    def do_dispatch():
+        if args.fp8_input:
+            b.dispatch_fp8_input(codes, scales, idx, wts)
+        else:
+            b.dispatch(x, idx, wts)
 
     def step():
         b.layout(idx)
-        b.dispatch(x, idx, wts)
+        do_dispatch()
         b.combine(y, wts)
 
     if args.direction == "backward":
@@ -332,7 +351,7 @@ def main():
     ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)] for n in names}
     for i in range(args.steps):
-        for n, fn in zip(names, (lambda: b.layout(idx), lambda: b.dispatch(x, idx, wts),
+        for n, fn in zip(names, (lambda: b.layout(idx), do_dispatch,
                                  lambda: b.combine(y, wts))):
             ev[n][i][0].record(stream)
             fn()
@@ -349,12 +368,12 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    by = algorithmic_bytes(w, M)
+    by = algorithmic_bytes(w, M, args.fp8_input)
     step_s = ms_per_step / 1e3
     gbps = by["total"] / step_s / 1e9
     dom = max(("dispatch", "combine"), key=lambda n: per_us[n])
     achieved = by[dom] / (per_us[dom] / 1e6) / 1e9
-    traffic = load_traffic(w.name, dom)
+    traffic = None if args.fp8_input else load_traffic(w.name, dom)
     rec = {
         "metric": METRIC,
         "value": round(gbps, 1),
@@ -374,7 +393,8 @@ def main():
                                f"{'FP8 E4M3' if w.fp8 else 'bf16'} dispatch, bf16 combine",
                    "tokens": w.num_tokens, "hidden": w.hidden, "topk": w.num_topk,
                    "experts": w.num_experts, "logical_ranks": w.num_ranks,
-                   "dispatch_payload": "fp8_e4m3" if w.fp8 else "bf16",
+                   "dispatch_payload": ("fp8_e4m3 (pre-quantised input)" if args.fp8_input
+                                        else "fp8_e4m3" if w.fp8 else "bf16"),
                    "valid_selections": M},
         "pct_of_peak": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
         "tokens_per_s": round(w.num_tokens / step_s, 1),
@@ -393,7 +413,7 @@ def main():
             "traffic": traffic,
         },
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.fp8_input:
         print("bench: CPU oracle baseline", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget)
     print(json.dumps(rec), flush=True)

@@ -72,10 +72,12 @@ def lib() -> ctypes.CDLL:
     L.ep_read_status.argtypes = [P, P]
     L.ep_workspace_init.argtypes = [P, S, P]
     L.ep_dispatch_backward.argtypes = [ctypes.POINTER(ep_handle_t), P, P, P]
+    L.ep_dispatch_fp8_input.argtypes = [cfgp, P, P, P, P, P, P, S, i64, P, P, P, P, P, P,
+                                        ctypes.POINTER(ep_handle_t), P]
     L.ep_combine_backward.argtypes = [ctypes.POINTER(ep_handle_t), P, P, P, P, P, P]
     for f in ("ep_layout_workspace_bytes", "ep_recv_capacity_rows", "ep_get_dispatch_layout",
               "ep_dispatch", "ep_combine", "ep_read_status", "ep_workspace_init",
-              "ep_dispatch_backward", "ep_combine_backward"):
+              "ep_dispatch_backward", "ep_combine_backward", "ep_dispatch_fp8_input"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -190,6 +192,31 @@ def ep_dispatch(cfg, recv_dtype, x, topk_idx, topk_weights, expert_offsets, work
         _ptr(row_src, torch.int32, (cap,), "row_src"),
         _ptr(status, torch.int32, (1,), "status"), ctypes.byref(handle), _stream(stream))
     _check(st, "ep_dispatch")
+    return handle
+
+
+def ep_dispatch_fp8_input(cfg, x_codes, x_scales, topk_idx, topk_weights, expert_offsets,
+                          workspace, capacity, recv_x, recv_scales, recv_weights, tok_slot_row,
+                          row_src, status, stream=None) -> ep_handle_t:
+    import torch
+
+    T, H, k, E = cfg.num_tokens, cfg.hidden, cfg.num_topk, cfg.num_experts
+    cap = int(capacity)
+    handle = ep_handle_t()
+    st = lib().ep_dispatch_fp8_input(
+        ctypes.byref(cfg), _ptr(x_codes, torch.uint8, (T, H), "x_codes"),
+        _ptr(x_scales, torch.float32, (T, H // 128), "x_scales"),
+        _ptr(topk_idx, torch.int32, (T, k), "topk_idx"),
+        _ptr(topk_weights, torch.float32, (T, k), "topk_weights"),
+        _ptr(expert_offsets, torch.int32, (E + 1,), "expert_offsets"),
+        _ptr(workspace, torch.uint8, name="workspace"), workspace.numel(), cap,
+        _ptr(recv_x, torch.uint8, (cap, H), "recv_x"),
+        _ptr(recv_scales, torch.float32, (cap, H // 128), "recv_scales"),
+        _ptr(recv_weights, torch.float32, (cap,), "recv_weights"),
+        _ptr(tok_slot_row, torch.int32, (T, k), "tok_slot_row"),
+        _ptr(row_src, torch.int32, (cap,), "row_src"),
+        _ptr(status, torch.int32, (1,), "status"), ctypes.byref(handle), _stream(stream))
+    _check(st, "ep_dispatch_fp8_input")
     return handle
 
 
@@ -321,6 +348,16 @@ class EpBuffers:
                                   self.capacity, self.recv_x, self.recv_scales,
                                   self.recv_weights if topk_weights is not None else None,
                                   self.tok_slot_row, self.row_src, self.status, stream=stream)
+        return self.handle
+
+    def dispatch_fp8_input(self, x_codes, x_scales, topk_idx, topk_weights, stream=None):
+        if not self.fp8:
+            raise ValueError("dispatch_fp8_input needs buffers built with fp8=True")
+        self.handle = ep_dispatch_fp8_input(
+            self.cfg, x_codes, x_scales, topk_idx, topk_weights, self.expert_offsets,
+            self.workspace, self.capacity, self.recv_x, self.recv_scales,
+            self.recv_weights if topk_weights is not None else None, self.tok_slot_row,
+            self.row_src, self.status, stream=stream)
         return self.handle
 
     def combine(self, expert_out, topk_weights, out=None, stream=None):

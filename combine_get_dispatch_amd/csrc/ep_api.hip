@@ -209,6 +209,49 @@ ep_status_t ep_dispatch(const ep_config_t *cfg, ep_dtype_t recv_dtype, const uin
   return EP_OK;
 }
 
+ep_status_t ep_dispatch_fp8_input(const ep_config_t *cfg, const uint8_t *x_codes,
+                                  const float *x_scales, const int32_t *topk_idx,
+                                  const float *topk_weights, const int32_t *expert_offsets,
+                                  const void *workspace, size_t workspace_bytes,
+                                  int64_t capacity, uint8_t *recv_x, float *recv_scales,
+                                  float *recv_weights, int32_t *tok_slot_row, int32_t *row_src,
+                                  int32_t *status, ep_handle_t *handle_host,
+                                  hipStream_t stream) {
+  ep_status_t st = check_config(cfg);
+  if (st != EP_OK) return st;
+  if (cfg->hidden % 128 != 0)
+    return fail(EP_ERR_INVALID_ARG, "FP8 rows need hidden %% 128 == 0 (hidden %d)", cfg->hidden);
+  if (capacity < 0 || capacity >= INT32_MAX)
+    return fail(EP_ERR_INVALID_ARG, "capacity %lld outside [0, 2^31 - 1)", (long long)capacity);
+  const bool empty = cfg->num_tokens == 0;
+  if ((!empty && (x_codes == nullptr || x_scales == nullptr || topk_idx == nullptr ||
+                  tok_slot_row == nullptr)) ||
+      expert_offsets == nullptr || workspace == nullptr || status == nullptr ||
+      (capacity > 0 && (recv_x == nullptr || recv_scales == nullptr || row_src == nullptr)))
+    return fail(EP_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(x_codes) || !aligned16(recv_x))
+    return fail(EP_ERR_INVALID_ARG, "x_codes and recv_x must be 16-byte aligned");
+  const size_t need =
+      ep::workspace_layout(cfg->num_tokens, cfg->num_topk, cfg->num_experts, cfg->num_ranks)
+          .total;
+  if (workspace_bytes < need)
+    return fail(EP_ERR_INVALID_ARG, "workspace has %zu bytes, dispatch needs %zu",
+                workspace_bytes, need);
+  hipError_t err = ep::launch_dispatch_fp8_input(
+      dims_of(cfg), x_codes, x_scales, topk_idx, topk_weights, expert_offsets,
+      static_cast<const char *>(workspace), capacity, recv_x, recv_scales, recv_weights,
+      tok_slot_row, row_src, status, stream);
+  if (err != hipSuccess) return hip_fail(err, "dispatch launch");
+  if (handle_host != nullptr) {
+    handle_host->config = *cfg;
+    handle_host->capacity = capacity;
+    handle_host->tok_slot_row = tok_slot_row;
+    handle_host->row_src = row_src;
+    handle_host->expert_offsets = expert_offsets;
+  }
+  return EP_OK;
+}
+
 ep_status_t ep_combine(const ep_handle_t *handle, const uint16_t *expert_out,
                        const float *topk_weights, uint16_t *out, hipStream_t stream) {
   if (handle == nullptr) return fail(EP_ERR_INVALID_ARG, "handle is NULL");

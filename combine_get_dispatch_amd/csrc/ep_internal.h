@@ -54,6 +54,13 @@ hipError_t launch_dispatch(const Dims &d, bool fp8, const uint16_t *x, const int
                            float *recv_weights, int32_t *tok_slot_row, int32_t *row_src,
                            int32_t *status, hipStream_t stream);
 
+hipError_t launch_dispatch_fp8_input(const Dims &d, const uint8_t *x_codes, const float *x_scales,
+                                     const int32_t *topk_idx, const float *topk_weights,
+                                     const int32_t *expert_offsets, const char *ws,
+                                     int64_t capacity, uint8_t *recv_x, float *recv_scales,
+                                     float *recv_weights, int32_t *tok_slot_row,
+                                     int32_t *row_src, int32_t *status, hipStream_t stream);
+
 hipError_t launch_combine(const Dims &d, int64_t capacity, const uint16_t *expert_out,
                           const int32_t *tok_slot_row, const float *topk_weights,
                           uint16_t *out, hipStream_t stream);

@@ -457,6 +457,49 @@ __global__ __launch_bounds__(kBlock) void dispatch_fp8_kernel(
   }
 }
 
+// Pre-quantised rows ("Deep Dive - DeepEP", "Dispatch: layout, move, and
+// epilogue": hidden states may arrive as FP8 values plus scale factors):
+// the token's E4M3 codes and per-128 scales are copied unchanged to each of
+// its receive rows.  Each lane moves 16 code bytes (a block is 8 lanes).
+__global__ __launch_bounds__(kBlock) void dispatch_fp8_input_kernel(
+    Dims d, int32_t nchunks, const uint8_t *__restrict__ x_codes,
+    const float *__restrict__ x_scales, const int32_t *__restrict__ topk_idx,
+    const float *__restrict__ topk_weights, const int32_t *__restrict__ expert_offsets,
+    const int32_t *__restrict__ header, const int32_t *__restrict__ tile_base,
+    const int32_t *__restrict__ slot_rank, int64_t capacity, uint8_t *__restrict__ recv_x,
+    float *__restrict__ recv_scales, float *__restrict__ recv_weights,
+    int32_t *__restrict__ tok_slot_row, int32_t *__restrict__ row_src,
+    int32_t *__restrict__ status) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int item = uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
+  if (item >= d.T * nchunks) return;
+  if (!workspace_ok(header, d)) {
+    if (lane == 0) flag(status, EP_STATUS_BIT_WORKSPACE);
+    return;
+  }
+  const int64_t t = item / nchunks;
+  const int chunk = item - (int)t * nchunks;
+  const int32_t row = selection_row(d, t, lane, chunk == 0, topk_idx, topk_weights,
+                                    expert_offsets, tile_base, slot_rank, capacity,
+                                    recv_weights, tok_slot_row, row_src, status);
+  const int64_t H = d.H;
+  const int64_t nblk = H / 128;
+  const int col = chunk * kChunkCols + lane * 16;
+  const bool in = col < H;
+  uint4 q = make_uint4(0, 0, 0, 0);
+  float scale = 0.0f;
+  if (in) {
+    q = *reinterpret_cast<const uint4 *>(x_codes + t * H + col);
+    if ((lane & 7) == 0) scale = x_scales[t * nblk + col / 128];
+  }
+  for (int j = 0; j < d.k; ++j) {
+    const int32_t r = lane_value(row, j);
+    if (r < 0 || !in) continue;
+    store_stream(recv_x + (int64_t)r * H + col, q);
+    if ((lane & 7) == 0) recv_scales[(int64_t)r * nblk + col / 128] = scale;
+  }
+}
+
 // Alignment padding rows of expert e (one workgroup per expert): zero
 // payload, zero scale, zero gate, no source ("Deep Dive - DeepEP",
 // "Dispatch: layout, move, and epilogue": padding is not a token).
@@ -743,6 +786,37 @@ hipError_t launch_dispatch(const Dims &d, bool fp8, const uint16_t *x, const int
                        expert_offsets, reinterpret_cast<const int32_t *>(ws + w.cnt), capacity,
                        recv_x, recv_scales, topk_weights != nullptr ? recv_weights : nullptr,
                        row_src);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_dispatch_fp8_input(const Dims &d, const uint8_t *x_codes, const float *x_scales,
+                                     const int32_t *topk_idx, const float *topk_weights,
+                                     const int32_t *expert_offsets, const char *ws,
+                                     int64_t capacity, uint8_t *recv_x, float *recv_scales,
+                                     float *recv_weights, int32_t *tok_slot_row,
+                                     int32_t *row_src, int32_t *status, hipStream_t stream) {
+  const WorkspaceLayout w = workspace_layout(d.T, d.k, d.E, d.R);
+  const int32_t *header = reinterpret_cast<const int32_t *>(ws);
+  const int32_t *tile_base = reinterpret_cast<const int32_t *>(ws + w.tile_cnt);
+  const int32_t *slot_rank = reinterpret_cast<const int32_t *>(ws + w.slot_rank);
+  const int32_t nchunks = (d.H + kChunkCols - 1) / kChunkCols;
+  if (d.T > 0) {
+    const int64_t items = (int64_t)d.T * nchunks;
+    const dim3 grid((unsigned)((items + kWavesPerBlock - 1) / kWavesPerBlock));
+    hipLaunchKernelGGL(dispatch_fp8_input_kernel, grid, dim3(kBlock), 0, stream, d, nchunks,
+                       x_codes, x_scales, topk_idx, topk_weights, expert_offsets, header,
+                       tile_base, slot_rank, capacity, recv_x, recv_scales, recv_weights,
+                       tok_slot_row, row_src, status);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (d.A > 1) {
+    hipLaunchKernelGGL(pad_fill_kernel, dim3(d.E), dim3(kBlock), 0, stream, d, true,
+                       expert_offsets, reinterpret_cast<const int32_t *>(ws + w.cnt), capacity,
+                       static_cast<void *>(recv_x), recv_scales,
+                       topk_weights != nullptr ? recv_weights : nullptr, row_src);
     return hipGetLastError();
   }
   return hipSuccess;

@@ -204,6 +204,28 @@ ep_status_t ep_dispatch(const ep_config_t *cfg, ep_dtype_t recv_dtype, const uin
                         hipStream_t stream);
 
 /*
+ * Dispatch of rows that arrive already quantised ("Deep Dive - DeepEP",
+ * "Dispatch: layout, move, and epilogue": hidden states are BF16 or FP8
+ * values plus scale factors; "Precision: FP8 on the wire, BF16 for the
+ * reduction": one fp32 scale per 128 values).  Same placement, handle and
+ * padding as ep_dispatch with EP_DTYPE_FP8_E4M3, but the token's codes and
+ * scales are copied unchanged instead of being computed from bf16.
+ *
+ *   x_codes   [T, H] uint8 E4M3 codes (any byte value travels unchanged)
+ *   x_scales  [T, H/128] fp32
+ *   recv_x    [capacity, H] uint8 out; recv_scales [capacity, H/128] fp32 out
+ *   other arguments as for ep_dispatch (H % 128 == 0 required)
+ */
+ep_status_t ep_dispatch_fp8_input(const ep_config_t *cfg, const uint8_t *x_codes,
+                                  const float *x_scales, const int32_t *topk_idx,
+                                  const float *topk_weights, const int32_t *expert_offsets,
+                                  const void *workspace, size_t workspace_bytes,
+                                  int64_t capacity, uint8_t *recv_x, float *recv_scales,
+                                  float *recv_weights, int32_t *tok_slot_row, int32_t *row_src,
+                                  int32_t *status, ep_handle_t *handle_host,
+                                  hipStream_t stream);
+
+/*
  * Combine: expert-major rows back to token-major ("GPU microarchitecture:
  * DeepEP first principles", section 1.2), each gate applied exactly once
  * ("Deep Dive - DeepEP", "Combine: reverse routing plus reduction"):

@@ -78,6 +78,9 @@ def _load():
                                     i64, P, P, P, P, P]
     lib.oracle_combine.restype = ctypes.c_int
     lib.oracle_combine.argtypes = [i32, i32, i32, i64, P, P, P, P, P]
+    lib.oracle_dispatch_fp8_input.restype = ctypes.c_int
+    lib.oracle_dispatch_fp8_input.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, i64,
+                                              P, P, P, P, P]
     lib.oracle_dispatch_backward.restype = ctypes.c_int
     lib.oracle_dispatch_backward.argtypes = [i32, i32, i32, i64, P, P, P, P]
     lib.oracle_combine_backward.restype = ctypes.c_int
@@ -183,6 +186,34 @@ def dispatch(x_bits, topk_idx, topk_weights, num_experts: int, num_ranks: int,
                                  _ptr(row_src))
     if rc:
         raise OracleError(rc, "dispatch")
+    return dict(recv_x=recv_x, recv_scales=recv_scales, recv_weights=recv_weights,
+                tok_slot_row=tok_slot_row, row_src=row_src)
+
+
+def dispatch_fp8_input(codes, scales, topk_idx, topk_weights, num_experts: int, num_ranks: int,
+                       alignment: int = 1, capacity: int | None = None,
+                       fill_recv: int = 0) -> dict:
+    """Dispatch of pre-quantised rows: E4M3 codes (uint8 [T,H]) and fp32
+    scales [T,H/128] copied to the receive rows."""
+    q = _c(codes, np.uint8)
+    sc = _c(scales, np.float32)
+    idx = _c(topk_idx, np.int32)
+    T, H = q.shape
+    k = idx.shape[1]
+    w = None if topk_weights is None else _c(topk_weights, np.float32)
+    if capacity is None:
+        capacity = T * k + num_experts * (alignment - 1)
+    recv_x = np.full((capacity, H), fill_recv & 0xFF, np.uint8)
+    recv_scales = np.zeros((capacity, max(H // 128, 1)), np.float32)
+    recv_weights = np.zeros(capacity, np.float32) if w is not None else None
+    tok_slot_row = np.zeros((T, k), np.int32)
+    row_src = np.full(capacity, -2, np.int32)
+    rc = _load().oracle_dispatch_fp8_input(T, H, k, num_experts, num_ranks, alignment, _ptr(q),
+                                           _ptr(sc), _ptr(idx), _ptr(w), capacity,
+                                           _ptr(recv_x), _ptr(recv_scales), _ptr(recv_weights),
+                                           _ptr(tok_slot_row), _ptr(row_src))
+    if rc:
+        raise OracleError(rc, "dispatch_fp8_input")
     return dict(recv_x=recv_x, recv_scales=recv_scales, recv_weights=recv_weights,
                 tok_slot_row=tok_slot_row, row_src=row_src)
 

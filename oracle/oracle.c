@@ -298,6 +298,56 @@ int oracle_dispatch(int32_t T, int32_t H, int32_t k, int32_t E, int32_t R,
   return ORACLE_OK;
 }
 
+/* [DD] "Dispatch: layout, move, and epilogue" (pre-quantised input): the
+ * same stable placement as oracle_dispatch, with the token's codes and
+ * scales copied unchanged. */
+int oracle_dispatch_fp8_input(int32_t T, int32_t H, int32_t k, int32_t E, int32_t R,
+                              int32_t A, const uint8_t *x_codes, const float *x_scales,
+                              const int32_t *topk_idx, const float *topk_weights,
+                              int64_t capacity, uint8_t *recv_codes, float *recv_scales,
+                              float *recv_weights, int32_t *tok_slot_row, int32_t *row_src) {
+  int rc = check_sizes(T, k, E, R, A);
+  if (rc) return rc;
+  if (H < 128 || H % 128 != 0 || capacity < 0) return ORACLE_BAD_ARG;
+  int32_t *cnt = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
+  int32_t *off = (int32_t *)malloc(sizeof(int32_t) * (size_t)(E + 1));
+  int32_t *rank_cnt = (int32_t *)malloc(sizeof(int32_t) * (size_t)R);
+  int32_t *rank_off = (int32_t *)malloc(sizeof(int32_t) * (size_t)(R + 1));
+  uint8_t *in_rank = (uint8_t *)malloc((size_t)T * (size_t)R + 1);
+  int32_t *fill = (int32_t *)calloc((size_t)E, sizeof(int32_t));
+  rc = oracle_layout(T, k, E, R, A, topk_idx, rank_cnt, cnt, in_rank, off, rank_off);
+  if (rc == ORACLE_OK && off[E] > capacity) rc = ORACLE_NO_CAPACITY;
+  if (rc == ORACLE_OK) {
+    const int32_t nblk = H / 128;
+    for (int64_t t = 0; t < T; ++t) {
+      for (int j = 0; j < k; ++j) {
+        int32_t e = topk_idx[t * k + j];
+        if (e < 0) {
+          tok_slot_row[t * k + j] = -1;
+          continue;
+        }
+        int64_t p = off[e] + fill[e];
+        fill[e] += 1;
+        tok_slot_row[t * k + j] = (int32_t)p;
+        row_src[p] = (int32_t)(t * k + j);
+        if (recv_weights && topk_weights) recv_weights[p] = topk_weights[t * k + j];
+        memcpy(recv_codes + p * H, x_codes + t * H, (size_t)H);
+        memcpy(recv_scales + p * nblk, x_scales + t * nblk, sizeof(float) * (size_t)nblk);
+      }
+    }
+    for (int e = 0; e < E; ++e) {
+      for (int64_t p = (int64_t)off[e] + cnt[e]; p < off[e + 1]; ++p) {
+        row_src[p] = -1;
+        if (recv_weights && topk_weights) recv_weights[p] = 0.0f;
+        memset(recv_codes + p * H, 0, (size_t)H);
+        for (int b = 0; b < nblk; ++b) recv_scales[p * nblk + b] = 0.0f;
+      }
+    }
+  }
+  free(cnt); free(off); free(rank_cnt); free(rank_off); free(in_rank); free(fill);
+  return rc;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Combine                                                                   */
 /* ------------------------------------------------------------------------ */

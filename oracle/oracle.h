@@ -82,6 +82,18 @@ int oracle_combine(int32_t T, int32_t H, int32_t k, int64_t capacity,
                    const uint16_t *y, const int32_t *tok_slot_row,
                    const float *topk_weights, uint16_t *out, float *acc_out);
 
+/* Dispatch of rows that arrive already quantised ([DD] "Dispatch: layout,
+ * move, and epilogue": hidden states are BF16, or FP8 values plus scale
+ * factors).  The E4M3 codes x_codes [T,H] and the fp32 scales
+ * x_scales [T, H/128] are copied bit for bit to every receive row of the
+ * token, at the rows oracle_dispatch would use.  Padding rows get zero
+ * codes and zero scales. */
+int oracle_dispatch_fp8_input(int32_t T, int32_t H, int32_t k, int32_t E, int32_t R,
+                              int32_t A, const uint8_t *x_codes, const float *x_scales,
+                              const int32_t *topk_idx, const float *topk_weights,
+                              int64_t capacity, uint8_t *recv_codes, float *recv_scales,
+                              float *recv_weights, int32_t *tok_slot_row, int32_t *row_src);
+
 /* Backward of dispatch ([DD] "Combine: reverse routing plus reduction",
  * backward duality: for the unweighted route, copying a row forward becomes
  * summing its gradients backward):

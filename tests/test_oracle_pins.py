@@ -130,7 +130,6 @@ def test_fp8_row_bytes(golden):
     fx = golden("fp8_row_bytes.txt")
     H = fx.num("hidden", int)
     rng = np.random.default_rng(2)
-    x = bf16_bits_exact(np.zeros((1, H), np.float32)) | 0  # zeros
     x = (rng.standard_normal((1, H)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
     idx = np.array([[0]], np.int32)
     d = oracle.dispatch(x, idx, np.ones((1, 1), np.float32), 1, 1, fp8=True)
@@ -447,3 +446,35 @@ def test_adjoint_identity_fp64():
         t, j = divmod(int(s), k)
         rhs += float(np.dot(yf[p], np.float64(d["recv_weights"][p]) * u[t]))
     assert abs(lhs - rhs) <= 1e-5 * (np.abs(acc).sum() + 1)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_fp8_input_dispatch_consistent_with_quantising_dispatch(seed):
+    """Pre-quantised input: rows are the token's codes and scales, at the
+    placement the brute-force test pins; quantising first and dispatching
+    the codes gives the quantising dispatch's result bit for bit."""
+    rng = np.random.default_rng(700 + seed)
+    T, H, k, E, R = int(rng.integers(0, 40)), 256, 3, 8, 2
+    A = int(rng.choice([1, 4]))
+    idx = random_routes(rng, T, E, k, mask_prob=0.2)
+    x = (rng.standard_normal((T, H)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    w = rng.random((T, k)).astype(np.float32)
+    q = oracle.dispatch(x, idx, w, E, R, A, fp8=True)
+    # the token's own codes/scales: quantise it alone (one row, one expert)
+    codes = np.zeros((T, H), np.uint8)
+    scales = np.zeros((T, H // 128), np.float32)
+    for t in range(T):
+        one = oracle.dispatch(x[t:t + 1], np.array([[0]], np.int32), None, 1, 1, fp8=True)
+        codes[t], scales[t] = one["recv_x"][0], one["recv_scales"][0]
+    f = oracle.dispatch_fp8_input(codes, scales, idx, w, E, R, A)
+    for key in ("recv_x", "recv_scales", "recv_weights", "tok_slot_row", "row_src"):
+        assert np.array_equal(f[key], q[key]), key
+    # random bytes (any code, any scale) travel unchanged
+    rc = rng.integers(0, 256, (T, H), dtype=np.uint8)
+    rs = rng.random((T, H // 128)).astype(np.float32)
+    f = oracle.dispatch_fp8_input(rc, rs, idx, w, E, R, A)
+    for t in range(T):
+        for j in range(k):
+            p = f["tok_slot_row"][t, j]
+            if p >= 0:
+                assert np.array_equal(f["recv_x"][p], rc[t]) and np.array_equal(f["recv_scales"][p], rs[t])
