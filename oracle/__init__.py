@@ -81,6 +81,15 @@ def _load():
     lib.oracle_dispatch_fp8_input.restype = ctypes.c_int
     lib.oracle_dispatch_fp8_input.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, i64,
                                               P, P, P, P, P]
+    lib.oracle_dispatch_ranked.restype = ctypes.c_int
+    lib.oracle_dispatch_ranked.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, i64,
+                                           P, P, P, P, P, P, P]
+    lib.oracle_expand.restype = ctypes.c_int
+    lib.oracle_expand.argtypes = [i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, i64,
+                                  P, P, P, P, P]
+    lib.oracle_combine_ranked.restype = ctypes.c_int
+    lib.oracle_combine_ranked.argtypes = [i32, i32, i32, i32, i64, i64, i32, P, P, P, P, P,
+                                          P, P, P, P]
     lib.oracle_dispatch_backward.restype = ctypes.c_int
     lib.oracle_dispatch_backward.argtypes = [i32, i32, i32, i64, P, P, P, P]
     lib.oracle_combine_backward.restype = ctypes.c_int
@@ -269,3 +278,85 @@ def combine_backward(grad_out_bits, tok_slot_row, topk_weights, expert_out_bits,
     if rc:
         raise OracleError(rc, "combine_backward")
     return dict(grad_expert_out=gy, grad_w=gw, grad_w_abs=ga)
+
+
+def dispatch_ranked(x_bits, topk_idx, topk_weights, num_experts: int, num_ranks: int,
+                    fp8: bool = False, capacity: int | None = None) -> dict:
+    """Non-expanded dispatch: one row per (token, destination rank)."""
+    x = _c(x_bits, np.uint16)
+    idx = _c(topk_idx, np.int32)
+    T, H = x.shape
+    k = idx.shape[1]
+    R = num_ranks
+    w = None if topk_weights is None else _c(topk_weights, np.float32)
+    if capacity is None:
+        capacity = T * min(k, R)
+    rto = np.zeros(R + 1, np.int32)
+    if fp8:
+        recv_x = np.zeros((capacity, H), np.uint8)
+        recv_scales = np.zeros((capacity, max(H // 128, 1)), np.float32)
+    else:
+        recv_x = np.zeros((capacity, H), np.uint16)
+        recv_scales = None
+    rti = np.full((capacity, k), -2, np.int32)
+    rtw = np.zeros((capacity, k), np.float32)
+    src = np.full(capacity, -2, np.int32)
+    trr = np.zeros((T, R), np.int32)
+    rc = _load().oracle_dispatch_ranked(T, H, k, num_experts, R, 1 if fp8 else 0, _ptr(x),
+                                        _ptr(idx), _ptr(w), capacity, _ptr(rto), _ptr(recv_x),
+                                        _ptr(recv_scales), _ptr(rti), _ptr(rtw), _ptr(src),
+                                        _ptr(trr))
+    if rc:
+        raise OracleError(rc, "dispatch_ranked")
+    return dict(rank_token_offsets=rto, recv_x=recv_x, recv_scales=recv_scales,
+                recv_topk_idx=rti, recv_topk_weights=rtw, recv_src=src, tok_rank_row=trr)
+
+
+def expand(ne: dict, T: int, k: int, num_experts: int, num_ranks: int, alignment: int = 1,
+           fp8: bool = False, capacity: int | None = None) -> dict:
+    """Receiver-side expand of dispatch_ranked's rows into the expert-major
+    layout (same outputs as dispatch)."""
+    H = ne["recv_x"].shape[1]
+    if capacity is None:
+        capacity = T * k + num_experts * (alignment - 1)
+    recv_x = np.zeros((capacity, H), np.uint8 if fp8 else np.uint16)
+    recv_scales = np.zeros((capacity, max(H // 128, 1)), np.float32) if fp8 else None
+    recv_weights = np.zeros(capacity, np.float32)
+    tsr = np.zeros((T, k), np.int32)
+    row_src = np.full(capacity, -2, np.int32)
+    rc = _load().oracle_expand(T, H, k, num_experts, num_ranks, alignment, 1 if fp8 else 0,
+                               _ptr(_c(ne["rank_token_offsets"], np.int32)),
+                               _ptr(np.ascontiguousarray(ne["recv_x"])),
+                               _ptr(None if ne["recv_scales"] is None
+                                    else _c(ne["recv_scales"], np.float32)),
+                               _ptr(_c(ne["recv_topk_idx"], np.int32)),
+                               _ptr(_c(ne["recv_topk_weights"], np.float32)),
+                               _ptr(_c(ne["recv_src"], np.int32)), capacity, _ptr(recv_x),
+                               _ptr(recv_scales), _ptr(recv_weights), _ptr(tsr), _ptr(row_src))
+    if rc:
+        raise OracleError(rc, "expand")
+    return dict(recv_x=recv_x, recv_scales=recv_scales, recv_weights=recv_weights,
+                tok_slot_row=tsr, row_src=row_src)
+
+
+def combine_ranked(y_bits, tok_slot_row, ne: dict, weighted: bool = True):
+    """Combine through per-rank fp32 partials: returns (out bf16 bits [T,H],
+    stage-2 fp32 accumulator [T,H], partials fp32 [rows,H])."""
+    y = _c(y_bits, np.uint16)
+    tsr = _c(tok_slot_row, np.int32)
+    cap, H = y.shape
+    T, k = tsr.shape
+    trr = _c(ne["tok_rank_row"], np.int32)
+    R = trr.shape[1]
+    rows = int(ne["rank_token_offsets"][-1])
+    part = np.zeros((max(rows, 1), H), np.float32)
+    out = np.empty((T, H), np.uint16)
+    acc = np.empty((T, H), np.float32)
+    rc = _load().oracle_combine_ranked(T, H, k, R, rows, cap, 1 if weighted else 0, _ptr(y),
+                                       _ptr(tsr), _ptr(_c(ne["recv_topk_idx"], np.int32)),
+                                       _ptr(_c(ne["recv_topk_weights"], np.float32)),
+                                       _ptr(_c(ne["recv_src"], np.int32)), _ptr(trr),
+                                       _ptr(part), _ptr(out), _ptr(acc))
+    if rc:
+        raise OracleError(rc, "combine_ranked")
+    return out, acc, part[:rows]

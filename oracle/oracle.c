@@ -387,6 +387,196 @@ int oracle_combine(int32_t T, int32_t H, int32_t k, int64_t capacity,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Non-expanded (rank-deduplicated) path                                      */
+/* ------------------------------------------------------------------------ */
+
+int oracle_dispatch_ranked(int32_t T, int32_t H, int32_t k, int32_t E, int32_t R,
+                           int32_t fp8, const uint16_t *x, const int32_t *topk_idx,
+                           const float *topk_weights, int64_t capacity,
+                           int32_t *rank_token_offsets, void *recv_x, float *recv_scales,
+                           int32_t *recv_topk_idx, float *recv_topk_weights,
+                           int32_t *recv_src, int32_t *tok_rank_row) {
+  int rc = check_sizes(T, k, E, R, 1);
+  if (rc) return rc;
+  if (H < 1 || capacity < 0) return ORACLE_BAD_ARG;
+  if (fp8 && (H % 128 != 0 || recv_scales == NULL)) return ORACLE_BAD_ARG;
+  rc = check_routes(T, k, E, topk_idx);
+  if (rc) return rc;
+  for (int64_t i = 0; i < (int64_t)T * H; ++i)
+    if (!isfinite(oracle_bf16_to_float(x[i]))) return ORACLE_BAD_ARG;
+  const int32_t epr = E / R;
+  const int32_t nblk = H / 128;
+
+  /* distinct tokens per rank, then rank partition starts */
+  rank_token_offsets[0] = 0;
+  for (int r = 0; r < R; ++r) {
+    int32_t n = 0;
+    for (int64_t t = 0; t < T; ++t) {
+      int in = 0;
+      for (int j = 0; j < k; ++j) {
+        int32_t e = topk_idx[t * k + j];
+        if (e >= 0 && e / epr == r) in = 1;
+      }
+      n += in;
+    }
+    rank_token_offsets[r + 1] = rank_token_offsets[r] + n;
+  }
+  if (rank_token_offsets[R] > capacity) return ORACLE_NO_CAPACITY;
+
+  uint8_t *qrow = fp8 ? (uint8_t *)malloc((size_t)H) : NULL;
+  float *srow = fp8 ? (float *)malloc(sizeof(float) * (size_t)(nblk > 0 ? nblk : 1)) : NULL;
+  int32_t *fill = (int32_t *)calloc((size_t)R, sizeof(int32_t));
+  for (int64_t t = 0; t < T; ++t) {
+    if (fp8) quantize_row_e4m3(H, x + t * H, qrow, srow);
+    for (int r = 0; r < R; ++r) {
+      int in = 0;
+      for (int j = 0; j < k; ++j) {
+        int32_t e = topk_idx[t * k + j];
+        if (e >= 0 && e / epr == r) in = 1;
+      }
+      if (!in) {
+        tok_rank_row[t * R + r] = -1;
+        continue;
+      }
+      int64_t q = rank_token_offsets[r] + fill[r];
+      fill[r] += 1;
+      tok_rank_row[t * R + r] = (int32_t)q;
+      recv_src[q] = (int32_t)t;
+      for (int j = 0; j < k; ++j) {
+        int32_t e = topk_idx[t * k + j];
+        int local = e >= 0 && e / epr == r;
+        recv_topk_idx[q * k + j] = local ? e - r * epr : -1;
+        if (recv_topk_weights)
+          recv_topk_weights[q * k + j] = (local && topk_weights) ? topk_weights[t * k + j] : 0.0f;
+      }
+      if (fp8) {
+        memcpy((uint8_t *)recv_x + q * H, qrow, (size_t)H);
+        memcpy(recv_scales + q * nblk, srow, sizeof(float) * (size_t)nblk);
+      } else {
+        memcpy((uint16_t *)recv_x + q * H, x + t * H, sizeof(uint16_t) * (size_t)H);
+      }
+    }
+  }
+  free(qrow); free(srow); free(fill);
+  return ORACLE_OK;
+}
+
+int oracle_expand(int32_t T, int32_t H, int32_t k, int32_t E, int32_t R, int32_t A,
+                  int32_t fp8, const int32_t *rank_token_offsets, const void *ne_x,
+                  const float *ne_scales, const int32_t *recv_topk_idx,
+                  const float *recv_topk_weights, const int32_t *recv_src,
+                  int64_t capacity, void *recv_x, float *recv_scales, float *recv_weights,
+                  int32_t *tok_slot_row, int32_t *row_src) {
+  int rc = check_sizes(T, k, E, R, A);
+  if (rc) return rc;
+  if (H < 1 || capacity < 0 || (fp8 && H % 128 != 0)) return ORACLE_BAD_ARG;
+  const int32_t epr = E / R;
+  const int32_t nblk = H / 128;
+  const int64_t rows = rank_token_offsets[R];
+  for (int64_t q = 0; q < rows; ++q)
+    for (int j = 0; j < k; ++j)
+      if (recv_topk_idx[q * k + j] < -1 || recv_topk_idx[q * k + j] >= epr) return ORACLE_BAD_ROUTE;
+
+  /* count each expert's rows from the received slices, then aligned starts */
+  int32_t *cnt = (int32_t *)calloc((size_t)E, sizeof(int32_t));
+  int32_t *off = (int32_t *)malloc(sizeof(int32_t) * (size_t)(E + 1));
+  int32_t *fill = (int32_t *)calloc((size_t)E, sizeof(int32_t));
+  for (int r = 0; r < R; ++r)
+    for (int64_t q = rank_token_offsets[r]; q < rank_token_offsets[r + 1]; ++q)
+      for (int j = 0; j < k; ++j)
+        if (recv_topk_idx[q * k + j] >= 0) cnt[r * epr + recv_topk_idx[q * k + j]] += 1;
+  off[0] = 0;
+  for (int e = 0; e < E; ++e) off[e + 1] = off[e] + (cnt[e] + A - 1) / A * A;
+  if (off[E] > capacity) {
+    free(cnt); free(off); free(fill);
+    return ORACLE_NO_CAPACITY;
+  }
+  for (int64_t i = 0; i < (int64_t)T * k; ++i) tok_slot_row[i] = -1;
+
+  /* rows of a rank arrive in ascending source order, so filling each expert
+   * segment while walking the rank's rows keeps the segment sorted */
+  for (int r = 0; r < R; ++r) {
+    for (int64_t q = rank_token_offsets[r]; q < rank_token_offsets[r + 1]; ++q) {
+      int64_t t = recv_src[q];
+      for (int j = 0; j < k; ++j) {
+        int32_t le = recv_topk_idx[q * k + j];
+        if (le < 0) continue;
+        int32_t e = r * epr + le;
+        int64_t p = off[e] + fill[e];
+        fill[e] += 1;
+        tok_slot_row[t * k + j] = (int32_t)p;
+        row_src[p] = (int32_t)(t * k + j);
+        if (recv_weights && recv_topk_weights) recv_weights[p] = recv_topk_weights[q * k + j];
+        if (fp8) {
+          memcpy((uint8_t *)recv_x + p * H, (const uint8_t *)ne_x + q * H, (size_t)H);
+          memcpy(recv_scales + p * nblk, ne_scales + q * nblk, sizeof(float) * (size_t)nblk);
+        } else {
+          memcpy((uint16_t *)recv_x + p * H, (const uint16_t *)ne_x + q * H,
+                 sizeof(uint16_t) * (size_t)H);
+        }
+      }
+    }
+  }
+  for (int e = 0; e < E; ++e) {
+    for (int64_t p = (int64_t)off[e] + cnt[e]; p < off[e + 1]; ++p) {
+      row_src[p] = -1;
+      if (recv_weights && recv_topk_weights) recv_weights[p] = 0.0f;
+      if (fp8) {
+        memset((uint8_t *)recv_x + p * H, 0, (size_t)H);
+        for (int b = 0; b < nblk; ++b) recv_scales[p * nblk + b] = 0.0f;
+      } else {
+        memset((uint16_t *)recv_x + p * H, 0, sizeof(uint16_t) * (size_t)H);
+      }
+    }
+  }
+  free(cnt); free(off); free(fill);
+  return ORACLE_OK;
+}
+
+int oracle_combine_ranked(int32_t T, int32_t H, int32_t k, int32_t R, int64_t rows,
+                          int64_t capacity, int32_t weighted, const uint16_t *y,
+                          const int32_t *tok_slot_row, const int32_t *recv_topk_idx,
+                          const float *recv_topk_weights, const int32_t *recv_src,
+                          const int32_t *tok_rank_row, float *partials, uint16_t *out,
+                          float *acc_out) {
+  if (T < 0 || H < 1 || k < 1 || R < 1 || rows < 0 || capacity < 0) return ORACLE_BAD_ARG;
+  float *part = partials ? partials : (float *)malloc(sizeof(float) * (size_t)(rows * H + 1));
+  /* stage 1: per (token, rank) row, the rank's experts' weighted rows */
+  for (int64_t q = 0; q < rows; ++q) {
+    int64_t t = recv_src[q];
+    for (int64_t c = 0; c < H; ++c) {
+      float acc = 0.0f;
+      for (int j = 0; j < k; ++j) {
+        if (recv_topk_idx[q * k + j] < 0) continue;
+        int64_t p = tok_slot_row[t * k + j];
+        if (p < 0 || p >= capacity) continue;
+        float yv = oracle_bf16_to_float(y[p * H + c]);
+        if (weighted)
+          acc = fmaf(recv_topk_weights[q * k + j], yv, acc);
+        else
+          acc = acc + yv;
+      }
+      part[q * H + c] = acc;
+    }
+  }
+  /* stage 2: per token, the partials of its ranks in rank order */
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t c = 0; c < H; ++c) {
+      float acc = 0.0f;
+      for (int r = 0; r < R; ++r) {
+        int64_t q = tok_rank_row[t * R + r];
+        if (q < 0) continue;
+        acc = acc + part[q * H + c];
+      }
+      out[t * H + c] = oracle_bf16_round(acc);
+      if (acc_out) acc_out[t * H + c] = acc;
+    }
+  }
+  if (!partials) free(part);
+  return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Backward                                                                  */
 /* ------------------------------------------------------------------------ */
 

@@ -94,6 +94,59 @@ int oracle_dispatch_fp8_input(int32_t T, int32_t H, int32_t k, int32_t E, int32_
                               int64_t capacity, uint8_t *recv_codes, float *recv_scales,
                               float *recv_weights, int32_t *tok_slot_row, int32_t *row_src);
 
+/* Non-expanded (rank-deduplicated) dispatch ([DD] "Why expert parallelism
+ * needs a communication layer": a token crosses to a destination rank once
+ * however many of its experts live there; "Dispatch: layout, move, and
+ * epilogue": in non-expanded mode a received row is a source token with its
+ * top-k metadata).  Rank r's rows are [rank_token_offsets[r],
+ * rank_token_offsets[r+1]), one per token with an expert on r, in ascending
+ * token order.  Row q carries the token's payload (bf16, or E4M3 codes and
+ * scales as oracle_dispatch computes them), recv_src[q] = t, and the token's
+ * top-k slice for this rank: recv_topk_idx[q,j] = e - r*E/R (local expert)
+ * when slot j's expert e lives on r, else -1; recv_topk_weights[q,j] = w[t,j]
+ * there, else 0.  tok_rank_row[t,r] = q, or -1.  Row count = the sum of
+ * num_tokens_per_rank; capacity must hold it. */
+int oracle_dispatch_ranked(int32_t T, int32_t H, int32_t k, int32_t E, int32_t R,
+                           int32_t fp8, const uint16_t *x, const int32_t *topk_idx,
+                           const float *topk_weights, int64_t capacity,
+                           int32_t *rank_token_offsets, void *recv_x, float *recv_scales,
+                           int32_t *recv_topk_idx, float *recv_topk_weights,
+                           int32_t *recv_src, int32_t *tok_rank_row);
+
+/* Receiver-side expand of non-expanded rows into the expert-major layout
+ * ([DD] "Dispatch: layout, move, and epilogue": the copy epilogue expands
+ * rows into the receive layout the expert GEMM uses).  Uses only what the
+ * receiver holds: the rows, recv_src, the local top-k slice and the rank
+ * partition bounds.  Experts' segments start at aligned offsets (alignment
+ * A) and fill in ascending source token order, so the result is the
+ * expanded dispatch of the same route: recv_x [capacity, H] (row_bytes per
+ * row: 2H for bf16, H for E4M3 plus H/128 scales), row_src = t*k + j,
+ * recv_weights, tok_slot_row [T,k], padding zeroed. */
+int oracle_expand(int32_t T, int32_t H, int32_t k, int32_t E, int32_t R, int32_t A,
+                  int32_t fp8, const int32_t *rank_token_offsets, const void *ne_x,
+                  const float *ne_scales, const int32_t *recv_topk_idx,
+                  const float *recv_topk_weights, const int32_t *recv_src,
+                  int64_t capacity, void *recv_x, float *recv_scales, float *recv_weights,
+                  int32_t *tok_slot_row, int32_t *row_src);
+
+/* Combine through per-rank partial sums ([DD] "Combine: reverse routing
+ * plus reduction": staging partial sums per rank sends fewer rows; kept in
+ * fp32 here because a bf16 subtotal can lose a small term to cancellation).
+ * Stage 1, per non-expanded row q of token t on rank r:
+ *   partial[q,c] = fp32 sum over slots j in order with recv_topk_idx[q,j] >= 0
+ *                  of w * y[tok_slot_row[t,j], c]   (one fused multiply-add each,
+ *                  from +0; w = recv_topk_weights[q,j], or a plain add when
+ *                  weighted == 0)
+ * Stage 2: out[t,c] = bf16(fp32 sum over r = 0..R-1 with tok_rank_row[t,r] >= 0
+ *                  of partial[tok_rank_row[t,r], c], from +0).
+ * partials (nullable) receives stage 1 [rows, H]; acc_out stage 2's fp32. */
+int oracle_combine_ranked(int32_t T, int32_t H, int32_t k, int32_t R, int64_t rows,
+                          int64_t capacity, int32_t weighted, const uint16_t *y,
+                          const int32_t *tok_slot_row, const int32_t *recv_topk_idx,
+                          const float *recv_topk_weights, const int32_t *recv_src,
+                          const int32_t *tok_rank_row, float *partials, uint16_t *out,
+                          float *acc_out);
+
 /* Backward of dispatch ([DD] "Combine: reverse routing plus reduction",
  * backward duality: for the unweighted route, copying a row forward becomes
  * summing its gradients backward):
