@@ -59,6 +59,22 @@ def backward_bytes(w, M: int) -> dict:
     return dict(dispatch_backward=db, combine_backward=cb, total=db + cb)
 
 
+def ranked_bytes(w, M: int, Q: int) -> dict:
+    """Algorithmic bytes of the non-expanded path with Q (token, rank) rows.
+    dispatch_ranked: T*2H (x) + T*k*8 (idx, gates) + Q*row + Q*(4 + 8k)
+                     (source, local slices) + T*R*4 + T*k*4 (both handles)
+    expand:          Q*row + Q*8k (received rows and slices) + M*row + M*8
+    combine_ranked:  M*2H + Q*8k + Q*4H (stage 1) + Q*4H + T*R*4 + T*2H (stage 2)"""
+    T, H, k, R = w.num_tokens, w.hidden, w.num_topk, w.num_ranks
+    row = (H + 4 * (H // 128)) if w.fp8 else 2 * H
+    layout = T * k * 4 + T * R + 4 * (w.num_experts + R) + 4 * (w.num_experts + R + 2)
+    disp = T * 2 * H + T * k * 8 + Q * row + Q * (4 + 8 * k) + T * R * 4 + T * k * 4
+    exp = Q * row + Q * 8 * k + M * row + M * 8
+    comb = M * 2 * H + Q * 8 * k + Q * 4 * H + Q * 4 * H + T * R * 4 + T * 2 * H
+    return dict(layout=layout, dispatch_ranked=disp, expand=exp, combine_ranked=comb,
+                total=layout + disp + exp + comb)
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
@@ -247,6 +263,61 @@ def run_backward(args, w, b, x, idx, wts, y, inp, dev, stream):
     print(json.dumps(rec), flush=True)
 
 
+def run_ranked(args, w, b, x, idx, wts, y, stream):
+    """Time the non-expanded path over one batch: layout, one row per
+    (token, rank), receiver-side expand to the expert-major layout, and the
+    combine through fp32 per-rank partials."""
+    import numpy as np
+    import torch
+
+    names = ("layout", "dispatch_ranked", "expand", "combine_ranked")
+    calls = (lambda: b.layout(idx), lambda: b.dispatch_ranked(x, idx, wts), lambda: b.expand(),
+             lambda: b.combine_ranked(y))
+    for _ in range(args.warmup):
+        for fn in calls:
+            fn()
+    b.check_status()
+    M = int(b.expert_offsets[-1].item())
+    Q = int(b.rank_token_offsets[-1].item())
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        for fn in calls:
+            fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)] for n in names}
+    for i in range(args.steps):
+        for n, fn in zip(names, calls):
+            ev[n][i][0].record(stream)
+            fn()
+            ev[n][i][1].record(stream)
+    torch.cuda.synchronize()
+    b.check_status()
+    per_us = {n: float(np.mean([a.elapsed_time(c) for a, c in ev[n]])) * 1e3 for n in names}
+    by = ranked_bytes(w, M, Q)
+    gbps = by["total"] / (ms / 1e3) / 1e9
+    rec = {
+        "metric": "non-expanded dispatch + expand + ranked combine HBM GB/s",
+        "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "pct_of_peak": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
+        "tokens_per_s": round(w.num_tokens / (ms / 1e3), 1),
+        "config": {"workload": w.name, "tokens": w.num_tokens, "hidden": w.hidden,
+                   "topk": w.num_topk, "experts": w.num_experts, "logical_ranks": w.num_ranks,
+                   "valid_selections": M, "token_rank_rows": Q,
+                   "rows_per_token": round(Q / max(w.num_tokens, 1), 4)},
+        "algorithmic_bytes_per_step": by,
+        "kernel_us": {n: round(v, 2) for n, v in per_us.items()},
+        "kernel_roofline_frac": {n: round(by[n] / (per_us[n] / 1e6) / 1e9 / PEAK_HBM_GBPS, 4)
+                                 for n in names},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -259,6 +330,9 @@ def main():
                     help="also run a plain device copy of this many MiB (counter scale)")
     ap.add_argument("--fp8-input", action="store_true",
                     help="dispatch pre-quantised rows (E4M3 codes + scales) instead of bf16")
+    ap.add_argument("--ranked", action="store_true",
+                    help="time the non-expanded path (dispatch_ranked + expand + "
+                         "combine_ranked; its own JSON line)")
     ap.add_argument("--direction", choices=("forward", "backward"), default="forward",
                     help="backward times ep_dispatch_backward + ep_combine_backward (its own "
                          "JSON line, not the forward metric)")
@@ -324,6 +398,9 @@ def main():
 
     if args.direction == "backward":
         run_backward(args, w, b, x, idx, wts, y, inp, dev, stream)
+        return
+    if args.ranked:
+        run_ranked(args, w, b, x, idx, wts, y, stream)
         return
 
     print(f"bench: warmup {args.warmup}", file=sys.stderr, flush=True)

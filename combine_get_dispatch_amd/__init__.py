@@ -45,6 +45,14 @@ class ep_handle_t(ctypes.Structure):
                 ("expert_offsets", ctypes.c_void_p)]
 
 
+class ep_ranked_handle_t(ctypes.Structure):
+    _fields_ = [("config", ep_config_t), ("capacity", ctypes.c_int64),
+                ("ranked_capacity", ctypes.c_int64), ("rank_token_offsets", ctypes.c_void_p),
+                ("tok_rank_row", ctypes.c_void_p), ("tok_slot_row", ctypes.c_void_p),
+                ("ne_topk_idx", ctypes.c_void_p), ("ne_topk_weights", ctypes.c_void_p),
+                ("ne_src", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -74,10 +82,18 @@ def lib() -> ctypes.CDLL:
     L.ep_dispatch_backward.argtypes = [ctypes.POINTER(ep_handle_t), P, P, P]
     L.ep_dispatch_fp8_input.argtypes = [cfgp, P, P, P, P, P, P, S, i64, P, P, P, P, P, P,
                                         ctypes.POINTER(ep_handle_t), P]
+    rhp = ctypes.POINTER(ep_ranked_handle_t)
+    L.ep_ranked_capacity_rows.argtypes = [cfgp, ctypes.POINTER(i64)]
+    L.ep_dispatch_ranked.argtypes = [cfgp, ctypes.c_int, P, P, P, P, P, S, i64, i64, P, P, P, P,
+                                     P, P, P, P, P, rhp, P]
+    L.ep_expand.argtypes = [rhp, ctypes.c_int, P, P, P, P, S, P, P, P, P, P,
+                            ctypes.POINTER(ep_handle_t), P]
+    L.ep_combine_ranked.argtypes = [rhp, P, ctypes.c_int32, P, P, P]
     L.ep_combine_backward.argtypes = [ctypes.POINTER(ep_handle_t), P, P, P, P, P, P]
     for f in ("ep_layout_workspace_bytes", "ep_recv_capacity_rows", "ep_get_dispatch_layout",
               "ep_dispatch", "ep_combine", "ep_read_status", "ep_workspace_init",
-              "ep_dispatch_backward", "ep_combine_backward", "ep_dispatch_fp8_input"):
+              "ep_dispatch_backward", "ep_combine_backward", "ep_dispatch_fp8_input",
+              "ep_ranked_capacity_rows", "ep_dispatch_ranked", "ep_expand", "ep_combine_ranked"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -272,6 +288,80 @@ def ep_combine_backward(handle: ep_handle_t, grad_out, topk_weights, expert_out,
     _check(st, "ep_combine_backward")
 
 
+def ep_ranked_capacity_rows(cfg: ep_config_t) -> int:
+    n = ctypes.c_int64()
+    _check(lib().ep_ranked_capacity_rows(ctypes.byref(cfg), ctypes.byref(n)),
+           "ep_ranked_capacity_rows")
+    return n.value
+
+
+def ep_dispatch_ranked(cfg, recv_dtype, x, topk_idx, topk_weights, expert_offsets, workspace,
+                       capacity, ranked_capacity, ne_x, ne_scales, ne_topk_idx, ne_topk_weights,
+                       ne_src, rank_token_offsets, tok_rank_row, tok_slot_row, status,
+                       stream=None) -> ep_ranked_handle_t:
+    import torch
+
+    T, H, k, E, R = cfg.num_tokens, cfg.hidden, cfg.num_topk, cfg.num_experts, cfg.num_ranks
+    qc = int(ranked_capacity)
+    fp8 = int(recv_dtype) == EP_DTYPE_FP8_E4M3
+    h = ep_ranked_handle_t()
+    st = lib().ep_dispatch_ranked(
+        ctypes.byref(cfg), int(recv_dtype), _ptr(x, torch.bfloat16, (T, H), "x"),
+        _ptr(topk_idx, torch.int32, (T, k), "topk_idx"),
+        _ptr(topk_weights, torch.float32, (T, k), "topk_weights"),
+        _ptr(expert_offsets, torch.int32, (E + 1,), "expert_offsets"),
+        _ptr(workspace, torch.uint8, name="workspace"), workspace.numel(), int(capacity), qc,
+        _ptr(ne_x, torch.uint8 if fp8 else torch.bfloat16, (qc, H), "ne_x"),
+        _ptr(ne_scales, torch.float32, (qc, H // 128), "ne_scales") if fp8 else None,
+        _ptr(ne_topk_idx, torch.int32, (qc, k), "ne_topk_idx"),
+        _ptr(ne_topk_weights, torch.float32, (qc, k), "ne_topk_weights"),
+        _ptr(ne_src, torch.int32, (qc,), "ne_src"),
+        _ptr(rank_token_offsets, torch.int32, (R + 1,), "rank_token_offsets"),
+        _ptr(tok_rank_row, torch.int32, (T, R), "tok_rank_row"),
+        _ptr(tok_slot_row, torch.int32, (T, k), "tok_slot_row"),
+        _ptr(status, torch.int32, (1,), "status"), ctypes.byref(h), _stream(stream))
+    _check(st, "ep_dispatch_ranked")
+    return h
+
+
+def ep_expand(ranked: ep_ranked_handle_t, recv_dtype, ne_x, ne_scales, expert_offsets, workspace,
+              recv_x, recv_scales, recv_weights, row_src, status, stream=None) -> ep_handle_t:
+    import torch
+
+    c = ranked.config
+    H, E = c.hidden, c.num_experts
+    qc, cap = ranked.ranked_capacity, ranked.capacity
+    fp8 = int(recv_dtype) == EP_DTYPE_FP8_E4M3
+    h = ep_handle_t()
+    st = lib().ep_expand(
+        ctypes.byref(ranked), int(recv_dtype),
+        _ptr(ne_x, torch.uint8 if fp8 else torch.bfloat16, (qc, H), "ne_x"),
+        _ptr(ne_scales, torch.float32, (qc, H // 128), "ne_scales") if fp8 else None,
+        _ptr(expert_offsets, torch.int32, (E + 1,), "expert_offsets"),
+        _ptr(workspace, torch.uint8, name="workspace"), workspace.numel(),
+        _ptr(recv_x, torch.uint8 if fp8 else torch.bfloat16, (cap, H), "recv_x"),
+        _ptr(recv_scales, torch.float32, (cap, H // 128), "recv_scales") if fp8 else None,
+        _ptr(recv_weights, torch.float32, (cap,), "recv_weights"),
+        _ptr(row_src, torch.int32, (cap,), "row_src"),
+        _ptr(status, torch.int32, (1,), "status"), ctypes.byref(h), _stream(stream))
+    _check(st, "ep_expand")
+    return h
+
+
+def ep_combine_ranked(ranked: ep_ranked_handle_t, expert_out, weighted: bool, partials, out,
+                      stream=None):
+    import torch
+
+    c = ranked.config
+    T, H = c.num_tokens, c.hidden
+    st = lib().ep_combine_ranked(
+        ctypes.byref(ranked), _rows_tensor(expert_out, ranked.capacity, H, "expert_out"),
+        1 if weighted else 0,
+        _ptr(partials, torch.float32, (ranked.ranked_capacity, H), "partials"),
+        _ptr(out, torch.bfloat16, (T, H), "out"), _stream(stream))
+    _check(st, "ep_combine_ranked")
+
+
 def make_handle(num_tokens, hidden, num_topk, capacity, tok_slot_row, row_src=None,
                 expert_offsets=None, num_experts=None, num_ranks=1, expert_alignment=1):
     """Build an ep_handle_t around existing device arrays (combine only reads
@@ -383,6 +473,57 @@ class EpBuffers:
         ep_combine_backward(self.handle, grad_out, topk_weights, expert_out, grad_expert_out,
                             grad_weights, stream=stream)
         return grad_expert_out
+
+    # --- non-expanded (rank-deduplicated) path; its buffers are made on first use
+
+    def _ranked_buffers(self):
+        import torch
+
+        if getattr(self, "ne_x", None) is not None:
+            return
+        c, dev = self.cfg, self.out.device
+        T, H, k, R = c.num_tokens, c.hidden, c.num_topk, c.num_ranks
+        qc = ep_ranked_capacity_rows(c)
+        self.ranked_capacity = qc
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.ne_x = torch.empty((qc, H), dtype=torch.uint8 if self.fp8 else torch.bfloat16,
+                                device=dev)
+        self.ne_scales = (torch.empty((qc, H // 128), dtype=torch.float32, device=dev)
+                          if self.fp8 else None)
+        self.ne_topk_idx = torch.empty((qc, k), **i32)
+        self.ne_topk_weights = torch.empty((qc, k), dtype=torch.float32, device=dev)
+        self.ne_src = torch.empty(qc, **i32)
+        self.rank_token_offsets = torch.empty(R + 1, **i32)
+        self.tok_rank_row = torch.empty((T, R), **i32)
+        self.partials = None
+
+    def dispatch_ranked(self, x, topk_idx, topk_weights, stream=None):
+        self._ranked_buffers()
+        self.ranked = ep_dispatch_ranked(
+            self.cfg, EP_DTYPE_FP8_E4M3 if self.fp8 else EP_DTYPE_BF16, x, topk_idx, topk_weights,
+            self.expert_offsets, self.workspace, self.capacity, self.ranked_capacity, self.ne_x,
+            self.ne_scales, self.ne_topk_idx, self.ne_topk_weights, self.ne_src,
+            self.rank_token_offsets, self.tok_rank_row, self.tok_slot_row, self.status,
+            stream=stream)
+        return self.ranked
+
+    def expand(self, with_weights=True, stream=None):
+        self.handle = ep_expand(self.ranked, EP_DTYPE_FP8_E4M3 if self.fp8 else EP_DTYPE_BF16,
+                                self.ne_x, self.ne_scales, self.expert_offsets, self.workspace,
+                                self.recv_x, self.recv_scales,
+                                self.recv_weights if with_weights else None, self.row_src,
+                                self.status, stream=stream)
+        return self.handle
+
+    def combine_ranked(self, expert_out, weighted=True, out=None, stream=None):
+        import torch
+
+        if self.partials is None:
+            self.partials = torch.empty((self.ranked_capacity, self.cfg.hidden),
+                                        dtype=torch.float32, device=self.out.device)
+        out = self.out if out is None else out
+        ep_combine_ranked(self.ranked, expert_out, weighted, self.partials, out, stream=stream)
+        return out
 
     def check_status(self, stream=None):
         ep_read_status(self.status, stream=stream)

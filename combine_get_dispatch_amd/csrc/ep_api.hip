@@ -320,4 +320,144 @@ ep_status_t ep_combine_backward(const ep_handle_t *handle, const uint16_t *grad_
   return EP_OK;
 }
 
+ep_status_t ep_ranked_capacity_rows(const ep_config_t *cfg, int64_t *rows_host) {
+  ep_status_t st = check_config(cfg);
+  if (st != EP_OK) return st;
+  if (rows_host == nullptr) return fail(EP_ERR_INVALID_ARG, "rows_host is NULL");
+  const int64_t per = cfg->num_topk < cfg->num_ranks ? cfg->num_topk : cfg->num_ranks;
+  *rows_host = (int64_t)cfg->num_tokens * per;
+  return EP_OK;
+}
+
+ep_status_t ep_dispatch_ranked(const ep_config_t *cfg, ep_dtype_t recv_dtype, const uint16_t *x,
+                               const int32_t *topk_idx, const float *topk_weights,
+                               const int32_t *expert_offsets, const void *workspace,
+                               size_t workspace_bytes, int64_t capacity, int64_t ranked_capacity,
+                               void *ne_x, float *ne_scales, int32_t *ne_topk_idx,
+                               float *ne_topk_weights, int32_t *ne_src,
+                               int32_t *rank_token_offsets, int32_t *tok_rank_row,
+                               int32_t *tok_slot_row, int32_t *status,
+                               ep_ranked_handle_t *handle_host, hipStream_t stream) {
+  ep_status_t st = check_config(cfg);
+  if (st != EP_OK) return st;
+  if (recv_dtype != EP_DTYPE_BF16 && recv_dtype != EP_DTYPE_FP8_E4M3)
+    return fail(EP_ERR_INVALID_ARG, "unknown recv_dtype %d", (int)recv_dtype);
+  const bool fp8 = recv_dtype == EP_DTYPE_FP8_E4M3;
+  if (fp8 && cfg->hidden % 128 != 0)
+    return fail(EP_ERR_INVALID_ARG, "FP8 rows need hidden %% 128 == 0 (hidden %d)", cfg->hidden);
+  if (capacity < 0 || capacity >= INT32_MAX || ranked_capacity < 0 || ranked_capacity >= INT32_MAX)
+    return fail(EP_ERR_INVALID_ARG, "capacities must be in [0, 2^31 - 1)");
+  const bool empty = cfg->num_tokens == 0;
+  if ((!empty && (x == nullptr || topk_idx == nullptr || tok_rank_row == nullptr ||
+                  tok_slot_row == nullptr)) ||
+      expert_offsets == nullptr || workspace == nullptr || status == nullptr ||
+      rank_token_offsets == nullptr ||
+      (ranked_capacity > 0 && (ne_x == nullptr || ne_topk_idx == nullptr || ne_src == nullptr ||
+                               (fp8 && ne_scales == nullptr))))
+    return fail(EP_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(x) || !aligned16(ne_x))
+    return fail(EP_ERR_INVALID_ARG, "x and ne_x must be 16-byte aligned");
+  const size_t need =
+      ep::workspace_layout(cfg->num_tokens, cfg->num_topk, cfg->num_experts, cfg->num_ranks)
+          .total;
+  if (workspace_bytes < need)
+    return fail(EP_ERR_INVALID_ARG, "workspace has %zu bytes, dispatch needs %zu",
+                workspace_bytes, need);
+  hipError_t err = ep::launch_dispatch_ranked(
+      dims_of(cfg), fp8, x, topk_idx, topk_weights, expert_offsets,
+      static_cast<const char *>(workspace), capacity, ranked_capacity, ne_x, ne_scales,
+      ne_topk_idx, ne_topk_weights, ne_src, rank_token_offsets, tok_rank_row, tok_slot_row,
+      status, stream);
+  if (err != hipSuccess) return hip_fail(err, "ranked dispatch launch");
+  if (handle_host != nullptr) {
+    handle_host->config = *cfg;
+    handle_host->capacity = capacity;
+    handle_host->ranked_capacity = ranked_capacity;
+    handle_host->rank_token_offsets = rank_token_offsets;
+    handle_host->tok_rank_row = tok_rank_row;
+    handle_host->tok_slot_row = tok_slot_row;
+    handle_host->ne_topk_idx = ne_topk_idx;
+    handle_host->ne_topk_weights = ne_topk_weights;
+    handle_host->ne_src = ne_src;
+  }
+  return EP_OK;
+}
+
+static ep_status_t check_ranked(const ep_ranked_handle_t *h) {
+  if (h == nullptr) return fail(EP_ERR_INVALID_ARG, "ranked handle is NULL");
+  ep_status_t st = check_config(&h->config);
+  if (st != EP_OK) return st;
+  if (h->capacity < 0 || h->capacity >= INT32_MAX || h->ranked_capacity < 0 ||
+      h->ranked_capacity >= INT32_MAX)
+    return fail(EP_ERR_INVALID_ARG, "ranked handle capacities invalid");
+  if (h->rank_token_offsets == nullptr ||
+      (h->config.num_tokens > 0 && (h->tok_rank_row == nullptr || h->tok_slot_row == nullptr)) ||
+      (h->ranked_capacity > 0 && (h->ne_topk_idx == nullptr || h->ne_src == nullptr)))
+    return fail(EP_ERR_INVALID_ARG, "ranked handle has a NULL array");
+  return EP_OK;
+}
+
+ep_status_t ep_expand(const ep_ranked_handle_t *ranked, ep_dtype_t recv_dtype, const void *ne_x,
+                      const float *ne_scales, const int32_t *expert_offsets,
+                      const void *workspace, size_t workspace_bytes, void *recv_x,
+                      float *recv_scales, float *recv_weights, int32_t *row_src,
+                      int32_t *status, ep_handle_t *handle_host, hipStream_t stream) {
+  ep_status_t st = check_ranked(ranked);
+  if (st != EP_OK) return st;
+  const ep_config_t *cfg = &ranked->config;
+  if (recv_dtype != EP_DTYPE_BF16 && recv_dtype != EP_DTYPE_FP8_E4M3)
+    return fail(EP_ERR_INVALID_ARG, "unknown recv_dtype %d", (int)recv_dtype);
+  const bool fp8 = recv_dtype == EP_DTYPE_FP8_E4M3;
+  if (fp8 && cfg->hidden % 128 != 0)
+    return fail(EP_ERR_INVALID_ARG, "FP8 rows need hidden %% 128 == 0 (hidden %d)", cfg->hidden);
+  if (expert_offsets == nullptr || workspace == nullptr || status == nullptr ||
+      (ranked->ranked_capacity > 0 && (ne_x == nullptr || (fp8 && ne_scales == nullptr))) ||
+      (ranked->capacity > 0 && (recv_x == nullptr || row_src == nullptr ||
+                                (fp8 && recv_scales == nullptr))))
+    return fail(EP_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(ne_x) || !aligned16(recv_x))
+    return fail(EP_ERR_INVALID_ARG, "ne_x and recv_x must be 16-byte aligned");
+  const size_t need =
+      ep::workspace_layout(cfg->num_tokens, cfg->num_topk, cfg->num_experts, cfg->num_ranks)
+          .total;
+  if (workspace_bytes < need)
+    return fail(EP_ERR_INVALID_ARG, "workspace has %zu bytes, expand needs %zu",
+                workspace_bytes, need);
+  hipError_t err = ep::launch_expand(
+      dims_of(cfg), fp8, ranked->ranked_capacity, ne_x, ne_scales, ranked->ne_topk_idx,
+      ranked->ne_topk_weights, ranked->ne_src, ranked->rank_token_offsets, expert_offsets,
+      static_cast<const char *>(workspace), ranked->capacity, recv_x, recv_scales, recv_weights,
+      row_src, status, stream);
+  if (err != hipSuccess) return hip_fail(err, "expand launch");
+  if (handle_host != nullptr) {
+    handle_host->config = *cfg;
+    handle_host->capacity = ranked->capacity;
+    handle_host->tok_slot_row = ranked->tok_slot_row;
+    handle_host->row_src = row_src;
+    handle_host->expert_offsets = expert_offsets;
+  }
+  return EP_OK;
+}
+
+ep_status_t ep_combine_ranked(const ep_ranked_handle_t *ranked, const uint16_t *expert_out,
+                              int32_t weighted, float *partials, uint16_t *out,
+                              hipStream_t stream) {
+  ep_status_t st = check_ranked(ranked);
+  if (st != EP_OK) return st;
+  if (weighted && ranked->ranked_capacity > 0 && ranked->ne_topk_weights == nullptr)
+    return fail(EP_ERR_INVALID_ARG, "weighted combine needs ne_topk_weights in the handle");
+  if ((ranked->config.num_tokens > 0 && out == nullptr) ||
+      (ranked->ranked_capacity > 0 && partials == nullptr) ||
+      (ranked->capacity > 0 && expert_out == nullptr))
+    return fail(EP_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(expert_out) || !aligned16(out) || !aligned16(partials))
+    return fail(EP_ERR_INVALID_ARG, "expert_out, partials and out must be 16-byte aligned");
+  hipError_t err = ep::launch_combine_ranked(
+      dims_of(&ranked->config), ranked->capacity, ranked->ranked_capacity, expert_out,
+      ranked->tok_slot_row, ranked->ne_topk_idx, weighted ? ranked->ne_topk_weights : nullptr,
+      ranked->ne_src, ranked->rank_token_offsets, ranked->tok_rank_row, partials, out, stream);
+  if (err != hipSuccess) return hip_fail(err, "ranked combine launch");
+  return EP_OK;
+}
+
 }  // extern "C"

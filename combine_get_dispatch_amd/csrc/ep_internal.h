@@ -29,9 +29,11 @@ constexpr int kHeaderTicket = 8;
 struct WorkspaceLayout {
   int32_t ntiles;
   size_t tile_cnt;       // int32 [ntiles, E]: tile histogram, then tile base
-  size_t tile_rank_cnt;  // int32 [ntiles, R]: distinct tokens per rank per tile
+  size_t tile_rank_cnt;  // int32 [ntiles, R]: tokens per rank per tile, then tile base
   size_t cnt;            // int32 [E]: unaligned count per expert
   size_t slot_rank;      // int32 [T, k]: rank of (t, j) inside its tile's run of e
+  size_t rank_ballot;    // u64 [ntiles, 4 waves, R]: which lanes' tokens have an expert on r
+  size_t rank_tok_off;   // int32 [R + 1]: starts of the ranks' token partitions
   size_t total;
 };
 
@@ -70,5 +72,28 @@ hipError_t launch_combine_backward(const Dims &d, int64_t capacity, const uint16
                                    const uint16_t *expert_out, uint16_t *grad_expert_out,
                                    float *grad_weights, const int32_t *expert_offsets,
                                    const int32_t *row_src, hipStream_t stream);
+
+hipError_t launch_dispatch_ranked(const Dims &d, bool fp8, const uint16_t *x,
+                                  const int32_t *topk_idx, const float *topk_weights,
+                                  const int32_t *expert_offsets, const char *ws, int64_t capacity,
+                                  int64_t ranked_capacity, void *ne_x, float *ne_scales,
+                                  int32_t *ne_topk_idx, float *ne_topk_weights, int32_t *ne_src,
+                                  int32_t *rank_token_offsets, int32_t *tok_rank_row,
+                                  int32_t *tok_slot_row, int32_t *status, hipStream_t stream);
+
+hipError_t launch_expand(const Dims &d, bool fp8, int64_t ranked_capacity, const void *ne_x,
+                         const float *ne_scales, const int32_t *ne_topk_idx,
+                         const float *ne_topk_weights, const int32_t *ne_src,
+                         const int32_t *rank_token_offsets, const int32_t *expert_offsets,
+                         const char *ws, int64_t capacity, void *recv_x, float *recv_scales,
+                         float *recv_weights, int32_t *row_src, int32_t *status,
+                         hipStream_t stream);
+
+hipError_t launch_combine_ranked(const Dims &d, int64_t capacity, int64_t ranked_capacity,
+                                 const uint16_t *y, const int32_t *tok_slot_row,
+                                 const int32_t *ne_topk_idx, const float *ne_topk_weights,
+                                 const int32_t *ne_src, const int32_t *rank_token_offsets,
+                                 const int32_t *tok_rank_row, float *partials, uint16_t *out,
+                                 hipStream_t stream);
 
 }  // namespace ep

@@ -106,6 +106,7 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
     int32_t *__restrict__ cnt_ws, int32_t *__restrict__ num_tokens_per_expert,
     int32_t *__restrict__ num_tokens_per_rank, int32_t *__restrict__ expert_offsets,
     int32_t *__restrict__ rank_offsets, int32_t *__restrict__ header,
+    unsigned long long *__restrict__ rank_ballot_ws, int32_t *__restrict__ rank_tok_off,
     int32_t *__restrict__ status) {
   // [kWavesPerBlock][E] expert bitmasks; the scanning workgroup then uses
   // the E + 1 words after them for aligned counts / offsets.
@@ -153,10 +154,15 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
     }
     if (bad) flag(status, EP_STATUS_BIT_ROUTE);
 
-    // Distinct tokens per rank in this tile.
+    // Distinct tokens per rank in this tile.  Each wave's ballot per rank
+    // goes to the workspace: the non-expanded dispatch places a token among
+    // a rank's tokens from these words.
     for (int r = 0; r < R; ++r) {
       const unsigned long long b = __ballot((rmask >> r) & 1ull);
-      if (lane == 0 && b) atomicAdd(&rank_cnt[r], (int32_t)__popcll(b));
+      if (lane == 0) {
+        rank_ballot_ws[((int64_t)tile * kWavesPerBlock + wave) * R + r] = b;
+        if (b) atomicAdd(&rank_cnt[r], (int32_t)__popcll(b));
+      }
     }
     __syncthreads();
 
@@ -201,7 +207,10 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
         }
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) {
-          if (t0 + b < ntiles) tile_cnt[(int64_t)(t0 + b) * E + e] = run;
+          if (t0 + b < ntiles) {
+            tile_cnt[(int64_t)(t0 + b) * E + e] = run;
+            if (e < R) tile_rank_cnt[(int64_t)(t0 + b) * R + e] = rank_sum;
+          }
           run += c[b];
           rank_sum += rc[b];
         }
@@ -210,7 +219,21 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
       num_tokens_per_expert[e] = run;
       aligned[e] = (run + d.A - 1) / d.A * d.A;
     }
+    // Thread r < R summed rank r's tile counts above (R <= E, so e = r is its
+    // first expert) and left exclusive tile bases per rank behind.  The
+    // first wave (R <= 64 lanes) scans the counts into the starts of the
+    // ranks' token partitions (the non-expanded layout).
     if (tid < R) num_tokens_per_rank[tid] = rank_sum;
+    if (wave == 0) {
+      const int32_t v = lane < R ? rank_sum : 0;
+      int32_t inc = v;
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int32_t u = __shfl_up(inc, off);
+        if (lane >= off) inc += u;
+      }
+      if (lane < R) rank_tok_off[lane] = inc - v;
+      if (lane == R - 1) rank_tok_off[R] = inc;
+    }
     __syncthreads();
 
     // Exclusive scan of the aligned counts over experts: each thread owns a
@@ -612,6 +635,344 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Non-expanded (rank-deduplicated) path ("Deep Dive - DeepEP", "Why expert
+// parallelism needs a communication layer": a token crosses to a rank once
+// however many of its experts live there; "Dispatch: layout, move, and
+// epilogue": a non-expanded row is a source token with its top-k metadata,
+// and the copy epilogue expands rows into the expert GEMM layout).
+// ---------------------------------------------------------------------------
+
+// One payload chunk of a token (16 values per lane): bf16 bits, or E4M3
+// codes plus the block scale (held by lanes 0, 8, 16, ...).
+struct Payload16 {
+  uint4 lo, hi;  // bf16: 16 values; FP8: lo = 16 codes
+  float scale;
+};
+
+// Lanes own 16 values; with H % 16 == 8 (bf16 rows) the last lane of a row
+// owns only its lower 8, so the upper half is guarded separately (FP8 rows
+// have H % 128 == 0).
+template <bool kFp8>
+__device__ __forceinline__ Payload16 load_payload(const uint16_t *__restrict__ x, int64_t t,
+                                                  int64_t H, int col, bool in) {
+  Payload16 p;
+  p.lo = make_uint4(0, 0, 0, 0);
+  p.hi = p.lo;
+  p.scale = 0.0f;
+  if (in) {
+    p.lo = *reinterpret_cast<const uint4 *>(x + t * H + col);
+    if (col + 8 < H) p.hi = *reinterpret_cast<const uint4 *>(x + t * H + col + 8);
+  }
+  if (kFp8) {
+    float amax = fmaxf(amax8(p.lo), amax8(p.hi));
+#pragma unroll
+    for (int m = 1; m < 8; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+    const float s = amax / 448.0f;
+    const uint2 q0 = quantize8(p.lo, s);
+    const uint2 q1 = quantize8(p.hi, s);
+    p.lo = make_uint4(q0.x, q0.y, q1.x, q1.y);
+    p.scale = s;
+  }
+  return p;
+}
+
+template <bool kFp8>
+__device__ __forceinline__ void store_payload(void *__restrict__ rows, float *__restrict__ scales,
+                                              int64_t r, int64_t H, int col, int lane,
+                                              const Payload16 &p) {
+  if (kFp8) {
+    store_stream(static_cast<uint8_t *>(rows) + r * H + col, p.lo);
+    if ((lane & 7) == 0) scales[r * (H / 128) + col / 128] = p.scale;
+  } else {
+    uint16_t *dst = static_cast<uint16_t *>(rows) + r * H + col;
+    store_stream(dst, p.lo);
+    if (col + 8 < H) store_stream(dst + 8, p.hi);
+  }
+}
+
+// Row of token t on rank r (lanes r < R), -1 if the token has no expert on
+// r: the rank's partition start, plus earlier tiles' tokens on r, plus the
+// tokens on r before t in its tile (earlier waves' ballots, then lanes below
+// in its own wave's ballot).
+__device__ __forceinline__ int32_t rank_row(const Dims &d, int64_t t, int lane,
+                                            const unsigned long long *__restrict__ rank_ballot,
+                                            const int32_t *__restrict__ rank_tok_off,
+                                            const int32_t *__restrict__ tile_rank_base,
+                                            int64_t ranked_capacity, int32_t *__restrict__ status) {
+  int32_t row = -1;
+  if (lane < d.R) {
+    const int64_t tile = t / kTileTokens;
+    const int w = (int)(t % kTileTokens) / kWave;
+    const int tl = (int)(t % kWave);
+    const unsigned long long *b = rank_ballot + tile * kWavesPerBlock * d.R + lane;
+    const unsigned long long mine = b[(int64_t)w * d.R];
+    if ((mine >> tl) & 1ull) {
+      int32_t pos = __popcll(mine & ((1ull << tl) - 1ull));
+      for (int ww = 0; ww < w; ++ww) pos += __popcll(b[(int64_t)ww * d.R]);
+      const int64_t r = (int64_t)rank_tok_off[lane] + tile_rank_base[tile * d.R + lane] + pos;
+      if (r < ranked_capacity)
+        row = (int32_t)r;
+      else
+        flag(status, EP_STATUS_BIT_CAPACITY);
+    }
+  }
+  return row;
+}
+
+template <bool kFp8>
+__global__ __launch_bounds__(kBlock) void dispatch_ranked_kernel(
+    Dims d, int32_t nchunks, const uint16_t *__restrict__ x, const int32_t *__restrict__ topk_idx,
+    const float *__restrict__ topk_weights, const int32_t *__restrict__ expert_offsets,
+    const int32_t *__restrict__ header, const int32_t *__restrict__ tile_base,
+    const int32_t *__restrict__ slot_rank, const int32_t *__restrict__ tile_rank_base,
+    const unsigned long long *__restrict__ rank_ballot, const int32_t *__restrict__ rank_tok_off,
+    int64_t capacity, int64_t ranked_capacity, void *__restrict__ ne_x,
+    float *__restrict__ ne_scales, int32_t *__restrict__ ne_topk_idx,
+    float *__restrict__ ne_topk_weights, int32_t *__restrict__ ne_src,
+    int32_t *__restrict__ rank_token_offsets, int32_t *__restrict__ tok_rank_row,
+    int32_t *__restrict__ tok_slot_row, int32_t *__restrict__ status) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int item = uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
+  if (item == 0) {
+    if (!workspace_ok(header, d)) {
+      if (lane == 0) flag(status, EP_STATUS_BIT_WORKSPACE);
+    } else {
+      for (int i = lane; i <= d.R; i += kWave) rank_token_offsets[i] = rank_tok_off[i];
+    }
+  }
+  if (item >= d.T * nchunks) return;
+  if (!workspace_ok(header, d)) return;
+  const int64_t t = item / nchunks;
+  const int chunk = item - (int)t * nchunks;
+  const int32_t row = rank_row(d, t, lane, rank_ballot, rank_tok_off, tile_rank_base,
+                               ranked_capacity, status);
+  if (chunk == 0) {
+    const int epr = d.E / d.R;
+    if (lane < d.R) {
+      tok_rank_row[t * d.R + lane] = row;
+      if (row >= 0) ne_src[row] = (int32_t)t;
+    }
+    // The token's top-k slice for each of its ranks: pairs (r, j) over
+    // lanes.  Every lane runs every round so the shuffle's source lane is
+    // always active.
+    for (int base = 0; base < d.R * d.k; base += kWave) {
+      const int pr = base + lane;
+      const int r = min(pr / d.k, d.R - 1);
+      const int j = pr - (pr / d.k) * d.k;
+      const int32_t rr = __shfl(row, r);
+      if (pr >= d.R * d.k || rr < 0) continue;
+      const int32_t e = topk_idx[t * d.k + j];
+      const bool local = e >= 0 && e < d.E && e / epr == r;
+      ne_topk_idx[(int64_t)rr * d.k + j] = local ? e - r * epr : -1;
+      if (ne_topk_weights != nullptr)
+        ne_topk_weights[(int64_t)rr * d.k + j] =
+            (local && topk_weights != nullptr) ? topk_weights[t * d.k + j] : 0.0f;
+    }
+    // The expanded handle (rows the receiver's expand will fill).
+    const int32_t srow = selection_row(d, t, lane, false, topk_idx, topk_weights, expert_offsets,
+                                       tile_base, slot_rank, capacity, nullptr, nullptr, nullptr,
+                                       status);
+    if (lane < d.k) tok_slot_row[t * d.k + lane] = srow;
+  }
+
+  const int64_t H = d.H;
+  const int col = chunk * kChunkCols + lane * 16;
+  const bool in = col < H;
+  const Payload16 p = load_payload<kFp8>(x, t, H, col, in);
+  for (int r = 0; r < d.R; ++r) {
+    const int32_t rr = lane_value(row, r);
+    if (rr < 0 || !in) continue;
+    store_payload<kFp8>(ne_x, ne_scales, rr, H, col, lane, p);
+  }
+}
+
+// Receiver-side expand: non-expanded row q (rank r, token t) goes to the
+// expert-major row of each of its local slots.
+template <bool kFp8>
+__global__ __launch_bounds__(kBlock) void expand_kernel(
+    Dims d, int32_t nchunks, int64_t ranked_capacity, const void *__restrict__ ne_x,
+    const float *__restrict__ ne_scales, const int32_t *__restrict__ ne_topk_idx,
+    const float *__restrict__ ne_topk_weights, const int32_t *__restrict__ ne_src,
+    const int32_t *__restrict__ rank_token_offsets, const int32_t *__restrict__ expert_offsets,
+    const int32_t *__restrict__ header, const int32_t *__restrict__ tile_base,
+    const int32_t *__restrict__ slot_rank, int64_t capacity, void *__restrict__ recv_x,
+    float *__restrict__ recv_scales, float *__restrict__ recv_weights,
+    int32_t *__restrict__ row_src, int32_t *__restrict__ status) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int item = uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
+  const int64_t q = item / nchunks;
+  const int chunk = item - (int)q * nchunks;
+  const int64_t rows = rank_token_offsets[d.R];
+  if (q >= rows || q >= ranked_capacity) return;
+  if (!workspace_ok(header, d)) {
+    if (lane == 0) flag(status, EP_STATUS_BIT_WORKSPACE);
+    return;
+  }
+  // The row's rank: how many partition starts 1..R are at or below q.
+  const bool le_q = lane >= 1 && lane <= d.R && rank_token_offsets[lane] <= q;
+  const int r = uniform((int)__popcll(__ballot(le_q)));
+  const int64_t t = uniform(ne_src[q]);
+  if (r >= d.R || t < 0 || t >= d.T) {
+    if (lane == 0) flag(status, EP_STATUS_BIT_ROUTE);
+    return;
+  }
+  const int epr = d.E / d.R;
+  int32_t row = -1;
+  if (lane < d.k) {
+    const int32_t le = ne_topk_idx[q * d.k + lane];
+    if (le >= 0 && le < epr) {
+      const int e = r * epr + le;
+      const int32_t rank = slot_rank[t * d.k + lane];
+      const int64_t p = rank < 0 ? -1
+                                 : (int64_t)expert_offsets[e] +
+                                       tile_base[(t / kTileTokens) * d.E + e] + rank;
+      if (p >= 0 && p < capacity) {
+        row = (int32_t)p;
+        if (chunk == 0) {
+          row_src[p] = (int32_t)(t * d.k + lane);
+          if (recv_weights != nullptr && ne_topk_weights != nullptr)
+            recv_weights[p] = ne_topk_weights[q * d.k + lane];
+        }
+      } else {
+        flag(status, EP_STATUS_BIT_CAPACITY);
+      }
+    }
+  }
+  const int64_t H = d.H;
+  const int col = chunk * kChunkCols + lane * 16;
+  const bool in = col < H;
+  Payload16 pl;
+  pl.lo = make_uint4(0, 0, 0, 0);
+  pl.hi = pl.lo;
+  pl.scale = 0.0f;
+  if (in) {
+    if (kFp8) {
+      pl.lo = *reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(ne_x) + q * H + col);
+      if ((lane & 7) == 0) pl.scale = ne_scales[q * (H / 128) + col / 128];
+    } else {
+      const uint16_t *src = static_cast<const uint16_t *>(ne_x) + q * H + col;
+      pl.lo = *reinterpret_cast<const uint4 *>(src);
+      if (col + 8 < H) pl.hi = *reinterpret_cast<const uint4 *>(src + 8);
+    }
+  }
+  for (int j = 0; j < d.k; ++j) {
+    const int32_t rr = lane_value(row, j);
+    if (rr < 0 || !in) continue;
+    store_payload<kFp8>(recv_x, recv_scales, rr, H, col, lane, pl);
+  }
+}
+
+// Ranked combine, stage 1: per non-expanded row, the fp32 sum of its local
+// slots' (weighted) expert rows in slot order.
+template <bool kWeighted>
+__global__ __launch_bounds__(kBlock) void combine_ranked_partial_kernel(
+    Dims d, int32_t nchunks, int64_t capacity, int64_t ranked_capacity,
+    const uint16_t *__restrict__ y, const int32_t *__restrict__ tok_slot_row,
+    const int32_t *__restrict__ ne_topk_idx, const float *__restrict__ ne_topk_weights,
+    const int32_t *__restrict__ ne_src, const int32_t *__restrict__ rank_token_offsets,
+    float *__restrict__ partials) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int item = uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
+  const int64_t q = item / nchunks;
+  const int chunk = item - (int)q * nchunks;
+  const int64_t rows = rank_token_offsets[d.R];
+  if (q >= rows || q >= ranked_capacity) return;
+  const int64_t t = uniform(ne_src[q]);
+  if (t < 0 || t >= d.T) return;
+  int32_t row = -1;
+  float gate = 0.0f;
+  if (lane < d.k && ne_topk_idx[q * d.k + lane] >= 0) {
+    const int32_t p = tok_slot_row[t * d.k + lane];
+    if (p >= 0 && p < capacity) {
+      row = p;
+      if (kWeighted) gate = ne_topk_weights[q * d.k + lane];
+    }
+  }
+  const int64_t H = d.H;
+  const int col = chunk * kCombineCols + lane * 8;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+  for (int jb = 0; jb < d.k; jb += 8) {
+    uint4 v[8];
+    int32_t r[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      r[jj] = (jb + jj < d.k) ? lane_value(row, jb + jj) : -1;
+      if (r[jj] >= 0 && col < H) v[jj] = load_stream(y + (int64_t)r[jj] * H + col);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      if (r[jj] < 0) continue;
+      const float g = kWeighted ? lane_value_f(gate, jb + jj) : 1.0f;
+      const uint32_t w4[4] = {v[jj].x, v[jj].y, v[jj].z, v[jj].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (kWeighted) {
+          acc[2 * i] = __builtin_fmaf(g, bf16_lo(w4[i]), acc[2 * i]);
+          acc[2 * i + 1] = __builtin_fmaf(g, bf16_hi(w4[i]), acc[2 * i + 1]);
+        } else {
+          acc[2 * i] = acc[2 * i] + bf16_lo(w4[i]);
+          acc[2 * i + 1] = acc[2 * i + 1] + bf16_hi(w4[i]);
+        }
+      }
+    }
+  }
+  if (col < H) {
+    float *dst = partials + q * H + col;
+    store_stream(dst, make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]),
+                                 __float_as_uint(acc[2]), __float_as_uint(acc[3])));
+    store_stream(dst + 4, make_uint4(__float_as_uint(acc[4]), __float_as_uint(acc[5]),
+                                     __float_as_uint(acc[6]), __float_as_uint(acc[7])));
+  }
+}
+
+// Ranked combine, stage 2: per token, the fp32 sum of its ranks' partials in
+// rank order, rounded once to bf16.
+__global__ __launch_bounds__(kBlock) void combine_ranked_sum_kernel(
+    Dims d, int32_t nchunks, int64_t ranked_capacity, const float *__restrict__ partials,
+    const int32_t *__restrict__ tok_rank_row, uint16_t *__restrict__ out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int item = uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
+  if (item >= d.T * nchunks) return;
+  const int64_t t = item / nchunks;
+  const int chunk = item - (int)t * nchunks;
+  int32_t q = -1;
+  if (lane < d.R) {
+    const int32_t v = tok_rank_row[t * d.R + lane];
+    if (v >= 0 && v < ranked_capacity) q = v;
+  }
+  const int64_t H = d.H;
+  const int col = chunk * kCombineCols + lane * 8;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+  for (int r = 0; r < d.R; ++r) {
+    const int32_t qr = lane_value(q, r);
+    if (qr < 0 || col >= H) continue;
+    const float *src = partials + (int64_t)qr * H + col;
+    const uint4 a = load_stream(src);
+    const uint4 b = load_stream(src + 4);
+    acc[0] += __uint_as_float(a.x);
+    acc[1] += __uint_as_float(a.y);
+    acc[2] += __uint_as_float(a.z);
+    acc[3] += __uint_as_float(a.w);
+    acc[4] += __uint_as_float(b.x);
+    acc[5] += __uint_as_float(b.y);
+    acc[6] += __uint_as_float(b.z);
+    acc[7] += __uint_as_float(b.w);
+  }
+  if (col < H) {
+    uint4 o;
+    o.x = pack_bf16(acc[0], acc[1]);
+    o.y = pack_bf16(acc[2], acc[3]);
+    o.z = pack_bf16(acc[4], acc[5]);
+    o.w = pack_bf16(acc[6], acc[7]);
+    store_stream(out + t * H + col, o);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Backward of combine ("Deep Dive - DeepEP", "Combine: reverse routing plus
 // reduction": backward duality, and the gate gradient the autograd wrapper
 // still owes).  One wave per token walks the whole row in 512-column steps:
@@ -725,6 +1086,10 @@ WorkspaceLayout workspace_layout(int32_t T, int32_t k, int32_t E, int32_t R) {
   off += align256(sizeof(int32_t) * (size_t)E);
   w.slot_rank = off;
   off += align256(sizeof(int32_t) * (size_t)T * k);
+  w.rank_ballot = off;
+  off += align256(sizeof(unsigned long long) * (size_t)w.ntiles * kWavesPerBlock * R);
+  w.rank_tok_off = off;
+  off += align256(sizeof(int32_t) * ((size_t)R + 1));
   w.total = off;
   return w;
 }
@@ -745,7 +1110,9 @@ hipError_t launch_layout(const Dims &d, const int32_t *topk_idx, int32_t *num_to
                      reinterpret_cast<int32_t *>(ws + w.slot_rank), is_token_in_rank,
                      reinterpret_cast<int32_t *>(ws + w.cnt), num_tokens_per_expert,
                      num_tokens_per_rank, expert_offsets, rank_offsets,
-                     reinterpret_cast<int32_t *>(ws), status);
+                     reinterpret_cast<int32_t *>(ws),
+                     reinterpret_cast<unsigned long long *>(ws + w.rank_ballot),
+                     reinterpret_cast<int32_t *>(ws + w.rank_tok_off), status);
   return hipGetLastError();
 }
 
@@ -859,6 +1226,97 @@ hipError_t launch_combine_backward(const Dims &d, int64_t capacity, const uint16
   if (d.A > 1) {
     hipLaunchKernelGGL(zero_padding_rows_kernel, dim3(d.E), dim3(kBlock), 0, stream, d,
                        expert_offsets, row_src, capacity, grad_expert_out);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+}  // namespace ep
+
+namespace ep {
+
+hipError_t launch_dispatch_ranked(const Dims &d, bool fp8, const uint16_t *x,
+                                  const int32_t *topk_idx, const float *topk_weights,
+                                  const int32_t *expert_offsets, const char *ws, int64_t capacity,
+                                  int64_t ranked_capacity, void *ne_x, float *ne_scales,
+                                  int32_t *ne_topk_idx, float *ne_topk_weights, int32_t *ne_src,
+                                  int32_t *rank_token_offsets, int32_t *tok_rank_row,
+                                  int32_t *tok_slot_row, int32_t *status, hipStream_t stream) {
+  const WorkspaceLayout w = workspace_layout(d.T, d.k, d.E, d.R);
+  const int32_t nchunks = (d.H + kChunkCols - 1) / kChunkCols;
+  const int64_t items = d.T > 0 ? (int64_t)d.T * nchunks : 1;  // item 0 also copies offsets
+  const dim3 grid((unsigned)((items + kWavesPerBlock - 1) / kWavesPerBlock));
+  auto kernel = fp8 ? dispatch_ranked_kernel<true> : dispatch_ranked_kernel<false>;
+  hipLaunchKernelGGL(kernel, grid, dim3(kBlock), 0, stream, d, nchunks, x, topk_idx, topk_weights,
+                     expert_offsets, reinterpret_cast<const int32_t *>(ws),
+                     reinterpret_cast<const int32_t *>(ws + w.tile_cnt),
+                     reinterpret_cast<const int32_t *>(ws + w.slot_rank),
+                     reinterpret_cast<const int32_t *>(ws + w.tile_rank_cnt),
+                     reinterpret_cast<const unsigned long long *>(ws + w.rank_ballot),
+                     reinterpret_cast<const int32_t *>(ws + w.rank_tok_off), capacity,
+                     ranked_capacity, ne_x, ne_scales, ne_topk_idx, ne_topk_weights, ne_src,
+                     rank_token_offsets, tok_rank_row, tok_slot_row, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_expand(const Dims &d, bool fp8, int64_t ranked_capacity, const void *ne_x,
+                         const float *ne_scales, const int32_t *ne_topk_idx,
+                         const float *ne_topk_weights, const int32_t *ne_src,
+                         const int32_t *rank_token_offsets, const int32_t *expert_offsets,
+                         const char *ws, int64_t capacity, void *recv_x, float *recv_scales,
+                         float *recv_weights, int32_t *row_src, int32_t *status,
+                         hipStream_t stream) {
+  const WorkspaceLayout w = workspace_layout(d.T, d.k, d.E, d.R);
+  const int32_t nchunks = (d.H + kChunkCols - 1) / kChunkCols;
+  if (ranked_capacity > 0) {
+    const int64_t items = ranked_capacity * nchunks;
+    const dim3 grid((unsigned)((items + kWavesPerBlock - 1) / kWavesPerBlock));
+    auto kernel = fp8 ? expand_kernel<true> : expand_kernel<false>;
+    hipLaunchKernelGGL(kernel, grid, dim3(kBlock), 0, stream, d, nchunks, ranked_capacity, ne_x,
+                       ne_scales, ne_topk_idx, ne_topk_weights, ne_src, rank_token_offsets,
+                       expert_offsets, reinterpret_cast<const int32_t *>(ws),
+                       reinterpret_cast<const int32_t *>(ws + w.tile_cnt),
+                       reinterpret_cast<const int32_t *>(ws + w.slot_rank), capacity, recv_x,
+                       recv_scales, recv_weights, row_src, status);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (d.A > 1) {
+    hipLaunchKernelGGL(pad_fill_kernel, dim3(d.E), dim3(kBlock), 0, stream, d, fp8,
+                       expert_offsets, reinterpret_cast<const int32_t *>(ws + w.cnt), capacity,
+                       recv_x, recv_scales, ne_topk_weights != nullptr ? recv_weights : nullptr,
+                       row_src);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_combine_ranked(const Dims &d, int64_t capacity, int64_t ranked_capacity,
+                                 const uint16_t *y, const int32_t *tok_slot_row,
+                                 const int32_t *ne_topk_idx, const float *ne_topk_weights,
+                                 const int32_t *ne_src, const int32_t *rank_token_offsets,
+                                 const int32_t *tok_rank_row, float *partials, uint16_t *out,
+                                 hipStream_t stream) {
+  const int32_t nchunks = (d.H + kCombineCols - 1) / kCombineCols;
+  if (ranked_capacity > 0) {
+    const int64_t items = ranked_capacity * nchunks;
+    const dim3 grid((unsigned)((items + kWavesPerBlock - 1) / kWavesPerBlock));
+    if (ne_topk_weights != nullptr)
+      hipLaunchKernelGGL(combine_ranked_partial_kernel<true>, grid, dim3(kBlock), 0, stream, d,
+                         nchunks, capacity, ranked_capacity, y, tok_slot_row, ne_topk_idx,
+                         ne_topk_weights, ne_src, rank_token_offsets, partials);
+    else
+      hipLaunchKernelGGL(combine_ranked_partial_kernel<false>, grid, dim3(kBlock), 0, stream, d,
+                         nchunks, capacity, ranked_capacity, y, tok_slot_row, ne_topk_idx,
+                         ne_topk_weights, ne_src, rank_token_offsets, partials);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (d.T > 0) {
+    const int64_t items = (int64_t)d.T * nchunks;
+    const dim3 grid((unsigned)((items + kWavesPerBlock - 1) / kWavesPerBlock));
+    hipLaunchKernelGGL(combine_ranked_sum_kernel, grid, dim3(kBlock), 0, stream, d, nchunks,
+                       ranked_capacity, partials, tok_rank_row, out);
     return hipGetLastError();
   }
   return hipSuccess;

@@ -100,6 +100,23 @@ typedef struct ep_handle {
   const int32_t *expert_offsets; /* [E + 1]: aligned start of each expert segment */
 } ep_handle_t;
 
+/*
+ * Handle of the non-expanded (rank-deduplicated) dispatch: what the source
+ * keeps to expand and to combine through per-rank partial sums.  A plain
+ * host struct borrowing the caller's device arrays, valid for one route.
+ */
+typedef struct ep_ranked_handle {
+  ep_config_t config;
+  int64_t capacity;                  /* expanded rows (expert-major buffers) */
+  int64_t ranked_capacity;           /* non-expanded rows */
+  const int32_t *rank_token_offsets; /* [R + 1]: rank r's rows are [off[r], off[r+1]) */
+  const int32_t *tok_rank_row;       /* [T, R]: non-expanded row of (t, r), -1 if none */
+  const int32_t *tok_slot_row;       /* [T, k]: expanded row of (t, j), -1 if unused */
+  const int32_t *ne_topk_idx;        /* [ranked_capacity, k]: local expert of slot j or -1 */
+  const float *ne_topk_weights;      /* [ranked_capacity, k]: gate of slot j there, else 0 */
+  const int32_t *ne_src;             /* [ranked_capacity]: source token of the row */
+} ep_ranked_handle_t;
+
 /* Static description of a status code (never NULL). */
 const char *ep_status_string(ep_status_t status);
 
@@ -289,6 +306,83 @@ ep_status_t ep_combine_backward(const ep_handle_t *handle, const uint16_t *grad_
                                 const float *topk_weights, const uint16_t *expert_out,
                                 uint16_t *grad_expert_out, float *grad_weights,
                                 hipStream_t stream);
+
+/* Host only.  Non-expanded rows that always suffice: T * min(k, R). */
+ep_status_t ep_ranked_capacity_rows(const ep_config_t *cfg, int64_t *rows_host);
+
+/*
+ * Non-expanded dispatch ("Deep Dive - DeepEP", "Why expert parallelism
+ * needs a communication layer": a token crosses to a destination rank once
+ * however many of its experts live there; "Dispatch: layout, move, and
+ * epilogue": in non-expanded mode a received row is a source token with its
+ * top-k metadata).  Rank r's rows are [rank_token_offsets[r],
+ * rank_token_offsets[r+1]), one per token with an expert on r, in ascending
+ * token order; the row count is the sum of num_tokens_per_rank.  Row q
+ * carries the token's payload (bf16, or E4M3 codes + scales exactly as
+ * ep_dispatch computes them), ne_src[q] = t and the token's top-k slice for
+ * the rank: ne_topk_idx[q, j] = e - r*E/R when slot j's expert e lives on
+ * r, else -1; ne_topk_weights[q, j] = w[t, j] there, else 0.  It also
+ * writes tok_rank_row and the expanded handle tok_slot_row (the rows
+ * ep_expand will fill, as ep_dispatch would place them).
+ *
+ *   workspace / expert_offsets  from ep_get_dispatch_layout of this route
+ *   capacity         rows of the expanded buffers (for tok_slot_row)
+ *   ranked_capacity  rows of ne_x / ne_scales / ne_topk_* / ne_src
+ *   ne_x             [ranked_capacity, H] bf16 or uint8 (E4M3) out
+ *   ne_scales        [ranked_capacity, H/128] fp32 out (FP8 only)
+ *   ne_topk_idx      [ranked_capacity, k] int32 out
+ *   ne_topk_weights  [ranked_capacity, k] fp32 out, or NULL
+ *   ne_src           [ranked_capacity] int32 out
+ *   rank_token_offsets [R + 1] int32 out
+ *   tok_rank_row     [T, R] int32 out;  tok_slot_row [T, k] int32 out
+ */
+ep_status_t ep_dispatch_ranked(const ep_config_t *cfg, ep_dtype_t recv_dtype, const uint16_t *x,
+                               const int32_t *topk_idx, const float *topk_weights,
+                               const int32_t *expert_offsets, const void *workspace,
+                               size_t workspace_bytes, int64_t capacity, int64_t ranked_capacity,
+                               void *ne_x, float *ne_scales, int32_t *ne_topk_idx,
+                               float *ne_topk_weights, int32_t *ne_src,
+                               int32_t *rank_token_offsets, int32_t *tok_rank_row,
+                               int32_t *tok_slot_row, int32_t *status,
+                               ep_ranked_handle_t *handle_host, hipStream_t stream);
+
+/*
+ * Receiver-side expand of non-expanded rows into the expert-major layout
+ * ("Deep Dive - DeepEP", "Dispatch: layout, move, and epilogue": the copy
+ * epilogue expands rows into the layout the expert GEMM reads).  Each
+ * received row is copied to the expert row of each of its local slots;
+ * the result (recv_x, recv_scales, recv_weights, row_src, padding) is
+ * identical to ep_dispatch of the same route.  workspace / expert_offsets
+ * are the layout's.  recv_weights may be NULL.  handle_host (optional)
+ * receives the expanded handle for ep_combine.
+ */
+ep_status_t ep_expand(const ep_ranked_handle_t *ranked, ep_dtype_t recv_dtype, const void *ne_x,
+                      const float *ne_scales, const int32_t *expert_offsets,
+                      const void *workspace, size_t workspace_bytes, void *recv_x,
+                      float *recv_scales, float *recv_weights, int32_t *row_src,
+                      int32_t *status, ep_handle_t *handle_host, hipStream_t stream);
+
+/*
+ * Combine through per-rank partial sums ("Deep Dive - DeepEP", "Combine:
+ * reverse routing plus reduction": staging per rank sends fewer rows; the
+ * partials are kept in fp32 because a bf16 subtotal can lose a small term to
+ * cancellation).  Stage 1, per non-expanded row q of token t on rank r:
+ *     partials[q, c] = fp32 sum, slot order j = 0.., over slots local to r, of
+ *                      ne_topk_weights[q, j] * expert_out[tok_slot_row[t, j], c]
+ *                      (one fused multiply-add each from +0; plain adds when
+ *                      weighted == 0)
+ * Stage 2: out[t, c] = bf16( fp32 sum over r = 0..R-1 with a row on r of
+ *                      partials[tok_rank_row[t, r], c], from +0 ).
+ * The result differs from ep_combine only by fp32 re-association (grouped
+ * by rank).
+ *
+ *   expert_out  [capacity, H] bf16
+ *   partials    [ranked_capacity, H] fp32 scratch/out
+ *   out         [T, H] bf16 out
+ */
+ep_status_t ep_combine_ranked(const ep_ranked_handle_t *ranked, const uint16_t *expert_out,
+                              int32_t weighted, float *partials, uint16_t *out,
+                              hipStream_t stream);
 
 /* Synchronises `stream`, reads the device status word and returns the
  * first error it holds (route, then capacity, then workspace) or EP_OK. */
