@@ -787,7 +787,12 @@ __global__ __launch_bounds__(kBlock) void dispatch_ranked_kernel(
 }
 
 // Receiver-side expand: non-expanded row q (rank r, token t) goes to the
-// expert-major row of each of its local slots.
+// expert-major row of each of its local slots.  One wave per received row:
+// the row's metadata is resolved once, and the payload is streamed in
+// batches of kExpandBatch 1024-column chunks whose loads are issued before
+// the first store.
+constexpr int kExpandBatch = 4;
+
 template <bool kFp8>
 __global__ __launch_bounds__(kBlock) void expand_kernel(
     Dims d, int32_t nchunks, int64_t ranked_capacity, const void *__restrict__ ne_x,
@@ -799,15 +804,40 @@ __global__ __launch_bounds__(kBlock) void expand_kernel(
     float *__restrict__ recv_scales, float *__restrict__ recv_weights,
     int32_t *__restrict__ row_src, int32_t *__restrict__ status) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int item = uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
-  const int64_t q = item / nchunks;
-  const int chunk = item - (int)q * nchunks;
+  const int64_t q = uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
+  if (q >= ranked_capacity) return;
   const int64_t rows = rank_token_offsets[d.R];
-  if (q >= rows || q >= ranked_capacity) return;
+  if (q >= rows) return;
   if (!workspace_ok(header, d)) {
     if (lane == 0) flag(status, EP_STATUS_BIT_WORKSPACE);
     return;
   }
+  const int64_t H = d.H;
+
+  // The first batch of payload only depends on q: load it before the
+  // metadata chain.
+  Payload16 pl[kExpandBatch];
+  auto load_batch = [&](int c0) {
+#pragma unroll
+    for (int b = 0; b < kExpandBatch; ++b) {
+      const int col = (c0 + b) * kChunkCols + lane * 16;
+      pl[b].lo = make_uint4(0, 0, 0, 0);
+      pl[b].hi = pl[b].lo;
+      pl[b].scale = 0.0f;
+      if (c0 + b < nchunks && col < H) {
+        if (kFp8) {
+          pl[b].lo = *reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(ne_x) + q * H + col);
+          if ((lane & 7) == 0) pl[b].scale = ne_scales[q * (H / 128) + col / 128];
+        } else {
+          const uint16_t *src = static_cast<const uint16_t *>(ne_x) + q * H + col;
+          pl[b].lo = *reinterpret_cast<const uint4 *>(src);
+          if (col + 8 < H) pl[b].hi = *reinterpret_cast<const uint4 *>(src + 8);
+        }
+      }
+    }
+  };
+  load_batch(0);
+
   // The row's rank: how many partition starts 1..R are at or below q.
   const bool le_q = lane >= 1 && lane <= d.R && rank_token_offsets[lane] <= q;
   const int r = uniform((int)__popcll(__ballot(le_q)));
@@ -828,37 +858,27 @@ __global__ __launch_bounds__(kBlock) void expand_kernel(
                                        tile_base[(t / kTileTokens) * d.E + e] + rank;
       if (p >= 0 && p < capacity) {
         row = (int32_t)p;
-        if (chunk == 0) {
-          row_src[p] = (int32_t)(t * d.k + lane);
-          if (recv_weights != nullptr && ne_topk_weights != nullptr)
-            recv_weights[p] = ne_topk_weights[q * d.k + lane];
-        }
+        row_src[p] = (int32_t)(t * d.k + lane);
+        if (recv_weights != nullptr && ne_topk_weights != nullptr)
+          recv_weights[p] = ne_topk_weights[q * d.k + lane];
       } else {
         flag(status, EP_STATUS_BIT_CAPACITY);
       }
     }
   }
-  const int64_t H = d.H;
-  const int col = chunk * kChunkCols + lane * 16;
-  const bool in = col < H;
-  Payload16 pl;
-  pl.lo = make_uint4(0, 0, 0, 0);
-  pl.hi = pl.lo;
-  pl.scale = 0.0f;
-  if (in) {
-    if (kFp8) {
-      pl.lo = *reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(ne_x) + q * H + col);
-      if ((lane & 7) == 0) pl.scale = ne_scales[q * (H / 128) + col / 128];
-    } else {
-      const uint16_t *src = static_cast<const uint16_t *>(ne_x) + q * H + col;
-      pl.lo = *reinterpret_cast<const uint4 *>(src);
-      if (col + 8 < H) pl.hi = *reinterpret_cast<const uint4 *>(src + 8);
+
+  for (int c0 = 0; c0 < nchunks; c0 += kExpandBatch) {
+    if (c0 > 0) load_batch(c0);
+    for (int j = 0; j < d.k; ++j) {
+      const int32_t rr = lane_value(row, j);
+      if (rr < 0) continue;
+#pragma unroll
+      for (int b = 0; b < kExpandBatch; ++b) {
+        const int col = (c0 + b) * kChunkCols + lane * 16;
+        if (c0 + b < nchunks && col < H)
+          store_payload<kFp8>(recv_x, recv_scales, rr, H, col, lane, pl[b]);
+      }
     }
-  }
-  for (int j = 0; j < d.k; ++j) {
-    const int32_t rr = lane_value(row, j);
-    if (rr < 0 || !in) continue;
-    store_payload<kFp8>(recv_x, recv_scales, rr, H, col, lane, pl);
   }
 }
 
@@ -1269,8 +1289,7 @@ hipError_t launch_expand(const Dims &d, bool fp8, int64_t ranked_capacity, const
   const WorkspaceLayout w = workspace_layout(d.T, d.k, d.E, d.R);
   const int32_t nchunks = (d.H + kChunkCols - 1) / kChunkCols;
   if (ranked_capacity > 0) {
-    const int64_t items = ranked_capacity * nchunks;
-    const dim3 grid((unsigned)((items + kWavesPerBlock - 1) / kWavesPerBlock));
+    const dim3 grid((unsigned)((ranked_capacity + kWavesPerBlock - 1) / kWavesPerBlock));
     auto kernel = fp8 ? expand_kernel<true> : expand_kernel<false>;
     hipLaunchKernelGGL(kernel, grid, dim3(kBlock), 0, stream, d, nchunks, ranked_capacity, ne_x,
                        ne_scales, ne_topk_idx, ne_topk_weights, ne_src, rank_token_offsets,
