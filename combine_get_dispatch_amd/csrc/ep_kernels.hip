@@ -995,11 +995,13 @@ __global__ __launch_bounds__(kBlock) void combine_ranked_sum_kernel(
 // ---------------------------------------------------------------------------
 // Backward of combine ("Deep Dive - DeepEP", "Combine: reverse routing plus
 // reduction": backward duality, and the gate gradient the autograd wrapper
-// still owes).  One wave per token walks the whole row in 512-column steps:
+// still owes).  One 4-wave workgroup per token; wave w takes the 512-column
+// chunks w, w + 4, ...:
 //   grad_expert_out[row_j, c] = bf16(w[t,j] * grad_out[t,c])
 //   grad_w[t,j]               = sum_c expert_out[row_j, c] * grad_out[t,c]
-// Each lane accumulates its columns' products in fp32 in a fixed order and
-// an xor butterfly adds the 64 lane sums, so every run gives the same bits.
+// Each lane accumulates its columns' products in fp32 in a fixed order, an
+// xor butterfly adds the wave's 64 lane sums, and the four wave sums are
+// added in wave order: every run gives the same bits.
 // ---------------------------------------------------------------------------
 
 template <int K>
@@ -1008,18 +1010,19 @@ __global__ __launch_bounds__(kBlock) void combine_backward_kernel(
     const int32_t *__restrict__ tok_slot_row, const float *__restrict__ topk_weights,
     const uint16_t *__restrict__ expert_out, uint16_t *__restrict__ grad_expert_out,
     float *__restrict__ grad_weights) {
+  __shared__ float wave_dot[kWavesPerBlock][K];
   const int lane = threadIdx.x & (kWave - 1);
-  const int t = uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
-  if (t >= d.T) return;
+  const int wave = threadIdx.x / kWave;
+  const int64_t t = blockIdx.x;
   const int64_t H = d.H;
   const bool want_gate = grad_weights != nullptr;
 
   int32_t row = -1;
   float gate = 1.0f;
   if (lane < d.k) {
-    const int32_t r = tok_slot_row[(int64_t)t * d.k + lane];
+    const int32_t r = tok_slot_row[t * d.k + lane];
     if (r >= 0 && r < capacity) row = r;
-    if (topk_weights != nullptr) gate = topk_weights[(int64_t)t * d.k + lane];
+    if (topk_weights != nullptr) gate = topk_weights[t * d.k + lane];
   }
   int32_t rows[K];
   float gates[K];
@@ -1031,8 +1034,9 @@ __global__ __launch_bounds__(kBlock) void combine_backward_kernel(
     dot[j] = 0.0f;
   }
 
-  for (int64_t col = lane * 8; col < H; col += kCombineCols) {
-    const uint4 gv = *reinterpret_cast<const uint4 *>(grad_out + (int64_t)t * H + col);
+  for (int64_t col = (int64_t)wave * kCombineCols + lane * 8; col < H;
+       col += (int64_t)kWavesPerBlock * kCombineCols) {
+    const uint4 gv = *reinterpret_cast<const uint4 *>(grad_out + t * H + col);
     const float g[8] = {bf16_lo(gv.x), bf16_hi(gv.x), bf16_lo(gv.y), bf16_hi(gv.y),
                         bf16_lo(gv.z), bf16_hi(gv.z), bf16_lo(gv.w), bf16_hi(gv.w)};
     uint4 yv[K];
@@ -1067,7 +1071,16 @@ __global__ __launch_bounds__(kBlock) void combine_backward_kernel(
       float v = dot[j];
 #pragma unroll
       for (int m = kWave / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-      if (lane == 0 && j < d.k) grad_weights[(int64_t)t * d.k + j] = rows[j] >= 0 ? v : 0.0f;
+      if (lane == 0) wave_dot[wave][j] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < d.k) {
+      const int j = threadIdx.x;
+      float v = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWavesPerBlock; ++w) v += wave_dot[w][j];
+      const int32_t r = tok_slot_row[t * d.k + j];
+      grad_weights[t * d.k + j] = (r >= 0 && r < capacity) ? v : 0.0f;
     }
   }
 }
@@ -1235,7 +1248,7 @@ hipError_t launch_combine_backward(const Dims &d, int64_t capacity, const uint16
                                    float *grad_weights, const int32_t *expert_offsets,
                                    const int32_t *row_src, hipStream_t stream) {
   if (d.T > 0) {
-    const dim3 grid((unsigned)((d.T + kWavesPerBlock - 1) / kWavesPerBlock));
+    const dim3 grid((unsigned)d.T);
     auto kernel = d.k <= 8 ? combine_backward_kernel<8>
                            : (d.k <= 16 ? combine_backward_kernel<16> : combine_backward_kernel<32>);
     hipLaunchKernelGGL(kernel, grid, dim3(kBlock), 0, stream, d, capacity, grad_out, tok_slot_row,
