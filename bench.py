@@ -14,6 +14,12 @@ method must move:
   combine   M*2H (gathered rows) + T*k*8 (tok_slot_row, gates) + T*2H (out)
 with M valid selections.  Workspace traffic is overhead and not counted.
 
+`value` is the mean over K back-to-back steps.  `step_us` adds per-step
+median / p10 / p90 for warm steps and for cold ones, where an untimed pass
+over 1 GiB before each step evicts the 256 MB MALL and the L2s (`cold`: a
+read pass; `cold_dirty`: a write pass, whose dirty lines the step then
+writes back).
+
 Prints one JSON line.  --gpus above 1 exits: this build runs on one GPU.
 """
 from __future__ import annotations
@@ -437,6 +443,34 @@ def main():
     b.check_status()
     per_us = {n: float(np.mean([a.elapsed_time(c) for a, c in ev[n]])) * 1e3 for n in names}
 
+    # per-step distribution: warm (back to back), and cold, where an untimed
+    # pass over 1 GiB before each step evicts the 256 MB MALL and the L2s.  A
+    # read pass leaves the caches clean; a write pass leaves them dirty, so the
+    # step also pays for writing that data back.
+    def step_distribution(evict: str | None) -> dict:
+        n = min(args.steps, 30)
+        scratch = torch.ones(1 << 28, dtype=torch.int32, device=dev) if evict else None
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(n)]
+        for i, (a, c) in enumerate(pairs):
+            if evict == "read":
+                scratch.amax()
+            elif evict == "write":
+                scratch.fill_(i)
+            a.record(stream)
+            step()
+            c.record(stream)
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(c) * 1e3 for a, c in pairs])
+        del scratch
+        return {"median": round(float(np.median(us)), 2),
+                "p10": round(float(np.percentile(us, 10)), 2),
+                "p90": round(float(np.percentile(us, 90)), 2), "n": n}
+
+    step_us = {"warm": step_distribution(None), "cold": step_distribution("read"),
+               "cold_dirty": step_distribution("write")}
+    b.check_status()
+
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -479,6 +513,7 @@ def main():
         "kernel_us": {n: round(v, 2) for n, v in per_us.items()},
         "kernel_roofline_frac": {n: round(by[n] / (per_us[n] / 1e6) / 1e9 / PEAK_HBM_GBPS, 4)
                                  for n in names},
+        "step_us": step_us,
         "host_wall_s": round(wall, 4),
         "roofline": {
             "kernel": dom,

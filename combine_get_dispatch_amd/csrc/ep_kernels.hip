@@ -967,20 +967,32 @@ __global__ __launch_bounds__(kBlock) void combine_ranked_sum_kernel(
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-  for (int r = 0; r < d.R; ++r) {
-    const int32_t qr = lane_value(q, r);
-    if (qr < 0 || col >= H) continue;
-    const float *src = partials + (int64_t)qr * H + col;
-    const uint4 a = load_stream(src);
-    const uint4 b = load_stream(src + 4);
-    acc[0] += __uint_as_float(a.x);
-    acc[1] += __uint_as_float(a.y);
-    acc[2] += __uint_as_float(a.z);
-    acc[3] += __uint_as_float(a.w);
-    acc[4] += __uint_as_float(b.x);
-    acc[5] += __uint_as_float(b.y);
-    acc[6] += __uint_as_float(b.z);
-    acc[7] += __uint_as_float(b.w);
+  // Ranks in batches of 8: the batch's loads are all issued before the
+  // first add, and the adds run in rank order.
+  for (int rb = 0; rb < d.R; rb += 8) {
+    int32_t qq[8];
+    uint4 a[8], b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      qq[i] = rb + i < d.R ? lane_value(q, rb + i) : -1;
+      if (qq[i] >= 0 && col < H) {
+        const float *src = partials + (int64_t)qq[i] * H + col;
+        a[i] = load_stream(src);
+        b[i] = load_stream(src + 4);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (qq[i] < 0 || col >= H) continue;
+      acc[0] += __uint_as_float(a[i].x);
+      acc[1] += __uint_as_float(a[i].y);
+      acc[2] += __uint_as_float(a[i].z);
+      acc[3] += __uint_as_float(a[i].w);
+      acc[4] += __uint_as_float(b[i].x);
+      acc[5] += __uint_as_float(b[i].y);
+      acc[6] += __uint_as_float(b[i].z);
+      acc[7] += __uint_as_float(b[i].w);
+    }
   }
   if (col < H) {
     uint4 o;
