@@ -339,6 +339,8 @@ def main():
     ap.add_argument("--ranked", action="store_true",
                     help="time the non-expanded path (dispatch_ranked + expand + "
                          "combine_ranked; its own JSON line)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one forward step as a HIP graph and time its replays")
     ap.add_argument("--direction", choices=("forward", "backward"), default="forward",
                     help="backward times ep_dispatch_backward + ep_combine_backward (its own "
                          "JSON line, not the forward metric)")
@@ -414,6 +416,26 @@ def main():
         step()
     b.check_status()
     M = int(b.expert_offsets[-1].item())
+
+    eager_step = step
+    if args.graph:
+        # one step captured as a HIP graph; replays launch its kernels without
+        # the host's per-call launch overhead
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            eager_step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            eager_step()
+        torch.cuda.synchronize()
+        step = graph.replay
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        b.check_status()
 
     # whole steps
     torch.cuda.synchronize()
@@ -506,7 +528,8 @@ def main():
                    "experts": w.num_experts, "logical_ranks": w.num_ranks,
                    "dispatch_payload": ("fp8_e4m3 (pre-quantised input)" if args.fp8_input
                                         else "fp8_e4m3" if w.fp8 else "bf16"),
-                   "valid_selections": M},
+                   "valid_selections": M,
+                   "launch": "hip_graph" if args.graph else "eager"},
         "pct_of_peak": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
         "tokens_per_s": round(w.num_tokens / step_s, 1),
         "algorithmic_bytes_per_step": by,
