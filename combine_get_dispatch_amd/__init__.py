@@ -425,19 +425,76 @@ class EpBuffers:
         self.row_src = torch.empty(cap, **i32)
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         self.handle = None
+        self._shape_tk = (T, k)
+        self._shape_th = (T, H)
+        self._handle_out = ep_handle_t()
+        self._marshal()
+
+    # The buffers' pointers are marshalled once (and again whenever one of
+    # them is replaced); each call then checks only the caller's tensors.
+    _MARSHALLED = frozenset({"num_tokens_per_rank", "num_tokens_per_expert", "is_token_in_rank",
+                             "expert_offsets", "rank_offsets", "workspace", "status", "recv_x",
+                             "recv_scales", "recv_weights", "tok_slot_row", "row_src", "out"})
+
+    def __setattr__(self, name, value):
+        object.__setattr__(self, name, value)
+        if name in EpBuffers._MARSHALLED and "_layout_args" in self.__dict__:
+            self._marshal()
+
+    def _marshal(self):
+        import torch
+
+        c = self.cfg
+        T, H, k, E, R = c.num_tokens, c.hidden, c.num_topk, c.num_experts, c.num_ranks
+        cap, i32, d = self.capacity, torch.int32, self.__dict__
+        d["_cfg_ref"] = ctypes.byref(self.cfg)
+        ws_bytes = self.workspace.numel()
+        ws = _ptr(self.workspace, torch.uint8, name="workspace")
+        offs = _ptr(self.expert_offsets, i32, (E + 1,), "expert_offsets")
+        status = _ptr(self.status, i32, (1,), "status")
+        d["_layout_args"] = (_ptr(self.num_tokens_per_rank, i32, (R,), "num_tokens_per_rank"),
+                             _ptr(self.num_tokens_per_expert, i32, (E,), "num_tokens_per_expert"),
+                             _ptr(self.is_token_in_rank, torch.uint8, (T, R), "is_token_in_rank"),
+                             offs, _ptr(self.rank_offsets, i32, (R + 1,), "rank_offsets"),
+                             ws, ws_bytes, status)
+        # the scales' width is left to the library, which rejects FP8 with H % 128 != 0
+        d["_dispatch_args"] = (offs, ws, ws_bytes, cap,
+                               _ptr(self.recv_x, torch.uint8 if self.fp8 else torch.bfloat16,
+                                    (cap, H), "recv_x"),
+                               _ptr(self.recv_scales, torch.float32, name="recv_scales")
+                               if self.fp8 else None)
+        d["_dispatch_tail"] = (_ptr(self.tok_slot_row, i32, (T, k), "tok_slot_row"),
+                               _ptr(self.row_src, i32, (cap,), "row_src"), status)
+        d["_recv_weights_ptr"] = _ptr(self.recv_weights, torch.float32, (cap,), "recv_weights")
+        d["_dtype"] = EP_DTYPE_FP8_E4M3 if self.fp8 else EP_DTYPE_BF16
+        d["_out_ptr"] = _ptr(self.out, torch.bfloat16, (T, H), "out")
 
     def layout(self, topk_idx, sync=False, stream=None):
-        return ep_get_dispatch_layout(self.cfg, topk_idx, self.num_tokens_per_rank,
-                                      self.num_tokens_per_expert, self.is_token_in_rank,
-                                      self.expert_offsets, self.rank_offsets, self.workspace,
-                                      self.status, sync=sync, stream=stream)
+        import torch
+
+        if sync:
+            return ep_get_dispatch_layout(self.cfg, topk_idx, self.num_tokens_per_rank,
+                                          self.num_tokens_per_expert, self.is_token_in_rank,
+                                          self.expert_offsets, self.rank_offsets,
+                                          self.workspace, self.status, sync=True, stream=stream)
+        st = lib().ep_get_dispatch_layout(
+            self._cfg_ref, _ptr(topk_idx, torch.int32, self._shape_tk, "topk_idx"),
+            *self._layout_args, None, _stream(stream))
+        _check(st, "ep_get_dispatch_layout")
+        return None
 
     def dispatch(self, x, topk_idx, topk_weights, stream=None):
-        self.handle = ep_dispatch(self.cfg, EP_DTYPE_FP8_E4M3 if self.fp8 else EP_DTYPE_BF16,
-                                  x, topk_idx, topk_weights, self.expert_offsets, self.workspace,
-                                  self.capacity, self.recv_x, self.recv_scales,
-                                  self.recv_weights if topk_weights is not None else None,
-                                  self.tok_slot_row, self.row_src, self.status, stream=stream)
+        import torch
+
+        st = lib().ep_dispatch(
+            self._cfg_ref, self._dtype, _ptr(x, torch.bfloat16, self._shape_th, "x"),
+            _ptr(topk_idx, torch.int32, self._shape_tk, "topk_idx"),
+            _ptr(topk_weights, torch.float32, self._shape_tk, "topk_weights"),
+            *self._dispatch_args,
+            self._recv_weights_ptr if topk_weights is not None else None,
+            *self._dispatch_tail, ctypes.byref(self._handle_out), _stream(stream))
+        _check(st, "ep_dispatch")
+        self.handle = self._handle_out
         return self.handle
 
     def dispatch_fp8_input(self, x_codes, x_scales, topk_idx, topk_weights, stream=None):
@@ -451,9 +508,22 @@ class EpBuffers:
         return self.handle
 
     def combine(self, expert_out, topk_weights, out=None, stream=None):
-        out = self.out if out is None else out
-        ep_combine(self.handle, expert_out, topk_weights, out, stream=stream)
-        return out
+        import torch
+
+        if out is not None or self.handle is not self._handle_out:
+            out = self.out if out is None else out
+            ep_combine(self.handle, expert_out, topk_weights, out, stream=stream)
+            return out
+        H, cap = self.cfg.hidden, self.capacity
+        if expert_out is None or expert_out.dim() != 2 or expert_out.shape[1] != H \
+                or expert_out.shape[0] < cap:
+            raise ValueError(f"expert_out must be bf16 [>= {cap}, {H}]")
+        y = _ptr(expert_out, torch.bfloat16, name="expert_out") if expert_out.numel() else None
+        st = lib().ep_combine(ctypes.byref(self._handle_out), y,
+                              _ptr(topk_weights, torch.float32, self._shape_tk, "topk_weights"),
+                              self._out_ptr, _stream(stream))
+        _check(st, "ep_combine")
+        return self.out
 
     def dispatch_backward(self, grad_recv_x, grad_x=None, stream=None):
         import torch
