@@ -9,8 +9,9 @@
 //                         popcounts give the tile histogram and each
 //                         selection's stable rank inside the tile; ballots
 //                         give distinct tokens per rank.  The last
-//                         workgroup to finish scans: per expert over tiles
-//                         (tile bases), then over experts (segment starts).
+//                         workgroup to finish (or the only one) scans: per
+//                         expert over tiles (tile bases), then over experts
+//                         (segment starts).
 //   dispatch_*_kernel     one wave per (token, 1024-column chunk): reads the
 //                         x chunk once with 16-byte loads, optionally
 //                         quantises it to E4M3 in registers, and stores it to
@@ -89,11 +90,13 @@ __device__ __forceinline__ bool workspace_ok(const int32_t *hdr, const Dims &d) 
 // ---------------------------------------------------------------------------
 // Layout (count, then prefix sum: "GPU microarchitecture: DeepEP first
 // principles", "7.1 Does Sort Exist?"), in one launch.  Every workgroup
-// counts one 256-token tile.  The last workgroup to finish (it draws the
-// last ticket from a device-scope counter after a release fence) then scans
-// all tile histograms.  The ticket lives in the workspace header; it starts
-// at zero (ep_workspace_init) and the scanning workgroup resets it, so
-// consecutive layouts on one stream can reuse the workspace.
+// counts one 256-token tile.  With several tiles, the last workgroup to
+// finish (it draws the last ticket from a device-scope counter, a
+// release-acquire read-modify-write) scans all tile histograms; a single
+// workgroup scans its own counts straight from LDS.  The ticket lives in the
+// workspace header; it starts at zero (ep_workspace_init) and the scanning
+// workgroup resets it, so consecutive layouts on one stream can reuse the
+// workspace.
 // ---------------------------------------------------------------------------
 
 // K is a compile-time bound on k (k <= K) so that a token's expert ids stay
@@ -108,8 +111,9 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
     int32_t *__restrict__ rank_offsets, int32_t *__restrict__ header,
     unsigned long long *__restrict__ rank_ballot_ws, int32_t *__restrict__ rank_tok_off,
     int32_t *__restrict__ status) {
-  // [kWavesPerBlock][E] expert bitmasks; the scanning workgroup then uses
-  // the E + 1 words after them for aligned counts / offsets.
+  // LDS: [kWavesPerBlock][E] expert bitmasks; [kWavesPerBlock][E] counts of
+  // each expert in the earlier waves of the tile; [E + 1] words holding the
+  // tile's (later the batch's) count per expert, then the aligned offsets.
   extern __shared__ unsigned long long masks[];
   __shared__ int32_t rank_cnt[EP_MAX_RANKS];
   __shared__ int32_t wave_total[kWavesPerBlock];
@@ -119,6 +123,9 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
   const int wave = tid / kWave;
   const int tile = blockIdx.x;
   const int E = d.E, k = d.k, R = d.R;
+  int32_t *prefix = reinterpret_cast<int32_t *>(masks + kWavesPerBlock * E);
+  int32_t *counts = prefix + kWavesPerBlock * E;
+  const bool many = gridDim.x > 1;
   const bool has_tile = tile < ntiles;
   const int64_t t = (int64_t)tile * kTileTokens + tid;
   const bool live = has_tile && t < d.T;
@@ -154,130 +161,68 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
     }
     if (bad) flag(status, EP_STATUS_BIT_ROUTE);
 
-    // Distinct tokens per rank in this tile.  Each wave's ballot per rank
-    // goes to the workspace: the non-expanded dispatch places a token among
-    // a rank's tokens from these words.
+    // Distinct tokens per rank in this tile: lane r keeps the wave's ballot
+    // for rank r.  The ballots also go to the workspace: the non-expanded
+    // dispatch places a token among a rank's tokens from these words.
+    unsigned long long mine = 0ull;
     for (int r = 0; r < R; ++r) {
       const unsigned long long b = __ballot((rmask >> r) & 1ull);
-      if (lane == 0) {
-        rank_ballot_ws[((int64_t)tile * kWavesPerBlock + wave) * R + r] = b;
-        if (b) atomicAdd(&rank_cnt[r], (int32_t)__popcll(b));
-      }
+      if (lane == r) mine = b;
+    }
+    if (lane < R) {
+      rank_ballot_ws[((int64_t)tile * kWavesPerBlock + wave) * R + lane] = mine;
+      if (mine) atomicAdd(&rank_cnt[lane], (int32_t)__popcll(mine));
     }
     __syncthreads();
 
-    // Publish the tile's counts first: only they are needed by the scan.
+    // Per expert: its count in the earlier waves (for the stable ranks) and
+    // in the tile.  With several tiles the tile's counts are published.
     for (int e = tid; e < E; e += kBlock) {
-      int32_t c = 0;
-#pragma unroll
-      for (int w = 0; w < kWavesPerBlock; ++w) c += __popcll(masks[w * E + e]);
-      tile_cnt[(int64_t)tile * E + e] = c;
-    }
-    for (int r = tid; r < R; r += kBlock) tile_rank_cnt[(int64_t)tile * R + r] = rank_cnt[r];
-  }
-
-  // Ticket: the workgroup that draws the last one scans.  The release fence
-  // covers the tile counts above; the per-token outputs below are written
-  // after it and overlap the scan.  A single workgroup needs neither fence
-  // nor ticket (the barrier orders its own writes).
-  const bool many = gridDim.x > 1;
-  if (many) __threadfence();
-  __syncthreads();
-  if (tid == 0) is_last = many ? atomicAdd(&header[kHeaderTicket], 1) == (int)gridDim.x - 1 : 1;
-  __syncthreads();
-
-  if (is_last) {
-    if (many) __threadfence();
-    int32_t *aligned = reinterpret_cast<int32_t *>(masks + kWavesPerBlock * E);  // [E + 1]
-    // Per expert: tile histogram -> exclusive tile bases (in place) and its
-    // total; thread r < R also sums rank r's tile counts (R <= E, so e = r is
-    // its first expert).  Tiles go in batches whose loads are all issued
-    // before any store.
-    int32_t rank_sum = 0;
-    for (int e = tid; e < E; e += kBlock) {
-      constexpr int kBatch = 16;
       int32_t run = 0;
-      for (int t0 = 0; t0 < ntiles; t0 += kBatch) {
-        int32_t c[kBatch], rc[kBatch];
 #pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
-          const bool in = t0 + b < ntiles;
-          c[b] = in ? tile_cnt[(int64_t)(t0 + b) * E + e] : 0;
-          rc[b] = (in && e < R) ? tile_rank_cnt[(int64_t)(t0 + b) * R + e] : 0;
-        }
-#pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
-          if (t0 + b < ntiles) {
-            tile_cnt[(int64_t)(t0 + b) * E + e] = run;
-            if (e < R) tile_rank_cnt[(int64_t)(t0 + b) * R + e] = rank_sum;
-          }
-          run += c[b];
-          rank_sum += rc[b];
-        }
+      for (int w = 0; w < kWavesPerBlock; ++w) {
+        prefix[w * E + e] = run;
+        run += __popcll(masks[w * E + e]);
       }
-      cnt_ws[e] = run;
-      num_tokens_per_expert[e] = run;
-      aligned[e] = (run + d.A - 1) / d.A * d.A;
+      counts[e] = run;
+      if (many) tile_cnt[(int64_t)tile * E + e] = run;
     }
-    // Thread r < R summed rank r's tile counts above (R <= E, so e = r is its
-    // first expert) and left exclusive tile bases per rank behind.  The
-    // first wave (R <= 64 lanes) scans the counts into the starts of the
-    // ranks' token partitions (the non-expanded layout).
-    if (tid < R) num_tokens_per_rank[tid] = rank_sum;
-    if (wave == 0) {
-      const int32_t v = lane < R ? rank_sum : 0;
-      int32_t inc = v;
-      for (int off = 1; off < kWave; off <<= 1) {
-        const int32_t u = __shfl_up(inc, off);
-        if (lane >= off) inc += u;
-      }
-      if (lane < R) rank_tok_off[lane] = inc - v;
-      if (lane == R - 1) rank_tok_off[R] = inc;
-    }
-    __syncthreads();
+    if (many)
+      for (int r = tid; r < R; r += kBlock) tile_rank_cnt[(int64_t)tile * R + r] = rank_cnt[r];
+  } else {
+    // An empty batch: one workgroup writes zero counts and offsets.
+    for (int e = tid; e < E; e += kBlock) counts[e] = 0;
+    for (int i = tid; i < R; i += kBlock) rank_cnt[i] = 0;
+  }
+  __syncthreads();
 
-    // Exclusive scan of the aligned counts over experts: each thread owns a
-    // run of G consecutive experts; runs are scanned across the wave with
-    // shuffles and across the four waves through LDS.
-    const int G = (E + kBlock - 1) / kBlock;
-    const int e0 = tid * G;
-    int32_t local = 0;
-    for (int i = 0; i < G; ++i)
-      if (e0 + i < E) local += aligned[e0 + i];
-    int32_t incl = local;
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int32_t v = __shfl_up(incl, off);
-      if (lane >= off) incl += v;
-    }
-    if (lane == kWave - 1) wave_total[wave] = incl;
+  // Ticket: the workgroup that draws the last one scans.  The barrier above
+  // orders the workgroup's published counts before thread 0's release.
+  if (many) {
+    if (tid == 0)
+      is_last = __hip_atomic_fetch_add(&header[kHeaderTicket], 1, __ATOMIC_ACQ_REL,
+                                       __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1;
     __syncthreads();
-    int32_t base = incl - local;
-    for (int w = 0; w < wave; ++w) base += wave_total[w];
-    int32_t total = 0;
-    for (int w = 0; w < kWavesPerBlock; ++w) total += wave_total[w];
-    for (int i = 0; i < G; ++i) {
-      if (e0 + i < E) {
-        const int32_t a = aligned[e0 + i];
-        aligned[e0 + i] = base;
-        expert_offsets[e0 + i] = base;
-        base += a;
+  }
+  const bool scans = !many || is_last;
+
+  // The scanning workgroup's first batch of tile counts (expert tid, tiles
+  // 0..15) is loaded here, so that it arrives while the per-token outputs
+  // below are written.
+  constexpr int kBatch = 16;
+  int32_t c0[kBatch], rc0[kBatch];
+#pragma unroll
+  for (int b = 0; b < kBatch; ++b) c0[b] = rc0[b] = 0;
+  if (many && scans) {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (tid < E) {
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        if (b < ntiles) {
+          c0[b] = tile_cnt[(int64_t)b * E + tid];
+          if (tid < R) rc0[b] = tile_rank_cnt[(int64_t)b * R + tid];
+        }
       }
-    }
-    if (tid == 0) {
-      aligned[E] = total;
-      expert_offsets[E] = total;
-    }
-    __syncthreads();
-    if (tid <= R) rank_offsets[tid] = aligned[tid * experts_per_rank];
-    if (tid == 0) {
-      header[1] = d.T;
-      header[2] = d.k;
-      header[3] = d.E;
-      header[4] = d.R;
-      header[5] = d.A;
-      header[6] = ntiles;
-      header[0] = kWorkspaceMagic;
-      if (many) atomicExch(&header[kHeaderTicket], 0);
     }
   }
 
@@ -299,15 +244,121 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
 #pragma unroll
     for (int j = 0; j < K; ++j) {
       const int32_t e = ex[j];
-      int32_t rank = -1;
-      if (e >= 0) {
-        rank = __popcll(masks[wave * E + e] & below);
-#pragma unroll
-        for (int w = 0; w < kWavesPerBlock - 1; ++w)
-          if (w < wave) rank += __popcll(masks[w * E + e]);
-      }
+      const int32_t rank =
+          e >= 0 ? __popcll(masks[wave * E + e] & below) + prefix[wave * E + e] : -1;
       if (j < k) slot_rank[t * k + j] = rank;
     }
+  }
+  if (!scans) return;
+
+  // Per expert: tile histograms -> exclusive tile bases (in place) and the
+  // batch total; thread r < R also sums rank r's tile counts (R <= E, so
+  // e = r is its first expert).  Tiles go in batches whose loads are all
+  // issued before any store.  A single workgroup already holds its counts
+  // and its tile's bases are zero.
+  int32_t rank_sum = 0;
+  if (many) {
+    for (int e = tid; e < E; e += kBlock) {
+      int32_t run = 0;
+      for (int t0 = 0; t0 < ntiles; t0 += kBatch) {
+        int32_t c[kBatch], rc[kBatch];
+        if (e == tid && t0 == 0) {
+#pragma unroll
+          for (int b = 0; b < kBatch; ++b) {
+            c[b] = c0[b];
+            rc[b] = rc0[b];
+          }
+        } else {
+#pragma unroll
+          for (int b = 0; b < kBatch; ++b) {
+            const bool in = t0 + b < ntiles;
+            c[b] = in ? tile_cnt[(int64_t)(t0 + b) * E + e] : 0;
+            rc[b] = (in && e < R) ? tile_rank_cnt[(int64_t)(t0 + b) * R + e] : 0;
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+          if (t0 + b < ntiles) {
+            tile_cnt[(int64_t)(t0 + b) * E + e] = run;
+            if (e < R) tile_rank_cnt[(int64_t)(t0 + b) * R + e] = rank_sum;
+          }
+          run += c[b];
+          rank_sum += rc[b];
+        }
+      }
+      counts[e] = run;
+    }
+  } else if (ntiles > 0) {
+    for (int e = tid; e < E; e += kBlock) tile_cnt[e] = 0;
+    if (tid < R) {
+      rank_sum = rank_cnt[tid];
+      tile_rank_cnt[tid] = 0;
+    }
+  }
+  for (int e = tid; e < E; e += kBlock) {
+    const int32_t run = counts[e];
+    cnt_ws[e] = run;
+    num_tokens_per_expert[e] = run;
+    counts[e] = (run + d.A - 1) / d.A * d.A;
+  }
+  // Thread r < R holds rank r's token count.  The first wave (R <= 64
+  // lanes) scans the counts into the starts of the ranks' token partitions
+  // (the non-expanded layout).
+  if (tid < R) num_tokens_per_rank[tid] = rank_sum;
+  if (wave == 0) {
+    const int32_t v = lane < R ? rank_sum : 0;
+    int32_t inc = v;
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int32_t u = __shfl_up(inc, off);
+      if (lane >= off) inc += u;
+    }
+    if (lane < R) rank_tok_off[lane] = inc - v;
+    if (lane == R - 1) rank_tok_off[R] = inc;
+  }
+  __syncthreads();
+
+  // Exclusive scan of the aligned counts over experts: each thread owns a
+  // run of G consecutive experts; runs are scanned across the wave with
+  // shuffles and across the four waves through LDS.
+  const int G = (E + kBlock - 1) / kBlock;
+  const int e0 = tid * G;
+  int32_t local = 0;
+  for (int i = 0; i < G; ++i)
+    if (e0 + i < E) local += counts[e0 + i];
+  int32_t incl = local;
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int32_t v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
+  }
+  if (lane == kWave - 1) wave_total[wave] = incl;
+  __syncthreads();
+  int32_t base = incl - local;
+  for (int w = 0; w < wave; ++w) base += wave_total[w];
+  int32_t total = 0;
+  for (int w = 0; w < kWavesPerBlock; ++w) total += wave_total[w];
+  for (int i = 0; i < G; ++i) {
+    if (e0 + i < E) {
+      const int32_t a = counts[e0 + i];
+      counts[e0 + i] = base;
+      expert_offsets[e0 + i] = base;
+      base += a;
+    }
+  }
+  if (tid == 0) {
+    counts[E] = total;
+    expert_offsets[E] = total;
+  }
+  __syncthreads();
+  if (tid <= R) rank_offsets[tid] = counts[tid * experts_per_rank];
+  if (tid == 0) {
+    header[1] = d.T;
+    header[2] = d.k;
+    header[3] = d.E;
+    header[4] = d.R;
+    header[5] = d.A;
+    header[6] = ntiles;
+    header[0] = kWorkspaceMagic;
+    if (many) atomicExch(&header[kHeaderTicket], 0);
   }
 }
 
@@ -1145,6 +1196,7 @@ hipError_t launch_layout(const Dims &d, const int32_t *topk_idx, int32_t *num_to
                          int32_t *status, hipStream_t stream) {
   const WorkspaceLayout w = workspace_layout(d.T, d.k, d.E, d.R);
   const size_t lds = sizeof(unsigned long long) * kWavesPerBlock * (size_t)d.E +
+                     sizeof(int32_t) * kWavesPerBlock * (size_t)d.E +
                      sizeof(int32_t) * ((size_t)d.E + 1);
   auto kernel = d.k <= 8 ? layout_kernel<8> : (d.k <= 16 ? layout_kernel<16> : layout_kernel<32>);
   // An empty batch still needs one workgroup to write zero counts and offsets.
