@@ -990,11 +990,15 @@ __global__ __launch_bounds__(kBlock) void combine_ranked_partial_kernel(
     }
   }
   if (col < H) {
+    // Plain (not streaming) stores: the partials are read again by stage 2
+    // right away.  Measured over a whole non-expanded step, they save more
+    // here than the deferred write-back of their lines costs later.
     float *dst = partials + q * H + col;
-    store_stream(dst, make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]),
-                                 __float_as_uint(acc[2]), __float_as_uint(acc[3])));
-    store_stream(dst + 4, make_uint4(__float_as_uint(acc[4]), __float_as_uint(acc[5]),
-                                     __float_as_uint(acc[6]), __float_as_uint(acc[7])));
+    *reinterpret_cast<uint4 *>(dst) = make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]),
+                                                 __float_as_uint(acc[2]), __float_as_uint(acc[3]));
+    *reinterpret_cast<uint4 *>(dst + 4) =
+        make_uint4(__float_as_uint(acc[4]), __float_as_uint(acc[5]), __float_as_uint(acc[6]),
+                   __float_as_uint(acc[7]));
   }
 }
 
