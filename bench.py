@@ -28,6 +28,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -81,11 +82,63 @@ def ranked_bytes(w, M: int, Q: int) -> dict:
                 total=layout + disp + exp + comb)
 
 
-def kernel_source_hash() -> str:
+# The kernel and launcher each counter summary measures.
+KERNEL_FUNCS = {"combine": ("combine_kernel", "launch_combine"),
+                "dispatch": ("dispatch_fp8_kernel", "launch_dispatch"),
+                "dispatch_bf16": ("dispatch_bf16_kernel", "launch_dispatch"),
+                "layout": ("layout_kernel", "launch_layout")}
+BUILD_SCRIPT = os.path.join(ROOT, "combine_get_dispatch_amd", "_build.py")
+
+
+def split_functions(src: str) -> list:
+    """Top-level pieces of a kernel source: each ends with a line that is a
+    lone closing brace (a function) or brace-semicolon (a struct), and
+    carries the comments above it."""
+    pieces, cur = [], []
+    for line in src.splitlines(keepends=True):
+        cur.append(line)
+        if line.rstrip() in ("}", "};"):
+            pieces.append("".join(cur))
+            cur = []
+    if cur:
+        pieces.append("".join(cur))
+    return pieces
+
+
+def _piece_name(piece: str):
+    m = re.search(r"__global__\s+(?:__launch_bounds__\([^)]*\)\s+)?void\s+(\w+)\s*\(", piece)
+    if m:
+        return "kernel", m.group(1)
+    m = re.search(r"\bhipError_t\s+(launch_\w+)\s*\(", piece)
+    if m:
+        return "launcher", m.group(1)
+    return "helper", None
+
+
+def kernel_source_hash(kernel: str = None, src: str = None, extra: bytes = None) -> str:
+    """Hash of what a kernel's measured behaviour depends on: every helper
+    piece of the kernel source (anything that is neither a kernel nor a
+    launcher), the kernel's own function and launcher, the internal header
+    and the build flags.  With kernel=None, the whole sources.  Editing
+    another kernel leaves a kernel's hash unchanged."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+    if src is None:
+        with open(KERNEL_SOURCES[0]) as f:
+            src = f.read()
+    if extra is None:
+        extra = b""
+        for path in KERNEL_SOURCES[1:] + [BUILD_SCRIPT]:
+            with open(path, "rb") as f:
+                extra += f.read()
+    h.update(extra)
+    if kernel is None:
+        h.update(src.encode())
+        return h.hexdigest()[:16]
+    kname, lname = KERNEL_FUNCS[kernel]
+    for piece in split_functions(src):
+        kind, name = _piece_name(piece)
+        if kind == "helper" or name in (kname, lname):
+            h.update(piece.encode())
     return h.hexdigest()[:16]
 
 
@@ -106,7 +159,7 @@ def load_traffic(workload: str, kernel: str):
     if not os.path.exists(path):
         return None
     rec = _read_kv(path)
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(kernel):
         return None
     return int(float(rec["hbm_bytes_per_launch"]))
 
@@ -177,7 +230,7 @@ def pmc_summary(run_dir: str, workload: str, copy_mib: int, cmds: dict):
             f"hbm_write_bytes_per_launch = {wkib * wf * 1024:.0f}",
             f"hbm_bytes_per_launch = {(fkib * ff + wkib * wf) * 1024:.0f}",
             f"average_duration_us = {avg_ns[0] / 1e3:.2f}" if avg_ns else "average_duration_us = nan",
-            f"kernel_source_hash = {src_hash}",
+            f"kernel_source_hash = {kernel_source_hash(key)}",
         ]
         with open(os.path.join(ROOT, "profiles", f"{key}_{workload}_hbm_traffic.txt"), "w") as f:
             f.write("\n".join(body) + "\n")

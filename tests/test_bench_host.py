@@ -1,0 +1,58 @@
+"""Host-side checks of bench.py (CPU only): the algorithmic byte counts and
+the scoping of the kernel-source hash that decides whether a stored HBM
+counter summary still describes the kernel being timed."""
+import bench
+import ep_workloads as W
+
+SRC = """// helpers
+__device__ int helper(int v) { return v + 1;
+}
+template <bool kWeighted, int KB>
+__global__ __launch_bounds__(kBlock) void combine_kernel(int *p) {
+  p[0] = helper(1);
+}
+__global__ __launch_bounds__(kBlock) void dispatch_fp8_kernel(int *p) {
+  p[0] = 2;
+}
+hipError_t launch_combine(int *p) {
+  return hipSuccess;
+}
+"""
+
+
+def _h(src, kernel="combine"):
+    return bench.kernel_source_hash(kernel, src=src, extra=b"")
+
+
+def test_hash_ignores_other_kernels():
+    assert _h(SRC) == _h(SRC.replace("p[0] = 2;", "p[0] = 3;"))
+
+
+def test_hash_follows_kernel_launcher_and_helpers():
+    base = _h(SRC)
+    assert base != _h(SRC.replace("helper(1)", "helper(2)"))
+    assert base != _h(SRC.replace("v + 1", "v + 2"))
+    assert base != _h(SRC.replace("return hipSuccess;", "return hipErrorUnknown;"))
+    assert _h(SRC, "dispatch") != _h(SRC.replace("p[0] = 2;", "p[0] = 3;"), "dispatch")
+
+
+def test_every_measured_kernel_is_found_in_the_source():
+    with open(bench.KERNEL_SOURCES[0]) as f:
+        src = f.read()
+    pieces = bench.split_functions(src)
+    assert "".join(pieces) == src
+    names = {bench._piece_name(p)[1] for p in pieces}
+    for kname, lname in bench.KERNEL_FUNCS.values():
+        assert kname in names and lname in names
+
+
+def test_algorithmic_bytes_prefill_closed_form():
+    """Prefill: 4096 x 7168, top-8, E=256, R=8, FP8 rows of H + H/32 bytes,
+    every selection valid (M = T*k)."""
+    w = W.WORKLOADS["prefill"]
+    T, H, k, E, R = 4096, 7168, 8, 256, 8
+    M = T * k
+    by = bench.algorithmic_bytes(w, M)
+    assert by["layout"] == T * k * 4 + T * R + 4 * (E + R) + 4 * (E + R + 2) == 165960
+    assert by["dispatch"] == T * H * 2 + T * k * 12 + M * (H + H // 32 + 8) == 301596672
+    assert by["combine"] == M * 2 * H + T * k * 8 + T * 2 * H == 528744448
