@@ -191,7 +191,13 @@ def pmc_summary(run_dir: str, workload: str, copy_mib: int, cmds: dict):
 
     def copy_factor(vals):
         cands = [max(v) for k, v in vals.items() if "copyBuffer" in k]
-        return copy_kib / max(cands)
+        f = copy_kib / max(cands)
+        # the counters read whole or half the copied bytes on this chip; any
+        # other factor means the run held a copy of another size
+        if not (0.9 <= f <= 2.2):
+            raise SystemExit(f"copy counter factor {f:.4f} is implausible; was the only "
+                             f"device copy the {copy_mib} MiB probe?")
+        return f
 
     ff, wf = copy_factor(fetch), copy_factor(write)
     stats = {r["Name"]: r for r in rows("trace", "ep_kernel_stats.csv")}
@@ -406,8 +412,8 @@ def main():
                 f"--no-cpu-baseline --copy-probe-mib 256")
         cmds = {
             "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace -o ep -- "
-                     f"python3 bench.py --workload {args.workload} --steps 20 --warmup 5 "
-                     "--no-cpu-baseline --copy-probe-mib 256",
+                     + ("python3 bench.py" if args.workload == "prefill"
+                        else f"python3 bench.py --workload {args.workload}"),
             "fetch": f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch -o ep -- {base}",
             "write": f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write -o ep -- {base}",
         }
@@ -553,6 +559,24 @@ def main():
         for _ in range(5):
             dst.copy_(src)
         torch.cuda.synchronize()
+        del src, dst
+
+    # Context: the runtime's own device-to-device copy of 1 GiB on this machine
+    # (read + write bytes per second).  Counter runs (--copy-probe-mib) skip
+    # it: their only copy must be the one of known size.
+    copy_gbps = None
+    if not args.copy_probe_mib:
+        csrc = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        cdst = torch.empty_like(csrc)
+        cdst.copy_(csrc)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for _ in range(5):
+            cdst.copy_(csrc)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        copy_gbps = round(2 * (1 << 30) * 5 / (c0.elapsed_time(c1) / 1e3) / 1e9, 1)
+        del csrc, cdst
 
     by = algorithmic_bytes(w, M, args.fp8_input)
     step_s = ms_per_step / 1e3
@@ -590,6 +614,7 @@ def main():
         "kernel_roofline_frac": {n: round(by[n] / (per_us[n] / 1e6) / 1e9 / PEAK_HBM_GBPS, 4)
                                  for n in names},
         "step_us": step_us,
+        "device_copy_gbps": copy_gbps,
         "host_wall_s": round(wall, 4),
         "roofline": {
             "kernel": dom,
