@@ -14,6 +14,10 @@ method must move:
   combine   M*2H (gathered rows) + T*k*8 (tok_slot_row, gates) + T*2H (out)
 with M valid selections.  Workspace traffic is overhead and not counted.
 
+`device_copy_gbps` (the runtime's copy of 1 GiB) and `hbm_probe_gbps` (a
+streaming read / write / copy of 1 GiB with 16-byte accesses, streaming or
+plain) give the rates this machine's HBM sustains, as context for the roofline.
+
 `value` is the mean over K back-to-back steps.  `step_us` adds per-step
 median / p10 / p90 for warm steps and for cold ones, where an untimed pass
 over 1 GiB before each step evicts the 256 MB MALL and the L2s (`cold`: a
@@ -87,7 +91,6 @@ KERNEL_FUNCS = {"combine": ("combine_kernel", "launch_combine"),
                 "dispatch": ("dispatch_fp8_kernel", "launch_dispatch"),
                 "dispatch_bf16": ("dispatch_bf16_kernel", "launch_dispatch"),
                 "layout": ("layout_kernel", "launch_layout")}
-BUILD_SCRIPT = os.path.join(ROOT, "combine_get_dispatch_amd", "_build.py")
 
 
 def split_functions(src: str) -> list:
@@ -119,7 +122,7 @@ def kernel_source_hash(kernel: str = None, src: str = None, extra: bytes = None)
     """Hash of what a kernel's measured behaviour depends on: every helper
     piece of the kernel source (anything that is neither a kernel nor a
     launcher), the kernel's own function and launcher, the internal header
-    and the build flags.  With kernel=None, the whole sources.  Editing
+    and the compiler flags.  With kernel=None, the whole sources.  Editing
     another kernel leaves a kernel's hash unchanged."""
     h = hashlib.sha256()
     if src is None:
@@ -127,9 +130,12 @@ def kernel_source_hash(kernel: str = None, src: str = None, extra: bytes = None)
             src = f.read()
     if extra is None:
         extra = b""
-        for path in KERNEL_SOURCES[1:] + [BUILD_SCRIPT]:
+        for path in KERNEL_SOURCES[1:]:
             with open(path, "rb") as f:
                 extra += f.read()
+        from combine_get_dispatch_amd import _build
+
+        extra += " ".join(_build.HIPCC_FLAGS).encode()
     h.update(extra)
     if kernel is None:
         h.update(src.encode())
@@ -578,6 +584,33 @@ def main():
         copy_gbps = round(2 * (1 << 30) * 5 / (c0.elapsed_time(c1) / 1e3) / 1e9, 1)
         del csrc, cdst
 
+    # Context: the box's streaming read / write / copy rates over 1 GiB with
+    # the kernels' own 16-byte accesses, streaming (nt) or plain.
+    hbm_probe = None
+    if not args.copy_probe_mib:
+        nb = 1 << 30
+        pa = torch.ones(nb, dtype=torch.uint8, device=dev)
+        pb = torch.empty_like(pa)
+        hbm_probe = {}
+        for name, kind, nt, moved in (("read_nt", ep.EP_PROBE_READ, 1, nb),
+                                      ("read", ep.EP_PROBE_READ, 0, nb),
+                                      ("write_nt", ep.EP_PROBE_WRITE, 1, nb),
+                                      ("write", ep.EP_PROBE_WRITE, 0, nb),
+                                      ("copy_nt", ep.EP_PROBE_COPY, 1, 2 * nb),
+                                      ("copy", ep.EP_PROBE_COPY, 0, 2 * nb)):
+            best = 0.0
+            for wgs in (1024, 4096, 16384, 65536):
+                ep.ep_hbm_probe(kind, nt, wgs, pa, pb, nb)
+                p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                p0.record(stream)
+                for _ in range(5):
+                    ep.ep_hbm_probe(kind, nt, wgs, pa, pb, nb)
+                p1.record(stream)
+                torch.cuda.synchronize()
+                best = max(best, moved * 5 / (p0.elapsed_time(p1) / 1e3) / 1e9)
+            hbm_probe[name] = round(best, 1)
+        del pa, pb
+
     by = algorithmic_bytes(w, M, args.fp8_input)
     step_s = ms_per_step / 1e3
     gbps = by["total"] / step_s / 1e9
@@ -615,6 +648,7 @@ def main():
                                  for n in names},
         "step_us": step_us,
         "device_copy_gbps": copy_gbps,
+        "hbm_probe_gbps": hbm_probe,
         "host_wall_s": round(wall, 4),
         "roofline": {
             "kernel": dom,

@@ -20,6 +20,7 @@ import re
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libep.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "ep.h")
+HEADER_PATHS = [HEADER_PATH, os.path.join(os.path.dirname(_PKG), "include", "ep_probe.h")]
 
 EP_OK, EP_ERR_INVALID_ARG, EP_ERR_INVALID_ROUTE, EP_ERR_CAPACITY, EP_ERR_WORKSPACE, EP_ERR_HIP = range(6)
 EP_DTYPE_BF16, EP_DTYPE_FP8_E4M3 = 0, 1
@@ -90,20 +91,25 @@ def lib() -> ctypes.CDLL:
                             ctypes.POINTER(ep_handle_t), P]
     L.ep_combine_ranked.argtypes = [rhp, P, ctypes.c_int32, P, P, P]
     L.ep_combine_backward.argtypes = [ctypes.POINTER(ep_handle_t), P, P, P, P, P, P]
+    L.ep_hbm_probe.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, S, P]
     for f in ("ep_layout_workspace_bytes", "ep_recv_capacity_rows", "ep_get_dispatch_layout",
               "ep_dispatch", "ep_combine", "ep_read_status", "ep_workspace_init",
               "ep_dispatch_backward", "ep_combine_backward", "ep_dispatch_fp8_input",
-              "ep_ranked_capacity_rows", "ep_dispatch_ranked", "ep_expand", "ep_combine_ranked"):
+              "ep_ranked_capacity_rows", "ep_dispatch_ranked", "ep_expand", "ep_combine_ranked",
+              "ep_hbm_probe"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
 
 
 def header_functions() -> list[str]:
-    """Names of the functions include/ep.h declares."""
-    text = open(HEADER_PATH).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return re.findall(r"\b(ep_[a-z_]+)\s*\(", text)
+    """Names of the functions the headers in include/ declare."""
+    names = []
+    for path in HEADER_PATHS:
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"\b(ep_[a-z_]+)\s*\(", text)
+    return names
 
 
 def _check(status: int, func: str):
@@ -383,6 +389,19 @@ def ep_read_status(status, stream=None):
     import torch
 
     _check(lib().ep_read_status(_ptr(status, torch.int32), _stream(stream)), "ep_read_status")
+
+
+EP_PROBE_READ, EP_PROBE_WRITE, EP_PROBE_COPY = 0, 1, 2
+
+
+def ep_hbm_probe(kind: int, nontemporal: bool, workgroups: int, src, dst, nbytes: int,
+                 stream=None):
+    """Enqueue one streaming read / write / copy pass over nbytes (a
+    measurement aid, include/ep_probe.h)."""
+    _check(lib().ep_hbm_probe(int(kind), int(bool(nontemporal)), int(workgroups),
+                              None if src is None else ctypes.c_void_p(src.data_ptr()),
+                              ctypes.c_void_p(dst.data_ptr()), int(nbytes), _stream(stream)),
+           "ep_hbm_probe")
 
 
 # --------------------------------------------------------------------------

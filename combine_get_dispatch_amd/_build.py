@@ -15,7 +15,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = [os.path.join(PKG, "csrc", "ep_kernels.hip"), os.path.join(PKG, "csrc", "ep_api.hip")]
+SOURCES = [os.path.join(PKG, "csrc", f) for f in ("ep_kernels.hip", "ep_api.hip", "hbm_probe.hip")]
 LIB = os.path.join(PKG, "libep.so")
 
 HIPCC_FLAGS = [

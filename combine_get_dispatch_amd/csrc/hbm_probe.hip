@@ -1,0 +1,122 @@
+// Streaming HBM probe: what this GPU's memory system sustains for a plain
+// read, write or copy of a large buffer, with the same 16-byte accesses and
+// cache policies the dispatch / combine kernels use.  The benchmark reports
+// these rates beside the kernels' own, as the box's achievable ceilings.
+// Declared in include/ep_probe.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ep.h"
+#include "ep_probe.h"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;  // 16-byte accesses in flight per thread per pass
+
+template <bool kNT>
+__device__ __forceinline__ u32x4 load16(const u32x4 *p) {
+  if (kNT) return __builtin_nontemporal_load(p);
+  return *p;
+}
+
+template <bool kNT>
+__device__ __forceinline__ void store16(u32x4 *p, u32x4 v) {
+  if (kNT)
+    __builtin_nontemporal_store(v, p);
+  else
+    *p = v;
+}
+
+// Every kernel walks [0, n) in passes of kUnroll grid-wide strides; the
+// first phase of a pass issues all its loads before any store.
+template <bool kNT>
+__global__ __launch_bounds__(kThreads) void probe_read(const u32x4 *__restrict__ src, int64_t n,
+                                                      u32x4 *__restrict__ sink) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  uint32_t acc = 0;
+  for (int64_t base = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; base < n;
+       base += stride * kUnroll) {
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i = base + u * stride;
+      v[u] = i < n ? load16<kNT>(src + i) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  // Keeps the loads live without writing anything in practice.
+  if (acc == 0x9E3779B9u) sink[0] = u32x4{acc, 0, 0, 0};
+}
+
+template <bool kNT>
+__global__ __launch_bounds__(kThreads) void probe_write(u32x4 *__restrict__ dst, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t base = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; base < n;
+       base += stride * kUnroll) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i = base + u * stride;
+      if (i < n) store16<kNT>(dst + i, u32x4{(uint32_t)i, (uint32_t)(i >> 32), 0u, 0u});
+    }
+  }
+}
+
+template <bool kNT>
+__global__ __launch_bounds__(kThreads) void probe_copy(const u32x4 *__restrict__ src,
+                                                      u32x4 *__restrict__ dst, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t base = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; base < n;
+       base += stride * kUnroll) {
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i = base + u * stride;
+      if (i < n) v[u] = load16<kNT>(src + i);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i = base + u * stride;
+      if (i < n) store16<kNT>(dst + i, v[u]);
+    }
+  }
+}
+
+}  // namespace
+
+extern "C" ep_status_t ep_hbm_probe(int32_t kind, int32_t nontemporal, int32_t workgroups,
+                                    const void *src, void *dst, size_t bytes,
+                                    hipStream_t stream) {
+  if (kind != EP_PROBE_READ && kind != EP_PROBE_WRITE && kind != EP_PROBE_COPY)
+    return EP_ERR_INVALID_ARG;
+  if (workgroups < 1 || workgroups > (1 << 20)) return EP_ERR_INVALID_ARG;
+  if (bytes == 0 || bytes % 16 != 0) return EP_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u)
+    return EP_ERR_INVALID_ARG;
+  if (dst == nullptr || (kind != EP_PROBE_WRITE && src == nullptr)) return EP_ERR_INVALID_ARG;
+  const int64_t n = (int64_t)(bytes / 16);
+  const u32x4 *s = static_cast<const u32x4 *>(src);
+  u32x4 *d = static_cast<u32x4 *>(dst);
+  const dim3 grid((unsigned)workgroups), block(kThreads);
+  const bool nt = nontemporal != 0;
+  if (kind == EP_PROBE_READ) {
+    if (nt)
+      hipLaunchKernelGGL(probe_read<true>, grid, block, 0, stream, s, n, d);
+    else
+      hipLaunchKernelGGL(probe_read<false>, grid, block, 0, stream, s, n, d);
+  } else if (kind == EP_PROBE_WRITE) {
+    if (nt)
+      hipLaunchKernelGGL(probe_write<true>, grid, block, 0, stream, d, n);
+    else
+      hipLaunchKernelGGL(probe_write<false>, grid, block, 0, stream, d, n);
+  } else {
+    if (nt)
+      hipLaunchKernelGGL(probe_copy<true>, grid, block, 0, stream, s, d, n);
+    else
+      hipLaunchKernelGGL(probe_copy<false>, grid, block, 0, stream, s, d, n);
+  }
+  return hipGetLastError() == hipSuccess ? EP_OK : EP_ERR_HIP;
+}
