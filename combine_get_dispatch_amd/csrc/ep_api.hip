@@ -63,6 +63,11 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 }  // namespace
 
+namespace ep {
+// Lets the probe entry point (hbm_probe.hip) report through ep_last_error().
+ep_status_t set_error(ep_status_t st, const char *message) { return fail(st, "%s", message); }
+}  // namespace ep
+
 extern "C" {
 
 const char *ep_status_string(ep_status_t status) {

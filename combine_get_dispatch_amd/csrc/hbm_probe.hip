@@ -9,6 +9,12 @@
 #include "ep.h"
 #include "ep_probe.h"
 
+namespace ep {
+// Defined with the other entry points: records the message ep_last_error()
+// returns on this thread and returns st.
+ep_status_t set_error(ep_status_t st, const char *message);
+}  // namespace ep
+
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -91,12 +97,15 @@ extern "C" ep_status_t ep_hbm_probe(int32_t kind, int32_t nontemporal, int32_t w
                                     const void *src, void *dst, size_t bytes,
                                     hipStream_t stream) {
   if (kind != EP_PROBE_READ && kind != EP_PROBE_WRITE && kind != EP_PROBE_COPY)
-    return EP_ERR_INVALID_ARG;
-  if (workgroups < 1 || workgroups > (1 << 20)) return EP_ERR_INVALID_ARG;
-  if (bytes == 0 || bytes % 16 != 0) return EP_ERR_INVALID_ARG;
+    return ep::set_error(EP_ERR_INVALID_ARG, "probe kind must be read, write or copy");
+  if (workgroups < 1 || workgroups > (1 << 20))
+    return ep::set_error(EP_ERR_INVALID_ARG, "probe workgroups outside [1, 2^20]");
+  if (bytes == 0 || bytes % 16 != 0)
+    return ep::set_error(EP_ERR_INVALID_ARG, "probe bytes must be a positive multiple of 16");
+  if (dst == nullptr || (kind != EP_PROBE_WRITE && src == nullptr))
+    return ep::set_error(EP_ERR_INVALID_ARG, "probe buffer is NULL");
   if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u)
-    return EP_ERR_INVALID_ARG;
-  if (dst == nullptr || (kind != EP_PROBE_WRITE && src == nullptr)) return EP_ERR_INVALID_ARG;
+    return ep::set_error(EP_ERR_INVALID_ARG, "probe buffers must be 16-byte aligned");
   const int64_t n = (int64_t)(bytes / 16);
   const u32x4 *s = static_cast<const u32x4 *>(src);
   u32x4 *d = static_cast<u32x4 *>(dst);
@@ -118,5 +127,7 @@ extern "C" ep_status_t ep_hbm_probe(int32_t kind, int32_t nontemporal, int32_t w
     else
       hipLaunchKernelGGL(probe_copy<false>, grid, block, 0, stream, s, d, n);
   }
-  return hipGetLastError() == hipSuccess ? EP_OK : EP_ERR_HIP;
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return ep::set_error(EP_ERR_HIP, hipGetErrorString(err));
+  return EP_OK;
 }

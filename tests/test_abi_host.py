@@ -105,3 +105,19 @@ def test_layout_and_combine_rejections():
     assert L.ep_workspace_init(None, 1024, None) == ep.EP_ERR_INVALID_ARG
     assert L.ep_workspace_init(ctypes.c_void_p(0x100010), 1024, None) == ep.EP_ERR_INVALID_ARG
     assert L.ep_workspace_init(_fake(1), 64, None) == ep.EP_ERR_INVALID_ARG
+
+
+def test_probe_rejects_bad_arguments_before_launch():
+    """The HBM probe checks kind, workgroup count, size and pointers before
+    any HIP call (include/ep_probe.h)."""
+    L = ep.lib()
+    buf = ctypes.c_void_p(256)  # never dereferenced: every call below is rejected first
+    cases = [(7, 1, 1024, buf, buf, 4096),       # unknown kind
+             (ep.EP_PROBE_COPY, 1, 0, buf, buf, 4096),       # no workgroups
+             (ep.EP_PROBE_COPY, 1, 1024, buf, buf, 100),     # not a multiple of 16
+             (ep.EP_PROBE_COPY, 1, 1024, None, buf, 4096),   # copy needs a source
+             (ep.EP_PROBE_WRITE, 1, 1024, None, ctypes.c_void_p(264), 4096)]  # misaligned
+    for kind, nt, wgs, src, dst, nbytes in cases:
+        st = L.ep_hbm_probe(kind, nt, wgs, src, dst, nbytes, None)
+        assert st == ep.EP_ERR_INVALID_ARG
+        assert L.ep_last_error().decode().startswith("probe")
