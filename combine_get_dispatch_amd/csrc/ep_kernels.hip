@@ -838,10 +838,10 @@ __global__ __launch_bounds__(kBlock) void dispatch_ranked_kernel(
 }
 
 // Receiver-side expand: non-expanded row q (rank r, token t) goes to the
-// expert-major row of each of its local slots.  One wave per received row:
-// the row's metadata is resolved once, and the payload is streamed in
-// batches of kExpandBatch 1024-column chunks whose loads are issued before
-// the first store.
+// expert-major row of each of its local slots.  One wave per (received row,
+// batch of kExpandBatch 1024-column chunks): the batch's payload loads are
+// issued before the row's metadata chain, so they overlap it; the first
+// batch's wave also writes the rows' sources and gates.
 constexpr int kExpandBatch = 4;
 
 template <bool kFp8>
@@ -855,7 +855,10 @@ __global__ __launch_bounds__(kBlock) void expand_kernel(
     float *__restrict__ recv_scales, float *__restrict__ recv_weights,
     int32_t *__restrict__ row_src, int32_t *__restrict__ status) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t q = uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
+  const int nbatches = (nchunks + kExpandBatch - 1) / kExpandBatch;
+  const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + uniform(threadIdx.x / kWave);
+  const int64_t q = item / nbatches;
+  const int batch = (int)(item - q * nbatches);
   if (q >= ranked_capacity) return;
   const int64_t rows = rank_token_offsets[d.R];
   if (q >= rows) return;
@@ -865,8 +868,8 @@ __global__ __launch_bounds__(kBlock) void expand_kernel(
   }
   const int64_t H = d.H;
 
-  // The first batch of payload only depends on q: load it before the
-  // metadata chain.
+  // The batch's payload only depends on q: load it before the metadata
+  // chain.
   Payload16 pl[kExpandBatch];
   auto load_batch = [&](int c0) {
 #pragma unroll
@@ -887,7 +890,7 @@ __global__ __launch_bounds__(kBlock) void expand_kernel(
       }
     }
   };
-  load_batch(0);
+  load_batch(batch * kExpandBatch);
 
   // The row's rank: how many partition starts 1..R are at or below q.
   const bool le_q = lane >= 1 && lane <= d.R && rank_token_offsets[lane] <= q;
@@ -909,17 +912,19 @@ __global__ __launch_bounds__(kBlock) void expand_kernel(
                                        tile_base[(t / kTileTokens) * d.E + e] + rank;
       if (p >= 0 && p < capacity) {
         row = (int32_t)p;
-        row_src[p] = (int32_t)(t * d.k + lane);
-        if (recv_weights != nullptr && ne_topk_weights != nullptr)
-          recv_weights[p] = ne_topk_weights[q * d.k + lane];
-      } else {
+        if (batch == 0) {
+          row_src[p] = (int32_t)(t * d.k + lane);
+          if (recv_weights != nullptr && ne_topk_weights != nullptr)
+            recv_weights[p] = ne_topk_weights[q * d.k + lane];
+        }
+      } else if (batch == 0) {
         flag(status, EP_STATUS_BIT_CAPACITY);
       }
     }
   }
 
-  for (int c0 = 0; c0 < nchunks; c0 += kExpandBatch) {
-    if (c0 > 0) load_batch(c0);
+  {
+    const int c0 = batch * kExpandBatch;
     for (int j = 0; j < d.k; ++j) {
       const int32_t rr = lane_value(row, j);
       if (rr < 0) continue;
@@ -1370,7 +1375,8 @@ hipError_t launch_expand(const Dims &d, bool fp8, int64_t ranked_capacity, const
   const WorkspaceLayout w = workspace_layout(d.T, d.k, d.E, d.R);
   const int32_t nchunks = (d.H + kChunkCols - 1) / kChunkCols;
   if (ranked_capacity > 0) {
-    const dim3 grid((unsigned)((ranked_capacity + kWavesPerBlock - 1) / kWavesPerBlock));
+    const int64_t items = ranked_capacity * ((nchunks + kExpandBatch - 1) / kExpandBatch);
+    const dim3 grid((unsigned)((items + kWavesPerBlock - 1) / kWavesPerBlock));
     auto kernel = fp8 ? expand_kernel<true> : expand_kernel<false>;
     hipLaunchKernelGGL(kernel, grid, dim3(kBlock), 0, stream, d, nchunks, ranked_capacity, ne_x,
                        ne_scales, ne_topk_idx, ne_topk_weights, ne_src, rank_token_offsets,
