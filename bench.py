@@ -249,6 +249,35 @@ def pmc_summary(run_dir: str, workload: str, copy_mib: int, cmds: dict):
     print(f"profiles written for {workload} (copy factors fetch {ff:.4f}, write {wf:.4f})")
 
 
+def run_receipt(w, inp, b, dev) -> dict:
+    """What identifies the run: toolchain and GPU, the workload's seed, and
+    the route's shape (expert load skew; the share of selections whose
+    expert lives on the token's own logical rank, with token t owned by
+    rank t*R/T)."""
+    import subprocess
+
+    import numpy as np
+    import torch
+
+    props = torch.cuda.get_device_properties(dev)
+    try:
+        sha = subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT, text=True,
+                             capture_output=True, timeout=10).stdout.strip() or None
+    except (OSError, subprocess.SubprocessError):
+        sha = None
+    idx = inp["topk_idx"]
+    T, E, R = w.num_tokens, w.num_experts, w.num_ranks
+    valid = idx >= 0
+    own = (np.arange(T, dtype=np.int64) * R // T)[:, None]
+    local = (idx // (E // R) == own) & valid
+    load = b.num_tokens_per_expert.cpu().numpy()
+    return {"git": sha, "torch": torch.__version__, "hip": torch.version.hip,
+            "gpu": props.name, "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count,
+            "seed": w.seed, "max_over_mean_expert_load": round(float(load.max() / load.mean()), 3),
+            "local_rank_fraction": round(float(local.sum() / max(1, valid.sum())), 4)}
+
+
 def cpu_baseline(w, inp, budget_s: float):
     """The CPU oracle as it stands (single-threaded C), timed on this host on
     whole steps of the same batch, repeated until about budget_s seconds."""
@@ -611,6 +640,7 @@ def main():
             hbm_probe[name] = round(best, 1)
         del pa, pb
 
+    receipt = run_receipt(w, inp, b, dev)
     by = algorithmic_bytes(w, M, args.fp8_input)
     step_s = ms_per_step / 1e3
     gbps = by["total"] / step_s / 1e9
@@ -647,6 +677,7 @@ def main():
         "kernel_roofline_frac": {n: round(by[n] / (per_us[n] / 1e6) / 1e9 / PEAK_HBM_GBPS, 4)
                                  for n in names},
         "step_us": step_us,
+        "receipt": receipt,
         "device_copy_gbps": copy_gbps,
         "hbm_probe_gbps": hbm_probe,
         "host_wall_s": round(wall, 4),
