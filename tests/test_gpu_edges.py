@@ -357,3 +357,28 @@ def test_no_sync_valid_ranges():
         assert np.all(rs[pad] == -1) and np.all(rx[pad] == 0)
     assert off[-1] <= b.capacity
     assert np.all(rs[off[-1]:] == -7)  # past the last segment nothing is written
+
+
+def test_layout_scan_hand_off_repeated():
+    """The scanning workgroup reads the other workgroups' tile counts after
+    a release-acquire ticket.  Forty layouts of fresh routes over 64 tiles,
+    with no synchronisation between launch and dispatch, must each match
+    the oracle bit for bit (counts, offsets, rank partitions, positions)."""
+    rng = np.random.default_rng(77)
+    T, H, k, E, R = 16384, 8, 8, 256, 8
+    b = ep.EpBuffers(T, H, k, E, R, 1)
+    x = W.normal_bf16(rng, (T, H))
+    x_d = dev_bf16(x)
+    for rep in range(40):
+        idx = W.random_routes(rng, T, E, k, mask_prob=0.02 * (rep % 3))
+        idx_d = dev(idx)
+        b.layout(idx_d)
+        b.dispatch(x_d, idx_d, None)
+        torch.cuda.synchronize()
+        b.check_status()
+        lo = oracle.layout(idx, E, R, 1)
+        do = oracle.dispatch(x, idx, None, E, R, capacity=T * k)
+        for key in ("num_tokens_per_expert", "num_tokens_per_rank", "expert_offsets",
+                    "rank_offsets"):
+            assert np.array_equal(getattr(b, key).cpu().numpy(), lo[key]), (rep, key)
+        assert np.array_equal(b.tok_slot_row.cpu().numpy(), do["tok_slot_row"]), rep
