@@ -88,8 +88,8 @@ def ranked_bytes(w, M: int, Q: int) -> dict:
 
 # The kernel and launcher each counter summary measures.
 KERNEL_FUNCS = {"combine": ("combine_kernel", "launch_combine"),
-                "dispatch": ("dispatch_fp8_kernel", "launch_dispatch"),
-                "dispatch_bf16": ("dispatch_bf16_kernel", "launch_dispatch"),
+                "dispatch": ("dispatch_kernel", "launch_dispatch"),
+                "dispatch_bf16": ("dispatch_kernel", "launch_dispatch"),
                 "layout": ("layout_kernel", "launch_layout")}
 
 
@@ -170,8 +170,8 @@ def load_traffic(workload: str, kernel: str):
     return int(float(rec["hbm_bytes_per_launch"]))
 
 
-KERNEL_KEYS = {"layout": "layout_kernel", "dispatch": "dispatch_fp8_kernel",
-               "dispatch_bf16": "dispatch_bf16_kernel", "combine": "combine_kernel"}
+KERNEL_KEYS = {"layout": "layout_kernel", "dispatch": "dispatch_kernel<true>",
+               "dispatch_bf16": "dispatch_kernel<false>", "combine": "combine_kernel"}
 
 
 def pmc_summary(run_dir: str, workload: str, copy_mib: int, cmds: dict):

@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
                                          ctypes.POINTER(ctypes.c_int32), P]
     L.ep_dispatch.argtypes = [cfgp, ctypes.c_int, P, P, P, P, P, S, i64, P, P, P, P, P, P,
                               ctypes.POINTER(ep_handle_t), P]
+    L.ep_layout_dispatch.argtypes = [cfgp, ctypes.c_int, P, P, P, P, P, P, P, P, P, S, i64, P, P,
+                                     P, P, P, P, ctypes.POINTER(ep_handle_t), P]
     L.ep_combine.argtypes = [ctypes.POINTER(ep_handle_t), P, P, P, P]
     L.ep_read_status.argtypes = [P, P]
     L.ep_workspace_init.argtypes = [P, S, P]
@@ -93,7 +95,8 @@ def lib() -> ctypes.CDLL:
     L.ep_combine_backward.argtypes = [ctypes.POINTER(ep_handle_t), P, P, P, P, P, P]
     L.ep_hbm_probe.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, S, P]
     for f in ("ep_layout_workspace_bytes", "ep_recv_capacity_rows", "ep_get_dispatch_layout",
-              "ep_dispatch", "ep_combine", "ep_read_status", "ep_workspace_init",
+              "ep_dispatch", "ep_layout_dispatch", "ep_combine", "ep_read_status",
+              "ep_workspace_init",
               "ep_dispatch_backward", "ep_combine_backward", "ep_dispatch_fp8_input",
               "ep_ranked_capacity_rows", "ep_dispatch_ranked", "ep_expand", "ep_combine_ranked",
               "ep_hbm_probe"):
@@ -214,6 +217,40 @@ def ep_dispatch(cfg, recv_dtype, x, topk_idx, topk_weights, expert_offsets, work
         _ptr(row_src, torch.int32, (cap,), "row_src"),
         _ptr(status, torch.int32, (1,), "status"), ctypes.byref(handle), _stream(stream))
     _check(st, "ep_dispatch")
+    return handle
+
+
+LAYOUT_DISPATCH_MAX_TOKENS = 256
+
+
+def ep_layout_dispatch(cfg, recv_dtype, x, topk_idx, topk_weights, num_tokens_per_rank,
+                       num_tokens_per_expert, is_token_in_rank, expert_offsets, rank_offsets,
+                       workspace, capacity, recv_x, recv_scales, recv_weights, tok_slot_row,
+                       row_src, status, stream=None) -> ep_handle_t:
+    """Layout and dispatch in one launch (at most 256 tokens)."""
+    import torch
+
+    T, H, k, E, R = cfg.num_tokens, cfg.hidden, cfg.num_topk, cfg.num_experts, cfg.num_ranks
+    cap = int(capacity)
+    fp8 = int(recv_dtype) == EP_DTYPE_FP8_E4M3
+    handle = ep_handle_t()
+    st = lib().ep_layout_dispatch(
+        ctypes.byref(cfg), int(recv_dtype), _ptr(x, torch.bfloat16, (T, H), "x"),
+        _ptr(topk_idx, torch.int32, (T, k), "topk_idx"),
+        _ptr(topk_weights, torch.float32, (T, k), "topk_weights"),
+        _ptr(num_tokens_per_rank, torch.int32, (R,), "num_tokens_per_rank"),
+        _ptr(num_tokens_per_expert, torch.int32, (E,), "num_tokens_per_expert"),
+        _ptr(is_token_in_rank, torch.uint8, (T, R), "is_token_in_rank"),
+        _ptr(expert_offsets, torch.int32, (E + 1,), "expert_offsets"),
+        _ptr(rank_offsets, torch.int32, (R + 1,), "rank_offsets"),
+        _ptr(workspace, torch.uint8, name="workspace"), workspace.numel(), cap,
+        _ptr(recv_x, torch.uint8 if fp8 else torch.bfloat16, (cap, H), "recv_x"),
+        _ptr(recv_scales, torch.float32, (cap, H // 128), "recv_scales") if fp8 else None,
+        _ptr(recv_weights, torch.float32, (cap,), "recv_weights"),
+        _ptr(tok_slot_row, torch.int32, (T, k), "tok_slot_row"),
+        _ptr(row_src, torch.int32, (cap,), "row_src"),
+        _ptr(status, torch.int32, (1,), "status"), ctypes.byref(handle), _stream(stream))
+    _check(st, "ep_layout_dispatch")
     return handle
 
 
@@ -513,6 +550,25 @@ class EpBuffers:
             self._recv_weights_ptr if topk_weights is not None else None,
             *self._dispatch_tail, ctypes.byref(self._handle_out), _stream(stream))
         _check(st, "ep_dispatch")
+        self.handle = self._handle_out
+        return self.handle
+
+    def layout_dispatch(self, x, topk_idx, topk_weights, stream=None):
+        """Layout and dispatch in one launch (at most 256 tokens); leaves the
+        same buffers, workspace and handle as layout() then dispatch()."""
+        import torch
+
+        la = self._layout_args
+        st = lib().ep_layout_dispatch(
+            self._cfg_ref, self._dtype, _ptr(x, torch.bfloat16, self._shape_th, "x"),
+            _ptr(topk_idx, torch.int32, self._shape_tk, "topk_idx"),
+            _ptr(topk_weights, torch.float32, self._shape_tk, "topk_weights"),
+            la[0], la[1], la[2], la[3], la[4], la[5], la[6], self.capacity,
+            self._dispatch_args[4], self._dispatch_args[5],
+            self._recv_weights_ptr if topk_weights is not None else None,
+            self._dispatch_tail[0], self._dispatch_tail[1], self._dispatch_tail[2],
+            ctypes.byref(self._handle_out), _stream(stream))
+        _check(st, "ep_layout_dispatch")
         self.handle = self._handle_out
         return self.handle
 

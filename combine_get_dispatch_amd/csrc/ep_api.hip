@@ -214,6 +214,60 @@ ep_status_t ep_dispatch(const ep_config_t *cfg, ep_dtype_t recv_dtype, const uin
   return EP_OK;
 }
 
+ep_status_t ep_layout_dispatch(const ep_config_t *cfg, ep_dtype_t recv_dtype, const uint16_t *x,
+                               const int32_t *topk_idx, const float *topk_weights,
+                               int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
+                               uint8_t *is_token_in_rank, int32_t *expert_offsets,
+                               int32_t *rank_offsets, void *workspace, size_t workspace_bytes,
+                               int64_t capacity, void *recv_x, float *recv_scales,
+                               float *recv_weights, int32_t *tok_slot_row, int32_t *row_src,
+                               int32_t *status, ep_handle_t *handle_host, hipStream_t stream) {
+  ep_status_t st = check_config(cfg);
+  if (st != EP_OK) return st;
+  if (cfg->num_tokens > EP_LAYOUT_DISPATCH_MAX_TOKENS)
+    return fail(EP_ERR_INVALID_ARG, "ep_layout_dispatch takes at most %d tokens (got %d)",
+                EP_LAYOUT_DISPATCH_MAX_TOKENS, cfg->num_tokens);
+  if (recv_dtype != EP_DTYPE_BF16 && recv_dtype != EP_DTYPE_FP8_E4M3)
+    return fail(EP_ERR_INVALID_ARG, "unknown recv_dtype %d", (int)recv_dtype);
+  const bool fp8 = recv_dtype == EP_DTYPE_FP8_E4M3;
+  if (fp8 && cfg->hidden % 128 != 0)
+    return fail(EP_ERR_INVALID_ARG, "FP8 dispatch needs hidden %% 128 == 0 (hidden %d)",
+                cfg->hidden);
+  if (capacity < 0 || capacity >= INT32_MAX)
+    return fail(EP_ERR_INVALID_ARG, "capacity %lld outside [0, 2^31 - 1)", (long long)capacity);
+  const bool empty = cfg->num_tokens == 0;
+  if ((!empty && (x == nullptr || topk_idx == nullptr || is_token_in_rank == nullptr ||
+                  tok_slot_row == nullptr)) ||
+      num_tokens_per_rank == nullptr || num_tokens_per_expert == nullptr ||
+      expert_offsets == nullptr || rank_offsets == nullptr || workspace == nullptr ||
+      status == nullptr || (capacity > 0 && (recv_x == nullptr || row_src == nullptr)) ||
+      (fp8 && capacity > 0 && recv_scales == nullptr))
+    return fail(EP_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(x) || !aligned16(recv_x))
+    return fail(EP_ERR_INVALID_ARG, "x and recv_x must be 16-byte aligned");
+  const size_t need =
+      ep::workspace_layout(cfg->num_tokens, cfg->num_topk, cfg->num_experts, cfg->num_ranks)
+          .total;
+  if (workspace_bytes < need)
+    return fail(EP_ERR_INVALID_ARG, "workspace has %zu bytes, layout needs %zu",
+                workspace_bytes, need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(EP_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  hipError_t err = ep::launch_layout_dispatch(
+      dims_of(cfg), fp8, x, topk_idx, topk_weights, num_tokens_per_rank, num_tokens_per_expert,
+      is_token_in_rank, expert_offsets, rank_offsets, static_cast<char *>(workspace), capacity,
+      recv_x, recv_scales, recv_weights, tok_slot_row, row_src, status, stream);
+  if (err != hipSuccess) return hip_fail(err, "layout-dispatch launch");
+  if (handle_host != nullptr) {
+    handle_host->config = *cfg;
+    handle_host->capacity = capacity;
+    handle_host->tok_slot_row = tok_slot_row;
+    handle_host->row_src = row_src;
+    handle_host->expert_offsets = expert_offsets;
+  }
+  return EP_OK;
+}
+
 ep_status_t ep_dispatch_fp8_input(const ep_config_t *cfg, const uint8_t *x_codes,
                                   const float *x_scales, const int32_t *topk_idx,
                                   const float *topk_weights, const int32_t *expert_offsets,

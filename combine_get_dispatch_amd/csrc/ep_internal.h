@@ -50,6 +50,18 @@ hipError_t launch_layout(const Dims &d, const int32_t *topk_idx, int32_t *num_to
 
 hipError_t launch_workspace_init(char *ws, hipStream_t stream);
 
+// Dynamic LDS bytes of a layout workgroup with E experts.
+size_t layout_lds_bytes(int32_t E);
+
+// Layout and dispatch in one launch (T <= kTileTokens).
+hipError_t launch_layout_dispatch(const Dims &d, bool fp8, const uint16_t *x,
+                                  const int32_t *topk_idx, const float *topk_weights,
+                                  int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
+                                  uint8_t *is_token_in_rank, int32_t *expert_offsets,
+                                  int32_t *rank_offsets, char *ws, int64_t capacity, void *recv_x,
+                                  float *recv_scales, float *recv_weights, int32_t *tok_slot_row,
+                                  int32_t *row_src, int32_t *status, hipStream_t stream);
+
 hipError_t launch_dispatch(const Dims &d, bool fp8, const uint16_t *x, const int32_t *topk_idx,
                            const float *topk_weights, const int32_t *expert_offsets,
                            const char *ws, int64_t capacity, void *recv_x, float *recv_scales,

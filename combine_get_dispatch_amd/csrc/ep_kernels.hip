@@ -12,7 +12,7 @@
 //                         workgroup to finish (or the only one) scans: per
 //                         expert over tiles (tile bases), then over experts
 //                         (segment starts).
-//   dispatch_*_kernel     one wave per (token, 1024-column chunk): reads the
+//   dispatch_kernel       one wave per (token, 1024-column chunk): reads the
 //                         x chunk once with 16-byte loads, optionally
 //                         quantises it to E4M3 in registers, and stores it to
 //                         each of the token's receive rows.
@@ -96,8 +96,229 @@ __device__ __forceinline__ bool workspace_ok(const int32_t *hdr, const Dims &d) 
 // workgroup scans its own counts straight from LDS.  The ticket lives in the
 // workspace header; it starts at zero (ep_workspace_init) and the scanning
 // workgroup resets it, so consecutive layouts on one stream can reuse the
-// workspace.
+// workspace.  The phases below are shared with layout_dispatch_kernel.
 // ---------------------------------------------------------------------------
+
+// The layout's LDS: [kWavesPerBlock][E] expert bitmasks; [kWavesPerBlock][E]
+// counts of each expert in the earlier waves of the tile; [E + 1] words
+// holding the tile's (later the batch's) count per expert, then the aligned
+// offsets; per-rank token counts and per-wave scan totals.
+struct LayoutLds {
+  unsigned long long *masks;
+  int32_t *prefix;
+  int32_t *counts;
+  int32_t *rank_cnt;
+  int32_t *wave_total;
+};
+
+__device__ __forceinline__ LayoutLds layout_lds(unsigned long long *dyn, int E,
+                                                int32_t *rank_cnt, int32_t *wave_total) {
+  LayoutLds L;
+  L.masks = dyn;
+  L.prefix = reinterpret_cast<int32_t *>(dyn + kWavesPerBlock * E);
+  L.counts = L.prefix + kWavesPerBlock * E;
+  L.rank_cnt = rank_cnt;
+  L.wave_total = wave_total;
+  return L;
+}
+
+// Count phase of one tile, thread tid = token tile * 256 + tid.  Loads the
+// token's k expert ids into ex (ids outside [-1, E) become -1), marks them
+// in the wave's LDS bitmask of each expert, counts distinct tokens per rank
+// and leaves per expert its count in the earlier waves (prefix) and in the
+// tile (counts).  A repeated or out-of-range id sets the route bit when
+// status is given; the per-wave rank ballots go to rank_ballot when given.
+template <int K>
+__device__ __forceinline__ void count_tile(const Dims &d, int tile, int64_t t, bool live,
+                                           int experts_per_rank,
+                                           const int32_t *__restrict__ topk_idx,
+                                           const LayoutLds &L, int32_t (&ex)[K],
+                                           unsigned long long &rmask,
+                                           unsigned long long *__restrict__ rank_ballot,
+                                           int32_t *__restrict__ status) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int E = d.E, k = d.k, R = d.R;
+  const unsigned long long me = 1ull << lane;
+
+  // The token's expert ids, loaded together before any LDS traffic.
+#pragma unroll
+  for (int j = 0; j < K; ++j) ex[j] = (live && j < k) ? topk_idx[t * k + j] : -1;
+
+  for (int i = tid; i < kWavesPerBlock * E; i += kBlock) L.masks[i] = 0ull;
+  for (int i = tid; i < R; i += kBlock) L.rank_cnt[i] = 0;
+  __syncthreads();
+
+  // Mark this token in its wave's bitmask of every expert it selected;
+  // reject ids outside [-1, E) and ids repeated within the token.
+  bool bad = false;
+  rmask = 0ull;
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const int32_t e = ex[j];
+    if (e < -1 || e >= E) {
+      bad = true;
+      ex[j] = -1;
+      continue;
+    }
+    if (e < 0) continue;
+#pragma unroll
+    for (int jj = 0; jj < j; ++jj) bad |= ex[jj] == e;
+    atomicOr(&L.masks[wave * E + e], me);
+    rmask |= 1ull << (e / experts_per_rank);
+  }
+  if (bad && status != nullptr) flag(status, EP_STATUS_BIT_ROUTE);
+
+  // Distinct tokens per rank in this tile: lane r keeps the wave's ballot
+  // for rank r.  The ballots also go to the workspace: the non-expanded
+  // dispatch places a token among a rank's tokens from these words.
+  unsigned long long mine = 0ull;
+  for (int r = 0; r < R; ++r) {
+    const unsigned long long b = __ballot((rmask >> r) & 1ull);
+    if (lane == r) mine = b;
+  }
+  if (lane < R) {
+    if (rank_ballot != nullptr)
+      rank_ballot[((int64_t)tile * kWavesPerBlock + wave) * R + lane] = mine;
+    if (mine) atomicAdd(&L.rank_cnt[lane], (int32_t)__popcll(mine));
+  }
+  __syncthreads();
+
+  // Per expert: its count in the earlier waves (for the stable ranks) and
+  // in the tile.
+  for (int e = tid; e < E; e += kBlock) {
+    int32_t run = 0;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w) {
+      L.prefix[w * E + e] = run;
+      run += __popcll(L.masks[w * E + e]);
+    }
+    L.counts[e] = run;
+  }
+}
+
+// Stable rank of selection e of token (wave, lane) inside its tile: tokens
+// of earlier waves that chose e, plus lanes below this one in its own wave
+// that chose e.
+__device__ __forceinline__ int32_t tile_rank(const LayoutLds &L, int E, int wave, int lane,
+                                             int32_t e) {
+  return __popcll(L.masks[wave * E + e] & ((1ull << lane) - 1ull)) + L.prefix[wave * E + e];
+}
+
+// Per-token outputs: the rank mask and the stable in-tile rank of each
+// selection.
+template <int K>
+__device__ __forceinline__ void token_outputs(const Dims &d, int64_t t, const LayoutLds &L,
+                                              const int32_t (&ex)[K], unsigned long long rmask,
+                                              uint8_t *__restrict__ is_token_in_rank,
+                                              int32_t *__restrict__ slot_rank) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int R = d.R;
+  uint8_t *dst = is_token_in_rank + t * R;
+  if ((R & 3) == 0) {
+    for (int r = 0; r < R; r += 4) {
+      const uint32_t b = (uint32_t)(rmask >> r);
+      *reinterpret_cast<uint32_t *>(dst + r) =
+          (b & 1u) | ((b >> 1) & 1u) << 8 | ((b >> 2) & 1u) << 16 | ((b >> 3) & 1u) << 24;
+    }
+  } else {
+    for (int r = 0; r < R; ++r) dst[r] = (uint8_t)((rmask >> r) & 1ull);
+  }
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const int32_t e = ex[j];
+    const int32_t rank = e >= 0 ? tile_rank(L, d.E, wave, lane, e) : -1;
+    if (j < d.k) slot_rank[t * d.k + j] = rank;
+  }
+}
+
+// Scan phase, by a whole workgroup, once L.counts holds the batch's count
+// per expert and thread r < R holds rank r's token count in rank_sum.
+// Leaves the aligned segment starts in L.counts[0..E] and, with write set,
+// stores the counts, offsets and rank partitions.
+__device__ __forceinline__ void scan_counts(const Dims &d, int experts_per_rank,
+                                            const LayoutLds &L, int32_t rank_sum, bool write,
+                                            int32_t *__restrict__ cnt_ws,
+                                            int32_t *__restrict__ num_tokens_per_expert,
+                                            int32_t *__restrict__ num_tokens_per_rank,
+                                            int32_t *__restrict__ rank_tok_off,
+                                            int32_t *__restrict__ expert_offsets,
+                                            int32_t *__restrict__ rank_offsets) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int E = d.E, R = d.R;
+  for (int e = tid; e < E; e += kBlock) {
+    const int32_t run = L.counts[e];
+    if (write) {
+      cnt_ws[e] = run;
+      num_tokens_per_expert[e] = run;
+    }
+    L.counts[e] = (run + d.A - 1) / d.A * d.A;
+  }
+  // The first wave (R <= 64 lanes) scans the rank counts into the starts of
+  // the ranks' token partitions (the non-expanded layout).
+  if (write && tid < R) num_tokens_per_rank[tid] = rank_sum;
+  if (write && wave == 0) {
+    const int32_t v = lane < R ? rank_sum : 0;
+    int32_t inc = v;
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int32_t u = __shfl_up(inc, off);
+      if (lane >= off) inc += u;
+    }
+    if (lane < R) rank_tok_off[lane] = inc - v;
+    if (lane == R - 1) rank_tok_off[R] = inc;
+  }
+  __syncthreads();
+
+  // Exclusive scan of the aligned counts over experts: each thread owns a
+  // run of G consecutive experts; runs are scanned across the wave with
+  // shuffles and across the four waves through LDS.
+  const int G = (E + kBlock - 1) / kBlock;
+  const int e0 = tid * G;
+  int32_t local = 0;
+  for (int i = 0; i < G; ++i)
+    if (e0 + i < E) local += L.counts[e0 + i];
+  int32_t incl = local;
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int32_t v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
+  }
+  if (lane == kWave - 1) L.wave_total[wave] = incl;
+  __syncthreads();
+  int32_t base = incl - local;
+  for (int w = 0; w < wave; ++w) base += L.wave_total[w];
+  int32_t total = 0;
+  for (int w = 0; w < kWavesPerBlock; ++w) total += L.wave_total[w];
+  for (int i = 0; i < G; ++i) {
+    if (e0 + i < E) {
+      const int32_t a = L.counts[e0 + i];
+      L.counts[e0 + i] = base;
+      if (write) expert_offsets[e0 + i] = base;
+      base += a;
+    }
+  }
+  if (tid == 0) {
+    L.counts[E] = total;
+    if (write) expert_offsets[E] = total;
+  }
+  __syncthreads();
+  if (write && tid <= R) rank_offsets[tid] = L.counts[tid * experts_per_rank];
+}
+
+// Marks the workspace as written by a layout of this configuration.
+__device__ __forceinline__ void write_header(int32_t *__restrict__ header, const Dims &d,
+                                             int32_t ntiles) {
+  header[1] = d.T;
+  header[2] = d.k;
+  header[3] = d.E;
+  header[4] = d.R;
+  header[5] = d.A;
+  header[6] = ntiles;
+  header[0] = kWorkspaceMagic;
+}
 
 // K is a compile-time bound on k (k <= K) so that a token's expert ids stay
 // in registers between the marking pass and the ranking pass.
@@ -111,88 +332,33 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
     int32_t *__restrict__ rank_offsets, int32_t *__restrict__ header,
     unsigned long long *__restrict__ rank_ballot_ws, int32_t *__restrict__ rank_tok_off,
     int32_t *__restrict__ status) {
-  // LDS: [kWavesPerBlock][E] expert bitmasks; [kWavesPerBlock][E] counts of
-  // each expert in the earlier waves of the tile; [E + 1] words holding the
-  // tile's (later the batch's) count per expert, then the aligned offsets.
-  extern __shared__ unsigned long long masks[];
+  extern __shared__ unsigned long long dyn_lds[];
   __shared__ int32_t rank_cnt[EP_MAX_RANKS];
   __shared__ int32_t wave_total[kWavesPerBlock];
   __shared__ int is_last;
+  const LayoutLds L = layout_lds(dyn_lds, d.E, rank_cnt, wave_total);
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
   const int tile = blockIdx.x;
-  const int E = d.E, k = d.k, R = d.R;
-  int32_t *prefix = reinterpret_cast<int32_t *>(masks + kWavesPerBlock * E);
-  int32_t *counts = prefix + kWavesPerBlock * E;
+  const int E = d.E, R = d.R;
   const bool many = gridDim.x > 1;
   const bool has_tile = tile < ntiles;
   const int64_t t = (int64_t)tile * kTileTokens + tid;
   const bool live = has_tile && t < d.T;
-  const unsigned long long me = 1ull << lane;
   unsigned long long rmask = 0ull;
   int32_t ex[K];
 
   if (has_tile) {
-    // The token's expert ids, loaded together before any LDS traffic.
-#pragma unroll
-    for (int j = 0; j < K; ++j) ex[j] = (live && j < k) ? topk_idx[t * k + j] : -1;
-
-    for (int i = tid; i < kWavesPerBlock * E; i += kBlock) masks[i] = 0ull;
-    for (int i = tid; i < R; i += kBlock) rank_cnt[i] = 0;
-    __syncthreads();
-
-    // Mark this token in its wave's bitmask of every expert it selected;
-    // reject ids outside [-1, E) and ids repeated within the token.
-    bool bad = false;
-#pragma unroll
-    for (int j = 0; j < K; ++j) {
-      const int32_t e = ex[j];
-      if (e < -1 || e >= E) {
-        bad = true;
-        ex[j] = -1;
-        continue;
-      }
-      if (e < 0) continue;
-#pragma unroll
-      for (int jj = 0; jj < j; ++jj) bad |= ex[jj] == e;
-      atomicOr(&masks[wave * E + e], me);
-      rmask |= 1ull << (e / experts_per_rank);
+    count_tile<K>(d, tile, t, live, experts_per_rank, topk_idx, L, ex, rmask, rank_ballot_ws,
+                  status);
+    // With several tiles the tile's counts are published for the scan.
+    if (many) {
+      for (int e = tid; e < E; e += kBlock) tile_cnt[(int64_t)tile * E + e] = L.counts[e];
+      for (int r = tid; r < R; r += kBlock) tile_rank_cnt[(int64_t)tile * R + r] = L.rank_cnt[r];
     }
-    if (bad) flag(status, EP_STATUS_BIT_ROUTE);
-
-    // Distinct tokens per rank in this tile: lane r keeps the wave's ballot
-    // for rank r.  The ballots also go to the workspace: the non-expanded
-    // dispatch places a token among a rank's tokens from these words.
-    unsigned long long mine = 0ull;
-    for (int r = 0; r < R; ++r) {
-      const unsigned long long b = __ballot((rmask >> r) & 1ull);
-      if (lane == r) mine = b;
-    }
-    if (lane < R) {
-      rank_ballot_ws[((int64_t)tile * kWavesPerBlock + wave) * R + lane] = mine;
-      if (mine) atomicAdd(&rank_cnt[lane], (int32_t)__popcll(mine));
-    }
-    __syncthreads();
-
-    // Per expert: its count in the earlier waves (for the stable ranks) and
-    // in the tile.  With several tiles the tile's counts are published.
-    for (int e = tid; e < E; e += kBlock) {
-      int32_t run = 0;
-#pragma unroll
-      for (int w = 0; w < kWavesPerBlock; ++w) {
-        prefix[w * E + e] = run;
-        run += __popcll(masks[w * E + e]);
-      }
-      counts[e] = run;
-      if (many) tile_cnt[(int64_t)tile * E + e] = run;
-    }
-    if (many)
-      for (int r = tid; r < R; r += kBlock) tile_rank_cnt[(int64_t)tile * R + r] = rank_cnt[r];
   } else {
     // An empty batch: one workgroup writes zero counts and offsets.
-    for (int e = tid; e < E; e += kBlock) counts[e] = 0;
-    for (int i = tid; i < R; i += kBlock) rank_cnt[i] = 0;
+    for (int e = tid; e < E; e += kBlock) L.counts[e] = 0;
+    for (int i = tid; i < R; i += kBlock) L.rank_cnt[i] = 0;
   }
   __syncthreads();
 
@@ -226,29 +392,7 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
     }
   }
 
-  // Per-token outputs: the rank mask and the stable rank of (t, e) inside
-  // the tile (tokens of earlier waves that chose e, plus lanes below this
-  // one in its own wave that chose e).
-  if (live) {
-    uint8_t *dst = is_token_in_rank + t * R;
-    if ((R & 3) == 0) {
-      for (int r = 0; r < R; r += 4) {
-        const uint32_t b = (uint32_t)(rmask >> r);
-        *reinterpret_cast<uint32_t *>(dst + r) =
-            (b & 1u) | ((b >> 1) & 1u) << 8 | ((b >> 2) & 1u) << 16 | ((b >> 3) & 1u) << 24;
-      }
-    } else {
-      for (int r = 0; r < R; ++r) dst[r] = (uint8_t)((rmask >> r) & 1ull);
-    }
-    const unsigned long long below = me - 1ull;
-#pragma unroll
-    for (int j = 0; j < K; ++j) {
-      const int32_t e = ex[j];
-      const int32_t rank =
-          e >= 0 ? __popcll(masks[wave * E + e] & below) + prefix[wave * E + e] : -1;
-      if (j < k) slot_rank[t * k + j] = rank;
-    }
-  }
+  if (live) token_outputs<K>(d, t, L, ex, rmask, is_token_in_rank, slot_rank);
   if (!scans) return;
 
   // Per expert: tile histograms -> exclusive tile bases (in place) and the
@@ -286,78 +430,20 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
           rank_sum += rc[b];
         }
       }
-      counts[e] = run;
+      L.counts[e] = run;
     }
-  } else if (ntiles > 0) {
-    for (int e = tid; e < E; e += kBlock) tile_cnt[e] = 0;
+  } else {
+    if (ntiles > 0)
+      for (int e = tid; e < E; e += kBlock) tile_cnt[e] = 0;
     if (tid < R) {
-      rank_sum = rank_cnt[tid];
-      tile_rank_cnt[tid] = 0;
+      rank_sum = L.rank_cnt[tid];
+      if (ntiles > 0) tile_rank_cnt[tid] = 0;
     }
   }
-  for (int e = tid; e < E; e += kBlock) {
-    const int32_t run = counts[e];
-    cnt_ws[e] = run;
-    num_tokens_per_expert[e] = run;
-    counts[e] = (run + d.A - 1) / d.A * d.A;
-  }
-  // Thread r < R holds rank r's token count.  The first wave (R <= 64
-  // lanes) scans the counts into the starts of the ranks' token partitions
-  // (the non-expanded layout).
-  if (tid < R) num_tokens_per_rank[tid] = rank_sum;
-  if (wave == 0) {
-    const int32_t v = lane < R ? rank_sum : 0;
-    int32_t inc = v;
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int32_t u = __shfl_up(inc, off);
-      if (lane >= off) inc += u;
-    }
-    if (lane < R) rank_tok_off[lane] = inc - v;
-    if (lane == R - 1) rank_tok_off[R] = inc;
-  }
-  __syncthreads();
-
-  // Exclusive scan of the aligned counts over experts: each thread owns a
-  // run of G consecutive experts; runs are scanned across the wave with
-  // shuffles and across the four waves through LDS.
-  const int G = (E + kBlock - 1) / kBlock;
-  const int e0 = tid * G;
-  int32_t local = 0;
-  for (int i = 0; i < G; ++i)
-    if (e0 + i < E) local += counts[e0 + i];
-  int32_t incl = local;
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int32_t v = __shfl_up(incl, off);
-    if (lane >= off) incl += v;
-  }
-  if (lane == kWave - 1) wave_total[wave] = incl;
-  __syncthreads();
-  int32_t base = incl - local;
-  for (int w = 0; w < wave; ++w) base += wave_total[w];
-  int32_t total = 0;
-  for (int w = 0; w < kWavesPerBlock; ++w) total += wave_total[w];
-  for (int i = 0; i < G; ++i) {
-    if (e0 + i < E) {
-      const int32_t a = counts[e0 + i];
-      counts[e0 + i] = base;
-      expert_offsets[e0 + i] = base;
-      base += a;
-    }
-  }
+  scan_counts(d, experts_per_rank, L, rank_sum, true, cnt_ws, num_tokens_per_expert,
+              num_tokens_per_rank, rank_tok_off, expert_offsets, rank_offsets);
   if (tid == 0) {
-    counts[E] = total;
-    expert_offsets[E] = total;
-  }
-  __syncthreads();
-  if (tid <= R) rank_offsets[tid] = counts[tid * experts_per_rank];
-  if (tid == 0) {
-    header[1] = d.T;
-    header[2] = d.k;
-    header[3] = d.E;
-    header[4] = d.R;
-    header[5] = d.A;
-    header[6] = ntiles;
-    header[0] = kWorkspaceMagic;
+    write_header(header, d, ntiles);
     if (many) atomicExch(&header[kHeaderTicket], 0);
   }
 }
@@ -414,52 +500,10 @@ __device__ __forceinline__ int32_t selection_row(const Dims &d, int64_t t, int l
   return row;
 }
 
-// bf16 rows: a bit copy of the x chunk into each receive row.
-__global__ __launch_bounds__(kBlock) void dispatch_bf16_kernel(
-    Dims d, int32_t nchunks, const uint16_t *__restrict__ x, const int32_t *__restrict__ topk_idx,
-    const float *__restrict__ topk_weights, const int32_t *__restrict__ expert_offsets,
-    const int32_t *__restrict__ header, const int32_t *__restrict__ tile_base,
-    const int32_t *__restrict__ slot_rank, int64_t capacity, uint16_t *__restrict__ recv_x,
-    float *__restrict__ recv_weights, int32_t *__restrict__ tok_slot_row,
-    int32_t *__restrict__ row_src, int32_t *__restrict__ status) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int item = uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
-  if (item >= d.T * nchunks) return;
-  if (!workspace_ok(header, d)) {
-    if (lane == 0) flag(status, EP_STATUS_BIT_WORKSPACE);
-    return;
-  }
-  const int64_t t = item / nchunks;
-  const int chunk = item - (int)t * nchunks;
-  const int32_t row = selection_row(d, t, lane, chunk == 0, topk_idx, topk_weights,
-                                    expert_offsets, tile_base, slot_rank, capacity,
-                                    recv_weights, tok_slot_row, row_src, status);
-
-  constexpr int U = kChunkCols / (kWave * 8);
-  const int64_t H = d.H;
-  uint4 v[U];
-  int col[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    col[u] = chunk * kChunkCols + u * (kWave * 8) + lane * 8;
-    if (col[u] < H) v[u] = *reinterpret_cast<const uint4 *>(x + t * H + col[u]);
-  }
-  for (int j = 0; j < d.k; ++j) {
-    const int32_t r = lane_value(row, j);
-    if (r < 0) continue;
-    uint16_t *dst = recv_x + (int64_t)r * H;
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (col[u] < H) store_stream(dst + col[u], v[u]);
-  }
-}
-
 // FP8 rows: per token and 128-value block, amax over the block, scale =
 // amax / 448 and codes = E4M3(x / scale), both rounded to nearest even
 // ("Deep Dive - DeepEP", "Precision: FP8 on the wire, BF16 for the
-// reduction").  An all-zero block gets scale 0 and zero codes.  Each lane
-// owns 16 consecutive values (two 16-byte loads, one 16-byte store of
-// codes), so a block is 8 lanes and a wave covers 1024 columns.
+// reduction").  An all-zero block gets scale 0 and zero codes.
 __device__ __forceinline__ float amax8(const uint4 v) {
   float m = fabsf(bf16_lo(v.x));
   m = fmaxf(m, fabsf(bf16_hi(v.x)));
@@ -484,11 +528,81 @@ __device__ __forceinline__ uint2 quantize8(const uint4 v, float s) {
   return make_uint2((uint32_t)lo, (uint32_t)hi);
 }
 
-__global__ __launch_bounds__(kBlock) void dispatch_fp8_kernel(
+// One dispatch work item's slice of x (token t, 1024-column chunk): 16 bf16
+// values per lane in two 16-byte loads.  bf16 rows take columns
+// c + lane * 8 and c + 512 + lane * 8; FP8 rows take the 16 consecutive
+// columns c + lane * 16, so that 8 lanes hold one 128-value block.
+struct XSlice {
+  uint4 v[2];
+};
+
+template <bool kFp8>
+__device__ __forceinline__ int slice_col(int chunk, int lane, int u) {
+  return kFp8 ? chunk * kChunkCols + lane * 16 + u * 8
+              : chunk * kChunkCols + u * (kWave * 8) + lane * 8;
+}
+
+template <bool kFp8>
+__device__ __forceinline__ XSlice load_x_slice(const uint16_t *__restrict__ x, int64_t t,
+                                               int64_t H, int chunk, int lane) {
+  XSlice xs;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    // FP8 needs H % 128 == 0, so the 8 lanes of a block are all in range or
+    // all out; bf16 guards each 8-column part.
+    const int col = slice_col<kFp8>(chunk, lane, u);
+    const bool in = kFp8 ? slice_col<kFp8>(chunk, lane, 0) < H : col < H;
+    xs.v[u] = in ? *reinterpret_cast<const uint4 *>(x + t * H + col) : make_uint4(0, 0, 0, 0);
+  }
+  return xs;
+}
+
+// Stores the slice to each of the token's receive rows (lane j holds the
+// row of slot j, -1 for none): bf16 bits, or E4M3 codes plus one scale per
+// 128-value block.  One 16-byte non-temporal store per lane per row part.
+template <bool kFp8>
+__device__ __forceinline__ void store_x_slice(const XSlice &xs, int32_t row, int k, int64_t H,
+                                              int chunk, int lane, void *__restrict__ recv_x,
+                                              float *__restrict__ recv_scales) {
+  if (kFp8) {
+    const int col = slice_col<true>(chunk, lane, 0);
+    const bool in = col < H;
+    float amax = fmaxf(amax8(xs.v[0]), amax8(xs.v[1]));
+#pragma unroll
+    for (int m = 1; m < 8; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+    const float scale = amax / 448.0f;
+    const uint2 q0 = quantize8(xs.v[0], scale);
+    const uint2 q1 = quantize8(xs.v[1], scale);
+    const uint4 q = make_uint4(q0.x, q0.y, q1.x, q1.y);
+    const int64_t nblk = H / 128;
+    for (int j = 0; j < k; ++j) {
+      const int32_t r = lane_value(row, j);
+      if (r < 0 || !in) continue;
+      store_stream(static_cast<uint8_t *>(recv_x) + (int64_t)r * H + col, q);
+      if ((lane & 7) == 0) recv_scales[(int64_t)r * nblk + col / 128] = scale;
+    }
+  } else {
+    for (int j = 0; j < k; ++j) {
+      const int32_t r = lane_value(row, j);
+      if (r < 0) continue;
+      uint16_t *dst = static_cast<uint16_t *>(recv_x) + (int64_t)r * H;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int col = slice_col<false>(chunk, lane, u);
+        if (col < H) store_stream(dst + col, xs.v[u]);
+      }
+    }
+  }
+}
+
+// One wave per (token, 1024-column chunk): the selection rows, then the x
+// slice to each of them (bf16 bit copy, or fused FP8 quantisation).
+template <bool kFp8>
+__global__ __launch_bounds__(kBlock) void dispatch_kernel(
     Dims d, int32_t nchunks, const uint16_t *__restrict__ x, const int32_t *__restrict__ topk_idx,
     const float *__restrict__ topk_weights, const int32_t *__restrict__ expert_offsets,
     const int32_t *__restrict__ header, const int32_t *__restrict__ tile_base,
-    const int32_t *__restrict__ slot_rank, int64_t capacity, uint8_t *__restrict__ recv_x,
+    const int32_t *__restrict__ slot_rank, int64_t capacity, void *__restrict__ recv_x,
     float *__restrict__ recv_scales, float *__restrict__ recv_weights,
     int32_t *__restrict__ tok_slot_row, int32_t *__restrict__ row_src,
     int32_t *__restrict__ status) {
@@ -504,31 +618,102 @@ __global__ __launch_bounds__(kBlock) void dispatch_fp8_kernel(
   const int32_t row = selection_row(d, t, lane, chunk == 0, topk_idx, topk_weights,
                                     expert_offsets, tile_base, slot_rank, capacity,
                                     recv_weights, tok_slot_row, row_src, status);
+  const XSlice xs = load_x_slice<kFp8>(x, t, d.H, chunk, lane);
+  store_x_slice<kFp8>(xs, row, d.k, d.H, chunk, lane, recv_x, recv_scales);
+}
 
-  const int64_t H = d.H;
-  const int64_t nblk = H / 128;
-  // H % 128 == 0, so the 8 lanes of a block are all in range or all out.
-  const int col = chunk * kChunkCols + lane * 16;
-  const bool in = col < H;
-  uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
-  if (in) {
-    v0 = *reinterpret_cast<const uint4 *>(x + t * H + col);
-    v1 = *reinterpret_cast<const uint4 *>(x + t * H + col + 8);
-  }
-  float amax = fmaxf(amax8(v0), amax8(v1));
-#pragma unroll
-  for (int m = 1; m < 8; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
-  const float scale = amax / 448.0f;
-  const uint2 q0 = quantize8(v0, scale);
-  const uint2 q1 = quantize8(v1, scale);
-  const uint4 q = make_uint4(q0.x, q0.y, q1.x, q1.y);
+// Layout and dispatch in one launch, for a batch of at most one tile (256
+// tokens): count, prefix sum and scatter in a single pass ("GPU
+// microarchitecture: DeepEP first principles", 6.1).  Every workgroup counts
+// and scans the whole batch in LDS, then moves its own work items (token,
+// 1024-column chunk) to the rows the scan gives.  Workgroup 0 also writes
+// every layout output and the workspace, so later calls (combine, the
+// non-expanded path, backward) see exactly what ep_get_dispatch_layout and
+// ep_dispatch leave.  The x slice and the token's expert ids are loaded
+// first, so their loads overlap the count.
+template <int K, bool kFp8>
+__global__ __launch_bounds__(kBlock) void layout_dispatch_kernel(
+    const int32_t *__restrict__ topk_idx, Dims d, int32_t ntiles, int32_t experts_per_rank,
+    int32_t nchunks, const uint16_t *__restrict__ x, const float *__restrict__ topk_weights,
+    int32_t *__restrict__ tile_cnt, int32_t *__restrict__ tile_rank_cnt,
+    int32_t *__restrict__ slot_rank, uint8_t *__restrict__ is_token_in_rank,
+    int32_t *__restrict__ cnt_ws, int32_t *__restrict__ num_tokens_per_expert,
+    int32_t *__restrict__ num_tokens_per_rank, int32_t *__restrict__ expert_offsets,
+    int32_t *__restrict__ rank_offsets, int32_t *__restrict__ header,
+    unsigned long long *__restrict__ rank_ballot_ws, int32_t *__restrict__ rank_tok_off,
+    int64_t capacity, void *__restrict__ recv_x, float *__restrict__ recv_scales,
+    float *__restrict__ recv_weights, int32_t *__restrict__ tok_slot_row,
+    int32_t *__restrict__ row_src, int32_t *__restrict__ status) {
+  extern __shared__ unsigned long long dyn_lds[];
+  __shared__ int32_t rank_cnt[EP_MAX_RANKS];
+  __shared__ int32_t wave_total[kWavesPerBlock];
+  const LayoutLds L = layout_lds(dyn_lds, d.E, rank_cnt, wave_total);
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const bool lead = blockIdx.x == 0;
+  const int64_t t = tid;  // the batch is tile 0: thread = token
+  const bool live = ntiles > 0 && t < d.T;
 
-  for (int j = 0; j < d.k; ++j) {
-    const int32_t r = lane_value(row, j);
-    if (r < 0 || !in) continue;
-    store_stream(recv_x + (int64_t)r * H + col, q);
-    if ((lane & 7) == 0) recv_scales[(int64_t)r * nblk + col / 128] = scale;
+  // This wave's work item, its x slice and its token's expert ids.
+  const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + uniform(tid / kWave);
+  const bool has_item = item < (int64_t)d.T * nchunks;
+  const int64_t ti = has_item ? item / nchunks : 0;
+  const int chunk = has_item ? (int)(item - ti * nchunks) : 0;
+  XSlice xs;
+  xs.v[0] = xs.v[1] = make_uint4(0, 0, 0, 0);
+  int32_t eid = -1;
+  if (has_item) {
+    xs = load_x_slice<kFp8>(x, ti, d.H, chunk, lane);
+    if (lane < d.k) eid = topk_idx[ti * d.k + lane];
   }
+
+  unsigned long long rmask = 0ull;
+  int32_t ex[K];
+  if (ntiles > 0) {
+    count_tile<K>(d, 0, t, live, experts_per_rank, topk_idx, L, ex, rmask,
+                  lead ? rank_ballot_ws : nullptr, lead ? status : nullptr);
+  } else {
+    for (int e = tid; e < d.E; e += kBlock) L.counts[e] = 0;
+    for (int i = tid; i < d.R; i += kBlock) L.rank_cnt[i] = 0;
+  }
+  __syncthreads();
+  if (lead && live) token_outputs<K>(d, t, L, ex, rmask, is_token_in_rank, slot_rank);
+  scan_counts(d, experts_per_rank, L, tid < d.R ? L.rank_cnt[tid] : 0, lead, cnt_ws,
+              num_tokens_per_expert, num_tokens_per_rank, rank_tok_off, expert_offsets,
+              rank_offsets);
+  if (lead) {
+    // One tile: its bases are zero.
+    if (ntiles > 0) {
+      for (int e = tid; e < d.E; e += kBlock) tile_cnt[e] = 0;
+      if (tid < d.R) tile_rank_cnt[tid] = 0;
+    }
+    if (tid == 0) write_header(header, d, ntiles);
+  }
+  if (!has_item) return;
+
+  // Receive rows of the token's selections: segment start plus the stable
+  // rank inside the batch, as selection_row gives them.
+  int32_t row = -1;
+  if (lane < d.k) {
+    if (eid >= 0 && eid < d.E) {
+      const int64_t r = (int64_t)L.counts[eid] +
+                        tile_rank(L, d.E, (int)(ti / kWave), (int)(ti % kWave), eid);
+      if (r < capacity)
+        row = (int32_t)r;
+      else
+        flag(status, EP_STATUS_BIT_CAPACITY);
+    }
+    if (chunk == 0) {
+      const int64_t sidx = ti * d.k + lane;
+      tok_slot_row[sidx] = row;
+      if (row >= 0) {
+        row_src[row] = (int32_t)sidx;
+        if (recv_weights != nullptr && topk_weights != nullptr)
+          recv_weights[row] = topk_weights[sidx];
+      }
+    }
+  }
+  store_x_slice<kFp8>(xs, row, d.k, d.H, chunk, lane, recv_x, recv_scales);
 }
 
 // Pre-quantised rows ("Deep Dive - DeepEP", "Dispatch: layout, move, and
@@ -1204,9 +1389,7 @@ hipError_t launch_layout(const Dims &d, const int32_t *topk_idx, int32_t *num_to
                          int32_t *expert_offsets, int32_t *rank_offsets, char *ws,
                          int32_t *status, hipStream_t stream) {
   const WorkspaceLayout w = workspace_layout(d.T, d.k, d.E, d.R);
-  const size_t lds = sizeof(unsigned long long) * kWavesPerBlock * (size_t)d.E +
-                     sizeof(int32_t) * kWavesPerBlock * (size_t)d.E +
-                     sizeof(int32_t) * ((size_t)d.E + 1);
+  const size_t lds = layout_lds_bytes(d.E);
   auto kernel = d.k <= 8 ? layout_kernel<8> : (d.k <= 16 ? layout_kernel<16> : layout_kernel<32>);
   // An empty batch still needs one workgroup to write zero counts and offsets.
   const unsigned grid = w.ntiles > 0 ? (unsigned)w.ntiles : 1u;
@@ -1241,19 +1424,57 @@ hipError_t launch_dispatch(const Dims &d, bool fp8, const uint16_t *x, const int
   if (d.T > 0) {
     const int64_t items = (int64_t)d.T * nchunks;
     const dim3 grid((unsigned)((items + kWavesPerBlock - 1) / kWavesPerBlock));
-    if (fp8)
-      hipLaunchKernelGGL(dispatch_fp8_kernel, grid, dim3(kBlock), 0, stream, d, nchunks, x,
-                         topk_idx, topk_weights, expert_offsets, header, tile_base, slot_rank,
-                         capacity, static_cast<uint8_t *>(recv_x), recv_scales, recv_weights,
-                         tok_slot_row, row_src, status);
-    else
-      hipLaunchKernelGGL(dispatch_bf16_kernel, grid, dim3(kBlock), 0, stream, d, nchunks, x,
-                         topk_idx, topk_weights, expert_offsets, header, tile_base, slot_rank,
-                         capacity, static_cast<uint16_t *>(recv_x), recv_weights, tok_slot_row,
-                         row_src, status);
+    auto kernel = fp8 ? dispatch_kernel<true> : dispatch_kernel<false>;
+    hipLaunchKernelGGL(kernel, grid, dim3(kBlock), 0, stream, d, nchunks, x, topk_idx,
+                       topk_weights, expert_offsets, header, tile_base, slot_rank, capacity,
+                       recv_x, recv_scales, recv_weights, tok_slot_row, row_src, status);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
+  if (d.A > 1) {
+    hipLaunchKernelGGL(pad_fill_kernel, dim3(d.E), dim3(kBlock), 0, stream, d, fp8,
+                       expert_offsets, reinterpret_cast<const int32_t *>(ws + w.cnt), capacity,
+                       recv_x, recv_scales, topk_weights != nullptr ? recv_weights : nullptr,
+                       row_src);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+size_t layout_lds_bytes(int32_t E) {
+  return sizeof(unsigned long long) * kWavesPerBlock * (size_t)E +
+         sizeof(int32_t) * kWavesPerBlock * (size_t)E + sizeof(int32_t) * ((size_t)E + 1);
+}
+
+hipError_t launch_layout_dispatch(const Dims &d, bool fp8, const uint16_t *x,
+                                  const int32_t *topk_idx, const float *topk_weights,
+                                  int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
+                                  uint8_t *is_token_in_rank, int32_t *expert_offsets,
+                                  int32_t *rank_offsets, char *ws, int64_t capacity, void *recv_x,
+                                  float *recv_scales, float *recv_weights, int32_t *tok_slot_row,
+                                  int32_t *row_src, int32_t *status, hipStream_t stream) {
+  const WorkspaceLayout w = workspace_layout(d.T, d.k, d.E, d.R);
+  const int32_t nchunks = (d.H + kChunkCols - 1) / kChunkCols;
+  const int64_t items = (int64_t)d.T * nchunks;
+  const unsigned grid = items > 0 ? (unsigned)((items + kWavesPerBlock - 1) / kWavesPerBlock) : 1u;
+  auto pick = [&](auto k8, auto k16, auto k32) { return d.k <= 8 ? k8 : (d.k <= 16 ? k16 : k32); };
+  auto kernel = fp8 ? pick(layout_dispatch_kernel<8, true>, layout_dispatch_kernel<16, true>,
+                           layout_dispatch_kernel<32, true>)
+                    : pick(layout_dispatch_kernel<8, false>, layout_dispatch_kernel<16, false>,
+                           layout_dispatch_kernel<32, false>);
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kBlock), layout_lds_bytes(d.E), stream, topk_idx, d,
+                     w.ntiles, d.E / d.R, nchunks, x, topk_weights,
+                     reinterpret_cast<int32_t *>(ws + w.tile_cnt),
+                     reinterpret_cast<int32_t *>(ws + w.tile_rank_cnt),
+                     reinterpret_cast<int32_t *>(ws + w.slot_rank), is_token_in_rank,
+                     reinterpret_cast<int32_t *>(ws + w.cnt), num_tokens_per_expert,
+                     num_tokens_per_rank, expert_offsets, rank_offsets,
+                     reinterpret_cast<int32_t *>(ws),
+                     reinterpret_cast<unsigned long long *>(ws + w.rank_ballot),
+                     reinterpret_cast<int32_t *>(ws + w.rank_tok_off), capacity, recv_x,
+                     recv_scales, recv_weights, tok_slot_row, row_src, status);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
   if (d.A > 1) {
     hipLaunchKernelGGL(pad_fill_kernel, dim3(d.E), dim3(kBlock), 0, stream, d, fp8,
                        expert_offsets, reinterpret_cast<const int32_t *>(ws + w.cnt), capacity,

@@ -74,6 +74,7 @@ typedef enum ep_dtype {
 #define EP_MAX_EXPERTS 1024
 #define EP_MAX_TOPK 32
 #define EP_MAX_RANKS 64
+#define EP_LAYOUT_DISPATCH_MAX_TOKENS 256 /* batch bound of ep_layout_dispatch */
 
 typedef struct ep_config {
   int32_t num_tokens;       /* T >= 0 */
@@ -219,6 +220,30 @@ ep_status_t ep_dispatch(const ep_config_t *cfg, ep_dtype_t recv_dtype, const uin
                         float *recv_scales, float *recv_weights, int32_t *tok_slot_row,
                         int32_t *row_src, int32_t *status, ep_handle_t *handle_host,
                         hipStream_t stream);
+
+/*
+ * Layout and dispatch in one launch, for a batch of at most
+ * EP_LAYOUT_DISPATCH_MAX_TOKENS tokens (count, prefix sum and scatter in a
+ * single pass: "GPU microarchitecture: DeepEP first principles", "6.1
+ * Layout Metadata"; "Deep Dive - DeepEP", "Dispatch: layout, move, and
+ * epilogue").  It writes exactly what ep_get_dispatch_layout followed by
+ * ep_dispatch writes, bit for bit: every layout output, the workspace (so
+ * combine, the non-expanded path and backward work after it unchanged), the
+ * receive rows and the handle.  It saves the small-batch path one launch
+ * and a round trip through the workspace.  The arguments are those two
+ * calls' arguments; there is no synchronising row count.
+ *
+ * Returns EP_ERR_INVALID_ARG (nothing enqueued) when num_tokens exceeds
+ * EP_LAYOUT_DISPATCH_MAX_TOKENS or for any argument the two calls reject.
+ */
+ep_status_t ep_layout_dispatch(const ep_config_t *cfg, ep_dtype_t recv_dtype, const uint16_t *x,
+                               const int32_t *topk_idx, const float *topk_weights,
+                               int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
+                               uint8_t *is_token_in_rank, int32_t *expert_offsets,
+                               int32_t *rank_offsets, void *workspace, size_t workspace_bytes,
+                               int64_t capacity, void *recv_x, float *recv_scales,
+                               float *recv_weights, int32_t *tok_slot_row, int32_t *row_src,
+                               int32_t *status, ep_handle_t *handle_host, hipStream_t stream);
 
 /*
  * Dispatch of rows that arrive already quantised ("Deep Dive - DeepEP",

@@ -121,3 +121,15 @@ def test_probe_rejects_bad_arguments_before_launch():
         st = L.ep_hbm_probe(kind, nt, wgs, src, dst, nbytes, None)
         assert st == ep.EP_ERR_INVALID_ARG
         assert L.ep_last_error().decode().startswith("probe")
+
+
+def test_layout_dispatch_rejects_large_batches_before_launch():
+    """ep_layout_dispatch takes one tile of tokens at most; more is an
+    argument error returned before anything is enqueued."""
+    L = ep.lib()
+    cfg = ep.ep_config_t(257, 256, 8, 256, 8, 1)
+    P = ctypes.c_void_p(256)
+    st = L.ep_layout_dispatch(ctypes.byref(cfg), ep.EP_DTYPE_BF16, P, P, P, P, P, P, P, P, P,
+                              1 << 20, 257 * 8, P, P, P, P, P, P, None, None)
+    assert st == ep.EP_ERR_INVALID_ARG
+    assert "at most 256" in L.ep_last_error().decode()

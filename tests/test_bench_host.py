@@ -11,7 +11,8 @@ template <bool kWeighted, int KB>
 __global__ __launch_bounds__(kBlock) void combine_kernel(int *p) {
   p[0] = helper(1);
 }
-__global__ __launch_bounds__(kBlock) void dispatch_fp8_kernel(int *p) {
+template <bool kFp8>
+__global__ __launch_bounds__(kBlock) void dispatch_kernel(int *p) {
   p[0] = 2;
 }
 hipError_t launch_combine(int *p) {
