@@ -433,6 +433,9 @@ def main():
     ap.add_argument("--ranked", action="store_true",
                     help="time the non-expanded path (dispatch_ranked + expand + "
                          "combine_ranked; its own JSON line)")
+    ap.add_argument("--fused", action="store_true",
+                    help="layout and dispatch in one launch (ep_layout_dispatch; at most 256 "
+                         "tokens)")
     ap.add_argument("--graph", action="store_true",
                     help="capture one forward step as a HIP graph and time its replays")
     ap.add_argument("--direction", choices=("forward", "backward"), default="forward",
@@ -493,9 +496,16 @@ def main():
         else:
             b.dispatch(x, idx, wts)
 
+    if args.fused and (w.num_tokens > ep.LAYOUT_DISPATCH_MAX_TOKENS or args.fp8_input):
+        raise SystemExit(f"--fused takes at most {ep.LAYOUT_DISPATCH_MAX_TOKENS} tokens "
+                         "(tiny, decode) and bf16 or quantising dispatch")
+
     def step():
-        b.layout(idx)
-        do_dispatch()
+        if args.fused:
+            b.layout_dispatch(x, idx, wts)
+        else:
+            b.layout(idx)
+            do_dispatch()
         b.combine(y, wts)
 
     if args.direction == "backward":
@@ -546,12 +556,16 @@ def main():
           flush=True)
 
     # per call, events on the launch stream
-    names = ("layout", "dispatch", "combine")
+    if args.fused:
+        names = ("layout_dispatch", "combine")
+        fns = (lambda: b.layout_dispatch(x, idx, wts), lambda: b.combine(y, wts))
+    else:
+        names = ("layout", "dispatch", "combine")
+        fns = (lambda: b.layout(idx), do_dispatch, lambda: b.combine(y, wts))
     ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)] for n in names}
     for i in range(args.steps):
-        for n, fn in zip(names, (lambda: b.layout(idx), do_dispatch,
-                                 lambda: b.combine(y, wts))):
+        for n, fn in zip(names, fns):
             ev[n][i][0].record(stream)
             fn()
             ev[n][i][1].record(stream)
@@ -642,9 +656,11 @@ def main():
 
     receipt = run_receipt(w, inp, b, dev)
     by = algorithmic_bytes(w, M, args.fp8_input)
+    if args.fused:
+        by["layout_dispatch"] = by["layout"] + by["dispatch"]
     step_s = ms_per_step / 1e3
     gbps = by["total"] / step_s / 1e9
-    dom = max(("dispatch", "combine"), key=lambda n: per_us[n])
+    dom = max(names[-2:], key=lambda n: per_us[n])
     achieved = by[dom] / (per_us[dom] / 1e6) / 1e9
     traffic = None if args.fp8_input else load_traffic(w.name, dom)
     rec = {
@@ -669,7 +685,8 @@ def main():
                    "dispatch_payload": ("fp8_e4m3 (pre-quantised input)" if args.fp8_input
                                         else "fp8_e4m3" if w.fp8 else "bf16"),
                    "valid_selections": M,
-                   "launch": "hip_graph" if args.graph else "eager"},
+                   "launch": "hip_graph" if args.graph else "eager",
+                   "layout": "fused with dispatch (one launch)" if args.fused else "own launch"},
         "pct_of_peak": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
         "tokens_per_s": round(w.num_tokens / step_s, 1),
         "algorithmic_bytes_per_step": by,
