@@ -118,12 +118,21 @@ def _piece_name(piece: str):
     return "helper", None
 
 
+def _code_only(text: str) -> str:
+    """The text without comments, trailing spaces or blank lines: edits to
+    those do not change what is compiled."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_source_hash(kernel: str = None, src: str = None, extra: bytes = None) -> str:
     """Hash of what a kernel's measured behaviour depends on: every helper
     piece of the kernel source (anything that is neither a kernel nor a
     launcher), the kernel's own function and launcher, the internal header
-    and the compiler flags.  With kernel=None, the whole sources.  Editing
-    another kernel leaves a kernel's hash unchanged."""
+    and the compiler flags, all without comments.  With kernel=None, the
+    whole sources.  Editing another kernel, or a comment, leaves a kernel's
+    hash unchanged."""
     h = hashlib.sha256()
     if src is None:
         with open(KERNEL_SOURCES[0]) as f:
@@ -131,20 +140,20 @@ def kernel_source_hash(kernel: str = None, src: str = None, extra: bytes = None)
     if extra is None:
         extra = b""
         for path in KERNEL_SOURCES[1:]:
-            with open(path, "rb") as f:
-                extra += f.read()
+            with open(path) as f:
+                extra += _code_only(f.read()).encode()
         from combine_get_dispatch_amd import _build
 
         extra += " ".join(_build.HIPCC_FLAGS).encode()
     h.update(extra)
     if kernel is None:
-        h.update(src.encode())
+        h.update(_code_only(src).encode())
         return h.hexdigest()[:16]
     kname, lname = KERNEL_FUNCS[kernel]
     for piece in split_functions(src):
         kind, name = _piece_name(piece)
         if kind == "helper" or name in (kname, lname):
-            h.update(piece.encode())
+            h.update(_code_only(piece).encode())
     return h.hexdigest()[:16]
 
 

@@ -19,8 +19,13 @@
 //   combine_kernel        one wave per (token, 512-column chunk): k gathered
 //                         16-byte loads per lane, fp32 FMAs in slot order,
 //                         one bf16 rounding, one 16-byte store.
-// Output positions never depend on atomics or scheduling, so every result
-// is deterministic.
+//   layout_dispatch_kernel  layout and dispatch in one launch for at most
+//                         256 tokens: every workgroup recounts the batch in
+//                         LDS, then moves its own items.
+// Also: the non-expanded path (dispatch_ranked_kernel, expand_kernel, the
+// two ranked combine stages), the backward of combine, and the alignment
+// padding fills.  Output positions never depend on atomics or scheduling,
+// so every result is deterministic.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

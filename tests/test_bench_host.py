@@ -29,6 +29,12 @@ def test_hash_ignores_other_kernels():
     assert _h(SRC) == _h(SRC.replace("p[0] = 2;", "p[0] = 3;"))
 
 
+def test_hash_ignores_comments_and_blank_lines():
+    edited = SRC.replace("// helpers", "// helper functions\n\n/* shared */")
+    edited = edited.replace("  p[0] = helper(1);", "  p[0] = helper(1);  // the helper")
+    assert _h(SRC) == _h(edited)
+
+
 def test_hash_follows_kernel_launcher_and_helpers():
     base = _h(SRC)
     assert base != _h(SRC.replace("helper(1)", "helper(2)"))
