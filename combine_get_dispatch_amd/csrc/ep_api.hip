@@ -61,6 +61,41 @@ ep::Dims dims_of(const ep_config_t *c) {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// recv_dtype is a known type; FP8 rows need hidden % 128 == 0.
+ep_status_t check_dtype(const ep_config_t *c, ep_dtype_t recv_dtype, bool *fp8) {
+  if (recv_dtype != EP_DTYPE_BF16 && recv_dtype != EP_DTYPE_FP8_E4M3)
+    return fail(EP_ERR_INVALID_ARG, "unknown recv_dtype %d", (int)recv_dtype);
+  *fp8 = recv_dtype == EP_DTYPE_FP8_E4M3;
+  if (*fp8 && c->hidden % 128 != 0)
+    return fail(EP_ERR_INVALID_ARG, "FP8 rows need hidden %% 128 == 0 (hidden %d)", c->hidden);
+  return EP_OK;
+}
+
+// A row count that int32 row indices can address.
+ep_status_t check_rows(const char *what, int64_t rows) {
+  if (rows < 0 || rows >= INT32_MAX)
+    return fail(EP_ERR_INVALID_ARG, "%s %lld outside [0, 2^31 - 1)", what, (long long)rows);
+  return EP_OK;
+}
+
+// The workspace holds this configuration's layout sections and is 256-byte
+// aligned.
+ep_status_t check_workspace(const ep_config_t *c, const void *workspace, size_t workspace_bytes) {
+  const size_t need =
+      ep::workspace_layout(c->num_tokens, c->num_topk, c->num_experts, c->num_ranks).total;
+  if (workspace_bytes < need)
+    return fail(EP_ERR_INVALID_ARG, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(EP_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  return EP_OK;
+}
+
+#define EP_TRY(expr)                  \
+  do {                                \
+    const ep_status_t st_ = (expr);   \
+    if (st_ != EP_OK) return st_;     \
+  } while (0)
+
 }  // namespace
 
 namespace ep {
@@ -85,8 +120,7 @@ const char *ep_status_string(ep_status_t status) {
 const char *ep_last_error(void) { return g_last_error; }
 
 ep_status_t ep_layout_workspace_bytes(const ep_config_t *cfg, size_t *bytes_host) {
-  ep_status_t st = check_config(cfg);
-  if (st != EP_OK) return st;
+  EP_TRY(check_config(cfg));
   if (bytes_host == nullptr) return fail(EP_ERR_INVALID_ARG, "bytes_host is NULL");
   *bytes_host = ep::workspace_layout(cfg->num_tokens, cfg->num_topk, cfg->num_experts,
                                      cfg->num_ranks)
@@ -95,8 +129,7 @@ ep_status_t ep_layout_workspace_bytes(const ep_config_t *cfg, size_t *bytes_host
 }
 
 ep_status_t ep_recv_capacity_rows(const ep_config_t *cfg, int64_t *rows_host) {
-  ep_status_t st = check_config(cfg);
-  if (st != EP_OK) return st;
+  EP_TRY(check_config(cfg));
   if (rows_host == nullptr) return fail(EP_ERR_INVALID_ARG, "rows_host is NULL");
   *rows_host = (int64_t)cfg->num_tokens * cfg->num_topk +
                (int64_t)cfg->num_experts * (cfg->expert_alignment - 1);
@@ -138,22 +171,14 @@ ep_status_t ep_get_dispatch_layout(const ep_config_t *cfg, const int32_t *topk_i
                                    int32_t *rank_offsets, void *workspace,
                                    size_t workspace_bytes, int32_t *status,
                                    int32_t *num_recv_rows_host, hipStream_t stream) {
-  ep_status_t st = check_config(cfg);
-  if (st != EP_OK) return st;
+  EP_TRY(check_config(cfg));
   const bool empty = cfg->num_tokens == 0;
   if ((!empty && (topk_idx == nullptr || is_token_in_rank == nullptr)) ||
       num_tokens_per_rank == nullptr || num_tokens_per_expert == nullptr ||
       expert_offsets == nullptr || rank_offsets == nullptr || workspace == nullptr ||
       status == nullptr)
     return fail(EP_ERR_INVALID_ARG, "a required pointer is NULL");
-  const size_t need =
-      ep::workspace_layout(cfg->num_tokens, cfg->num_topk, cfg->num_experts, cfg->num_ranks)
-          .total;
-  if (workspace_bytes < need)
-    return fail(EP_ERR_INVALID_ARG, "workspace has %zu bytes, layout needs %zu",
-                workspace_bytes, need);
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-    return fail(EP_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  EP_TRY(check_workspace(cfg, workspace, workspace_bytes));
   hipError_t err = ep::launch_layout(dims_of(cfg), topk_idx, num_tokens_per_rank,
                                      num_tokens_per_expert, is_token_in_rank, expert_offsets,
                                      rank_offsets, static_cast<char *>(workspace), status,
@@ -175,16 +200,10 @@ ep_status_t ep_dispatch(const ep_config_t *cfg, ep_dtype_t recv_dtype, const uin
                         float *recv_scales, float *recv_weights, int32_t *tok_slot_row,
                         int32_t *row_src, int32_t *status, ep_handle_t *handle_host,
                         hipStream_t stream) {
-  ep_status_t st = check_config(cfg);
-  if (st != EP_OK) return st;
-  if (recv_dtype != EP_DTYPE_BF16 && recv_dtype != EP_DTYPE_FP8_E4M3)
-    return fail(EP_ERR_INVALID_ARG, "unknown recv_dtype %d", (int)recv_dtype);
-  const bool fp8 = recv_dtype == EP_DTYPE_FP8_E4M3;
-  if (fp8 && cfg->hidden % 128 != 0)
-    return fail(EP_ERR_INVALID_ARG, "FP8 dispatch needs hidden %% 128 == 0 (hidden %d)",
-                cfg->hidden);
-  if (capacity < 0 || capacity >= INT32_MAX)
-    return fail(EP_ERR_INVALID_ARG, "capacity %lld outside [0, 2^31 - 1)", (long long)capacity);
+  EP_TRY(check_config(cfg));
+  bool fp8 = false;
+  EP_TRY(check_dtype(cfg, recv_dtype, &fp8));
+  EP_TRY(check_rows("capacity", capacity));
   const bool empty = cfg->num_tokens == 0;
   if ((!empty && (x == nullptr || topk_idx == nullptr || tok_slot_row == nullptr)) ||
       expert_offsets == nullptr || workspace == nullptr || status == nullptr ||
@@ -193,12 +212,7 @@ ep_status_t ep_dispatch(const ep_config_t *cfg, ep_dtype_t recv_dtype, const uin
     return fail(EP_ERR_INVALID_ARG, "a required pointer is NULL");
   if (!aligned16(x) || !aligned16(recv_x))
     return fail(EP_ERR_INVALID_ARG, "x and recv_x must be 16-byte aligned");
-  const size_t need =
-      ep::workspace_layout(cfg->num_tokens, cfg->num_topk, cfg->num_experts, cfg->num_ranks)
-          .total;
-  if (workspace_bytes < need)
-    return fail(EP_ERR_INVALID_ARG, "workspace has %zu bytes, dispatch needs %zu",
-                workspace_bytes, need);
+  EP_TRY(check_workspace(cfg, workspace, workspace_bytes));
   hipError_t err = ep::launch_dispatch(dims_of(cfg), fp8, x, topk_idx, topk_weights,
                                        expert_offsets, static_cast<const char *>(workspace),
                                        capacity, recv_x, recv_scales, recv_weights, tok_slot_row,
@@ -222,19 +236,13 @@ ep_status_t ep_layout_dispatch(const ep_config_t *cfg, ep_dtype_t recv_dtype, co
                                int64_t capacity, void *recv_x, float *recv_scales,
                                float *recv_weights, int32_t *tok_slot_row, int32_t *row_src,
                                int32_t *status, ep_handle_t *handle_host, hipStream_t stream) {
-  ep_status_t st = check_config(cfg);
-  if (st != EP_OK) return st;
+  EP_TRY(check_config(cfg));
   if (cfg->num_tokens > EP_LAYOUT_DISPATCH_MAX_TOKENS)
     return fail(EP_ERR_INVALID_ARG, "ep_layout_dispatch takes at most %d tokens (got %d)",
                 EP_LAYOUT_DISPATCH_MAX_TOKENS, cfg->num_tokens);
-  if (recv_dtype != EP_DTYPE_BF16 && recv_dtype != EP_DTYPE_FP8_E4M3)
-    return fail(EP_ERR_INVALID_ARG, "unknown recv_dtype %d", (int)recv_dtype);
-  const bool fp8 = recv_dtype == EP_DTYPE_FP8_E4M3;
-  if (fp8 && cfg->hidden % 128 != 0)
-    return fail(EP_ERR_INVALID_ARG, "FP8 dispatch needs hidden %% 128 == 0 (hidden %d)",
-                cfg->hidden);
-  if (capacity < 0 || capacity >= INT32_MAX)
-    return fail(EP_ERR_INVALID_ARG, "capacity %lld outside [0, 2^31 - 1)", (long long)capacity);
+  bool fp8 = false;
+  EP_TRY(check_dtype(cfg, recv_dtype, &fp8));
+  EP_TRY(check_rows("capacity", capacity));
   const bool empty = cfg->num_tokens == 0;
   if ((!empty && (x == nullptr || topk_idx == nullptr || is_token_in_rank == nullptr ||
                   tok_slot_row == nullptr)) ||
@@ -245,14 +253,7 @@ ep_status_t ep_layout_dispatch(const ep_config_t *cfg, ep_dtype_t recv_dtype, co
     return fail(EP_ERR_INVALID_ARG, "a required pointer is NULL");
   if (!aligned16(x) || !aligned16(recv_x))
     return fail(EP_ERR_INVALID_ARG, "x and recv_x must be 16-byte aligned");
-  const size_t need =
-      ep::workspace_layout(cfg->num_tokens, cfg->num_topk, cfg->num_experts, cfg->num_ranks)
-          .total;
-  if (workspace_bytes < need)
-    return fail(EP_ERR_INVALID_ARG, "workspace has %zu bytes, layout needs %zu",
-                workspace_bytes, need);
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-    return fail(EP_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  EP_TRY(check_workspace(cfg, workspace, workspace_bytes));
   hipError_t err = ep::launch_layout_dispatch(
       dims_of(cfg), fp8, x, topk_idx, topk_weights, num_tokens_per_rank, num_tokens_per_expert,
       is_token_in_rank, expert_offsets, rank_offsets, static_cast<char *>(workspace), capacity,
@@ -276,12 +277,10 @@ ep_status_t ep_dispatch_fp8_input(const ep_config_t *cfg, const uint8_t *x_codes
                                   float *recv_weights, int32_t *tok_slot_row, int32_t *row_src,
                                   int32_t *status, ep_handle_t *handle_host,
                                   hipStream_t stream) {
-  ep_status_t st = check_config(cfg);
-  if (st != EP_OK) return st;
-  if (cfg->hidden % 128 != 0)
-    return fail(EP_ERR_INVALID_ARG, "FP8 rows need hidden %% 128 == 0 (hidden %d)", cfg->hidden);
-  if (capacity < 0 || capacity >= INT32_MAX)
-    return fail(EP_ERR_INVALID_ARG, "capacity %lld outside [0, 2^31 - 1)", (long long)capacity);
+  EP_TRY(check_config(cfg));
+  bool fp8 = false;
+  EP_TRY(check_dtype(cfg, EP_DTYPE_FP8_E4M3, &fp8));
+  EP_TRY(check_rows("capacity", capacity));
   const bool empty = cfg->num_tokens == 0;
   if ((!empty && (x_codes == nullptr || x_scales == nullptr || topk_idx == nullptr ||
                   tok_slot_row == nullptr)) ||
@@ -290,12 +289,7 @@ ep_status_t ep_dispatch_fp8_input(const ep_config_t *cfg, const uint8_t *x_codes
     return fail(EP_ERR_INVALID_ARG, "a required pointer is NULL");
   if (!aligned16(x_codes) || !aligned16(recv_x))
     return fail(EP_ERR_INVALID_ARG, "x_codes and recv_x must be 16-byte aligned");
-  const size_t need =
-      ep::workspace_layout(cfg->num_tokens, cfg->num_topk, cfg->num_experts, cfg->num_ranks)
-          .total;
-  if (workspace_bytes < need)
-    return fail(EP_ERR_INVALID_ARG, "workspace has %zu bytes, dispatch needs %zu",
-                workspace_bytes, need);
+  EP_TRY(check_workspace(cfg, workspace, workspace_bytes));
   hipError_t err = ep::launch_dispatch_fp8_input(
       dims_of(cfg), x_codes, x_scales, topk_idx, topk_weights, expert_offsets,
       static_cast<const char *>(workspace), capacity, recv_x, recv_scales, recv_weights,
@@ -314,11 +308,8 @@ ep_status_t ep_dispatch_fp8_input(const ep_config_t *cfg, const uint8_t *x_codes
 ep_status_t ep_combine(const ep_handle_t *handle, const uint16_t *expert_out,
                        const float *topk_weights, uint16_t *out, hipStream_t stream) {
   if (handle == nullptr) return fail(EP_ERR_INVALID_ARG, "handle is NULL");
-  ep_status_t st = check_config(&handle->config);
-  if (st != EP_OK) return st;
-  if (handle->capacity < 0 || handle->capacity >= INT32_MAX)
-    return fail(EP_ERR_INVALID_ARG, "handle capacity %lld invalid",
-                (long long)handle->capacity);
+  EP_TRY(check_config(&handle->config));
+  EP_TRY(check_rows("handle capacity", handle->capacity));
   if (handle->config.num_tokens > 0 &&
       (handle->tok_slot_row == nullptr || out == nullptr ||
        (handle->capacity > 0 && expert_out == nullptr)))
@@ -334,11 +325,8 @@ ep_status_t ep_combine(const ep_handle_t *handle, const uint16_t *expert_out,
 ep_status_t ep_dispatch_backward(const ep_handle_t *handle, const uint16_t *grad_recv_x,
                                  uint16_t *grad_x, hipStream_t stream) {
   if (handle == nullptr) return fail(EP_ERR_INVALID_ARG, "handle is NULL");
-  ep_status_t st = check_config(&handle->config);
-  if (st != EP_OK) return st;
-  if (handle->capacity < 0 || handle->capacity >= INT32_MAX)
-    return fail(EP_ERR_INVALID_ARG, "handle capacity %lld invalid",
-                (long long)handle->capacity);
+  EP_TRY(check_config(&handle->config));
+  EP_TRY(check_rows("handle capacity", handle->capacity));
   if (handle->config.num_tokens > 0 &&
       (handle->tok_slot_row == nullptr || grad_x == nullptr ||
        (handle->capacity > 0 && grad_recv_x == nullptr)))
@@ -356,11 +344,8 @@ ep_status_t ep_combine_backward(const ep_handle_t *handle, const uint16_t *grad_
                                 uint16_t *grad_expert_out, float *grad_weights,
                                 hipStream_t stream) {
   if (handle == nullptr) return fail(EP_ERR_INVALID_ARG, "handle is NULL");
-  ep_status_t st = check_config(&handle->config);
-  if (st != EP_OK) return st;
-  if (handle->capacity < 0 || handle->capacity >= INT32_MAX)
-    return fail(EP_ERR_INVALID_ARG, "handle capacity %lld invalid",
-                (long long)handle->capacity);
+  EP_TRY(check_config(&handle->config));
+  EP_TRY(check_rows("handle capacity", handle->capacity));
   const bool empty = handle->config.num_tokens == 0;
   if ((!empty && (handle->tok_slot_row == nullptr || grad_out == nullptr)) ||
       (handle->capacity > 0 && grad_expert_out == nullptr) ||
@@ -380,8 +365,7 @@ ep_status_t ep_combine_backward(const ep_handle_t *handle, const uint16_t *grad_
 }
 
 ep_status_t ep_ranked_capacity_rows(const ep_config_t *cfg, int64_t *rows_host) {
-  ep_status_t st = check_config(cfg);
-  if (st != EP_OK) return st;
+  EP_TRY(check_config(cfg));
   if (rows_host == nullptr) return fail(EP_ERR_INVALID_ARG, "rows_host is NULL");
   const int64_t per = cfg->num_topk < cfg->num_ranks ? cfg->num_topk : cfg->num_ranks;
   *rows_host = (int64_t)cfg->num_tokens * per;
@@ -397,15 +381,11 @@ ep_status_t ep_dispatch_ranked(const ep_config_t *cfg, ep_dtype_t recv_dtype, co
                                int32_t *rank_token_offsets, int32_t *tok_rank_row,
                                int32_t *tok_slot_row, int32_t *status,
                                ep_ranked_handle_t *handle_host, hipStream_t stream) {
-  ep_status_t st = check_config(cfg);
-  if (st != EP_OK) return st;
-  if (recv_dtype != EP_DTYPE_BF16 && recv_dtype != EP_DTYPE_FP8_E4M3)
-    return fail(EP_ERR_INVALID_ARG, "unknown recv_dtype %d", (int)recv_dtype);
-  const bool fp8 = recv_dtype == EP_DTYPE_FP8_E4M3;
-  if (fp8 && cfg->hidden % 128 != 0)
-    return fail(EP_ERR_INVALID_ARG, "FP8 rows need hidden %% 128 == 0 (hidden %d)", cfg->hidden);
-  if (capacity < 0 || capacity >= INT32_MAX || ranked_capacity < 0 || ranked_capacity >= INT32_MAX)
-    return fail(EP_ERR_INVALID_ARG, "capacities must be in [0, 2^31 - 1)");
+  EP_TRY(check_config(cfg));
+  bool fp8 = false;
+  EP_TRY(check_dtype(cfg, recv_dtype, &fp8));
+  EP_TRY(check_rows("capacity", capacity));
+  EP_TRY(check_rows("ranked_capacity", ranked_capacity));
   const bool empty = cfg->num_tokens == 0;
   if ((!empty && (x == nullptr || topk_idx == nullptr || tok_rank_row == nullptr ||
                   tok_slot_row == nullptr)) ||
@@ -416,12 +396,7 @@ ep_status_t ep_dispatch_ranked(const ep_config_t *cfg, ep_dtype_t recv_dtype, co
     return fail(EP_ERR_INVALID_ARG, "a required pointer is NULL");
   if (!aligned16(x) || !aligned16(ne_x))
     return fail(EP_ERR_INVALID_ARG, "x and ne_x must be 16-byte aligned");
-  const size_t need =
-      ep::workspace_layout(cfg->num_tokens, cfg->num_topk, cfg->num_experts, cfg->num_ranks)
-          .total;
-  if (workspace_bytes < need)
-    return fail(EP_ERR_INVALID_ARG, "workspace has %zu bytes, dispatch needs %zu",
-                workspace_bytes, need);
+  EP_TRY(check_workspace(cfg, workspace, workspace_bytes));
   hipError_t err = ep::launch_dispatch_ranked(
       dims_of(cfg), fp8, x, topk_idx, topk_weights, expert_offsets,
       static_cast<const char *>(workspace), capacity, ranked_capacity, ne_x, ne_scales,
@@ -444,11 +419,9 @@ ep_status_t ep_dispatch_ranked(const ep_config_t *cfg, ep_dtype_t recv_dtype, co
 
 static ep_status_t check_ranked(const ep_ranked_handle_t *h) {
   if (h == nullptr) return fail(EP_ERR_INVALID_ARG, "ranked handle is NULL");
-  ep_status_t st = check_config(&h->config);
-  if (st != EP_OK) return st;
-  if (h->capacity < 0 || h->capacity >= INT32_MAX || h->ranked_capacity < 0 ||
-      h->ranked_capacity >= INT32_MAX)
-    return fail(EP_ERR_INVALID_ARG, "ranked handle capacities invalid");
+  EP_TRY(check_config(&h->config));
+  EP_TRY(check_rows("handle capacity", h->capacity));
+  EP_TRY(check_rows("handle ranked_capacity", h->ranked_capacity));
   if (h->rank_token_offsets == nullptr ||
       (h->config.num_tokens > 0 && (h->tok_rank_row == nullptr || h->tok_slot_row == nullptr)) ||
       (h->ranked_capacity > 0 && (h->ne_topk_idx == nullptr || h->ne_src == nullptr)))
@@ -461,14 +434,10 @@ ep_status_t ep_expand(const ep_ranked_handle_t *ranked, ep_dtype_t recv_dtype, c
                       const void *workspace, size_t workspace_bytes, void *recv_x,
                       float *recv_scales, float *recv_weights, int32_t *row_src,
                       int32_t *status, ep_handle_t *handle_host, hipStream_t stream) {
-  ep_status_t st = check_ranked(ranked);
-  if (st != EP_OK) return st;
+  EP_TRY(check_ranked(ranked));
   const ep_config_t *cfg = &ranked->config;
-  if (recv_dtype != EP_DTYPE_BF16 && recv_dtype != EP_DTYPE_FP8_E4M3)
-    return fail(EP_ERR_INVALID_ARG, "unknown recv_dtype %d", (int)recv_dtype);
-  const bool fp8 = recv_dtype == EP_DTYPE_FP8_E4M3;
-  if (fp8 && cfg->hidden % 128 != 0)
-    return fail(EP_ERR_INVALID_ARG, "FP8 rows need hidden %% 128 == 0 (hidden %d)", cfg->hidden);
+  bool fp8 = false;
+  EP_TRY(check_dtype(cfg, recv_dtype, &fp8));
   if (expert_offsets == nullptr || workspace == nullptr || status == nullptr ||
       (ranked->ranked_capacity > 0 && (ne_x == nullptr || (fp8 && ne_scales == nullptr))) ||
       (ranked->capacity > 0 && (recv_x == nullptr || row_src == nullptr ||
@@ -476,12 +445,7 @@ ep_status_t ep_expand(const ep_ranked_handle_t *ranked, ep_dtype_t recv_dtype, c
     return fail(EP_ERR_INVALID_ARG, "a required pointer is NULL");
   if (!aligned16(ne_x) || !aligned16(recv_x))
     return fail(EP_ERR_INVALID_ARG, "ne_x and recv_x must be 16-byte aligned");
-  const size_t need =
-      ep::workspace_layout(cfg->num_tokens, cfg->num_topk, cfg->num_experts, cfg->num_ranks)
-          .total;
-  if (workspace_bytes < need)
-    return fail(EP_ERR_INVALID_ARG, "workspace has %zu bytes, expand needs %zu",
-                workspace_bytes, need);
+  EP_TRY(check_workspace(cfg, workspace, workspace_bytes));
   hipError_t err = ep::launch_expand(
       dims_of(cfg), fp8, ranked->ranked_capacity, ne_x, ne_scales, ranked->ne_topk_idx,
       ranked->ne_topk_weights, ranked->ne_src, ranked->rank_token_offsets, expert_offsets,
@@ -501,8 +465,7 @@ ep_status_t ep_expand(const ep_ranked_handle_t *ranked, ep_dtype_t recv_dtype, c
 ep_status_t ep_combine_ranked(const ep_ranked_handle_t *ranked, const uint16_t *expert_out,
                               int32_t weighted, float *partials, uint16_t *out,
                               hipStream_t stream) {
-  ep_status_t st = check_ranked(ranked);
-  if (st != EP_OK) return st;
+  EP_TRY(check_ranked(ranked));
   if (weighted && ranked->ranked_capacity > 0 && ranked->ne_topk_weights == nullptr)
     return fail(EP_ERR_INVALID_ARG, "weighted combine needs ne_topk_weights in the handle");
   if ((ranked->config.num_tokens > 0 && out == nullptr) ||
