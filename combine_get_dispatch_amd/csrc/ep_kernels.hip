@@ -533,6 +533,19 @@ __device__ __forceinline__ uint2 quantize8(const uint4 v, float s) {
   return make_uint2((uint32_t)lo, (uint32_t)hi);
 }
 
+// The 16 values a lane owns (v0 then v1) as E4M3 codes, with the scale of
+// their 128-value block: the amax is taken over the block's 8 lanes, which
+// must all call this together.
+__device__ __forceinline__ uint4 quantize16(const uint4 v0, const uint4 v1, float &scale) {
+  float amax = fmaxf(amax8(v0), amax8(v1));
+#pragma unroll
+  for (int m = 1; m < 8; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+  scale = amax / 448.0f;
+  const uint2 q0 = quantize8(v0, scale);
+  const uint2 q1 = quantize8(v1, scale);
+  return make_uint4(q0.x, q0.y, q1.x, q1.y);
+}
+
 // One dispatch work item's slice of x (token t, 1024-column chunk): 16 bf16
 // values per lane in two 16-byte loads.  bf16 rows take columns
 // c + lane * 8 and c + 512 + lane * 8; FP8 rows take the 16 consecutive
@@ -572,13 +585,8 @@ __device__ __forceinline__ void store_x_slice(const XSlice &xs, int32_t row, int
   if (kFp8) {
     const int col = slice_col<true>(chunk, lane, 0);
     const bool in = col < H;
-    float amax = fmaxf(amax8(xs.v[0]), amax8(xs.v[1]));
-#pragma unroll
-    for (int m = 1; m < 8; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
-    const float scale = amax / 448.0f;
-    const uint2 q0 = quantize8(xs.v[0], scale);
-    const uint2 q1 = quantize8(xs.v[1], scale);
-    const uint4 q = make_uint4(q0.x, q0.y, q1.x, q1.y);
+    float scale;
+    const uint4 q = quantize16(xs.v[0], xs.v[1], scale);
     const int64_t nblk = H / 128;
     for (int j = 0; j < k; ++j) {
       const int32_t r = lane_value(row, j);
@@ -904,16 +912,7 @@ __device__ __forceinline__ Payload16 load_payload(const uint16_t *__restrict__ x
     p.lo = *reinterpret_cast<const uint4 *>(x + t * H + col);
     if (col + 8 < H) p.hi = *reinterpret_cast<const uint4 *>(x + t * H + col + 8);
   }
-  if (kFp8) {
-    float amax = fmaxf(amax8(p.lo), amax8(p.hi));
-#pragma unroll
-    for (int m = 1; m < 8; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
-    const float s = amax / 448.0f;
-    const uint2 q0 = quantize8(p.lo, s);
-    const uint2 q1 = quantize8(p.hi, s);
-    p.lo = make_uint4(q0.x, q0.y, q1.x, q1.y);
-    p.scale = s;
-  }
+  if (kFp8) p.lo = quantize16(p.lo, p.hi, p.scale);
   return p;
 }
 
