@@ -572,6 +572,14 @@ class EpBuffers:
         self.handle = self._handle_out
         return self.handle
 
+    def layout_and_dispatch(self, x, topk_idx, topk_weights, stream=None):
+        """Layout then dispatch: one launch when the batch fits one tile (at
+        most 256 tokens), else the two calls.  The results are the same."""
+        if self.cfg.num_tokens <= LAYOUT_DISPATCH_MAX_TOKENS:
+            return self.layout_dispatch(x, topk_idx, topk_weights, stream=stream)
+        self.layout(topk_idx, stream=stream)
+        return self.dispatch(x, topk_idx, topk_weights, stream=stream)
+
     def dispatch_fp8_input(self, x_codes, x_scales, topk_idx, topk_weights, stream=None):
         if not self.fp8:
             raise ValueError("dispatch_fp8_input needs buffers built with fp8=True")

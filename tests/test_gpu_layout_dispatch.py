@@ -140,3 +140,22 @@ def test_layout_dispatch_decode_workload():
     assert np.array_equal(host_bf16(b.recv_x[:used]), d["recv_x"][:used])
     ref, _ = oracle.combine(inp["y"], d["tok_slot_row"], inp["topk_weights"])
     assert np.array_equal(host_bf16(out), ref)
+
+
+@pytest.mark.parametrize("T", [256, 257])
+def test_layout_and_dispatch_picks_either_path(T):
+    """EpBuffers.layout_and_dispatch fuses up to 256 tokens and falls back to
+    the two calls above; both give the oracle's rows."""
+    H, k, E, R = 256, 4, 32, 4
+    say(f"layout_and_dispatch T={T}")
+    rng = np.random.default_rng(T)
+    idx = W.random_routes(rng, T, E, k, mask_prob=0.05)
+    w = rng.random((T, k)).astype(np.float32)
+    x = W.normal_bf16(rng, (T, H))
+    b = ep.EpBuffers(T, H, k, E, R, 1)
+    b.layout_and_dispatch(dev_bf16(x), dev(idx), dev(w))
+    b.check_status()
+    d = oracle.dispatch(x, idx, w, E, R, 1)
+    used = int(b.expert_offsets[-1].item())
+    assert np.array_equal(b.tok_slot_row.cpu().numpy(), d["tok_slot_row"])
+    assert np.array_equal(host_bf16(b.recv_x[:used]), d["recv_x"][:used])
