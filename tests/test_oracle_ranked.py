@@ -126,3 +126,23 @@ def test_combine_ranked_error_bound(seed):
     # and against the single-stage combine: within the combine tolerance
     ref, acc1 = oracle.combine(y, d["tok_slot_row"], w)
     assert np.all(np.abs(acc.astype(np.float64) - acc1) <= 2 * (k + R) * 2.0 ** -24 * mag + 1e-45)
+
+
+def test_cross_rank_sum_is_in_rank_order():
+    """The second stage adds the ranks' fp32 partials in rank order from +0
+    (the reading the GPU check is bit-exact against).  Partials 1, 2^24 and
+    -2^24 on ranks 0, 1, 2: in rank order 1 + 2^24 rounds to 2^24 (a tie,
+    to even) and the sum is 0; in reverse order it would be 1."""
+    T, H, k, E, R = 1, 8, 3, 3, 3
+    idx = np.array([[0, 1, 2]], np.int32)
+    w = np.ones((1, k), np.float32)
+    x = np.zeros((T, H), np.uint16)
+    ne = oracle.dispatch_ranked(x, idx, w, E, R)
+    d = oracle.dispatch(x, idx, w, E, R)
+    vals = np.array([1.0, 2.0 ** 24, -(2.0 ** 24)], np.float32)
+    y = np.zeros((T * k, H), np.uint16)
+    for j in range(k):
+        y[d["tok_slot_row"][0, j]] = np.uint16(vals[j:j + 1].view(np.uint32)[0] >> 16)
+    out, acc, part = oracle.combine_ranked(y, d["tok_slot_row"], ne)
+    assert np.array_equal(part[:, 0], vals)
+    assert np.all(acc == 0.0) and np.all(out == 0)
