@@ -49,9 +49,27 @@ def _fresh(T, H, k, E, R, A, fp8):
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "T{}_H{}_k{}_E{}_R{}_A{}_{}{}".format(
     *c[:6], "fp8" if c[6] else "bf16", "" if c[7] else "_noweights"))
 def test_layout_dispatch_equals_two_calls(case):
-    T, H, k, E, R, A, fp8, weighted = case
+    _check_against_two_calls(*case, seed=900 + case[0] + case[3] + case[2])
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_layout_dispatch_random_shapes(seed):
+    """Random shapes up to one tile: tokens, hidden size, experts, ranks,
+    top-k, alignment, payload type and gates all drawn from the seed."""
+    rng = np.random.default_rng(7000 + seed)
+    R = int(rng.choice([1, 2, 4, 8, 16]))
+    E = R * int(rng.integers(1, 9))
+    k = int(rng.integers(1, min(E, 8) + 1))
+    fp8 = bool(rng.integers(0, 2))
+    H = 128 * int(rng.integers(1, 7)) if fp8 else 8 * int(rng.integers(1, 161))
+    T = int(rng.integers(0, 257))
+    A = int(rng.choice([1, 2, 4]))
+    _check_against_two_calls(T, H, k, E, R, A, fp8, bool(rng.integers(0, 2)), seed=seed)
+
+
+def _check_against_two_calls(T, H, k, E, R, A, fp8, weighted, seed):
     say(f"layout_dispatch T={T} H={H} k={k} E={E} R={R} A={A} fp8={fp8} w={weighted}")
-    rng = np.random.default_rng(900 + T + E + k)
+    rng = np.random.default_rng(seed)
     idx = W.random_routes(rng, T, E, k, mask_prob=0.1) if T else np.zeros((0, k), np.int32)
     w = rng.random((T, k)).astype(np.float32)
     x = W.normal_bf16(rng, (T, H))

@@ -79,3 +79,23 @@ def test_ranked_random_small(case):
     x = W.normal_bf16(rng, (T, H))
     y = W.normal_bf16(rng, (T * k + E * (A - 1), H))
     check(T, H, k, E, R, A, fp8, idx, w, x, y, weighted=bool(T % 2))
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_ranked_random_shapes(seed):
+    """Random shapes: tokens across several tiles, hidden sizes with ragged
+    chunks, experts, ranks, top-k, alignment, payload type and gates drawn
+    from the seed."""
+    rng = np.random.default_rng(8000 + seed)
+    R = int(rng.choice([1, 2, 4, 8, 16]))
+    E = R * int(rng.integers(1, 9))
+    k = int(rng.integers(1, min(E, 8) + 1))
+    fp8 = bool(rng.integers(0, 2))
+    H = 128 * int(rng.integers(1, 7)) if fp8 else 8 * int(rng.integers(1, 161))
+    T = int(rng.integers(0, 1500))
+    A = int(rng.choice([1, 2, 4]))
+    idx = W.random_routes(rng, T, E, k, mask_prob=float(rng.choice([0.0, 0.1, 0.3])))
+    w = rng.random((T, k)).astype(np.float32)
+    x = W.normal_bf16(rng, (T, H))
+    y = W.normal_bf16(rng, (T * k + E * (A - 1), H))
+    check(T, H, k, E, R, A, fp8, idx, w, x, y, weighted=bool(rng.integers(0, 2)))
