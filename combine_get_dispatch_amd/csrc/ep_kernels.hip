@@ -772,9 +772,13 @@ __global__ __launch_bounds__(kBlock) void dispatch_fp8_input_kernel(
   }
 }
 
-// Alignment padding rows of expert e (one workgroup per expert): zero
-// payload, zero scale, zero gate, no source ("Deep Dive - DeepEP",
-// "Dispatch: layout, move, and epilogue": padding is not a token).
+// Alignment padding rows of expert e: zero payload, zero scale, zero gate,
+// no source ("Deep Dive - DeepEP", "Dispatch: layout, move, and epilogue":
+// padding is not a token).  Expert e's rows are split over kPadSplit
+// workgroups (blockIdx.y strides the rows), so that the fill keeps the
+// chip busy.
+constexpr int kPadSplit = 8;
+
 __global__ __launch_bounds__(kBlock) void pad_fill_kernel(
     Dims d, bool fp8, const int32_t *__restrict__ expert_offsets, const int32_t *__restrict__ cnt,
     int64_t capacity, void *__restrict__ recv_x, float *__restrict__ recv_scales,
@@ -785,7 +789,7 @@ __global__ __launch_bounds__(kBlock) void pad_fill_kernel(
   if (last > capacity) last = capacity;
   const int64_t row_bytes = fp8 ? (int64_t)d.H : (int64_t)d.H * 2;
   const int64_t nblk = d.H / 128;
-  for (int64_t r = first; r < last; ++r) {
+  for (int64_t r = first + blockIdx.y; r < last; r += gridDim.y) {
     uint4 *dst = reinterpret_cast<uint4 *>(static_cast<char *>(recv_x) + r * row_bytes);
     for (int64_t i = threadIdx.x; i < row_bytes / 16; i += kBlock) dst[i] = make_uint4(0, 0, 0, 0);
     if (fp8)
@@ -1436,7 +1440,7 @@ hipError_t launch_dispatch(const Dims &d, bool fp8, const uint16_t *x, const int
     if (err != hipSuccess) return err;
   }
   if (d.A > 1) {
-    hipLaunchKernelGGL(pad_fill_kernel, dim3(d.E), dim3(kBlock), 0, stream, d, fp8,
+    hipLaunchKernelGGL(pad_fill_kernel, dim3(d.E, kPadSplit), dim3(kBlock), 0, stream, d, fp8,
                        expert_offsets, reinterpret_cast<const int32_t *>(ws + w.cnt), capacity,
                        recv_x, recv_scales, topk_weights != nullptr ? recv_weights : nullptr,
                        row_src);
@@ -1480,7 +1484,7 @@ hipError_t launch_layout_dispatch(const Dims &d, bool fp8, const uint16_t *x,
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (d.A > 1) {
-    hipLaunchKernelGGL(pad_fill_kernel, dim3(d.E), dim3(kBlock), 0, stream, d, fp8,
+    hipLaunchKernelGGL(pad_fill_kernel, dim3(d.E, kPadSplit), dim3(kBlock), 0, stream, d, fp8,
                        expert_offsets, reinterpret_cast<const int32_t *>(ws + w.cnt), capacity,
                        recv_x, recv_scales, topk_weights != nullptr ? recv_weights : nullptr,
                        row_src);
@@ -1511,7 +1515,7 @@ hipError_t launch_dispatch_fp8_input(const Dims &d, const uint8_t *x_codes, cons
     if (err != hipSuccess) return err;
   }
   if (d.A > 1) {
-    hipLaunchKernelGGL(pad_fill_kernel, dim3(d.E), dim3(kBlock), 0, stream, d, true,
+    hipLaunchKernelGGL(pad_fill_kernel, dim3(d.E, kPadSplit), dim3(kBlock), 0, stream, d, true,
                        expert_offsets, reinterpret_cast<const int32_t *>(ws + w.cnt), capacity,
                        static_cast<void *>(recv_x), recv_scales,
                        topk_weights != nullptr ? recv_weights : nullptr, row_src);
@@ -1613,7 +1617,7 @@ hipError_t launch_expand(const Dims &d, bool fp8, int64_t ranked_capacity, const
     if (err != hipSuccess) return err;
   }
   if (d.A > 1) {
-    hipLaunchKernelGGL(pad_fill_kernel, dim3(d.E), dim3(kBlock), 0, stream, d, fp8,
+    hipLaunchKernelGGL(pad_fill_kernel, dim3(d.E, kPadSplit), dim3(kBlock), 0, stream, d, fp8,
                        expert_offsets, reinterpret_cast<const int32_t *>(ws + w.cnt), capacity,
                        recv_x, recv_scales, ne_topk_weights != nullptr ? recv_weights : nullptr,
                        row_src);
