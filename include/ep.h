@@ -13,6 +13,12 @@
  *   ep_combine              expert-major rows -> token-major, gate applied
  *                           once, fixed-order fp32 sum, bf16 result
  *
+ * Further calls on the same data: ep_layout_dispatch (the first two in one
+ * launch for batches of at most 256 tokens), ep_dispatch_fp8_input
+ * (pre-quantised rows), ep_dispatch_backward and ep_combine_backward, and
+ * the non-expanded path ep_dispatch_ranked -> ep_expand ->
+ * ep_combine_ranked.  A measurement aid is declared apart, in ep_probe.h.
+ *
  * Pages cited: "GPU microarchitecture: DeepEP first principles"
  * (backyes.github.io) and "Deep Dive - DeepEP" (leetllm.com), by section.
  *
