@@ -133,3 +133,29 @@ def test_layout_dispatch_rejects_large_batches_before_launch():
                               1 << 20, 257 * 8, P, P, P, P, P, P, None, None)
     assert st == ep.EP_ERR_INVALID_ARG
     assert "at most 256" in L.ep_last_error().decode()
+
+
+def test_missing_library_fails_loudly():
+    """Without libep.so every call raises: there is no CPU fallback on the
+    product path.  Run in a child process so this process keeps its library."""
+    import subprocess
+    import sys
+    import textwrap
+
+    code = textwrap.dedent("""
+        import combine_get_dispatch_amd as ep
+        ep.LIB_PATH = "/nonexistent/libep.so"
+        ep._lib = None
+        for call in (ep.lib, lambda: ep.ep_recv_capacity_rows(ep.ep_config_t(4, 8, 1, 2, 1, 1))):
+            try:
+                call()
+            except RuntimeError as err:
+                assert "not built" in str(err), err
+            else:
+                raise SystemExit("a call succeeded without the library")
+        print("raised")
+    """)
+    root = __import__("os").path.dirname(__import__("os").path.dirname(__file__))
+    res = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True,
+                         timeout=120)
+    assert res.returncode == 0 and "raised" in res.stdout, res.stderr
