@@ -127,16 +127,23 @@ __device__ __forceinline__ LayoutLds layout_lds(unsigned long long *dyn, int E,
   return L;
 }
 
-// Count phase of one tile, thread tid = token tile * 256 + tid.  Loads the
-// token's k expert ids into ex (ids outside [-1, E) become -1), marks them
+// The token's expert ids (-1 past k or for a token outside the batch),
+// loaded together.
+template <int K>
+__device__ __forceinline__ void load_ids(const Dims &d, int64_t t, bool live,
+                                         const int32_t *__restrict__ topk_idx, int32_t (&ex)[K]) {
+#pragma unroll
+  for (int j = 0; j < K; ++j) ex[j] = (live && j < d.k) ? topk_idx[t * d.k + j] : -1;
+}
+
+// Count phase of one tile, thread tid = token tile * 256 + tid.  Takes the
+// token's k expert ids in ex (from load_ids; ids outside [-1, E) become -1), marks them
 // in the wave's LDS bitmask of each expert, counts distinct tokens per rank
 // and leaves per expert its count in the earlier waves (prefix) and in the
 // tile (counts).  A repeated or out-of-range id sets the route bit when
 // status is given; the per-wave rank ballots go to rank_ballot when given.
 template <int K>
-__device__ __forceinline__ void count_tile(const Dims &d, int tile, int64_t t, bool live,
-                                           int experts_per_rank,
-                                           const int32_t *__restrict__ topk_idx,
+__device__ __forceinline__ void count_tile(const Dims &d, int tile, int experts_per_rank,
                                            const LayoutLds &L, int32_t (&ex)[K],
                                            unsigned long long &rmask,
                                            unsigned long long *__restrict__ rank_ballot,
@@ -144,12 +151,8 @@ __device__ __forceinline__ void count_tile(const Dims &d, int tile, int64_t t, b
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  const int E = d.E, k = d.k, R = d.R;
+  const int E = d.E, R = d.R;
   const unsigned long long me = 1ull << lane;
-
-  // The token's expert ids, loaded together before any LDS traffic.
-#pragma unroll
-  for (int j = 0; j < K; ++j) ex[j] = (live && j < k) ? topk_idx[t * k + j] : -1;
 
   for (int i = tid; i < kWavesPerBlock * E; i += kBlock) L.masks[i] = 0ull;
   for (int i = tid; i < R; i += kBlock) L.rank_cnt[i] = 0;
@@ -353,8 +356,8 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
   int32_t ex[K];
 
   if (has_tile) {
-    count_tile<K>(d, tile, t, live, experts_per_rank, topk_idx, L, ex, rmask, rank_ballot_ws,
-                  status);
+    load_ids<K>(d, t, live, topk_idx, ex);
+    count_tile<K>(d, tile, experts_per_rank, L, ex, rmask, rank_ballot_ws, status);
     // With several tiles the tile's counts are published for the scan.
     if (many) {
       for (int e = tid; e < E; e += kBlock) tile_cnt[(int64_t)tile * E + e] = L.counts[e];
@@ -672,6 +675,9 @@ __global__ __launch_bounds__(kBlock) void layout_dispatch_kernel(
   const bool has_item = item < (int64_t)d.T * nchunks;
   const int64_t ti = has_item ? item / nchunks : 0;
   const int chunk = has_item ? (int)(item - ti * nchunks) : 0;
+  // The count waits on the batch's ids, so they are loaded first.
+  int32_t ex[K];
+  load_ids<K>(d, t, live, topk_idx, ex);
   XSlice xs;
   xs.v[0] = xs.v[1] = make_uint4(0, 0, 0, 0);
   int32_t eid = -1;
@@ -681,10 +687,9 @@ __global__ __launch_bounds__(kBlock) void layout_dispatch_kernel(
   }
 
   unsigned long long rmask = 0ull;
-  int32_t ex[K];
   if (ntiles > 0) {
-    count_tile<K>(d, 0, t, live, experts_per_rank, topk_idx, L, ex, rmask,
-                  lead ? rank_ballot_ws : nullptr, lead ? status : nullptr);
+    count_tile<K>(d, 0, experts_per_rank, L, ex, rmask, lead ? rank_ballot_ws : nullptr,
+                  lead ? status : nullptr);
   } else {
     for (int e = tid; e < d.E; e += kBlock) L.counts[e] = 0;
     for (int i = tid; i < d.R; i += kBlock) L.rank_cnt[i] = 0;
