@@ -8,8 +8,7 @@ include/ep.h and take preallocated torch tensors; ``EpBuffers`` allocates
 the tensors for one configuration and chains the three calls.
 
 There is no fallback: if libep.so is missing or cannot be loaded, every call
-raises.  Build it with ``python -m combine_get_dispatch_amd._build`` (or
-``__graft_entry__.build()``).
+raises.  Build it with ``python -m combine_get_dispatch_amd._build``.
 """
 from __future__ import annotations
 
