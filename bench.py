@@ -222,7 +222,7 @@ def pmc_summary(run_dir: str, workload: str, copy_mib: int, cmds: dict):
              "", "Command:", "", "    " + cmds["trace"], "",
              "| kernel | calls | average (us) | min (us) | max (us) |", "|---|---|---|---|---|"]
     for name, r in stats.items():
-        short = name.split("(")[0].replace("void ", "")
+        short = short_kernel_name(name)
         lines.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
     lines += ["", f"kernel_source_hash = {src_hash}", ""]
@@ -257,6 +257,13 @@ def pmc_summary(run_dir: str, workload: str, copy_mib: int, cmds: dict):
         with open(os.path.join(ROOT, "profiles", f"{key}_{workload}_hbm_traffic.txt"), "w") as f:
             f.write("\n".join(body) + "\n")
     print(f"profiles written for {workload} (copy factors fetch {ff:.4f}, write {wf:.4f})")
+
+
+def short_kernel_name(name: str) -> str:
+    """A profiler's demangled kernel name without its return type and
+    argument list; an anonymous namespace keeps a readable tag."""
+    name = name.replace("(anonymous namespace)::", "anon::")
+    return name.split("(")[0].replace("void ", "")
 
 
 def run_receipt(w, inp, b, dev) -> dict:

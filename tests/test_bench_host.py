@@ -63,3 +63,13 @@ def test_algorithmic_bytes_prefill_closed_form():
     assert by["layout"] == T * k * 4 + T * R + 4 * (E + R) + 4 * (E + R + 2) == 165960
     assert by["dispatch"] == T * H * 2 + T * k * 12 + M * (H + H // 32 + 8) == 301596672
     assert by["combine"] == M * 2 * H + T * k * 8 + T * 2 * H == 528744448
+
+
+def test_short_kernel_name_keeps_anonymous_namespace_kernels():
+    """Profiler names lose their argument list but never their identity."""
+    assert bench.short_kernel_name(
+        "void ep::combine_kernel<true, 8>(ep::Dims, int, long)") == "ep::combine_kernel<true, 8>"
+    assert bench.short_kernel_name(
+        "void (anonymous namespace)::probe_copy<true>(unsigned int __vector(4) const*, long)"
+    ) == "anon::probe_copy<true>"
+    assert bench.short_kernel_name("__amd_rocclr_copyBuffer") == "__amd_rocclr_copyBuffer"
