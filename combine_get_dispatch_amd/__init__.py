@@ -124,12 +124,30 @@ def _cfg(T, H, k, E, R, A) -> ep_config_t:
     return ep_config_t(T, H, k, E, R, A)
 
 
+_current_stream = None
+
+
+def _current_stream_getter():
+    """A function returning torch's current stream handle on the current
+    device.  torch's raw getter is used when present: building a Stream
+    object per call (torch.cuda.current_stream()) costs about as much as a
+    kernel launch."""
+    import torch
+
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    device = getattr(torch._C, "_cuda_getDevice", None)
+    if raw is not None and device is not None:
+        return lambda: raw(device())
+    return lambda: torch.cuda.current_stream().cuda_stream
+
+
 def _stream(stream):
     if stream is not None:
         return ctypes.c_void_p(stream)
-    import torch
-
-    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    global _current_stream
+    if _current_stream is None:
+        _current_stream = _current_stream_getter()
+    return ctypes.c_void_p(_current_stream())
 
 
 def _ptr(t, dtype=None, shape=None, name="tensor"):

@@ -125,3 +125,19 @@ def test_graph_replay_matches_eager_and_oracle(case):
         assert np.array_equal(got, d["recv_x"][:used])
         ref, _ = oracle.combine(y, d["tok_slot_row"], w)
         assert np.array_equal(host_bf16(b.out), ref)
+
+
+def test_calls_enqueue_on_torch_current_stream():
+    """The binding's default stream is torch's current one, also inside a
+    `torch.cuda.stream` block."""
+    say("current stream handle")
+
+    def handle():
+        return ep._stream(None).value or 0  # the null stream marshals as None
+
+    assert handle() == torch.cuda.current_stream().cuda_stream
+    side = torch.cuda.Stream()
+    assert side.cuda_stream != 0
+    with torch.cuda.stream(side):
+        assert handle() == side.cuda_stream
+    assert handle() == torch.cuda.current_stream().cuda_stream
