@@ -217,7 +217,6 @@ def pmc_summary(run_dir: str, workload: str, copy_mib: int, cmds: dict):
 
     ff, wf = copy_factor(fetch), copy_factor(write)
     stats = {r["Name"]: r for r in rows("trace", "ep_kernel_stats.csv")}
-    src_hash = kernel_source_hash()
     lines = ["# Kernel durations, " + workload + " workload",
              "", "Command:", "", "    " + cmds["trace"], "",
              "| kernel | calls | average (us) | min (us) | max (us) |", "|---|---|---|---|---|"]
@@ -225,7 +224,10 @@ def pmc_summary(run_dir: str, workload: str, copy_mib: int, cmds: dict):
         short = short_kernel_name(name)
         lines.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
-    lines += ["", f"kernel_source_hash = {src_hash}", ""]
+    # a kernel's row stays valid while its own hash matches the sources
+    lines += [""] + [f"kernel_source_hash[{key}] = {kernel_source_hash(key)}"
+                     for key, kname in KERNEL_KEYS.items()
+                     if any(kname in n for n in stats)] + [""]
     with open(os.path.join(ROOT, "profiles", f"{workload}_kernel_trace.md"), "w") as f:
         f.write("\n".join(lines))
     for key, kname in KERNEL_KEYS.items():

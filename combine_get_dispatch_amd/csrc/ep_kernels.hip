@@ -21,7 +21,8 @@
 //                         one bf16 rounding, one 16-byte store.
 //   layout_dispatch_kernel  layout and dispatch in one launch for at most
 //                         256 tokens: every workgroup recounts the batch in
-//                         LDS, then moves its own items.
+//                         LDS; workgroup 0 writes the layout outputs and the
+//                         others move the rows.
 // Also: the non-expanded path (dispatch_ranked_kernel, expand_kernel, the
 // two ranked combine stages), the backward of combine, and the alignment
 // padding fills.  Output positions never depend on atomics or scheduling,
@@ -641,11 +642,11 @@ __global__ __launch_bounds__(kBlock) void dispatch_kernel(
 // Layout and dispatch in one launch, for a batch of at most one tile (256
 // tokens): count, prefix sum and scatter in a single pass ("GPU
 // microarchitecture: DeepEP first principles", 6.1).  Every workgroup counts
-// and scans the whole batch in LDS, then moves its own work items (token,
-// 1024-column chunk) to the rows the scan gives.  Workgroup 0 also writes
-// every layout output and the workspace, so later calls (combine, the
-// non-expanded path, backward) see exactly what ep_get_dispatch_layout and
-// ep_dispatch leave.  The x slice and the token's expert ids are loaded
+// and scans the whole batch in LDS.  Workgroup 0 then writes every layout
+// output and the workspace, so later calls (combine, the non-expanded path,
+// backward) see exactly what ep_get_dispatch_layout and ep_dispatch leave;
+// each other workgroup moves its four work items (token, 1024-column chunk)
+// to the rows the scan gives.  The x slice and the token's expert ids are loaded
 // first, so their loads overlap the count.
 template <int K, bool kFp8>
 __global__ __launch_bounds__(kBlock) void layout_dispatch_kernel(
@@ -671,8 +672,9 @@ __global__ __launch_bounds__(kBlock) void layout_dispatch_kernel(
   const bool live = ntiles > 0 && t < d.T;
 
   // This wave's work item, its x slice and its token's expert ids.
-  const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + uniform(tid / kWave);
-  const bool has_item = item < (int64_t)d.T * nchunks;
+  // Workgroup 0 moves no rows: its layout writes then delay no dispatch work.
+  const int64_t item = (int64_t)(blockIdx.x - 1) * kWavesPerBlock + uniform(tid / kWave);
+  const bool has_item = !lead && item < (int64_t)d.T * nchunks;
   const int64_t ti = has_item ? item / nchunks : 0;
   const int chunk = has_item ? (int)(item - ti * nchunks) : 0;
   // The count waits on the batch's ids, so they are loaded first.
@@ -1469,7 +1471,8 @@ hipError_t launch_layout_dispatch(const Dims &d, bool fp8, const uint16_t *x,
   const WorkspaceLayout w = workspace_layout(d.T, d.k, d.E, d.R);
   const int32_t nchunks = (d.H + kChunkCols - 1) / kChunkCols;
   const int64_t items = (int64_t)d.T * nchunks;
-  const unsigned grid = items > 0 ? (unsigned)((items + kWavesPerBlock - 1) / kWavesPerBlock) : 1u;
+  // one workgroup for the layout outputs, then one wave per work item
+  const unsigned grid = 1u + (unsigned)((items + kWavesPerBlock - 1) / kWavesPerBlock);
   auto pick = [&](auto k8, auto k16, auto k32) { return d.k <= 8 ? k8 : (d.k <= 16 ? k16 : k32); };
   auto kernel = fp8 ? pick(layout_dispatch_kernel<8, true>, layout_dispatch_kernel<16, true>,
                            layout_dispatch_kernel<32, true>)
