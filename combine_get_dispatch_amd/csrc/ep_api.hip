@@ -466,6 +466,11 @@ ep_status_t ep_combine_ranked(const ep_ranked_handle_t *ranked, const uint16_t *
                               int32_t weighted, float *partials, uint16_t *out,
                               hipStream_t stream) {
   EP_TRY(check_ranked(ranked));
+  // stage 1 numbers its (row, 512-column chunk) items with int32
+  const int64_t chunks = (ranked->config.hidden + ep::kCombineCols - 1) / ep::kCombineCols;
+  if (ranked->ranked_capacity * chunks >= INT32_MAX)
+    return fail(EP_ERR_INVALID_ARG, "ranked_capacity %lld x hidden %d too large",
+                (long long)ranked->ranked_capacity, ranked->config.hidden);
   if (weighted && ranked->ranked_capacity > 0 && ranked->ne_topk_weights == nullptr)
     return fail(EP_ERR_INVALID_ARG, "weighted combine needs ne_topk_weights in the handle");
   if ((ranked->config.num_tokens > 0 && out == nullptr) ||

@@ -673,7 +673,8 @@ __global__ __launch_bounds__(kBlock) void layout_dispatch_kernel(
 
   // This wave's work item, its x slice and its token's expert ids.
   // Workgroup 0 moves no rows: its layout writes then delay no dispatch work.
-  const int64_t item = (int64_t)(blockIdx.x - 1) * kWavesPerBlock + uniform(tid / kWave);
+  const int64_t item =
+      lead ? 0 : ((int64_t)blockIdx.x - 1) * kWavesPerBlock + uniform(tid / kWave);
   const bool has_item = !lead && item < (int64_t)d.T * nchunks;
   const int64_t ti = has_item ? item / nchunks : 0;
   const int chunk = has_item ? (int)(item - ti * nchunks) : 0;

@@ -135,6 +135,25 @@ def test_layout_dispatch_rejects_large_batches_before_launch():
     assert "at most 256" in L.ep_last_error().decode()
 
 
+def test_combine_ranked_rejects_item_overflow_before_launch():
+    """The ranked combine numbers its (row, 512-column chunk) items with
+    int32; a handle whose rows x chunks would overflow that is rejected
+    before anything is enqueued (2^24 tokens, top-32 over 32 ranks, hidden
+    7168: 2^29 rows x 14 chunks)."""
+    L = ep.lib()
+    h = ep.ep_ranked_handle_t()
+    h.config = ep.ep_config_t(1 << 24, 7168, 32, 32, 32, 1)
+    h.capacity = (1 << 24) * 32
+    h.ranked_capacity = (1 << 24) * 32
+    for i, name in enumerate(("rank_token_offsets", "tok_rank_row", "tok_slot_row",
+                              "ne_topk_idx", "ne_topk_weights", "ne_src")):
+        setattr(h, name, 0x100000 * (i + 1))
+    P = ctypes.c_void_p(256)
+    st = L.ep_combine_ranked(ctypes.byref(h), P, 1, P, P, None)
+    assert st == ep.EP_ERR_INVALID_ARG
+    assert "too large" in L.ep_last_error().decode()
+
+
 def test_missing_library_fails_loudly():
     """Without libep.so every call raises: there is no CPU fallback on the
     product path.  Run in a child process so this process keeps its library."""
