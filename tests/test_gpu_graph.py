@@ -20,10 +20,12 @@ import oracle  # noqa: E402
 from tests.gpu_backend import dev_bf16, host_bf16, say  # noqa: E402
 
 CASES = [
-    # T, H, k, E, R, A, fp8
-    (1000, 256, 4, 32, 4, 1, True),     # four tiles: the ticket path
-    (300, 264, 3, 24, 4, 4, False),     # alignment padding (pad fill kernel)
-    (128, 7168, 8, 256, 8, 1, False),   # the Decode shape
+    # T, H, k, E, R, A, fp8, fused (layout and dispatch in one launch)
+    (1000, 256, 4, 32, 4, 1, True, False),     # four tiles: the ticket path
+    (300, 264, 3, 24, 4, 4, False, False),     # alignment padding (pad fill kernel)
+    (128, 7168, 8, 256, 8, 1, False, False),   # the Decode shape
+    (128, 7168, 8, 256, 8, 1, False, True),    # the Decode shape, fused
+    (200, 512, 4, 32, 4, 4, True, True),       # fused, FP8 rows and padding
 ]
 
 
@@ -32,11 +34,11 @@ def _bf16_tensor(bits):
         torch.bfloat16)
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: "T{}_H{}_k{}_E{}_A{}_{}".format(
-    c[0], c[1], c[2], c[3], c[5], "fp8" if c[6] else "bf16"))
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "T{}_H{}_k{}_E{}_A{}_{}{}".format(
+    c[0], c[1], c[2], c[3], c[5], "fp8" if c[6] else "bf16", "_fused" if c[7] else ""))
 def test_graph_replay_matches_eager_and_oracle(case):
-    T, H, k, E, R, A, fp8 = case
-    say(f"graph T={T} H={H} k={k} E={E} R={R} A={A} fp8={fp8}")
+    T, H, k, E, R, A, fp8, fused = case
+    say(f"graph T={T} H={H} k={k} E={E} R={R} A={A} fp8={fp8} fused={fused}")
     rng = np.random.default_rng(4242 + T)
     b = ep.EpBuffers(T, H, k, E, R, A, fp8=fp8)
     cap = b.capacity
@@ -60,8 +62,11 @@ def test_graph_replay_matches_eager_and_oracle(case):
         y_d.copy_(_bf16_tensor(y))
 
     def step():
-        b.layout(idx_d)
-        b.dispatch(x_d, idx_d, w_d)
+        if fused:
+            b.layout_dispatch(x_d, idx_d, w_d)
+        else:
+            b.layout(idx_d)
+            b.dispatch(x_d, idx_d, w_d)
         b.combine(y_d, w_d)
 
     load(draw())
