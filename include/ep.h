@@ -84,7 +84,8 @@ typedef enum ep_dtype {
 
 typedef struct ep_config {
   int32_t num_tokens;       /* T >= 0 */
-  int32_t hidden;           /* H >= 8, H % 8 == 0 (H % 128 == 0 for FP8) */
+  int32_t hidden;           /* H >= 8, H % 8 == 0 (H % 128 == 0 for FP8);
+                               T * ceil(H / 512) < 2^31 */
   int32_t num_topk;         /* 1 <= k <= min(E, EP_MAX_TOPK) */
   int32_t num_experts;      /* 1 <= E <= EP_MAX_EXPERTS */
   int32_t num_ranks;        /* 1 <= R <= EP_MAX_RANKS, E % R == 0 */
@@ -410,6 +411,7 @@ ep_status_t ep_expand(const ep_ranked_handle_t *ranked, ep_dtype_t recv_dtype, c
  *   expert_out  [capacity, H] bf16
  *   partials    [ranked_capacity, H] fp32 scratch/out
  *   out         [T, H] bf16 out
+ * Also rejects (EP_ERR_INVALID_ARG) ranked_capacity * ceil(H / 512) >= 2^31.
  */
 ep_status_t ep_combine_ranked(const ep_ranked_handle_t *ranked, const uint16_t *expert_out,
                               int32_t weighted, float *partials, uint16_t *out,

@@ -5,6 +5,7 @@ documented sizes, and bad arguments are rejected before anything is enqueued
 import ctypes
 
 import pytest
+from hypothesis import event, given, settings, strategies as st
 
 import combine_get_dispatch_amd as ep
 
@@ -178,3 +179,52 @@ def test_missing_library_fails_loudly():
     res = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True,
                          timeout=120)
     assert res.returncode == 0 and "raised" in res.stdout, res.stderr
+
+
+def _config_is_valid(T, H, k, E, R, A):
+    """The rules include/ep.h states for ep_config_t, written out."""
+    int32_max = 2**31 - 1
+    return (T >= 0 and H >= 8 and H % 8 == 0 and 1 <= E <= 1024 and 1 <= k <= min(E, 32)
+            and 1 <= R <= 64 and E % R == 0 and A >= 1
+            and T * k + E * (A - 1) < int32_max
+            and T * -(-H // 512) < int32_max)
+
+
+@st.composite
+def _configs(draw):
+    """Configurations on both sides of every rule: a valid one is built,
+    then some fields are moved across (or near) their limits."""
+    R = draw(st.sampled_from([1, 2, 4, 8, 16, 64]))
+    E = R * draw(st.integers(1, 1024 // R))
+    k = draw(st.integers(1, min(E, 32)))
+    H = 8 * draw(st.integers(1, 2048))
+    A = draw(st.sampled_from([1, 2, 4, 128]))
+    T = draw(st.one_of(st.integers(0, 5000), st.sampled_from([
+        (2**31 - 1 - E * (A - 1)) // k, (2**31 - 1 - E * (A - 1)) // k + 1,
+        (2**31 - 1) // -(-H // 512), (2**31 - 1) // -(-H // 512) + 1])))
+    f = [T, H, k, E, R, A]
+    edits = {0: [-1, 2**31 - 1], 1: [0, 4, H + 4, 12], 2: [0, E + 1, 33], 3: [0, 1025, E + 1],
+             4: [0, 65, 3, E + 1], 5: [0, -1, 2**30]}
+    for i in draw(st.sets(st.integers(0, 5), max_size=2)):
+        f[i] = draw(st.sampled_from(edits[i]))
+    return tuple(max(-(2**31), min(v, 2**31 - 1)) for v in f)
+
+
+@settings(max_examples=3000, derandomize=True, deadline=None)
+@given(_configs())
+def test_config_accepted_exactly_when_the_stated_rules_hold(config):
+    """Every host entry point validates the config first; the size query
+    accepts exactly the configurations include/ep.h allows and then returns
+    T*k + E*(A-1) rows and a 256-byte multiple of workspace."""
+    T, H, k, E, R, A = config
+    cfg = ep.ep_config_t(T, H, k, E, R, A)
+    valid = _config_is_valid(T, H, k, E, R, A)
+    event("valid" if valid else "invalid")
+    if valid:
+        assert ep.ep_recv_capacity_rows(cfg) == T * k + E * (A - 1)
+        n = ep.ep_layout_workspace_bytes(cfg)
+        assert n % 256 == 0 and n >= 4 * T * k
+    else:
+        with pytest.raises(ep.EpError) as e:
+            ep.ep_recv_capacity_rows(cfg)
+        assert e.value.status == ep.EP_ERR_INVALID_ARG
