@@ -137,6 +137,30 @@ def test_implementation_limits(case):
                           oracle.combine(y, do["tok_slot_row"], w)[0])
 
 
+@pytest.mark.parametrize("H,fp8", [(65536 + 8, False), (32768, True)])
+def test_wide_rows(H, fp8):
+    """Rows of many chunks (64 and more per token), bf16 with a ragged
+    8-column tail and FP8 with 256 scale blocks, through dispatch and
+    combine."""
+    T, k, E, R = 37, 4, 16, 4
+    rng = np.random.default_rng(H)
+    idx = W.random_routes(rng, T, E, k, mask_prob=0.1)
+    x = W.normal_bf16(rng, (T, H))
+    w = rng.random((T, k)).astype(np.float32)
+    cap = T * k
+    dg = GPU.dispatch(x, idx, w, E, R, 1, fp8, cap)
+    do = oracle.dispatch(x, idx, w, E, R, 1, fp8=fp8, capacity=cap)
+    used = int(oracle.layout(idx, E, R, 1)["expert_offsets"][-1])
+    assert np.array_equal(dg["tok_slot_row"], do["tok_slot_row"])
+    assert np.array_equal(dg["recv_x"][:used], do["recv_x"][:used])
+    if fp8:
+        assert np.array_equal(dg["recv_scales"][:used].view(np.uint32),
+                              do["recv_scales"][:used].view(np.uint32))
+    y = W.normal_bf16(rng, (cap, H))
+    assert np.array_equal(GPU.combine(y, do["tok_slot_row"], w),
+                          oracle.combine(y, do["tok_slot_row"], w)[0])
+
+
 def _raw_run(T, H, k, E, R, idx, capacity=None, x=None):
     b = ep.EpBuffers(T, H, k, E, R, 1, capacity=capacity)
     b.status.zero_()
