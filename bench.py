@@ -703,7 +703,8 @@ def main():
     achieved = by[dom] / (per_us[dom] / 1e6) / 1e9
     # the committed counter summaries are of the default command only
     default_mode = not (args.fp8_input or args.alignment or args.replay or args.fused)
-    traffic = load_traffic(w.name, dom) if default_mode else None
+    traffic_key = "dispatch_bf16" if dom == "dispatch" and not w.fp8 else dom
+    traffic = load_traffic(w.name, traffic_key) if default_mode else None
     rec = {
         "metric": METRIC,
         "value": round(gbps, 1),
