@@ -293,13 +293,59 @@ def run_receipt(w, inp, b, dev) -> dict:
     return {"git": sha, "torch": torch.__version__, "hip": torch.version.hip,
             "gpu": props.name, "arch": getattr(props, "gcnArchName", None),
             "compute_units": props.multi_processor_count,
+            "host_cpu": host_cpu_model(), "host_cpus": host_cpus(),
             "seed": w.seed, "max_over_mean_expert_load": round(float(load.max() / load.mean()), 3),
             "local_rank_fraction": round(float(local.sum() / max(1, valid.sum())), 4)}
 
 
-def cpu_baseline(w, inp, budget_s: float):
+def step_outputs(b) -> dict:
+    """Host copies of what the last timed step left in the buffers."""
+    import numpy as np
+    import torch
+
+    rows = int(b.expert_offsets[-1].item())
+    got = {n: getattr(b, n).cpu().numpy() for n in
+           ("num_tokens_per_rank", "num_tokens_per_expert", "is_token_in_rank",
+            "expert_offsets", "rank_offsets", "tok_slot_row")}
+    got["row_src"] = b.row_src[:rows].cpu().numpy()
+    got["recv_weights"] = b.recv_weights[:rows].cpu().numpy()
+    rx = b.recv_x[:rows].cpu()
+    got["recv_x"] = rx.numpy() if b.fp8 else rx.view(torch.int16).numpy().view(np.uint16)
+    got["recv_scales"] = b.recv_scales[:rows].cpu().numpy() if b.fp8 else None
+    got["out"] = b.out.cpu().view(torch.int16).numpy().view(np.uint16)
+    return got
+
+
+def compare_step(got: dict, lay: dict, d: dict, ref_out) -> dict:
+    """The timed step's outputs against the oracle's for the same batch:
+    layout, handle, rows and scales bit for bit, combine as bf16 bits."""
+    import numpy as np
+
+    rows = int(lay["expert_offsets"][-1])
+    same = lambda a, b: bool(a is None and b is None or np.array_equal(a, b))
+    ok = {
+        "layout": all(same(got[n], lay[n]) for n in
+                      ("num_tokens_per_rank", "num_tokens_per_expert", "is_token_in_rank",
+                       "expert_offsets", "rank_offsets")),
+        "handle": same(got["tok_slot_row"], d["tok_slot_row"])
+                  and same(got["row_src"], d["row_src"][:rows])
+                  and same(got["recv_weights"].view(np.uint32),
+                           d["recv_weights"][:rows].view(np.uint32)),
+        "rows": same(got["recv_x"], d["recv_x"][:rows])
+                and (d["recv_scales"] is None
+                     or same(got["recv_scales"].view(np.uint32),
+                             d["recv_scales"][:rows].view(np.uint32))),
+        "combine_bits": same(got["out"], ref_out),
+    }
+    ok["all"] = all(ok.values())
+    return ok
+
+
+def cpu_baseline(w, inp, budget_s: float, got: dict | None = None):
     """The CPU oracle as it stands (single-threaded C), timed on this host on
-    whole steps of the same batch, repeated until about budget_s seconds."""
+    whole steps of the same batch, repeated until about budget_s seconds.
+    With got (the timed GPU step's outputs), the last oracle step's results
+    are also compared with them."""
     import oracle
 
     reps, t0 = 0, time.perf_counter()
@@ -307,16 +353,80 @@ def cpu_baseline(w, inp, budget_s: float):
         lay = oracle.layout(inp["topk_idx"], w.num_experts, w.num_ranks, w.alignment)
         d = oracle.dispatch(inp["x"], inp["topk_idx"], inp["topk_weights"], w.num_experts,
                             w.num_ranks, w.alignment, fp8=w.fp8)
-        oracle.combine(inp["y"], d["tok_slot_row"], inp["topk_weights"])
+        ref_out, _ = oracle.combine(inp["y"], d["tok_slot_row"], inp["topk_weights"])
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or reps >= 8:
             break
     M = int(lay["expert_offsets"][-1])
     b = algorithmic_bytes(w, M)["total"]
-    return dict(value=round(b * reps / el / 1e9, 3), unit="GB/s", cores=1, kind="oracle",
-                sample=f"{reps} full {w.name} step(s) (layout+dispatch+combine, "
-                       f"{w.num_tokens} tokens) in {el:.1f} s, single-threaded C",
+    rec = dict(value=round(b * reps / el / 1e9, 3), unit="GB/s", cores=1, kind="oracle",
+               sample=f"{reps} full {w.name} step(s) (layout+dispatch+combine, "
+                      f"{w.num_tokens} tokens) in {el:.1f} s, single-threaded C",
+               tokens_per_s=round(w.num_tokens * reps / el, 1))
+    if got is not None:
+        rec["timed_step_matches_oracle"] = compare_step(got, lay, d, ref_out)
+    return rec
+
+
+def host_cpus() -> int:
+    """Cores this process may run on (its affinity mask), capped at 16, the
+    host share that one GPU's jobs get."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def host_cpu_model() -> str | None:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline_all_cores(w, inp, budget_s: float, threads: int):
+    """The same oracle, unchanged, on every available core: `threads` host
+    threads each run whole steps (layout, dispatch, combine) of the batch
+    until about budget_s seconds have passed.  ctypes releases the GIL
+    around the C calls, so the steps run in parallel; each thread keeps its
+    own outputs.  The rate is the aggregate over all threads."""
+    import threading
+
+    import oracle
+
+    oracle.layout(inp["topk_idx"][:1], w.num_experts, w.num_ranks, w.alignment)  # load once
+    done = [0] * threads
+    t0 = time.perf_counter()
+
+    def work(i):
+        while True:
+            oracle.layout(inp["topk_idx"], w.num_experts, w.num_ranks, w.alignment)
+            d = oracle.dispatch(inp["x"], inp["topk_idx"], inp["topk_weights"], w.num_experts,
+                                w.num_ranks, w.alignment, fp8=w.fp8)
+            oracle.combine(inp["y"], d["tok_slot_row"], inp["topk_weights"])
+            del d
+            done[i] += 1
+            if time.perf_counter() - t0 >= budget_s:
+                return
+
+    pool = [threading.Thread(target=work, args=(i,)) for i in range(threads)]
+    for th in pool:
+        th.start()
+    for th in pool:
+        th.join()
+    el = time.perf_counter() - t0
+    reps = sum(done)
+    lay = oracle.layout(inp["topk_idx"], w.num_experts, w.num_ranks, w.alignment)
+    b = algorithmic_bytes(w, int(lay["expert_offsets"][-1]))["total"]
+    return dict(value=round(b * reps / el / 1e9, 3), unit="GB/s", cores=threads,
+                kind="oracle", sample=f"{reps} full {w.name} step(s) on {threads} threads at "
+                                      f"once (one step per thread at a time) in {el:.1f} s",
                 tokens_per_s=round(w.num_tokens * reps / el, 1))
 
 
@@ -754,7 +864,17 @@ def main():
     }
     if not args.no_cpu_baseline and not args.fp8_input:
         print("bench: CPU oracle baseline", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget)
+        got = step_outputs(b)
+        rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget, got)
+        del got
+        if not rec["cpu_baseline"]["timed_step_matches_oracle"]["all"]:
+            print("bench: WARNING: the timed step's outputs differ from the oracle's",
+                  file=sys.stderr, flush=True)
+        n = host_cpus()
+        if n > 1:
+            print(f"bench: CPU oracle baseline on {n} threads", file=sys.stderr, flush=True)
+            rec["cpu_baseline"]["all_cores"] = cpu_baseline_all_cores(w, inp, args.cpu_budget,
+                                                                      n)
     print(json.dumps(rec), flush=True)
 
 

@@ -73,3 +73,46 @@ def test_short_kernel_name_keeps_anonymous_namespace_kernels():
         "void (anonymous namespace)::probe_copy<true>(unsigned int __vector(4) const*, long)"
     ) == "anon::probe_copy<true>"
     assert bench.short_kernel_name("__amd_rocclr_copyBuffer") == "__amd_rocclr_copyBuffer"
+
+
+def _oracle_step(w):
+    import oracle
+
+    inp = W.generate(w)
+    lay = oracle.layout(inp["topk_idx"], w.num_experts, w.num_ranks, w.alignment)
+    d = oracle.dispatch(inp["x"], inp["topk_idx"], inp["topk_weights"], w.num_experts,
+                        w.num_ranks, w.alignment, fp8=w.fp8)
+    out, _ = oracle.combine(inp["y"], d["tok_slot_row"], inp["topk_weights"])
+    rows = int(lay["expert_offsets"][-1])
+    got = {n: lay[n].copy() for n in ("num_tokens_per_rank", "num_tokens_per_expert",
+                                      "is_token_in_rank", "expert_offsets", "rank_offsets")}
+    got["tok_slot_row"] = d["tok_slot_row"].copy()
+    for n in ("row_src", "recv_weights", "recv_x"):
+        got[n] = d[n][:rows].copy()
+    got["recv_scales"] = None if d["recv_scales"] is None else d["recv_scales"][:rows].copy()
+    got["out"] = out.copy()
+    return got, lay, d, out
+
+
+def test_step_comparison_flags_each_part():
+    """The bench's check of the timed step against the oracle: equal outputs
+    pass, and one changed value in any part fails that part only."""
+    import dataclasses
+
+    for w in (W.WORKLOADS["tiny"], dataclasses.replace(W.WORKLOADS["tiny"], fp8=True)):
+        got, lay, d, out = _oracle_step(w)
+        assert bench.compare_step(got, lay, d, out) == {
+            "layout": True, "handle": True, "rows": True, "combine_bits": True, "all": True}
+        cases = [("expert_offsets", "layout"), ("row_src", "handle"),
+                 ("recv_weights", "handle"), ("recv_x", "rows"), ("out", "combine_bits")]
+        if w.fp8:
+            cases.append(("recv_scales", "rows"))
+        for name, part in cases:
+            bad = dict(got)
+            arr = got[name].copy()
+            flat = arr.reshape(-1)
+            flat[flat.size // 2] = flat[flat.size // 2] + 1
+            bad[name] = arr
+            res = bench.compare_step(bad, lay, d, out)
+            assert not res[part] and not res["all"], (name, res)
+            assert all(v for k, v in res.items() if k not in (part, "all")), (name, res)
