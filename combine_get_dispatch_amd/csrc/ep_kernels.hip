@@ -486,6 +486,10 @@ __device__ __forceinline__ int32_t selection_row(const Dims &d, int64_t t, int l
   if (lane < d.k) {
     const int64_t s = t * d.k + lane;
     const int32_t e = topk_idx[s];
+    // Loaded before the handle's stores, so that no wait for those stores
+    // is needed before the gate is written.
+    const bool gates = write_handle && recv_weights != nullptr && topk_weights != nullptr;
+    const float gate = gates ? topk_weights[s] : 0.0f;
     if (e >= 0 && e < d.E) {
       const int32_t rank = slot_rank[s];
       if (rank >= 0) {
@@ -501,8 +505,7 @@ __device__ __forceinline__ int32_t selection_row(const Dims &d, int64_t t, int l
       tok_slot_row[s] = row;
       if (row >= 0) {
         row_src[row] = (int32_t)s;
-        if (recv_weights != nullptr && topk_weights != nullptr)
-          recv_weights[row] = topk_weights[s];
+        if (gates) recv_weights[row] = gate;
       }
     }
   }
@@ -626,16 +629,18 @@ __global__ __launch_bounds__(kBlock) void dispatch_kernel(
   const int lane = threadIdx.x & (kWave - 1);
   const int item = uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
   if (item >= d.T * nchunks) return;
+  const int64_t t = item / nchunks;
+  const int chunk = item - (int)t * nchunks;
+  // The x slice depends on nothing else, so its loads go first and overlap
+  // the chain of workspace reads that gives the rows.
+  const XSlice xs = load_x_slice<kFp8>(x, t, d.H, chunk, lane);
   if (!workspace_ok(header, d)) {
     if (lane == 0) flag(status, EP_STATUS_BIT_WORKSPACE);
     return;
   }
-  const int64_t t = item / nchunks;
-  const int chunk = item - (int)t * nchunks;
   const int32_t row = selection_row(d, t, lane, chunk == 0, topk_idx, topk_weights,
                                     expert_offsets, tile_base, slot_rank, capacity,
                                     recv_weights, tok_slot_row, row_src, status);
-  const XSlice xs = load_x_slice<kFp8>(x, t, d.H, chunk, lane);
   store_x_slice<kFp8>(xs, row, d.k, d.H, chunk, lane, recv_x, recv_scales);
 }
 
@@ -683,20 +688,27 @@ __global__ __launch_bounds__(kBlock) void layout_dispatch_kernel(
   load_ids<K>(d, t, live, topk_idx, ex);
   XSlice xs;
   xs.v[0] = xs.v[1] = make_uint4(0, 0, 0, 0);
+  // The gate is loaded here too: a load issued after the handle's stores
+  // would make the wave wait for those stores before its row stores.
   int32_t eid = -1;
+  float gate = 0.0f;
   if (has_item) {
     xs = load_x_slice<kFp8>(x, ti, d.H, chunk, lane);
-    if (lane < d.k) eid = topk_idx[ti * d.k + lane];
+    if (lane < d.k) {
+      eid = topk_idx[ti * d.k + lane];
+      if (chunk == 0 && recv_weights != nullptr && topk_weights != nullptr)
+        gate = topk_weights[ti * d.k + lane];
+    }
   }
 
+  // Every workgroup counts, also for an empty batch (no live token: zero
+  // counts, and no ballots, for which the workspace then has no room).  A
+  // branch around the count would leave the id loads pending on one path,
+  // and the compiler would then wait for all stores issued before the
+  // first later use of those registers.
   unsigned long long rmask = 0ull;
-  if (ntiles > 0) {
-    count_tile<K>(d, 0, experts_per_rank, L, ex, rmask, lead ? rank_ballot_ws : nullptr,
-                  lead ? status : nullptr);
-  } else {
-    for (int e = tid; e < d.E; e += kBlock) L.counts[e] = 0;
-    for (int i = tid; i < d.R; i += kBlock) L.rank_cnt[i] = 0;
-  }
+  count_tile<K>(d, 0, experts_per_rank, L, ex, rmask,
+                lead && ntiles > 0 ? rank_ballot_ws : nullptr, lead ? status : nullptr);
   __syncthreads();
   if (lead && live) token_outputs<K>(d, t, L, ex, rmask, is_token_in_rank, slot_rank);
   scan_counts(d, experts_per_rank, L, tid < d.R ? L.rank_cnt[tid] : 0, lead, cnt_ws,
@@ -729,8 +741,7 @@ __global__ __launch_bounds__(kBlock) void layout_dispatch_kernel(
       tok_slot_row[sidx] = row;
       if (row >= 0) {
         row_src[row] = (int32_t)sidx;
-        if (recv_weights != nullptr && topk_weights != nullptr)
-          recv_weights[row] = topk_weights[sidx];
+        if (recv_weights != nullptr && topk_weights != nullptr) recv_weights[row] = gate;
       }
     }
   }
@@ -753,15 +764,9 @@ __global__ __launch_bounds__(kBlock) void dispatch_fp8_input_kernel(
   const int lane = threadIdx.x & (kWave - 1);
   const int item = uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
   if (item >= d.T * nchunks) return;
-  if (!workspace_ok(header, d)) {
-    if (lane == 0) flag(status, EP_STATUS_BIT_WORKSPACE);
-    return;
-  }
   const int64_t t = item / nchunks;
   const int chunk = item - (int)t * nchunks;
-  const int32_t row = selection_row(d, t, lane, chunk == 0, topk_idx, topk_weights,
-                                    expert_offsets, tile_base, slot_rank, capacity,
-                                    recv_weights, tok_slot_row, row_src, status);
+  // The codes and scale first: they overlap the workspace reads.
   const int64_t H = d.H;
   const int64_t nblk = H / 128;
   const int col = chunk * kChunkCols + lane * 16;
@@ -772,6 +777,13 @@ __global__ __launch_bounds__(kBlock) void dispatch_fp8_input_kernel(
     q = *reinterpret_cast<const uint4 *>(x_codes + t * H + col);
     if ((lane & 7) == 0) scale = x_scales[t * nblk + col / 128];
   }
+  if (!workspace_ok(header, d)) {
+    if (lane == 0) flag(status, EP_STATUS_BIT_WORKSPACE);
+    return;
+  }
+  const int32_t row = selection_row(d, t, lane, chunk == 0, topk_idx, topk_weights,
+                                    expert_offsets, tile_base, slot_rank, capacity,
+                                    recv_weights, tok_slot_row, row_src, status);
   for (int j = 0; j < d.k; ++j) {
     const int32_t r = lane_value(row, j);
     if (r < 0 || !in) continue;
@@ -913,7 +925,6 @@ struct Payload16 {
 // Lanes own 16 values; with H % 16 == 8 (bf16 rows) the last lane of a row
 // owns only its lower 8, so the upper half is guarded separately (FP8 rows
 // have H % 128 == 0).
-template <bool kFp8>
 __device__ __forceinline__ Payload16 load_payload(const uint16_t *__restrict__ x, int64_t t,
                                                   int64_t H, int col, bool in) {
   Payload16 p;
@@ -924,8 +935,14 @@ __device__ __forceinline__ Payload16 load_payload(const uint16_t *__restrict__ x
     p.lo = *reinterpret_cast<const uint4 *>(x + t * H + col);
     if (col + 8 < H) p.hi = *reinterpret_cast<const uint4 *>(x + t * H + col + 8);
   }
-  if (kFp8) p.lo = quantize16(p.lo, p.hi, p.scale);
   return p;
+}
+
+// FP8 rows: the loaded bf16 values become codes and the block scale (all
+// lanes of the wave together); bf16 rows are left as loaded.
+template <bool kFp8>
+__device__ __forceinline__ void encode_payload(Payload16 &p) {
+  if (kFp8) p.lo = quantize16(p.lo, p.hi, p.scale);
 }
 
 template <bool kFp8>
@@ -993,9 +1010,15 @@ __global__ __launch_bounds__(kBlock) void dispatch_ranked_kernel(
     }
   }
   if (item >= d.T * nchunks) return;
-  if (!workspace_ok(header, d)) return;
   const int64_t t = item / nchunks;
   const int chunk = item - (int)t * nchunks;
+  // The payload's loads go first: they overlap the reads that give the
+  // token's rank rows.  FP8 encoding waits until those are issued.
+  const int64_t H = d.H;
+  const int col = chunk * kChunkCols + lane * 16;
+  const bool in = col < H;
+  Payload16 p = load_payload(x, t, H, col, in);
+  if (!workspace_ok(header, d)) return;
   const int32_t row = rank_row(d, t, lane, rank_ballot, rank_tok_off, tile_rank_base,
                                ranked_capacity, status);
   if (chunk == 0) {
@@ -1027,10 +1050,7 @@ __global__ __launch_bounds__(kBlock) void dispatch_ranked_kernel(
     if (lane < d.k) tok_slot_row[t * d.k + lane] = srow;
   }
 
-  const int64_t H = d.H;
-  const int col = chunk * kChunkCols + lane * 16;
-  const bool in = col < H;
-  const Payload16 p = load_payload<kFp8>(x, t, H, col, in);
+  encode_payload<kFp8>(p);
   for (int r = 0; r < d.R; ++r) {
     const int32_t rr = lane_value(row, r);
     if (rr < 0 || !in) continue;
