@@ -268,6 +268,29 @@ def short_kernel_name(name: str) -> str:
     return name.split("(")[0].replace("void ", "")
 
 
+def logical_network_bytes(w, b) -> dict:
+    """What an expert-parallel group of R GPUs would send over its links for
+    this batch, as DeepEP counts it: one row per (token, destination rank)
+    in dispatch (the payload row: bf16, or E4M3 codes + per-128 scales) and
+    one bf16 row back per (token, rank) in combine.  Nothing here moves
+    these bytes; they are reported beside the HBM bytes.  `remote` leaves
+    out each token's own rank, with token t owned by rank t*R/T."""
+    import numpy as np
+
+    T, H, R = w.num_tokens, w.hidden, w.num_ranks
+    mask = b.is_token_in_rank.cpu().numpy().astype(bool)
+    rows = int(mask.sum())
+    own = np.arange(T, dtype=np.int64) * R // max(T, 1)
+    remote = rows - int(mask[np.arange(T), own].sum()) if T else 0
+    row_b = H + 4 * (H // 128) if w.fp8 else 2 * H
+    return {"rows": rows, "rows_per_token": round(rows / max(T, 1), 4),
+            "expanded_rows_per_token": round(int(b.num_tokens_per_expert.sum().item())
+                                             / max(T, 1), 4),
+            "dispatch_bytes": rows * row_b, "combine_bytes": rows * 2 * H,
+            "remote_rows": remote, "remote_dispatch_bytes": remote * row_b,
+            "remote_combine_bytes": remote * 2 * H}
+
+
 def run_receipt(w, inp, b, dev) -> dict:
     """What identifies the run: toolchain and GPU, the workload's seed, and
     the route's shape (expert load skew; the share of selections whose
@@ -802,6 +825,7 @@ def main():
         del pa, pb
 
     receipt = run_receipt(w, inp, b, dev)
+    net_bytes = logical_network_bytes(w, b)
     by = algorithmic_bytes(w, M, args.fp8_input, pad_rows)
     if args.fused:
         by["layout_dispatch"] = by["layout"] + by["dispatch"]
@@ -849,6 +873,7 @@ def main():
                                  for n in names},
         "step_us": step_us,
         "receipt": receipt,
+        "logical_network_bytes": net_bytes,
         "device_copy_gbps": copy_gbps,
         "hbm_probe_gbps": hbm_probe,
         "host_wall_s": round(wall, 4),

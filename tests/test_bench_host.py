@@ -116,3 +116,31 @@ def test_step_comparison_flags_each_part():
             res = bench.compare_step(bad, lay, d, out)
             assert not res[part] and not res["all"], (name, res)
             assert all(v for k, v in res.items() if k not in (part, "all")), (name, res)
+
+
+def test_logical_network_bytes_counts_token_rank_rows():
+    """One row per (token, destination rank), counted from a layout the
+    oracle wrote for a hand-checked route: 6 rows for 8 assignments."""
+    import types
+
+    import numpy as np
+    import torch
+
+    import oracle
+
+    # tokens 0..3, 4 experts on 2 ranks (experts 0,1 on rank 0; 2,3 on rank 1)
+    idx = np.array([[0, 1], [0, 2], [2, 3], [1, 3]], np.int32)
+    lay = oracle.layout(idx, 4, 2, 1)
+    b = types.SimpleNamespace(
+        is_token_in_rank=torch.from_numpy(lay["is_token_in_rank"]),
+        num_tokens_per_expert=torch.from_numpy(lay["num_tokens_per_expert"]))
+    w = types.SimpleNamespace(num_tokens=4, hidden=256, num_ranks=2, fp8=False)
+    got = bench.logical_network_bytes(w, b)
+    # rows: token 0 -> {0}, 1 -> {0, 1}, 2 -> {1}, 3 -> {0, 1}: 6 rows
+    assert got["rows"] == 6 and got["expanded_rows_per_token"] == 2.0
+    assert got["dispatch_bytes"] == 6 * 512 and got["combine_bytes"] == 6 * 512
+    # owners t*R/T: tokens 0, 1 on rank 0, tokens 2, 3 on rank 1; remote rows:
+    # token 1 -> rank 1, token 3 -> rank 0
+    assert got["remote_rows"] == 2
+    w8 = types.SimpleNamespace(num_tokens=4, hidden=256, num_ranks=2, fp8=True)
+    assert bench.logical_network_bytes(w8, b)["dispatch_bytes"] == 6 * (256 + 8)
