@@ -228,3 +228,30 @@ def test_config_accepted_exactly_when_the_stated_rules_hold(config):
         with pytest.raises(ep.EpError) as e:
             ep.ep_recv_capacity_rows(cfg)
         assert e.value.status == ep.EP_ERR_INVALID_ARG
+
+
+def test_last_error_is_per_thread():
+    """ep_last_error describes the last failure of the calling thread: a
+    rejection in one thread leaves another thread's message untouched."""
+    import threading
+
+    L = ep.lib()
+    seen = {}
+
+    def fail():
+        st = L.ep_recv_capacity_rows(ctypes.byref(ep.ep_config_t(4, 8, 5, 4, 2, 1)),
+                                     ctypes.byref(ctypes.c_int64()))
+        seen["fail"] = (st, L.ep_last_error())
+
+    def quiet():
+        seen["quiet_before"] = L.ep_last_error()
+        th = threading.Thread(target=fail)
+        th.start()
+        th.join()
+        seen["quiet_after"] = L.ep_last_error()
+
+    th = threading.Thread(target=quiet)
+    th.start()
+    th.join()
+    assert seen["fail"][0] == ep.EP_ERR_INVALID_ARG and seen["fail"][1]
+    assert seen["quiet_before"] == b"" and seen["quiet_after"] == b""
