@@ -154,6 +154,12 @@ __device__ __forceinline__ void count_tile(const Dims &d, int tile, int experts_
   const int wave = tid / kWave;
   const int E = d.E, R = d.R;
   const unsigned long long me = 1ull << lane;
+  // rank of expert e = e / experts_per_rank as (e * magic) >> 21: exact for
+  // e < 1024 and experts_per_rank <= 1024, since e * experts_per_rank < 2^21
+  // (the identity also keeps e * magic below 2^32).
+  static_assert(EP_MAX_EXPERTS <= 1024, "the rank division below needs E <= 1024");
+  const uint32_t rank_magic = ((1u << 21) + (uint32_t)experts_per_rank - 1u) /
+                              (uint32_t)experts_per_rank;
 
   for (int i = tid; i < kWavesPerBlock * E; i += kBlock) L.masks[i] = 0ull;
   for (int i = tid; i < R; i += kBlock) L.rank_cnt[i] = 0;
@@ -175,7 +181,7 @@ __device__ __forceinline__ void count_tile(const Dims &d, int tile, int experts_
 #pragma unroll
     for (int jj = 0; jj < j; ++jj) bad |= ex[jj] == e;
     atomicOr(&L.masks[wave * E + e], me);
-    rmask |= 1ull << (e / experts_per_rank);
+    rmask |= 1ull << (((uint32_t)e * rank_magic) >> 21);
   }
   if (bad && status != nullptr) flag(status, EP_STATUS_BIT_ROUTE);
 
