@@ -252,7 +252,13 @@ __device__ __forceinline__ void token_outputs(const Dims &d, int64_t t, const La
 // Scan phase, by a whole workgroup, once L.counts holds the batch's count
 // per expert and thread r < R holds rank r's token count in rank_sum.
 // Leaves the aligned segment starts in L.counts[0..E] and, with write set,
-// stores the counts, offsets and rank partitions.
+// stores the counts, offsets and rank partitions.  With kLate every global
+// store comes after the last barrier: for a caller with no store pending,
+// a store issued earlier could make the compiler's wait for a later load
+// result (loads and stores share one counter on this chip) also wait for
+// that store.  Without kLate the stores go out as soon as each value is
+// known, which suits a caller whose own stores are pending anyway.
+template <bool kLate>
 __device__ __forceinline__ void scan_counts(const Dims &d, int experts_per_rank,
                                             const LayoutLds &L, int32_t rank_sum, bool write,
                                             int32_t *__restrict__ cnt_ws,
@@ -261,21 +267,30 @@ __device__ __forceinline__ void scan_counts(const Dims &d, int experts_per_rank,
                                             int32_t *__restrict__ rank_tok_off,
                                             int32_t *__restrict__ expert_offsets,
                                             int32_t *__restrict__ rank_offsets) {
+  constexpr int kMaxG = EP_MAX_EXPERTS / kBlock;  // experts per thread, at most
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int E = d.E, R = d.R;
-  for (int e = tid; e < E; e += kBlock) {
-    const int32_t run = L.counts[e];
-    if (write) {
-      cnt_ws[e] = run;
-      num_tokens_per_expert[e] = run;
+  // Counts of experts tid, tid + 256, ... (kept for the stores below), and
+  // their aligned sizes in LDS.
+  int32_t cnt[kMaxG];
+#pragma unroll
+  for (int i = 0; i < kMaxG; ++i) {
+    const int e = tid + i * kBlock;
+    cnt[i] = 0;
+    if (e < E) {
+      cnt[i] = L.counts[e];
+      if (!kLate && write) {
+        cnt_ws[e] = cnt[i];
+        num_tokens_per_expert[e] = cnt[i];
+      }
+      L.counts[e] = d.A == 1 ? cnt[i] : (cnt[i] + d.A - 1) / d.A * d.A;
     }
-    L.counts[e] = (run + d.A - 1) / d.A * d.A;
   }
   // The first wave (R <= 64 lanes) scans the rank counts into the starts of
   // the ranks' token partitions (the non-expanded layout).
-  if (write && tid < R) num_tokens_per_rank[tid] = rank_sum;
+  int32_t rank_start = 0, rank_total = 0;
   if (write && wave == 0) {
     const int32_t v = lane < R ? rank_sum : 0;
     int32_t inc = v;
@@ -283,8 +298,15 @@ __device__ __forceinline__ void scan_counts(const Dims &d, int experts_per_rank,
       const int32_t u = __shfl_up(inc, off);
       if (lane >= off) inc += u;
     }
-    if (lane < R) rank_tok_off[lane] = inc - v;
-    if (lane == R - 1) rank_tok_off[R] = inc;
+    rank_start = inc - v;
+    rank_total = inc;
+    if (!kLate) {
+      if (lane < R) {
+        num_tokens_per_rank[lane] = rank_sum;
+        rank_tok_off[lane] = rank_start;
+      }
+      if (lane == R - 1) rank_tok_off[R] = rank_total;
+    }
   }
   __syncthreads();
 
@@ -307,20 +329,41 @@ __device__ __forceinline__ void scan_counts(const Dims &d, int experts_per_rank,
   for (int w = 0; w < wave; ++w) base += L.wave_total[w];
   int32_t total = 0;
   for (int w = 0; w < kWavesPerBlock; ++w) total += L.wave_total[w];
-  for (int i = 0; i < G; ++i) {
-    if (e0 + i < E) {
+  int32_t off[kMaxG];
+#pragma unroll
+  for (int i = 0; i < kMaxG; ++i) {
+    off[i] = base;
+    if (i < G && e0 + i < E) {
       const int32_t a = L.counts[e0 + i];
       L.counts[e0 + i] = base;
-      if (write) expert_offsets[e0 + i] = base;
+      if (!kLate && write) expert_offsets[e0 + i] = base;
       base += a;
     }
   }
   if (tid == 0) {
     L.counts[E] = total;
-    if (write) expert_offsets[E] = total;
+    if (!kLate && write) expert_offsets[E] = total;
   }
   __syncthreads();
-  if (write && tid <= R) rank_offsets[tid] = L.counts[tid * experts_per_rank];
+  if (!write) return;
+  if (kLate) {
+    if (tid == 0) expert_offsets[E] = total;
+#pragma unroll
+    for (int i = 0; i < kMaxG; ++i) {
+      const int e = tid + i * kBlock;
+      if (e < E) {
+        cnt_ws[e] = cnt[i];
+        num_tokens_per_expert[e] = cnt[i];
+      }
+      if (i < G && e0 + i < E) expert_offsets[e0 + i] = off[i];
+    }
+    if (tid < R) {
+      num_tokens_per_rank[tid] = rank_sum;
+      rank_tok_off[tid] = rank_start;
+    }
+    if (tid == R - 1) rank_tok_off[R] = rank_total;
+  }
+  if (tid <= R) rank_offsets[tid] = L.counts[tid * experts_per_rank];
 }
 
 // Marks the workspace as written by a layout of this configuration.
@@ -388,8 +431,8 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
   const bool scans = !many || is_last;
 
   // The scanning workgroup's first batch of tile counts (expert tid, tiles
-  // 0..15) is loaded here, so that it arrives while the per-token outputs
-  // below are written.
+  // 0..15) is loaded here, so that its latency overlaps the acquire and
+  // (with several batches) the per-token outputs below.
   constexpr int kBatch = 16;
   int32_t c0[kBatch], rc0[kBatch];
 #pragma unroll
@@ -407,7 +450,17 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
     }
   }
 
-  if (live) token_outputs<K>(d, t, L, ex, rmask, is_token_in_rank, slot_rank);
+  // One batch of tiles with one expert per thread (Prefill: 16 tiles of 256
+  // experts): the scanner's totals come from the counts already in
+  // registers, and it issues every store (tile bases, its per-token outputs,
+  // the scan's outputs) only after its scan, so that the scan does not start
+  // behind a wait for any of them (see scan_counts).  With several batches
+  // the read-back itself stores between batches, and the scanner's
+  // per-token outputs are better overlapped with its first loads.
+  const bool one_batch = many && ntiles <= kBatch && E <= kBlock;
+  if (!scans || !one_batch) {
+    if (live) token_outputs<K>(d, t, L, ex, rmask, is_token_in_rank, slot_rank);
+  }
   if (!scans) return;
 
   // Per expert: tile histograms -> exclusive tile bases (in place) and the
@@ -416,7 +469,17 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
   // issued before any store.  A single workgroup already holds its counts
   // and its tile's bases are zero.
   int32_t rank_sum = 0;
-  if (many) {
+  if (one_batch) {
+    if (tid < E) {
+      int32_t run = 0;
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        run += c0[b];
+        rank_sum += rc0[b];
+      }
+      L.counts[tid] = run;
+    }
+  } else if (many) {
     for (int e = tid; e < E; e += kBlock) {
       int32_t run = 0;
       for (int t0 = 0; t0 < ntiles; t0 += kBatch) {
@@ -455,8 +518,25 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
       if (ntiles > 0) tile_rank_cnt[tid] = 0;
     }
   }
-  scan_counts(d, experts_per_rank, L, rank_sum, true, cnt_ws, num_tokens_per_expert,
-              num_tokens_per_rank, rank_tok_off, expert_offsets, rank_offsets);
+  if (one_batch)
+    scan_counts<true>(d, experts_per_rank, L, rank_sum, true, cnt_ws, num_tokens_per_expert,
+                      num_tokens_per_rank, rank_tok_off, expert_offsets, rank_offsets);
+  else
+    scan_counts<false>(d, experts_per_rank, L, rank_sum, true, cnt_ws, num_tokens_per_expert,
+                       num_tokens_per_rank, rank_tok_off, expert_offsets, rank_offsets);
+  if (one_batch && live) token_outputs<K>(d, t, L, ex, rmask, is_token_in_rank, slot_rank);
+  if (one_batch && tid < E) {
+    int32_t run = 0, rank_run = 0;
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      if (b < ntiles) {
+        tile_cnt[(int64_t)b * E + tid] = run;
+        if (tid < R) tile_rank_cnt[(int64_t)b * R + tid] = rank_run;
+      }
+      run += c0[b];
+      rank_run += rc0[b];
+    }
+  }
   if (tid == 0) {
     write_header(header, d, ntiles);
     if (many) atomicExch(&header[kHeaderTicket], 0);
@@ -717,9 +797,9 @@ __global__ __launch_bounds__(kBlock) void layout_dispatch_kernel(
                 lead && ntiles > 0 ? rank_ballot_ws : nullptr, lead ? status : nullptr);
   __syncthreads();
   if (lead && live) token_outputs<K>(d, t, L, ex, rmask, is_token_in_rank, slot_rank);
-  scan_counts(d, experts_per_rank, L, tid < d.R ? L.rank_cnt[tid] : 0, lead, cnt_ws,
-              num_tokens_per_expert, num_tokens_per_rank, rank_tok_off, expert_offsets,
-              rank_offsets);
+  scan_counts<true>(d, experts_per_rank, L, tid < d.R ? L.rank_cnt[tid] : 0, lead, cnt_ws,
+                    num_tokens_per_expert, num_tokens_per_rank, rank_tok_off, expert_offsets,
+                    rank_offsets);
   if (lead) {
     // One tile: its bases are zero.
     if (ntiles > 0) {
