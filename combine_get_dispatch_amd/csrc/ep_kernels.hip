@@ -379,8 +379,11 @@ __device__ __forceinline__ void write_header(int32_t *__restrict__ header, const
 }
 
 // K is a compile-time bound on k (k <= K) so that a token's expert ids stay
-// in registers between the marking pass and the ranking pass.
-template <int K>
+// in registers between the marking pass and the ranking pass.  kPre (1 or
+// 2) is the number of 16-tile batches of counts the scanning workgroup
+// prefetches into registers: 2 serves up to 32 tiles without a second
+// round trip, and costs registers and time that 16 tiles do not need.
+template <int K, int kPre>
 __global__ __launch_bounds__(kBlock) void layout_kernel(
     const int32_t *__restrict__ topk_idx, Dims d, int32_t ntiles, int32_t experts_per_rank,
     int32_t *__restrict__ tile_cnt, int32_t *__restrict__ tile_rank_cnt,
@@ -430,13 +433,14 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
   }
   const bool scans = !many || is_last;
 
-  // The scanning workgroup's first batch of tile counts (expert tid, tiles
-  // 0..15) is loaded here, so that its latency overlaps the acquire and
-  // (with several batches) the per-token outputs below.
+  // The scanning workgroup's first kPre batches of tile counts (expert tid,
+  // tiles 0..15 in c0 and, with kPre = 2, 16..31 in c1) are loaded here
+  // together, so that their latency overlaps the acquire and (with more
+  // batches) the per-token outputs below.
   constexpr int kBatch = 16;
-  int32_t c0[kBatch], rc0[kBatch];
+  int32_t c0[kBatch], rc0[kBatch], c1[kBatch], rc1[kBatch];
 #pragma unroll
-  for (int b = 0; b < kBatch; ++b) c0[b] = rc0[b] = 0;
+  for (int b = 0; b < kBatch; ++b) c0[b] = rc0[b] = c1[b] = rc1[b] = 0;
   if (many && scans) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     if (tid < E) {
@@ -446,18 +450,23 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
           c0[b] = tile_cnt[(int64_t)b * E + tid];
           if (tid < R) rc0[b] = tile_rank_cnt[(int64_t)b * R + tid];
         }
+        if (kPre > 1 && kBatch + b < ntiles) {
+          c1[b] = tile_cnt[(int64_t)(kBatch + b) * E + tid];
+          if (tid < R) rc1[b] = tile_rank_cnt[(int64_t)(kBatch + b) * R + tid];
+        }
       }
     }
   }
 
-  // One batch of tiles with one expert per thread (Prefill: 16 tiles of 256
-  // experts): the scanner's totals come from the counts already in
-  // registers, and it issues every store (tile bases, its per-token outputs,
-  // the scan's outputs) only after its scan, so that the scan does not start
-  // behind a wait for any of them (see scan_counts).  With several batches
-  // the read-back itself stores between batches, and the scanner's
-  // per-token outputs are better overlapped with its first loads.
-  const bool one_batch = many && ntiles <= kBatch && E <= kBlock;
+  // Up to two batches of tiles with one expert per thread (Prefill: 16
+  // tiles, Skewed: 32, each of at most 256 experts): the scanner's totals
+  // come from the counts already in registers, and it issues every store
+  // (tile bases, its per-token outputs, the scan's outputs) only after its
+  // scan, so that the scan does not start behind a wait for any of them (see
+  // scan_counts).  With more batches the read-back itself stores between
+  // batches, and the scanner's per-token outputs are better overlapped with
+  // its first loads.
+  const bool one_batch = many && ntiles <= kPre * kBatch && E <= kBlock;
   if (!scans || !one_batch) {
     if (live) token_outputs<K>(d, t, L, ex, rmask, is_token_in_rank, slot_rank);
   }
@@ -476,6 +485,10 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
       for (int b = 0; b < kBatch; ++b) {
         run += c0[b];
         rank_sum += rc0[b];
+        if (kPre > 1) {
+          run += c1[b];
+          rank_sum += rc1[b];
+        }
       }
       L.counts[tid] = run;
     }
@@ -484,11 +497,11 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
       int32_t run = 0;
       for (int t0 = 0; t0 < ntiles; t0 += kBatch) {
         int32_t c[kBatch], rc[kBatch];
-        if (e == tid && t0 == 0) {
+        if (e == tid && t0 < kPre * kBatch) {
 #pragma unroll
           for (int b = 0; b < kBatch; ++b) {
-            c[b] = c0[b];
-            rc[b] = rc0[b];
+            c[b] = t0 == 0 ? c0[b] : c1[b];
+            rc[b] = t0 == 0 ? rc0[b] : rc1[b];
           }
         } else {
 #pragma unroll
@@ -528,13 +541,13 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
   if (one_batch && tid < E) {
     int32_t run = 0, rank_run = 0;
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
+    for (int b = 0; b < kPre * kBatch; ++b) {
       if (b < ntiles) {
         tile_cnt[(int64_t)b * E + tid] = run;
         if (tid < R) tile_rank_cnt[(int64_t)b * R + tid] = rank_run;
       }
-      run += c0[b];
-      rank_run += rc0[b];
+      run += b < kBatch ? c0[b] : c1[b - kBatch];
+      rank_run += b < kBatch ? rc0[b] : rc1[b - kBatch];
     }
   }
   if (tid == 0) {
@@ -1512,7 +1525,11 @@ hipError_t launch_layout(const Dims &d, const int32_t *topk_idx, int32_t *num_to
                          int32_t *status, hipStream_t stream) {
   const WorkspaceLayout w = workspace_layout(d.T, d.k, d.E, d.R);
   const size_t lds = layout_lds_bytes(d.E);
-  auto kernel = d.k <= 8 ? layout_kernel<8> : (d.k <= 16 ? layout_kernel<16> : layout_kernel<32>);
+  auto kernel = w.ntiles > 16
+                    ? (d.k <= 8 ? layout_kernel<8, 2>
+                                : (d.k <= 16 ? layout_kernel<16, 2> : layout_kernel<32, 2>))
+                    : (d.k <= 8 ? layout_kernel<8, 1>
+                                : (d.k <= 16 ? layout_kernel<16, 1> : layout_kernel<32, 1>));
   // An empty batch still needs one workgroup to write zero counts and offsets.
   const unsigned grid = w.ntiles > 0 ? (unsigned)w.ntiles : 1u;
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(kBlock), lds, stream, topk_idx, d, w.ntiles,

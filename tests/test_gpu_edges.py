@@ -304,14 +304,16 @@ def test_workspace_reused_across_layouts():
 
 @pytest.mark.parametrize("T,E,k", [(255, 16, 3), (256, 16, 3), (257, 16, 3), (1, 256, 8),
                                    (2049, 256, 8), (1537, 512, 8), (1000, 1024, 4),
-                                   (4096, 64, 4), (4097, 256, 8), (9000, 128, 12),
+                                   (4096, 64, 4), (4097, 256, 8), (8192, 256, 8),
+                                   (8193, 64, 6), (9000, 128, 12),
                                    (16384, 64, 20), (16385, 32, 2), (70001, 32, 2)])
 def test_layout_tile_boundaries(T, E, k):
     """Layout counts 256-token tiles in separate workgroups (one workgroup
     skips the ticket); ranks must carry across tile boundaries.  The
-    scanning workgroup reads tile counts back in batches of 16 tiles: one
-    batch, several, and their edges, with k in each of the kernel's
-    register bounds (8, 16, 32)."""
+    scanning workgroup reads tile counts back in batches of 16 tiles, the
+    first two together and held in registers (up to 32 tiles it stores
+    nothing before its scan): one batch, two, more, and their edges, with k
+    in each of the kernel's register bounds (8, 16, 32)."""
     rng = np.random.default_rng(T + E)
     R = 8 if E % 8 == 0 else 1
     idx = W.random_routes(rng, T, E, k, mask_prob=0.03)
