@@ -84,6 +84,22 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no LDS):
+// shifts of 1, 2, 4 and 8 lanes inside each row of 16, then the last lane
+// of row 0 added to row 1 (and of row 2 to row 3), then the last lane of
+// row 1 to rows 2 and 3.  Lanes whose source falls outside the row add 0.
+// Integer sums, so the result does not depend on the order of the adds.
+__device__ __forceinline__ int32_t wave_inclusive_sum(int32_t v) {
+  constexpr int kRowShr = 0x110, kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+  v += __builtin_amdgcn_update_dpp(0, v, kRowShr + 1, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kRowShr + 2, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kRowShr + 4, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kRowShr + 8, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kRowBcast15, 0xa, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kRowBcast31, 0xc, 0xf, false);
+  return v;
+}
+
 // Workspace header check shared by the dispatch kernels: the workspace must
 // have been written by a layout of exactly this configuration.
 __device__ __forceinline__ bool workspace_ok(const int32_t *hdr, const Dims &d) {
@@ -293,11 +309,7 @@ __device__ __forceinline__ void scan_counts(const Dims &d, int experts_per_rank,
   int32_t rank_start = 0, rank_total = 0;
   if (write && wave == 0) {
     const int32_t v = lane < R ? rank_sum : 0;
-    int32_t inc = v;
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int32_t u = __shfl_up(inc, off);
-      if (lane >= off) inc += u;
-    }
+    const int32_t inc = wave_inclusive_sum(v);
     rank_start = inc - v;
     rank_total = inc;
     if (!kLate) {
@@ -318,11 +330,7 @@ __device__ __forceinline__ void scan_counts(const Dims &d, int experts_per_rank,
   int32_t local = 0;
   for (int i = 0; i < G; ++i)
     if (e0 + i < E) local += L.counts[e0 + i];
-  int32_t incl = local;
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int32_t v = __shfl_up(incl, off);
-    if (lane >= off) incl += v;
-  }
+  const int32_t incl = wave_inclusive_sum(local);
   if (lane == kWave - 1) L.wave_total[wave] = incl;
   __syncthreads();
   int32_t base = incl - local;
