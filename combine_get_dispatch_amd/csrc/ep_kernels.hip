@@ -182,24 +182,33 @@ __device__ __forceinline__ void count_tile(const Dims &d, int tile, int experts_
   __syncthreads();
 
   // Mark this token in its wave's bitmask of every expert it selected;
-  // reject ids outside [-1, E) and ids repeated within the token.
+  // reject ids outside [-1, E).  Branch-free: a masked or rejected slot ORs
+  // 0 into some in-range word (one per lane, so that these no-op atomics do
+  // not queue on one address).  Slots past k (uniform) are skipped.
   bool bad = false;
   rmask = 0ull;
+  const uint32_t spread = min((uint32_t)lane, (uint32_t)E - 1u);
 #pragma unroll
   for (int j = 0; j < K; ++j) {
+    if (j >= d.k) break;
     const int32_t e = ex[j];
-    if (e < -1 || e >= E) {
-      bad = true;
-      ex[j] = -1;
-      continue;
-    }
-    if (e < 0) continue;
-#pragma unroll
-    for (int jj = 0; jj < j; ++jj) bad |= ex[jj] == e;
-    atomicOr(&L.masks[wave * E + e], me);
-    rmask |= 1ull << (((uint32_t)e * rank_magic) >> 21);
+    const bool valid = (uint32_t)e < (uint32_t)E;
+    bad |= e < -1 || e >= E;
+    ex[j] = valid ? e : -1;
+    const uint32_t ev = valid ? (uint32_t)e : spread;
+    atomicOr(&L.masks[wave * E + ev], valid ? me : 0ull);
+    rmask |= valid ? 1ull << ((ev * rank_magic) >> 21) : 0ull;
   }
-  if (bad && status != nullptr) flag(status, EP_STATUS_BIT_ROUTE);
+  // A repeated expert within the token is checked where the route status
+  // is reported (the layout, and the fused kernel's lead workgroup).  A
+  // repeat sets one bit twice, so the counts stay in bounds either way.
+  if (status != nullptr) {
+#pragma unroll
+    for (int j = 1; j < K; ++j)
+#pragma unroll
+      for (int jj = 0; jj < j; ++jj) bad |= ex[j] >= 0 && ex[jj] == ex[j];
+    if (bad) flag(status, EP_STATUS_BIT_ROUTE);
+  }
 
   // Distinct tokens per rank in this tile: lane r keeps the wave's ballot
   // for rank r.  The ballots also go to the workspace: the non-expanded
