@@ -451,13 +451,15 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
   const bool scans = !many || is_last;
 
   // The scanning workgroup's first kPre batches of tile counts (expert tid,
-  // tiles 0..15 in c0 and, with kPre = 2, 16..31 in c1) are loaded here
-  // together, so that their latency overlaps the acquire and (with more
-  // batches) the per-token outputs below.
+  // tiles 0..15 in c0, 16..31 in c1, 32..47 in c2, 48..63 in c3) are loaded
+  // here together, so that their latency overlaps the acquire and (with
+  // more batches) the per-token outputs below.
   constexpr int kBatch = 16;
-  int32_t c0[kBatch], rc0[kBatch], c1[kBatch], rc1[kBatch];
+  int32_t c0[kBatch], rc0[kBatch], c1[kBatch], rc1[kBatch], c2[kBatch], rc2[kBatch],
+      c3[kBatch], rc3[kBatch];
 #pragma unroll
-  for (int b = 0; b < kBatch; ++b) c0[b] = rc0[b] = c1[b] = rc1[b] = 0;
+  for (int b = 0; b < kBatch; ++b)
+    c0[b] = rc0[b] = c1[b] = rc1[b] = c2[b] = rc2[b] = c3[b] = rc3[b] = 0;
   if (many && scans) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     if (tid < E) {
@@ -470,6 +472,14 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
         if (kPre > 1 && kBatch + b < ntiles) {
           c1[b] = tile_cnt[(int64_t)(kBatch + b) * E + tid];
           if (tid < R) rc1[b] = tile_rank_cnt[(int64_t)(kBatch + b) * R + tid];
+        }
+        if (kPre > 2 && 2 * kBatch + b < ntiles) {
+          c2[b] = tile_cnt[(int64_t)(2 * kBatch + b) * E + tid];
+          if (tid < R) rc2[b] = tile_rank_cnt[(int64_t)(2 * kBatch + b) * R + tid];
+        }
+        if (kPre > 2 && 3 * kBatch + b < ntiles) {
+          c3[b] = tile_cnt[(int64_t)(3 * kBatch + b) * E + tid];
+          if (tid < R) rc3[b] = tile_rank_cnt[(int64_t)(3 * kBatch + b) * R + tid];
         }
       }
     }
@@ -506,6 +516,10 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
           run += c1[b];
           rank_sum += rc1[b];
         }
+        if (kPre > 2) {
+          run += c2[b] + c3[b];
+          rank_sum += rc2[b] + rc3[b];
+        }
       }
       L.counts[tid] = run;
     }
@@ -517,8 +531,8 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
         if (e == tid && t0 < kPre * kBatch) {
 #pragma unroll
           for (int b = 0; b < kBatch; ++b) {
-            c[b] = t0 == 0 ? c0[b] : c1[b];
-            rc[b] = t0 == 0 ? rc0[b] : rc1[b];
+            c[b] = t0 == 0 ? c0[b] : t0 == kBatch ? c1[b] : t0 == 2 * kBatch ? c2[b] : c3[b];
+            rc[b] = t0 == 0 ? rc0[b] : t0 == kBatch ? rc1[b] : t0 == 2 * kBatch ? rc2[b] : rc3[b];
           }
         } else {
 #pragma unroll
@@ -563,8 +577,9 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
         tile_cnt[(int64_t)b * E + tid] = run;
         if (tid < R) tile_rank_cnt[(int64_t)b * R + tid] = rank_run;
       }
-      run += b < kBatch ? c0[b] : c1[b - kBatch];
-      rank_run += b < kBatch ? rc0[b] : rc1[b - kBatch];
+      const int q = b / kBatch, i = b % kBatch;
+      run += q == 0 ? c0[i] : q == 1 ? c1[i] : q == 2 ? c2[i] : c3[i];
+      rank_run += q == 0 ? rc0[i] : q == 1 ? rc1[i] : q == 2 ? rc2[i] : rc3[i];
     }
   }
   if (tid == 0) {
@@ -1542,11 +1557,10 @@ hipError_t launch_layout(const Dims &d, const int32_t *topk_idx, int32_t *num_to
                          int32_t *status, hipStream_t stream) {
   const WorkspaceLayout w = workspace_layout(d.T, d.k, d.E, d.R);
   const size_t lds = layout_lds_bytes(d.E);
-  auto kernel = w.ntiles > 16
-                    ? (d.k <= 8 ? layout_kernel<8, 2>
-                                : (d.k <= 16 ? layout_kernel<16, 2> : layout_kernel<32, 2>))
-                    : (d.k <= 8 ? layout_kernel<8, 1>
-                                : (d.k <= 16 ? layout_kernel<16, 1> : layout_kernel<32, 1>));
+  auto pick = [&](auto k8, auto k16, auto k32) { return d.k <= 8 ? k8 : (d.k <= 16 ? k16 : k32); };
+  auto kernel = w.ntiles > 32   ? pick(layout_kernel<8, 4>, layout_kernel<16, 4>, layout_kernel<32, 4>)
+                : w.ntiles > 16 ? pick(layout_kernel<8, 2>, layout_kernel<16, 2>, layout_kernel<32, 2>)
+                                : pick(layout_kernel<8, 1>, layout_kernel<16, 1>, layout_kernel<32, 1>);
   // An empty batch still needs one workgroup to write zero counts and offsets.
   const unsigned grid = w.ntiles > 0 ? (unsigned)w.ntiles : 1u;
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(kBlock), lds, stream, topk_idx, d, w.ntiles,
