@@ -54,9 +54,14 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        build_library()
-    lib = ctypes.CDLL(_LIB)
+    # EP_ORACLE_LIB names another build of oracle.c (the mutation check,
+    # tests/oracle_mutations.py, loads planted-mistake builds this way)
+    path = os.environ.get("EP_ORACLE_LIB")
+    if path is None:
+        path = _LIB
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build_library()
+    lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     i32, i64 = ctypes.c_int32, ctypes.c_int64
     lib.oracle_bf16_round.restype = ctypes.c_uint16

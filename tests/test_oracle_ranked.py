@@ -146,3 +146,19 @@ def test_cross_rank_sum_is_in_rank_order():
     out, acc, part = oracle.combine_ranked(y, d["tok_slot_row"], ne)
     assert np.array_equal(part[:, 0], vals)
     assert np.all(acc == 0.0) and np.all(out == 0)
+
+
+@pytest.mark.parametrize("bits", [0x7F80, 0xFF80, 0x7FC0])
+def test_ranked_dispatch_rejects_non_finite_rows(bits):
+    """A hidden row holding +inf, -inf or NaN is rejected, as the quantising
+    dispatch rejects it ("Deep Dive - DeepEP", "A runnable routing ledger":
+    a non-finite row fails the ledger's checks)."""
+    x = np.zeros((2, 128), np.uint16)
+    x[1, 77] = bits
+    idx = np.array([[0, 1], [2, 3]], np.int32)
+    for fp8 in (False, True):
+        with pytest.raises(oracle.OracleError) as e:
+            oracle.dispatch_ranked(x, idx, None, 4, 2, fp8=fp8)
+        assert e.value.code == oracle.BAD_ARG
+    x[1, 77] = 0x7F7F  # the largest finite bf16 passes
+    oracle.dispatch_ranked(x, idx, None, 4, 2)
