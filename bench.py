@@ -18,11 +18,14 @@ with M valid selections.  Workspace traffic is overhead and not counted.
 streaming read / write / copy of 1 GiB with 16-byte accesses, streaming or
 plain) give the rates this machine's HBM sustains, as context for the roofline.
 
-`value` is the mean over K back-to-back steps.  `step_us` adds per-step
-median / p10 / p90 for warm steps and for cold ones, where an untimed pass
-over 1 GiB before each step evicts the 256 MB MALL and the L2s (`cold`: a
-read pass; `cold_dirty`: a write pass, whose dirty lines the step then
-writes back).
+`value` and `ms_per_step` are the median over K cold steps: before each,
+an untimed read pass over 1 GiB evicts the 256 MB MALL and the L2s, so the
+step reads its inputs from HBM with clean caches.  `kernel_us` and the
+roofline time each call's kernel by its own start and stop events
+(ep_time_next_kernel) over K more cold steps.  Also reported: warm steps
+(back to back, part of x and the routes still in the MALL), and cold steps
+after a write pass (`cold_dirty`, which also pays for writing back the
+scratch's dirty lines).
 
 Prints one JSON line.  --gpus above 1 exits: this build runs on one GPU.
 """
@@ -184,9 +187,80 @@ KERNEL_KEYS = {"layout": "layout_kernel", "dispatch": "dispatch_kernel<true>",
                "dispatch_bf16": "dispatch_kernel<false>", "combine": "combine_kernel"}
 
 
+def phase_slices(warmup: int, steps: int) -> dict:
+    """Which launches of each step kernel belong to which phase of the
+    default command, in launch order: the warm-up steps, 2K cold steps
+    (whole steps, then per-call timing), 3K warm steps (back to back, per
+    step, per call) and min(K, 30) cold steps after a write pass."""
+    W, K = warmup, steps
+    return {"warmup": (0, W), "cold": (W, W + 2 * K), "warm": (W + 2 * K, W + 5 * K),
+            "cold_dirty": (W + 5 * K, W + 5 * K + min(K, 30))}
+
+
+def load_trace_cold_us(workload: str, kernel: str):
+    """A kernel's average duration over the cold steps, from the committed
+    kernel trace summary of the default command, if that summary was taken
+    on the kernel's current sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_kernel_trace.md")
+    if not os.path.exists(path):
+        return None
+    rec = _read_kv(path)
+    if rec.get(f"kernel_source_hash[{kernel}]") != kernel_source_hash(kernel):
+        return None
+    v = rec.get(f"cold_average_us[{kernel}]")
+    return float(v) if v is not None else None
+
+
+def trace_summary(run_dir: str, workload: str, cmd: str, warmup: int, steps: int) -> None:
+    """Summarise a rocprofv3 --kernel-trace --stats run of the default
+    command (run_dir/trace) into profiles/<workload>_kernel_trace.md: every
+    kernel's statistics over all launches, and the step kernels' averages
+    per phase (cold, warm, cold_dirty), taken from the launch order."""
+    import csv
+    import statistics
+
+    def rows(name):
+        with open(os.path.join(run_dir, "trace", name)) as f:
+            return list(csv.DictReader(f))
+
+    stats = {r["Name"]: r for r in rows("ep_kernel_stats.csv")}
+    launches = sorted(rows("ep_kernel_trace.csv"), key=lambda r: int(r["Dispatch_Id"]))
+    lines = ["# Kernel durations, " + workload + " workload", "", "Command:", "",
+             "    " + cmd, "", "All launches:", "",
+             "| kernel | calls | average (us) | min (us) | max (us) |", "|---|---|---|---|---|"]
+    for name, r in stats.items():
+        lines.append(f"| {short_kernel_name(name)} | {r['Calls']} | "
+                     f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} |")
+    ph = phase_slices(warmup, steps)
+    total = ph["cold_dirty"][1]
+    lines += ["", f"Step kernels per phase, by launch order (warm-up {warmup} steps, then "
+              f"cold {2 * steps}, warm {3 * steps}, cold after a write pass "
+              f"{ph['cold_dirty'][1] - ph['cold_dirty'][0]}; average us):", "",
+              "| kernel | cold | warm | cold_dirty |", "|---|---|---|---|"]
+    kv = []
+    for key, kname in KERNEL_KEYS.items():
+        durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                for r in launches if kname in r["Kernel_Name"]]
+        if not durs:
+            continue
+        if len(durs) != total:
+            lines.append(f"| {key} | ({len(durs)} launches, expected {total}) | | |")
+            continue
+        avg = {p: statistics.mean(durs[a:b]) for p, (a, b) in ph.items() if b > a}
+        lines.append(f"| {key} | {avg['cold']:.2f} | {avg['warm']:.2f} | "
+                     f"{avg['cold_dirty']:.2f} |")
+        kv += [f"cold_average_us[{key}] = {avg['cold']:.2f}",
+               f"warm_average_us[{key}] = {avg['warm']:.2f}",
+               f"kernel_source_hash[{key}] = {kernel_source_hash(key)}"]
+    with open(os.path.join(ROOT, "profiles", f"{workload}_kernel_trace.md"), "w") as f:
+        f.write("\n".join(lines + [""] + kv) + "\n")
+    print(f"trace summary written for {workload}")
+
+
 def pmc_summary(run_dir: str, workload: str, copy_mib: int, cmds: dict):
-    """Summarise rocprofv3 runs under run_dir (trace/, fetch/, write/) into
-    profiles/: per-kernel average durations, and HBM bytes per launch from
+    """Summarise rocprofv3 counter runs under run_dir (fetch/, write/, plus
+    trace/ for the durations) into profiles/: HBM bytes per launch from
     FETCH_SIZE / WRITE_SIZE scaled by what the counters read for a plain
     device copy of copy_mib MiB."""
     import csv
@@ -217,19 +291,6 @@ def pmc_summary(run_dir: str, workload: str, copy_mib: int, cmds: dict):
 
     ff, wf = copy_factor(fetch), copy_factor(write)
     stats = {r["Name"]: r for r in rows("trace", "ep_kernel_stats.csv")}
-    lines = ["# Kernel durations, " + workload + " workload",
-             "", "Command:", "", "    " + cmds["trace"], "",
-             "| kernel | calls | average (us) | min (us) | max (us) |", "|---|---|---|---|---|"]
-    for name, r in stats.items():
-        short = short_kernel_name(name)
-        lines.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
-    # a kernel's row stays valid while its own hash matches the sources
-    lines += [""] + [f"kernel_source_hash[{key}] = {kernel_source_hash(key)}"
-                     for key, kname in KERNEL_KEYS.items()
-                     if any(kname in n for n in stats)] + [""]
-    with open(os.path.join(ROOT, "profiles", f"{workload}_kernel_trace.md"), "w") as f:
-        f.write("\n".join(lines))
     for key, kname in KERNEL_KEYS.items():
         fk = [k for k in fetch if kname in k]
         wk = [k for k in write if kname in k]
@@ -258,7 +319,8 @@ def pmc_summary(run_dir: str, workload: str, copy_mib: int, cmds: dict):
         ]
         with open(os.path.join(ROOT, "profiles", f"{key}_{workload}_hbm_traffic.txt"), "w") as f:
             f.write("\n".join(body) + "\n")
-    print(f"profiles written for {workload} (copy factors fetch {ff:.4f}, write {wf:.4f})")
+    print(f"counter summaries written for {workload} (copy factors fetch {ff:.4f}, "
+          f"write {wf:.4f})")
 
 
 def short_kernel_name(name: str) -> str:
@@ -600,9 +662,12 @@ def main():
                          "JSON line, not the forward metric)")
     ap.add_argument("--pmc-summary", metavar="DIR", default=None,
                     help="summarise rocprofv3 trace/fetch/write runs in DIR into profiles/")
+    ap.add_argument("--trace-summary", metavar="DIR", default=None,
+                    help="summarise the rocprofv3 kernel trace run in DIR/trace into profiles/ "
+                         "(--warmup and --steps as in the traced command)")
     args = ap.parse_args()
 
-    if args.pmc_summary:
+    if args.pmc_summary or args.trace_summary:
         base = (f"python3 bench.py --workload {args.workload} --steps 3 --warmup 1 "
                 f"--no-cpu-baseline --copy-probe-mib 256")
         cmds = {
@@ -612,7 +677,10 @@ def main():
             "fetch": f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch -o ep -- {base}",
             "write": f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write -o ep -- {base}",
         }
-        pmc_summary(args.pmc_summary, args.workload, 256, cmds)
+        run_dir = args.pmc_summary or args.trace_summary
+        trace_summary(run_dir, args.workload, cmds["trace"], args.warmup, args.steps)
+        if args.pmc_summary:
+            pmc_summary(run_dir, args.workload, 256, cmds)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -708,21 +776,7 @@ def main():
         torch.cuda.synchronize()
         b.check_status()
 
-    # whole steps
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = e0.elapsed_time(e1) / args.steps
-    print(f"bench: {args.steps} steps, {ms_per_step * 1e3:.1f} us/step", file=sys.stderr,
-          flush=True)
-
-    # per call, events on the launch stream
+    # per call (the kernel each call launches)
     if args.fused:
         names = ("layout_dispatch", "combine")
         fns = (lambda: b.layout_dispatch(x, idx, wts), lambda: b.combine(y, wts))
@@ -732,44 +786,83 @@ def main():
     else:
         names = ("layout", "dispatch", "combine")
         fns = (lambda: b.layout(idx), do_dispatch, lambda: b.combine(y, wts))
-    ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)] for n in names}
-    for i in range(args.steps):
-        for n, fn in zip(names, fns):
-            ev[n][i][0].record(stream)
-            fn()
-            ev[n][i][1].record(stream)
-    torch.cuda.synchronize()
-    b.check_status()
-    per_us = {n: float(np.mean([a.elapsed_time(c) for a, c in ev[n]])) * 1e3 for n in names}
 
-    # per-step distribution: warm (back to back), and cold, where an untimed
-    # pass over 1 GiB before each step evicts the 256 MB MALL and the L2s.  A
-    # read pass leaves the caches clean; a write pass leaves them dirty, so the
-    # step also pays for writing that data back.
-    def step_distribution(evict: str | None) -> dict:
-        n = min(args.steps, 30)
-        scratch = torch.ones(1 << 28, dtype=torch.int32, device=dev) if evict else None
+    # Cold steps: an untimed pass over 1 GiB before each step evicts the
+    # 256 MB MALL and the L2s, so the step reads its inputs from HBM.  A read
+    # pass ("cold") leaves the caches clean; a write pass ("cold_dirty")
+    # leaves them dirty, so the step also pays for writing back the scratch's
+    # lines.  Warm steps run back to back and find part of the previous
+    # step's x and routes in the MALL.
+    scratch = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+
+    def evict(kind, i):
+        if kind == "read":
+            scratch.amax()
+        elif kind == "write":
+            scratch.fill_(i)
+
+    def timed_steps(n, kind):
+        """Per-step microseconds of n steps (events around each step)."""
         pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                  for _ in range(n)]
         for i, (a, c) in enumerate(pairs):
-            if evict == "read":
-                scratch.amax()
-            elif evict == "write":
-                scratch.fill_(i)
+            evict(kind, i)
             a.record(stream)
             step()
             c.record(stream)
         torch.cuda.synchronize()
-        us = np.array([a.elapsed_time(c) * 1e3 for a, c in pairs])
-        del scratch
-        return {"median": round(float(np.median(us)), 2),
-                "p10": round(float(np.percentile(us, 10)), 2),
-                "p90": round(float(np.percentile(us, 90)), 2), "n": n}
+        return np.array([a.elapsed_time(c) * 1e3 for a, c in pairs])
 
-    step_us = {"warm": step_distribution(None), "cold": step_distribution("read"),
-               "cold_dirty": step_distribution("write")}
+    def timed_kernels(n, kind):
+        """Mean duration (us) of each call's kernel over n steps, timed by
+        the kernel's own start and stop events (ep_time_next_kernel)."""
+        ev = {nm: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(n)] for nm in names}
+        for pairs in ev.values():  # creates the events on the device
+            for a, c in pairs:
+                a.record(stream)
+                c.record(stream)
+        torch.cuda.synchronize()
+        for i in range(n):
+            evict(kind, i)
+            for nm, fn in zip(names, fns):
+                ep.ep_time_next_kernel(*ev[nm][i])
+                fn()
+        torch.cuda.synchronize()
+        return {nm: float(np.mean([a.elapsed_time(c) for a, c in ev[nm]])) * 1e3
+                for nm in names}
+
+    def dist(us):
+        return {"median": round(float(np.median(us)), 2), "mean": round(float(np.mean(us)), 2),
+                "p10": round(float(np.percentile(us, 10)), 2),
+                "p90": round(float(np.percentile(us, 90)), 2), "n": int(len(us))}
+
+    # The headline: K cold steps (read eviction).
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    cold_us = timed_steps(args.steps, "read")
+    wall = time.perf_counter() - t0
+    ms_per_step = float(np.median(cold_us)) / 1e3
+    print(f"bench: {args.steps} cold steps, median {ms_per_step * 1e3:.1f} us/step",
+          file=sys.stderr, flush=True)
+    per_us = timed_kernels(args.steps, "read")
     b.check_status()
+
+    # Warm: K steps back to back (one event pair), then per step and per call.
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    warm_mean_us = e0.elapsed_time(e1) / args.steps * 1e3
+    warm_us = timed_steps(args.steps, None)
+    per_us_warm = timed_kernels(args.steps, None)
+    dirty_us = timed_steps(min(args.steps, 30), "write")
+    b.check_status()
+    del scratch
+    step_us = {"cold": dist(cold_us), "warm": dict(dist(warm_us), back_to_back_mean=round(
+        warm_mean_us, 2)), "cold_dirty": dist(dirty_us)}
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20
@@ -835,10 +928,12 @@ def main():
     gbps = by["total"] / step_s / 1e9
     dom = max(names[-2:], key=lambda n: per_us[n])
     achieved = by[dom] / (per_us[dom] / 1e6) / 1e9
-    # the committed counter summaries are of the default command only
-    default_mode = not (args.fp8_input or args.alignment or args.replay or args.fused)
+    # the committed counter and trace summaries are of the default command only
+    default_mode = not (args.fp8_input or args.alignment or args.replay or args.fused
+                        or args.graph)
     traffic_key = "dispatch_bf16" if dom == "dispatch" and not w.fp8 else dom
     traffic = load_traffic(w.name, traffic_key) if default_mode else None
+    trace_us = load_trace_cold_us(w.name, traffic_key) if default_mode else None
     rec = {
         "metric": METRIC,
         "value": round(gbps, 1),
@@ -850,7 +945,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": ("e4m3 dispatch (fp32 quantiser), bf16 combine with fp32 accumulation"
+                  if w.fp8 and not args.fp8_input else
+                  "e4m3 codes copied, bf16 combine with fp32 accumulation" if args.fp8_input
+                  else "bf16 dispatch (bit copy), bf16 combine with fp32 accumulation"),
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.num_tokens} tokens x {w.hidden} hidden, "
                                f"top-{w.num_topk} of {w.num_experts} experts on "
@@ -868,10 +966,17 @@ def main():
         "pct_of_peak": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
         "tokens_per_s": round(w.num_tokens / step_s, 1),
         "algorithmic_bytes_per_step": by,
+        "timing": ("value and ms_per_step: median of the K cold steps (an untimed read "
+                   "pass over 1 GiB evicts the MALL and L2s before each); kernel_us: each "
+                   "call's kernel timed by its own start/stop events over K more cold steps"),
         "kernel_us": {n: round(v, 2) for n, v in per_us.items()},
+        "kernel_us_warm": {n: round(v, 2) for n, v in per_us_warm.items()},
         "kernel_roofline_frac": {n: round(by[n] / (per_us[n] / 1e6) / 1e9 / PEAK_HBM_GBPS, 4)
                                  for n in names},
         "step_us": step_us,
+        "warm_value": round(by["total"] / (warm_mean_us / 1e6) / 1e9, 1),
+        "cold_dirty_value": round(by["total"] / (step_us["cold_dirty"]["median"] / 1e6) / 1e9,
+                                  1),
         "receipt": receipt,
         "logical_network_bytes": net_bytes,
         "device_copy_gbps": copy_gbps,
@@ -885,6 +990,12 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
             "traffic": traffic,
+            "kernel_us": round(per_us[dom], 2),
+            "timing": "kernel start/stop events, cold steps",
+            "trace_us": trace_us,
+            "trace_frac": (round(by[dom] / (trace_us / 1e6) / 1e9 / PEAK_HBM_GBPS, 4)
+                           if trace_us else None),
+            "trace_file": f"profiles/{w.name}_kernel_trace.md" if trace_us else None,
         },
     }
     if not args.no_cpu_baseline and not args.fp8_input:

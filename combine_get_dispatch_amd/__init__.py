@@ -21,7 +21,10 @@ LIB_PATH = os.path.join(_PKG, "libep.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "ep.h")
 HEADER_PATHS = [HEADER_PATH, os.path.join(os.path.dirname(_PKG), "include", "ep_probe.h")]
 
-EP_OK, EP_ERR_INVALID_ARG, EP_ERR_INVALID_ROUTE, EP_ERR_CAPACITY, EP_ERR_WORKSPACE, EP_ERR_HIP = range(6)
+(EP_OK, EP_ERR_INVALID_ARG, EP_ERR_INVALID_ROUTE, EP_ERR_CAPACITY, EP_ERR_WORKSPACE, EP_ERR_HIP,
+ EP_ERR_NONFINITE) = range(7)
+EP_STATUS_BIT_ROUTE, EP_STATUS_BIT_CAPACITY, EP_STATUS_BIT_WORKSPACE, EP_STATUS_BIT_NONFINITE = (
+    0x1, 0x2, 0x4, 0x8)
 EP_DTYPE_BF16, EP_DTYPE_FP8_E4M3 = 0, 1
 
 
@@ -68,37 +71,40 @@ def lib() -> ctypes.CDLL:
     cfgp = ctypes.POINTER(ep_config_t)
     L.ep_status_string.restype = ctypes.c_char_p
     L.ep_status_string.argtypes = [ctypes.c_int]
-    L.ep_last_error.restype = ctypes.c_char_p
-    L.ep_last_error.argtypes = []
+    for f in ("ep_last_error", "ep_last_error_string"):
+        getattr(L, f).restype = ctypes.c_char_p
+        getattr(L, f).argtypes = []
     L.ep_layout_workspace_bytes.argtypes = [cfgp, ctypes.POINTER(S)]
     L.ep_recv_capacity_rows.argtypes = [cfgp, ctypes.POINTER(i64)]
     L.ep_get_dispatch_layout.argtypes = [cfgp, P, P, P, P, P, P, P, S, P,
                                          ctypes.POINTER(ctypes.c_int32), P]
-    L.ep_dispatch.argtypes = [cfgp, ctypes.c_int, P, P, P, P, P, S, i64, P, P, P, P, P, P,
+    i32 = ctypes.c_int32
+    L.ep_dispatch.argtypes = [cfgp, ctypes.c_int, P, P, P, P, P, S, i64, i32, P, P, P, P, P, P,
                               ctypes.POINTER(ep_handle_t), P]
-    L.ep_layout_dispatch.argtypes = [cfgp, ctypes.c_int, P, P, P, P, P, P, P, P, P, S, i64, P, P,
-                                     P, P, P, P, ctypes.POINTER(ep_handle_t), P]
+    L.ep_layout_dispatch.argtypes = [cfgp, ctypes.c_int, P, P, P, P, P, P, P, P, P, S, i64, i32, P,
+                                     P, P, P, P, P, ctypes.POINTER(ep_handle_t), P]
     L.ep_combine.argtypes = [ctypes.POINTER(ep_handle_t), P, P, P, P]
     L.ep_read_status.argtypes = [P, P]
     L.ep_workspace_init.argtypes = [P, S, P]
     L.ep_dispatch_backward.argtypes = [ctypes.POINTER(ep_handle_t), P, P, P]
-    L.ep_dispatch_fp8_input.argtypes = [cfgp, P, P, P, P, P, P, S, i64, P, P, P, P, P, P,
+    L.ep_dispatch_fp8_input.argtypes = [cfgp, P, P, P, P, P, P, S, i64, i32, P, P, P, P, P, P,
                                         ctypes.POINTER(ep_handle_t), P]
     rhp = ctypes.POINTER(ep_ranked_handle_t)
     L.ep_ranked_capacity_rows.argtypes = [cfgp, ctypes.POINTER(i64)]
     L.ep_dispatch_ranked.argtypes = [cfgp, ctypes.c_int, P, P, P, P, P, S, i64, i64, P, P, P, P,
                                      P, P, P, P, P, rhp, P]
-    L.ep_expand.argtypes = [rhp, ctypes.c_int, P, P, P, P, S, P, P, P, P, P,
+    L.ep_expand.argtypes = [rhp, ctypes.c_int, P, P, P, P, S, i32, P, P, P, P, P,
                             ctypes.POINTER(ep_handle_t), P]
     L.ep_combine_ranked.argtypes = [rhp, P, ctypes.c_int32, P, P, P]
     L.ep_combine_backward.argtypes = [ctypes.POINTER(ep_handle_t), P, P, P, P, P, P]
     L.ep_hbm_probe.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, S, P]
+    L.ep_time_next_kernel.argtypes = [P, P]
     for f in ("ep_layout_workspace_bytes", "ep_recv_capacity_rows", "ep_get_dispatch_layout",
               "ep_dispatch", "ep_layout_dispatch", "ep_combine", "ep_read_status",
               "ep_workspace_init",
               "ep_dispatch_backward", "ep_combine_backward", "ep_dispatch_fp8_input",
               "ep_ranked_capacity_rows", "ep_dispatch_ranked", "ep_expand", "ep_combine_ranked",
-              "ep_hbm_probe"):
+              "ep_hbm_probe", "ep_time_next_kernel"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -116,7 +122,7 @@ def header_functions() -> list[str]:
 
 def _check(status: int, func: str):
     if status != EP_OK:
-        msg = lib().ep_last_error().decode()
+        msg = lib().ep_last_error_string().decode()
         raise EpError(status, func, msg)
 
 
@@ -214,7 +220,7 @@ def ep_get_dispatch_layout(cfg, topk_idx, num_tokens_per_rank, num_tokens_per_ex
 
 def ep_dispatch(cfg, recv_dtype, x, topk_idx, topk_weights, expert_offsets, workspace,
                 capacity, recv_x, recv_scales, recv_weights, tok_slot_row, row_src, status,
-                stream=None) -> ep_handle_t:
+                stream=None, zero_padding: bool = True) -> ep_handle_t:
     import torch
 
     T, H, k, E = cfg.num_tokens, cfg.hidden, cfg.num_topk, cfg.num_experts
@@ -227,6 +233,7 @@ def ep_dispatch(cfg, recv_dtype, x, topk_idx, topk_weights, expert_offsets, work
         _ptr(topk_weights, torch.float32, (T, k), "topk_weights"),
         _ptr(expert_offsets, torch.int32, (E + 1,), "expert_offsets"),
         _ptr(workspace, torch.uint8, name="workspace"), workspace.numel(), cap,
+        1 if zero_padding else 0,
         _ptr(recv_x, torch.uint8 if fp8 else torch.bfloat16, (cap, H), "recv_x"),
         _ptr(recv_scales, torch.float32, (cap, H // 128), "recv_scales") if fp8 else None,
         _ptr(recv_weights, torch.float32, (cap,), "recv_weights"),
@@ -243,7 +250,7 @@ LAYOUT_DISPATCH_MAX_TOKENS = 256
 def ep_layout_dispatch(cfg, recv_dtype, x, topk_idx, topk_weights, num_tokens_per_rank,
                        num_tokens_per_expert, is_token_in_rank, expert_offsets, rank_offsets,
                        workspace, capacity, recv_x, recv_scales, recv_weights, tok_slot_row,
-                       row_src, status, stream=None) -> ep_handle_t:
+                       row_src, status, stream=None, zero_padding: bool = True) -> ep_handle_t:
     """Layout and dispatch in one launch (at most 256 tokens)."""
     import torch
 
@@ -261,6 +268,7 @@ def ep_layout_dispatch(cfg, recv_dtype, x, topk_idx, topk_weights, num_tokens_pe
         _ptr(expert_offsets, torch.int32, (E + 1,), "expert_offsets"),
         _ptr(rank_offsets, torch.int32, (R + 1,), "rank_offsets"),
         _ptr(workspace, torch.uint8, name="workspace"), workspace.numel(), cap,
+        1 if zero_padding else 0,
         _ptr(recv_x, torch.uint8 if fp8 else torch.bfloat16, (cap, H), "recv_x"),
         _ptr(recv_scales, torch.float32, (cap, H // 128), "recv_scales") if fp8 else None,
         _ptr(recv_weights, torch.float32, (cap,), "recv_weights"),
@@ -273,7 +281,7 @@ def ep_layout_dispatch(cfg, recv_dtype, x, topk_idx, topk_weights, num_tokens_pe
 
 def ep_dispatch_fp8_input(cfg, x_codes, x_scales, topk_idx, topk_weights, expert_offsets,
                           workspace, capacity, recv_x, recv_scales, recv_weights, tok_slot_row,
-                          row_src, status, stream=None) -> ep_handle_t:
+                          row_src, status, stream=None, zero_padding: bool = True) -> ep_handle_t:
     import torch
 
     T, H, k, E = cfg.num_tokens, cfg.hidden, cfg.num_topk, cfg.num_experts
@@ -286,7 +294,7 @@ def ep_dispatch_fp8_input(cfg, x_codes, x_scales, topk_idx, topk_weights, expert
         _ptr(topk_weights, torch.float32, (T, k), "topk_weights"),
         _ptr(expert_offsets, torch.int32, (E + 1,), "expert_offsets"),
         _ptr(workspace, torch.uint8, name="workspace"), workspace.numel(), cap,
-        _ptr(recv_x, torch.uint8, (cap, H), "recv_x"),
+        1 if zero_padding else 0, _ptr(recv_x, torch.uint8, (cap, H), "recv_x"),
         _ptr(recv_scales, torch.float32, (cap, H // 128), "recv_scales"),
         _ptr(recv_weights, torch.float32, (cap,), "recv_weights"),
         _ptr(tok_slot_row, torch.int32, (T, k), "tok_slot_row"),
@@ -385,7 +393,8 @@ def ep_dispatch_ranked(cfg, recv_dtype, x, topk_idx, topk_weights, expert_offset
 
 
 def ep_expand(ranked: ep_ranked_handle_t, recv_dtype, ne_x, ne_scales, expert_offsets, workspace,
-              recv_x, recv_scales, recv_weights, row_src, status, stream=None) -> ep_handle_t:
+              recv_x, recv_scales, recv_weights, row_src, status, stream=None,
+              zero_padding: bool = True) -> ep_handle_t:
     import torch
 
     c = ranked.config
@@ -399,6 +408,7 @@ def ep_expand(ranked: ep_ranked_handle_t, recv_dtype, ne_x, ne_scales, expert_of
         _ptr(ne_scales, torch.float32, (qc, H // 128), "ne_scales") if fp8 else None,
         _ptr(expert_offsets, torch.int32, (E + 1,), "expert_offsets"),
         _ptr(workspace, torch.uint8, name="workspace"), workspace.numel(),
+        1 if zero_padding else 0,
         _ptr(recv_x, torch.uint8 if fp8 else torch.bfloat16, (cap, H), "recv_x"),
         _ptr(recv_scales, torch.float32, (cap, H // 128), "recv_scales") if fp8 else None,
         _ptr(recv_weights, torch.float32, (cap,), "recv_weights"),
@@ -458,6 +468,15 @@ def ep_hbm_probe(kind: int, nontemporal: bool, workgroups: int, src, dst, nbytes
            "ep_hbm_probe")
 
 
+def ep_time_next_kernel(start, stop):
+    """The calling thread's next layout, dispatch or combine kernel records
+    the two torch timing events when it starts and ends (include/ep_probe.h);
+    start.elapsed_time(stop) is then that kernel's own duration.  The events
+    must already exist on the device (recorded once)."""
+    _check(lib().ep_time_next_kernel(ctypes.c_void_p(start.cuda_event),
+                                     ctypes.c_void_p(stop.cuda_event)), "ep_time_next_kernel")
+
+
 # --------------------------------------------------------------------------
 # Buffers for one configuration
 # --------------------------------------------------------------------------
@@ -468,11 +487,13 @@ class EpBuffers:
     reused; outputs are views into them."""
 
     def __init__(self, num_tokens, hidden, num_topk, num_experts, num_ranks,
-                 expert_alignment=1, fp8=False, capacity=None, device="cuda"):
+                 expert_alignment=1, fp8=False, capacity=None, device="cuda", zero_padding=True):
         import torch
 
         self.cfg = _cfg(num_tokens, hidden, num_topk, num_experts, num_ranks, expert_alignment)
         self.fp8 = bool(fp8)
+        # alignment padding rows: zero payload and scales (True), or left as they are
+        self.zero_padding = bool(zero_padding)
         self.capacity = ep_recv_capacity_rows(self.cfg) if capacity is None else int(capacity)
         T, H, k, E, R = num_tokens, hidden, num_topk, num_experts, num_ranks
         dev = torch.device(device)
@@ -507,7 +528,8 @@ class EpBuffers:
     # them is replaced); each call then checks only the caller's tensors.
     _MARSHALLED = frozenset({"num_tokens_per_rank", "num_tokens_per_expert", "is_token_in_rank",
                              "expert_offsets", "rank_offsets", "workspace", "status", "recv_x",
-                             "recv_scales", "recv_weights", "tok_slot_row", "row_src", "out"})
+                             "recv_scales", "recv_weights", "tok_slot_row", "row_src", "out",
+                             "zero_padding"})
 
     def __setattr__(self, name, value):
         object.__setattr__(self, name, value)
@@ -531,7 +553,7 @@ class EpBuffers:
                              offs, _ptr(self.rank_offsets, i32, (R + 1,), "rank_offsets"),
                              ws, ws_bytes, status)
         # the scales' width is left to the library, which rejects FP8 with H % 128 != 0
-        d["_dispatch_args"] = (offs, ws, ws_bytes, cap,
+        d["_dispatch_args"] = (offs, ws, ws_bytes, cap, 1 if self.zero_padding else 0,
                                _ptr(self.recv_x, torch.uint8 if self.fp8 else torch.bfloat16,
                                     (cap, H), "recv_x"),
                                _ptr(self.recv_scales, torch.float32, name="recv_scales")
@@ -581,7 +603,7 @@ class EpBuffers:
             _ptr(topk_idx, torch.int32, self._shape_tk, "topk_idx"),
             _ptr(topk_weights, torch.float32, self._shape_tk, "topk_weights"),
             la[0], la[1], la[2], la[3], la[4], la[5], la[6], self.capacity,
-            self._dispatch_args[4], self._dispatch_args[5],
+            self._dispatch_args[4], self._dispatch_args[5], self._dispatch_args[6],
             self._recv_weights_ptr if topk_weights is not None else None,
             self._dispatch_tail[0], self._dispatch_tail[1], self._dispatch_tail[2],
             ctypes.byref(self._handle_out), _stream(stream))
@@ -604,7 +626,7 @@ class EpBuffers:
             self.cfg, x_codes, x_scales, topk_idx, topk_weights, self.expert_offsets,
             self.workspace, self.capacity, self.recv_x, self.recv_scales,
             self.recv_weights if topk_weights is not None else None, self.tok_slot_row,
-            self.row_src, self.status, stream=stream)
+            self.row_src, self.status, stream=stream, zero_padding=self.zero_padding)
         return self.handle
 
     def combine(self, expert_out, topk_weights, out=None, stream=None):
@@ -682,7 +704,7 @@ class EpBuffers:
                                 self.ne_x, self.ne_scales, self.expert_offsets, self.workspace,
                                 self.recv_x, self.recv_scales,
                                 self.recv_weights if with_weights else None, self.row_src,
-                                self.status, stream=stream)
+                                self.status, stream=stream, zero_padding=self.zero_padding)
         return self.handle
 
     def combine_ranked(self, expert_out, weighted=True, out=None, stream=None):

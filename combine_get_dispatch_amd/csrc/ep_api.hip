@@ -113,9 +113,12 @@ const char *ep_status_string(ep_status_t status) {
     case EP_ERR_CAPACITY: return "receive buffer too small";
     case EP_ERR_WORKSPACE: return "workspace not written by a layout of this configuration";
     case EP_ERR_HIP: return "HIP runtime error";
+    case EP_ERR_NONFINITE: return "a hidden value or a valid selection's gate is inf or NaN";
   }
   return "unknown status";
 }
+
+const char *ep_last_error_string(void) { return g_last_error; }
 
 const char *ep_last_error(void) { return g_last_error; }
 
@@ -161,6 +164,9 @@ ep_status_t ep_read_status(const int32_t *status, hipStream_t stream) {
     return fail(EP_ERR_CAPACITY, "a selection did not fit in the receive rows");
   if (host & EP_STATUS_BIT_WORKSPACE)
     return fail(EP_ERR_WORKSPACE, "dispatch workspace does not match its configuration");
+  if (host & EP_STATUS_BIT_NONFINITE)
+    return fail(EP_ERR_NONFINITE,
+                "a hidden value or the gate of a valid selection is an infinity or NaN");
   return EP_OK;
 }
 
@@ -196,10 +202,10 @@ ep_status_t ep_get_dispatch_layout(const ep_config_t *cfg, const int32_t *topk_i
 ep_status_t ep_dispatch(const ep_config_t *cfg, ep_dtype_t recv_dtype, const uint16_t *x,
                         const int32_t *topk_idx, const float *topk_weights,
                         const int32_t *expert_offsets, const void *workspace,
-                        size_t workspace_bytes, int64_t capacity, void *recv_x,
-                        float *recv_scales, float *recv_weights, int32_t *tok_slot_row,
-                        int32_t *row_src, int32_t *status, ep_handle_t *handle_host,
-                        hipStream_t stream) {
+                        size_t workspace_bytes, int64_t capacity, int32_t zero_padding,
+                        void *recv_x, float *recv_scales, float *recv_weights,
+                        int32_t *tok_slot_row, int32_t *row_src, int32_t *status,
+                        ep_handle_t *handle_host, hipStream_t stream) {
   EP_TRY(check_config(cfg));
   bool fp8 = false;
   EP_TRY(check_dtype(cfg, recv_dtype, &fp8));
@@ -213,8 +219,9 @@ ep_status_t ep_dispatch(const ep_config_t *cfg, ep_dtype_t recv_dtype, const uin
   if (!aligned16(x) || !aligned16(recv_x))
     return fail(EP_ERR_INVALID_ARG, "x and recv_x must be 16-byte aligned");
   EP_TRY(check_workspace(cfg, workspace, workspace_bytes));
-  hipError_t err = ep::launch_dispatch(dims_of(cfg), fp8, x, topk_idx, topk_weights,
-                                       expert_offsets, static_cast<const char *>(workspace),
+  hipError_t err = ep::launch_dispatch(dims_of(cfg), fp8, zero_padding != 0, x, topk_idx,
+                                       topk_weights, expert_offsets,
+                                       static_cast<const char *>(workspace),
                                        capacity, recv_x, recv_scales, recv_weights, tok_slot_row,
                                        row_src, status, stream);
   if (err != hipSuccess) return hip_fail(err, "dispatch launch");
@@ -233,7 +240,8 @@ ep_status_t ep_layout_dispatch(const ep_config_t *cfg, ep_dtype_t recv_dtype, co
                                int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
                                uint8_t *is_token_in_rank, int32_t *expert_offsets,
                                int32_t *rank_offsets, void *workspace, size_t workspace_bytes,
-                               int64_t capacity, void *recv_x, float *recv_scales,
+                               int64_t capacity, int32_t zero_padding, void *recv_x,
+                               float *recv_scales,
                                float *recv_weights, int32_t *tok_slot_row, int32_t *row_src,
                                int32_t *status, ep_handle_t *handle_host, hipStream_t stream) {
   EP_TRY(check_config(cfg));
@@ -255,9 +263,10 @@ ep_status_t ep_layout_dispatch(const ep_config_t *cfg, ep_dtype_t recv_dtype, co
     return fail(EP_ERR_INVALID_ARG, "x and recv_x must be 16-byte aligned");
   EP_TRY(check_workspace(cfg, workspace, workspace_bytes));
   hipError_t err = ep::launch_layout_dispatch(
-      dims_of(cfg), fp8, x, topk_idx, topk_weights, num_tokens_per_rank, num_tokens_per_expert,
-      is_token_in_rank, expert_offsets, rank_offsets, static_cast<char *>(workspace), capacity,
-      recv_x, recv_scales, recv_weights, tok_slot_row, row_src, status, stream);
+      dims_of(cfg), fp8, zero_padding != 0, x, topk_idx, topk_weights, num_tokens_per_rank,
+      num_tokens_per_expert, is_token_in_rank, expert_offsets, rank_offsets,
+      static_cast<char *>(workspace), capacity, recv_x, recv_scales, recv_weights, tok_slot_row,
+      row_src, status, stream);
   if (err != hipSuccess) return hip_fail(err, "layout-dispatch launch");
   if (handle_host != nullptr) {
     handle_host->config = *cfg;
@@ -273,7 +282,8 @@ ep_status_t ep_dispatch_fp8_input(const ep_config_t *cfg, const uint8_t *x_codes
                                   const float *x_scales, const int32_t *topk_idx,
                                   const float *topk_weights, const int32_t *expert_offsets,
                                   const void *workspace, size_t workspace_bytes,
-                                  int64_t capacity, uint8_t *recv_x, float *recv_scales,
+                                  int64_t capacity, int32_t zero_padding, uint8_t *recv_x,
+                                  float *recv_scales,
                                   float *recv_weights, int32_t *tok_slot_row, int32_t *row_src,
                                   int32_t *status, ep_handle_t *handle_host,
                                   hipStream_t stream) {
@@ -291,7 +301,7 @@ ep_status_t ep_dispatch_fp8_input(const ep_config_t *cfg, const uint8_t *x_codes
     return fail(EP_ERR_INVALID_ARG, "x_codes and recv_x must be 16-byte aligned");
   EP_TRY(check_workspace(cfg, workspace, workspace_bytes));
   hipError_t err = ep::launch_dispatch_fp8_input(
-      dims_of(cfg), x_codes, x_scales, topk_idx, topk_weights, expert_offsets,
+      dims_of(cfg), zero_padding != 0, x_codes, x_scales, topk_idx, topk_weights, expert_offsets,
       static_cast<const char *>(workspace), capacity, recv_x, recv_scales, recv_weights,
       tok_slot_row, row_src, status, stream);
   if (err != hipSuccess) return hip_fail(err, "dispatch launch");
@@ -431,8 +441,8 @@ static ep_status_t check_ranked(const ep_ranked_handle_t *h) {
 
 ep_status_t ep_expand(const ep_ranked_handle_t *ranked, ep_dtype_t recv_dtype, const void *ne_x,
                       const float *ne_scales, const int32_t *expert_offsets,
-                      const void *workspace, size_t workspace_bytes, void *recv_x,
-                      float *recv_scales, float *recv_weights, int32_t *row_src,
+                      const void *workspace, size_t workspace_bytes, int32_t zero_padding,
+                      void *recv_x, float *recv_scales, float *recv_weights, int32_t *row_src,
                       int32_t *status, ep_handle_t *handle_host, hipStream_t stream) {
   EP_TRY(check_ranked(ranked));
   const ep_config_t *cfg = &ranked->config;
@@ -447,10 +457,10 @@ ep_status_t ep_expand(const ep_ranked_handle_t *ranked, ep_dtype_t recv_dtype, c
     return fail(EP_ERR_INVALID_ARG, "ne_x and recv_x must be 16-byte aligned");
   EP_TRY(check_workspace(cfg, workspace, workspace_bytes));
   hipError_t err = ep::launch_expand(
-      dims_of(cfg), fp8, ranked->ranked_capacity, ne_x, ne_scales, ranked->ne_topk_idx,
-      ranked->ne_topk_weights, ranked->ne_src, ranked->rank_token_offsets, expert_offsets,
-      static_cast<const char *>(workspace), ranked->capacity, recv_x, recv_scales, recv_weights,
-      row_src, status, stream);
+      dims_of(cfg), fp8, zero_padding != 0, ranked->ranked_capacity, ne_x, ne_scales,
+      ranked->ne_topk_idx, ranked->ne_topk_weights, ranked->ne_src, ranked->rank_token_offsets,
+      expert_offsets, static_cast<const char *>(workspace), ranked->capacity, recv_x, recv_scales,
+      recv_weights, row_src, status, stream);
   if (err != hipSuccess) return hip_fail(err, "expand launch");
   if (handle_host != nullptr) {
     handle_host->config = *cfg;

@@ -50,27 +50,33 @@ hipError_t launch_layout(const Dims &d, const int32_t *topk_idx, int32_t *num_to
 
 hipError_t launch_workspace_init(char *ws, hipStream_t stream);
 
+// The next hot-path kernel this thread launches records start and stop.
+void time_next_kernel(hipEvent_t start, hipEvent_t stop);
+
 // Dynamic LDS bytes of a layout workgroup with E experts.
 size_t layout_lds_bytes(int32_t E);
 
 // Layout and dispatch in one launch (T <= kTileTokens).
-hipError_t launch_layout_dispatch(const Dims &d, bool fp8, const uint16_t *x,
-                                  const int32_t *topk_idx, const float *topk_weights,
+hipError_t launch_layout_dispatch(const Dims &d, bool fp8, bool zero_padding,
+                                  const uint16_t *x, const int32_t *topk_idx,
+                                  const float *topk_weights,
                                   int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
                                   uint8_t *is_token_in_rank, int32_t *expert_offsets,
                                   int32_t *rank_offsets, char *ws, int64_t capacity, void *recv_x,
                                   float *recv_scales, float *recv_weights, int32_t *tok_slot_row,
                                   int32_t *row_src, int32_t *status, hipStream_t stream);
 
-hipError_t launch_dispatch(const Dims &d, bool fp8, const uint16_t *x, const int32_t *topk_idx,
-                           const float *topk_weights, const int32_t *expert_offsets,
-                           const char *ws, int64_t capacity, void *recv_x, float *recv_scales,
-                           float *recv_weights, int32_t *tok_slot_row, int32_t *row_src,
-                           int32_t *status, hipStream_t stream);
+hipError_t launch_dispatch(const Dims &d, bool fp8, bool zero_padding, const uint16_t *x,
+                           const int32_t *topk_idx, const float *topk_weights,
+                           const int32_t *expert_offsets, const char *ws, int64_t capacity,
+                           void *recv_x, float *recv_scales, float *recv_weights,
+                           int32_t *tok_slot_row, int32_t *row_src, int32_t *status,
+                           hipStream_t stream);
 
-hipError_t launch_dispatch_fp8_input(const Dims &d, const uint8_t *x_codes, const float *x_scales,
-                                     const int32_t *topk_idx, const float *topk_weights,
-                                     const int32_t *expert_offsets, const char *ws,
+hipError_t launch_dispatch_fp8_input(const Dims &d, bool zero_padding, const uint8_t *x_codes,
+                                     const float *x_scales, const int32_t *topk_idx,
+                                     const float *topk_weights, const int32_t *expert_offsets,
+                                     const char *ws,
                                      int64_t capacity, uint8_t *recv_x, float *recv_scales,
                                      float *recv_weights, int32_t *tok_slot_row,
                                      int32_t *row_src, int32_t *status, hipStream_t stream);
@@ -93,8 +99,8 @@ hipError_t launch_dispatch_ranked(const Dims &d, bool fp8, const uint16_t *x,
                                   int32_t *rank_token_offsets, int32_t *tok_rank_row,
                                   int32_t *tok_slot_row, int32_t *status, hipStream_t stream);
 
-hipError_t launch_expand(const Dims &d, bool fp8, int64_t ranked_capacity, const void *ne_x,
-                         const float *ne_scales, const int32_t *ne_topk_idx,
+hipError_t launch_expand(const Dims &d, bool fp8, bool zero_padding, int64_t ranked_capacity,
+                         const void *ne_x, const float *ne_scales, const int32_t *ne_topk_idx,
                          const float *ne_topk_weights, const int32_t *ne_src,
                          const int32_t *rank_token_offsets, const int32_t *expert_offsets,
                          const char *ws, int64_t capacity, void *recv_x, float *recv_scales,

@@ -27,6 +27,7 @@
 // two ranked combine stages), the backward of combine, and the alignment
 // padding fills.  Output positions never depend on atomics or scheduling,
 // so every result is deterministic.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -429,9 +430,14 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
     load_ids<K>(d, t, live, topk_idx, ex);
     count_tile<K>(d, tile, experts_per_rank, L, ex, rmask, rank_ballot_ws, status);
     // With several tiles the tile's counts are published for the scan.
+    // Every wave releases its own stores at device scope before the
+    // barrier, so the scanning workgroup's acquire sees them without
+    // relying on the barrier to carry one wave's stores into another
+    // wave's release.
     if (many) {
       for (int e = tid; e < E; e += kBlock) tile_cnt[(int64_t)tile * E + e] = L.counts[e];
       for (int r = tid; r < R; r += kBlock) tile_rank_cnt[(int64_t)tile * R + r] = L.rank_cnt[r];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     }
   } else {
     // An empty batch: one workgroup writes zero counts and offsets.
@@ -440,8 +446,10 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
   }
   __syncthreads();
 
-  // Ticket: the workgroup that draws the last one scans.  The barrier above
-  // orders the workgroup's published counts before thread 0's release.
+  // Ticket: the workgroup that draws the last one scans.  Each wave has
+  // released its published counts (above); thread 0's release-acquire
+  // increment then orders the workgroup's arrival after them, and the
+  // scanner's acquire makes every tile's counts visible to it.
   if (many) {
     if (tid == 0)
       is_last = __hip_atomic_fetch_add(&header[kHeaderTicket], 1, __ATOMIC_ACQ_REL,
@@ -618,9 +626,12 @@ __device__ __forceinline__ int32_t selection_row(const Dims &d, int64_t t, int l
     const int64_t s = t * d.k + lane;
     const int32_t e = topk_idx[s];
     // Loaded before the handle's stores, so that no wait for those stores
-    // is needed before the gate is written.
-    const bool gates = write_handle && recv_weights != nullptr && topk_weights != nullptr;
+    // is needed before the gate is written.  A valid selection's gate must
+    // be finite ("Deep Dive - DeepEP", "A runnable routing ledger").
+    const bool gates = write_handle && topk_weights != nullptr;
     const float gate = gates ? topk_weights[s] : 0.0f;
+    if (gates && e >= 0 && e < d.E && !__builtin_isfinite(gate))
+      flag(status, EP_STATUS_BIT_NONFINITE);
     if (e >= 0 && e < d.E) {
       const int32_t rank = slot_rank[s];
       if (rank >= 0) {
@@ -636,27 +647,49 @@ __device__ __forceinline__ int32_t selection_row(const Dims &d, int64_t t, int l
       tok_slot_row[s] = row;
       if (row >= 0) {
         row_src[row] = (int32_t)s;
-        if (gates) recv_weights[row] = gate;
+        if (gates && recv_weights != nullptr) recv_weights[row] = gate;
       }
     }
   }
   return row;
 }
 
+// Largest magnitude of the 16 bf16 values of v0 and v1, as bf16 bits with
+// the sign cleared.  For finite values the integer order of these bits is
+// the order of the magnitudes, and an infinity (0x7F80) or a NaN (above it)
+// sorts above every finite value: one compare of the result with 0x7F80
+// tells whether all 16 values are finite.  Packed 16-bit maxima, two values
+// per instruction.
+typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u16x2_t magnitudes(uint32_t w) {
+  return __builtin_bit_cast(u16x2_t, w & 0x7FFF7FFFu);
+}
+
+__device__ __forceinline__ uint32_t absmax_bits16(const uint4 v0, const uint4 v1) {
+  u16x2_t m = __builtin_elementwise_max(magnitudes(v0.x), magnitudes(v0.y));
+  m = __builtin_elementwise_max(m, magnitudes(v0.z));
+  m = __builtin_elementwise_max(m, magnitudes(v0.w));
+  m = __builtin_elementwise_max(m, magnitudes(v1.x));
+  m = __builtin_elementwise_max(m, magnitudes(v1.y));
+  m = __builtin_elementwise_max(m, magnitudes(v1.z));
+  m = __builtin_elementwise_max(m, magnitudes(v1.w));
+  return m.x > m.y ? m.x : m.y;
+}
+
+constexpr uint32_t kBf16Inf = 0x7F80u;  // magnitude bits of an infinity
+
+// A hidden value that is an infinity or NaN is an error at the boundary
+// ("Deep Dive - DeepEP", "A runnable routing ledger": a row that is not
+// finite is rejected): the wave reports it once in the status word.
+__device__ __forceinline__ void report_nonfinite(bool bad, int lane, int32_t *status) {
+  if (__ballot(bad) != 0ull && lane == 0) flag(status, EP_STATUS_BIT_NONFINITE);
+}
+
 // FP8 rows: per token and 128-value block, amax over the block, scale =
 // amax / 448 and codes = E4M3(x / scale), both rounded to nearest even
 // ("Deep Dive - DeepEP", "Precision: FP8 on the wire, BF16 for the
 // reduction").  An all-zero block gets scale 0 and zero codes.
-__device__ __forceinline__ float amax8(const uint4 v) {
-  float m = fabsf(bf16_lo(v.x));
-  m = fmaxf(m, fabsf(bf16_hi(v.x)));
-  m = fmaxf(m, fabsf(bf16_lo(v.y)));
-  m = fmaxf(m, fabsf(bf16_hi(v.y)));
-  m = fmaxf(m, fabsf(bf16_lo(v.z)));
-  m = fmaxf(m, fabsf(bf16_hi(v.z)));
-  m = fmaxf(m, fabsf(bf16_lo(v.w)));
-  return fmaxf(m, fabsf(bf16_hi(v.w)));
-}
 
 // Eight bf16 values divided by s (correctly rounded fp32 division) and
 // converted to E4M3 with round to nearest even, packed little-endian.
@@ -673,12 +706,15 @@ __device__ __forceinline__ uint2 quantize8(const uint4 v, float s) {
 
 // The 16 values a lane owns (v0 then v1) as E4M3 codes, with the scale of
 // their 128-value block: the amax is taken over the block's 8 lanes, which
-// must all call this together.
-__device__ __forceinline__ uint4 quantize16(const uint4 v0, const uint4 v1, float &scale) {
-  float amax = fmaxf(amax8(v0), amax8(v1));
+// must all call this together.  finite is false when the block holds an
+// infinity or NaN (its scale and codes are then meaningless).
+__device__ __forceinline__ uint4 quantize16(const uint4 v0, const uint4 v1, float &scale,
+                                            bool &finite) {
+  uint32_t mbits = absmax_bits16(v0, v1);
 #pragma unroll
-  for (int m = 1; m < 8; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
-  scale = amax / 448.0f;
+  for (int m = 1; m < 8; m <<= 1) mbits = max(mbits, (uint32_t)__shfl_xor((int)mbits, m));
+  finite = mbits < kBf16Inf;
+  scale = __uint_as_float(mbits << 16) / 448.0f;
   const uint2 q0 = quantize8(v0, scale);
   const uint2 q1 = quantize8(v1, scale);
   return make_uint4(q0.x, q0.y, q1.x, q1.y);
@@ -719,12 +755,15 @@ __device__ __forceinline__ XSlice load_x_slice(const uint16_t *__restrict__ x, i
 template <bool kFp8>
 __device__ __forceinline__ void store_x_slice(const XSlice &xs, int32_t row, int k, int64_t H,
                                               int chunk, int lane, void *__restrict__ recv_x,
-                                              float *__restrict__ recv_scales) {
+                                              float *__restrict__ recv_scales,
+                                              int32_t *__restrict__ status) {
   if (kFp8) {
     const int col = slice_col<true>(chunk, lane, 0);
     const bool in = col < H;
     float scale;
-    const uint4 q = quantize16(xs.v[0], xs.v[1], scale);
+    bool finite;
+    const uint4 q = quantize16(xs.v[0], xs.v[1], scale, finite);
+    report_nonfinite(!finite, lane, status);
     const int64_t nblk = H / 128;
     for (int j = 0; j < k; ++j) {
       const int32_t r = lane_value(row, j);
@@ -733,6 +772,8 @@ __device__ __forceinline__ void store_x_slice(const XSlice &xs, int32_t row, int
       if ((lane & 7) == 0) recv_scales[(int64_t)r * nblk + col / 128] = scale;
     }
   } else {
+    // lanes past the row's end hold zeros, which are finite
+    report_nonfinite(absmax_bits16(xs.v[0], xs.v[1]) >= kBf16Inf, lane, status);
     for (int j = 0; j < k; ++j) {
       const int32_t r = lane_value(row, j);
       if (r < 0) continue;
@@ -772,7 +813,7 @@ __global__ __launch_bounds__(kBlock) void dispatch_kernel(
   const int32_t row = selection_row(d, t, lane, chunk == 0, topk_idx, topk_weights,
                                     expert_offsets, tile_base, slot_rank, capacity,
                                     recv_weights, tok_slot_row, row_src, status);
-  store_x_slice<kFp8>(xs, row, d.k, d.H, chunk, lane, recv_x, recv_scales);
+  store_x_slice<kFp8>(xs, row, d.k, d.H, chunk, lane, recv_x, recv_scales, status);
 }
 
 // Layout and dispatch in one launch, for a batch of at most one tile (256
@@ -827,8 +868,7 @@ __global__ __launch_bounds__(kBlock) void layout_dispatch_kernel(
     xs = load_x_slice<kFp8>(x, ti, d.H, chunk, lane);
     if (lane < d.k) {
       eid = topk_idx[ti * d.k + lane];
-      if (chunk == 0 && recv_weights != nullptr && topk_weights != nullptr)
-        gate = topk_weights[ti * d.k + lane];
+      if (chunk == 0 && topk_weights != nullptr) gate = topk_weights[ti * d.k + lane];
     }
   }
 
@@ -869,6 +909,8 @@ __global__ __launch_bounds__(kBlock) void layout_dispatch_kernel(
     }
     if (chunk == 0) {
       const int64_t sidx = ti * d.k + lane;
+      if (eid >= 0 && eid < d.E && !__builtin_isfinite(gate))
+        flag(status, EP_STATUS_BIT_NONFINITE);
       tok_slot_row[sidx] = row;
       if (row >= 0) {
         row_src[row] = (int32_t)sidx;
@@ -876,7 +918,7 @@ __global__ __launch_bounds__(kBlock) void layout_dispatch_kernel(
       }
     }
   }
-  store_x_slice<kFp8>(xs, row, d.k, d.H, chunk, lane, recv_x, recv_scales);
+  store_x_slice<kFp8>(xs, row, d.k, d.H, chunk, lane, recv_x, recv_scales, status);
 }
 
 // Pre-quantised rows ("Deep Dive - DeepEP", "Dispatch: layout, move, and
@@ -923,28 +965,44 @@ __global__ __launch_bounds__(kBlock) void dispatch_fp8_input_kernel(
   }
 }
 
-// Alignment padding rows of expert e: zero payload, zero scale, zero gate,
-// no source ("Deep Dive - DeepEP", "Dispatch: layout, move, and epilogue":
-// padding is not a token).  Expert e's rows are split over kPadSplit
-// workgroups (blockIdx.y strides the rows), so that the fill keeps the
-// chip busy.
+// Alignment padding rows of expert e: no source, zero gate and, with
+// zero_padding, zero payload and zero scales ("Deep Dive - DeepEP",
+// "Dispatch: layout, move, and epilogue": padding is not a token, and
+// clearing its payload is the caller's choice).  Expert e's rows are split
+// over kPadSplit workgroups (blockIdx.y strides the rows), so that the fill
+// keeps the chip busy.  The workspace must hold a layout of this
+// configuration (else nothing is written and the workspace bit is set), and
+// the rows written stay inside [expert_offsets[e], expert_offsets[e+1]) and
+// below capacity whatever the counts hold.
 constexpr int kPadSplit = 8;
 
 __global__ __launch_bounds__(kBlock) void pad_fill_kernel(
-    Dims d, bool fp8, const int32_t *__restrict__ expert_offsets, const int32_t *__restrict__ cnt,
-    int64_t capacity, void *__restrict__ recv_x, float *__restrict__ recv_scales,
-    float *__restrict__ recv_weights, int32_t *__restrict__ row_src) {
+    Dims d, bool fp8, bool zero_payload, const int32_t *__restrict__ header,
+    const int32_t *__restrict__ expert_offsets, const int32_t *__restrict__ cnt, int64_t capacity,
+    void *__restrict__ recv_x, float *__restrict__ recv_scales, float *__restrict__ recv_weights,
+    int32_t *__restrict__ row_src, int32_t *__restrict__ status) {
+  if (!workspace_ok(header, d)) {
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
+      flag(status, EP_STATUS_BIT_WORKSPACE);
+    return;
+  }
   const int e = blockIdx.x;
-  const int64_t first = (int64_t)expert_offsets[e] + cnt[e];
+  const int64_t start = expert_offsets[e];
   int64_t last = expert_offsets[e + 1];
   if (last > capacity) last = capacity;
+  const int32_t c = cnt[e];
+  if (start < 0 || c < 0) return;
+  const int64_t first = start + c;
   const int64_t row_bytes = fp8 ? (int64_t)d.H : (int64_t)d.H * 2;
   const int64_t nblk = d.H / 128;
   for (int64_t r = first + blockIdx.y; r < last; r += gridDim.y) {
-    uint4 *dst = reinterpret_cast<uint4 *>(static_cast<char *>(recv_x) + r * row_bytes);
-    for (int64_t i = threadIdx.x; i < row_bytes / 16; i += kBlock) dst[i] = make_uint4(0, 0, 0, 0);
-    if (fp8)
-      for (int64_t i = threadIdx.x; i < nblk; i += kBlock) recv_scales[r * nblk + i] = 0.0f;
+    if (zero_payload) {
+      uint4 *dst = reinterpret_cast<uint4 *>(static_cast<char *>(recv_x) + r * row_bytes);
+      for (int64_t i = threadIdx.x; i < row_bytes / 16; i += kBlock)
+        dst[i] = make_uint4(0, 0, 0, 0);
+      if (fp8)
+        for (int64_t i = threadIdx.x; i < nblk; i += kBlock) recv_scales[r * nblk + i] = 0.0f;
+    }
     if (threadIdx.x == 0) {
       row_src[r] = -1;
       if (recv_weights != nullptr) recv_weights[r] = 0.0f;
@@ -1072,8 +1130,13 @@ __device__ __forceinline__ Payload16 load_payload(const uint16_t *__restrict__ x
 // FP8 rows: the loaded bf16 values become codes and the block scale (all
 // lanes of the wave together); bf16 rows are left as loaded.
 template <bool kFp8>
-__device__ __forceinline__ void encode_payload(Payload16 &p) {
-  if (kFp8) p.lo = quantize16(p.lo, p.hi, p.scale);
+__device__ __forceinline__ void encode_payload(Payload16 &p, int lane, int32_t *status) {
+  bool finite = true;
+  if (kFp8)
+    p.lo = quantize16(p.lo, p.hi, p.scale, finite);
+  else
+    finite = absmax_bits16(p.lo, p.hi) < kBf16Inf;
+  report_nonfinite(!finite, lane, status);
 }
 
 template <bool kFp8>
@@ -1170,9 +1233,11 @@ __global__ __launch_bounds__(kBlock) void dispatch_ranked_kernel(
       const int32_t e = topk_idx[t * d.k + j];
       const bool local = e >= 0 && e < d.E && e / epr == r;
       ne_topk_idx[(int64_t)rr * d.k + j] = local ? e - r * epr : -1;
-      if (ne_topk_weights != nullptr)
-        ne_topk_weights[(int64_t)rr * d.k + j] =
-            (local && topk_weights != nullptr) ? topk_weights[t * d.k + j] : 0.0f;
+      // each valid slot is local to exactly one rank, so its gate is
+      // checked once
+      const float gate = (local && topk_weights != nullptr) ? topk_weights[t * d.k + j] : 0.0f;
+      if (!__builtin_isfinite(gate)) flag(status, EP_STATUS_BIT_NONFINITE);
+      if (ne_topk_weights != nullptr) ne_topk_weights[(int64_t)rr * d.k + j] = gate;
     }
     // The expanded handle (rows the receiver's expand will fill).
     const int32_t srow = selection_row(d, t, lane, false, topk_idx, topk_weights, expert_offsets,
@@ -1181,7 +1246,7 @@ __global__ __launch_bounds__(kBlock) void dispatch_ranked_kernel(
     if (lane < d.k) tok_slot_row[t * d.k + lane] = srow;
   }
 
-  encode_payload<kFp8>(p);
+  encode_payload<kFp8>(p, lane, status);
   for (int r = 0; r < d.R; ++r) {
     const int32_t rr = lane_value(row, r);
     if (rr < 0 || !in) continue;
@@ -1518,7 +1583,8 @@ __global__ __launch_bounds__(kBlock) void zero_padding_rows_kernel(
   int64_t last = expert_offsets[e + 1];
   if (last > capacity) last = capacity;
   const int64_t H = d.H;
-  for (int64_t r = expert_offsets[e]; r < last; ++r) {
+  const int64_t first = expert_offsets[e] > 0 ? expert_offsets[e] : 0;
+  for (int64_t r = first; r < last; ++r) {
     if (row_src[r] >= 0) continue;
     uint4 *dst = reinterpret_cast<uint4 *>(rows_out + r * H);
     for (int64_t i = threadIdx.x; i < H / 8; i += kBlock) dst[i] = make_uint4(0, 0, 0, 0);
@@ -1530,6 +1596,32 @@ __global__ __launch_bounds__(kBlock) void zero_padding_rows_kernel(
 // ---------------------------------------------------------------------------
 
 static size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Kernel timing requested by ep_time_next_kernel: the first kernel of the
+// thread's next layout / dispatch / combine call records the start event
+// when it begins, and that call's last kernel records the stop event when
+// it ends (both launched through hipExtLaunchKernelGGL).
+namespace {
+thread_local hipEvent_t t_time_start = nullptr, t_time_stop = nullptr;
+}  // namespace
+
+void time_next_kernel(hipEvent_t start, hipEvent_t stop) {
+  t_time_start = start;
+  t_time_stop = stop;
+}
+
+// A launch of one of those calls' kernels; `last` marks the call's last one.
+template <typename F, typename... Args>
+static void launch_kernel(bool last, F kernel, dim3 grid, dim3 block, uint32_t lds,
+                          hipStream_t stream, Args... args) {
+  const hipEvent_t start = t_time_start, stop = last ? t_time_stop : nullptr;
+  t_time_start = nullptr;
+  if (last) t_time_stop = nullptr;
+  if (start != nullptr || stop != nullptr)
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, start, stop, 0u, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, stream, args...);
+}
 
 WorkspaceLayout workspace_layout(int32_t T, int32_t k, int32_t E, int32_t R) {
   WorkspaceLayout w;
@@ -1563,15 +1655,14 @@ hipError_t launch_layout(const Dims &d, const int32_t *topk_idx, int32_t *num_to
                                 : pick(layout_kernel<8, 1>, layout_kernel<16, 1>, layout_kernel<32, 1>);
   // An empty batch still needs one workgroup to write zero counts and offsets.
   const unsigned grid = w.ntiles > 0 ? (unsigned)w.ntiles : 1u;
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kBlock), lds, stream, topk_idx, d, w.ntiles,
-                     d.E / d.R, reinterpret_cast<int32_t *>(ws + w.tile_cnt),
-                     reinterpret_cast<int32_t *>(ws + w.tile_rank_cnt),
-                     reinterpret_cast<int32_t *>(ws + w.slot_rank), is_token_in_rank,
-                     reinterpret_cast<int32_t *>(ws + w.cnt), num_tokens_per_expert,
-                     num_tokens_per_rank, expert_offsets, rank_offsets,
-                     reinterpret_cast<int32_t *>(ws),
-                     reinterpret_cast<unsigned long long *>(ws + w.rank_ballot),
-                     reinterpret_cast<int32_t *>(ws + w.rank_tok_off), status);
+  launch_kernel(true, kernel, dim3(grid), dim3(kBlock), (uint32_t)lds, stream, topk_idx, d,
+                w.ntiles, d.E / d.R, reinterpret_cast<int32_t *>(ws + w.tile_cnt),
+                reinterpret_cast<int32_t *>(ws + w.tile_rank_cnt),
+                reinterpret_cast<int32_t *>(ws + w.slot_rank), is_token_in_rank,
+                reinterpret_cast<int32_t *>(ws + w.cnt), num_tokens_per_expert,
+                num_tokens_per_rank, expert_offsets, rank_offsets, reinterpret_cast<int32_t *>(ws),
+                reinterpret_cast<unsigned long long *>(ws + w.rank_ballot),
+                reinterpret_cast<int32_t *>(ws + w.rank_tok_off), status);
   return hipGetLastError();
 }
 
@@ -1581,11 +1672,12 @@ hipError_t launch_workspace_init(char *ws, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_dispatch(const Dims &d, bool fp8, const uint16_t *x, const int32_t *topk_idx,
-                           const float *topk_weights, const int32_t *expert_offsets,
-                           const char *ws, int64_t capacity, void *recv_x, float *recv_scales,
-                           float *recv_weights, int32_t *tok_slot_row, int32_t *row_src,
-                           int32_t *status, hipStream_t stream) {
+hipError_t launch_dispatch(const Dims &d, bool fp8, bool zero_padding, const uint16_t *x,
+                           const int32_t *topk_idx, const float *topk_weights,
+                           const int32_t *expert_offsets, const char *ws, int64_t capacity,
+                           void *recv_x, float *recv_scales, float *recv_weights,
+                           int32_t *tok_slot_row, int32_t *row_src, int32_t *status,
+                           hipStream_t stream) {
   const WorkspaceLayout w = workspace_layout(d.T, d.k, d.E, d.R);
   const int32_t *header = reinterpret_cast<const int32_t *>(ws);
   const int32_t *tile_base = reinterpret_cast<const int32_t *>(ws + w.tile_cnt);
@@ -1595,17 +1687,17 @@ hipError_t launch_dispatch(const Dims &d, bool fp8, const uint16_t *x, const int
     const int64_t items = (int64_t)d.T * nchunks;
     const dim3 grid((unsigned)((items + kWavesPerBlock - 1) / kWavesPerBlock));
     auto kernel = fp8 ? dispatch_kernel<true> : dispatch_kernel<false>;
-    hipLaunchKernelGGL(kernel, grid, dim3(kBlock), 0, stream, d, nchunks, x, topk_idx,
-                       topk_weights, expert_offsets, header, tile_base, slot_rank, capacity,
-                       recv_x, recv_scales, recv_weights, tok_slot_row, row_src, status);
+    launch_kernel(d.A == 1, kernel, grid, dim3(kBlock), 0u, stream, d, nchunks, x, topk_idx,
+                  topk_weights, expert_offsets, header, tile_base, slot_rank, capacity, recv_x,
+                  recv_scales, recv_weights, tok_slot_row, row_src, status);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   if (d.A > 1) {
-    hipLaunchKernelGGL(pad_fill_kernel, dim3(d.E, kPadSplit), dim3(kBlock), 0, stream, d, fp8,
-                       expert_offsets, reinterpret_cast<const int32_t *>(ws + w.cnt), capacity,
-                       recv_x, recv_scales, topk_weights != nullptr ? recv_weights : nullptr,
-                       row_src);
+    launch_kernel(true, pad_fill_kernel, dim3(d.E, kPadSplit), dim3(kBlock), 0u, stream, d, fp8,
+                  zero_padding, reinterpret_cast<const int32_t *>(ws), expert_offsets,
+                  reinterpret_cast<const int32_t *>(ws + w.cnt), capacity, recv_x, recv_scales,
+                  topk_weights != nullptr ? recv_weights : nullptr, row_src, status);
     return hipGetLastError();
   }
   return hipSuccess;
@@ -1616,8 +1708,9 @@ size_t layout_lds_bytes(int32_t E) {
          sizeof(int32_t) * kWavesPerBlock * (size_t)E + sizeof(int32_t) * ((size_t)E + 1);
 }
 
-hipError_t launch_layout_dispatch(const Dims &d, bool fp8, const uint16_t *x,
-                                  const int32_t *topk_idx, const float *topk_weights,
+hipError_t launch_layout_dispatch(const Dims &d, bool fp8, bool zero_padding,
+                                  const uint16_t *x, const int32_t *topk_idx,
+                                  const float *topk_weights,
                                   int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
                                   uint8_t *is_token_in_rank, int32_t *expert_offsets,
                                   int32_t *rank_offsets, char *ws, int64_t capacity, void *recv_x,
@@ -1633,32 +1726,32 @@ hipError_t launch_layout_dispatch(const Dims &d, bool fp8, const uint16_t *x,
                            layout_dispatch_kernel<32, true>)
                     : pick(layout_dispatch_kernel<8, false>, layout_dispatch_kernel<16, false>,
                            layout_dispatch_kernel<32, false>);
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kBlock), layout_lds_bytes(d.E), stream, topk_idx, d,
-                     w.ntiles, d.E / d.R, nchunks, x, topk_weights,
-                     reinterpret_cast<int32_t *>(ws + w.tile_cnt),
-                     reinterpret_cast<int32_t *>(ws + w.tile_rank_cnt),
-                     reinterpret_cast<int32_t *>(ws + w.slot_rank), is_token_in_rank,
-                     reinterpret_cast<int32_t *>(ws + w.cnt), num_tokens_per_expert,
-                     num_tokens_per_rank, expert_offsets, rank_offsets,
-                     reinterpret_cast<int32_t *>(ws),
-                     reinterpret_cast<unsigned long long *>(ws + w.rank_ballot),
-                     reinterpret_cast<int32_t *>(ws + w.rank_tok_off), capacity, recv_x,
-                     recv_scales, recv_weights, tok_slot_row, row_src, status);
+  launch_kernel(d.A == 1, kernel, dim3(grid), dim3(kBlock), (uint32_t)layout_lds_bytes(d.E),
+                stream, topk_idx, d, w.ntiles, d.E / d.R, nchunks, x, topk_weights,
+                reinterpret_cast<int32_t *>(ws + w.tile_cnt),
+                reinterpret_cast<int32_t *>(ws + w.tile_rank_cnt),
+                reinterpret_cast<int32_t *>(ws + w.slot_rank), is_token_in_rank,
+                reinterpret_cast<int32_t *>(ws + w.cnt), num_tokens_per_expert,
+                num_tokens_per_rank, expert_offsets, rank_offsets, reinterpret_cast<int32_t *>(ws),
+                reinterpret_cast<unsigned long long *>(ws + w.rank_ballot),
+                reinterpret_cast<int32_t *>(ws + w.rank_tok_off), capacity, recv_x, recv_scales,
+                recv_weights, tok_slot_row, row_src, status);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (d.A > 1) {
-    hipLaunchKernelGGL(pad_fill_kernel, dim3(d.E, kPadSplit), dim3(kBlock), 0, stream, d, fp8,
-                       expert_offsets, reinterpret_cast<const int32_t *>(ws + w.cnt), capacity,
-                       recv_x, recv_scales, topk_weights != nullptr ? recv_weights : nullptr,
-                       row_src);
+    launch_kernel(true, pad_fill_kernel, dim3(d.E, kPadSplit), dim3(kBlock), 0u, stream, d, fp8,
+                  zero_padding, reinterpret_cast<const int32_t *>(ws), expert_offsets,
+                  reinterpret_cast<const int32_t *>(ws + w.cnt), capacity, recv_x, recv_scales,
+                  topk_weights != nullptr ? recv_weights : nullptr, row_src, status);
     return hipGetLastError();
   }
   return hipSuccess;
 }
 
-hipError_t launch_dispatch_fp8_input(const Dims &d, const uint8_t *x_codes, const float *x_scales,
-                                     const int32_t *topk_idx, const float *topk_weights,
-                                     const int32_t *expert_offsets, const char *ws,
+hipError_t launch_dispatch_fp8_input(const Dims &d, bool zero_padding, const uint8_t *x_codes,
+                                     const float *x_scales, const int32_t *topk_idx,
+                                     const float *topk_weights, const int32_t *expert_offsets,
+                                     const char *ws,
                                      int64_t capacity, uint8_t *recv_x, float *recv_scales,
                                      float *recv_weights, int32_t *tok_slot_row,
                                      int32_t *row_src, int32_t *status, hipStream_t stream) {
@@ -1670,18 +1763,19 @@ hipError_t launch_dispatch_fp8_input(const Dims &d, const uint8_t *x_codes, cons
   if (d.T > 0) {
     const int64_t items = (int64_t)d.T * nchunks;
     const dim3 grid((unsigned)((items + kWavesPerBlock - 1) / kWavesPerBlock));
-    hipLaunchKernelGGL(dispatch_fp8_input_kernel, grid, dim3(kBlock), 0, stream, d, nchunks,
-                       x_codes, x_scales, topk_idx, topk_weights, expert_offsets, header,
-                       tile_base, slot_rank, capacity, recv_x, recv_scales, recv_weights,
-                       tok_slot_row, row_src, status);
+    launch_kernel(d.A == 1, dispatch_fp8_input_kernel, grid, dim3(kBlock), 0u, stream, d,
+                  nchunks, x_codes, x_scales, topk_idx, topk_weights, expert_offsets, header,
+                  tile_base, slot_rank, capacity, recv_x, recv_scales, recv_weights,
+                  tok_slot_row, row_src, status);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   if (d.A > 1) {
-    hipLaunchKernelGGL(pad_fill_kernel, dim3(d.E, kPadSplit), dim3(kBlock), 0, stream, d, true,
-                       expert_offsets, reinterpret_cast<const int32_t *>(ws + w.cnt), capacity,
-                       static_cast<void *>(recv_x), recv_scales,
-                       topk_weights != nullptr ? recv_weights : nullptr, row_src);
+    launch_kernel(true, pad_fill_kernel, dim3(d.E, kPadSplit), dim3(kBlock), 0u, stream, d, true,
+                  zero_padding, reinterpret_cast<const int32_t *>(ws), expert_offsets,
+                  reinterpret_cast<const int32_t *>(ws + w.cnt), capacity,
+                  static_cast<void *>(recv_x), recv_scales,
+                  topk_weights != nullptr ? recv_weights : nullptr, row_src, status);
     return hipGetLastError();
   }
   return hipSuccess;
@@ -1695,11 +1789,11 @@ hipError_t launch_combine(const Dims &d, int64_t capacity, const uint16_t *exper
   const int64_t items = (int64_t)d.T * nchunks;
   const dim3 grid((unsigned)((items + kWavesPerBlock - 1) / kWavesPerBlock));
   if (topk_weights != nullptr)
-    hipLaunchKernelGGL((combine_kernel<true, 8>), grid, dim3(kBlock), 0, stream, d, nchunks,
-                       capacity, expert_out, tok_slot_row, topk_weights, out);
+    launch_kernel(true, combine_kernel<true, 8>, grid, dim3(kBlock), 0u, stream, d, nchunks,
+                  capacity, expert_out, tok_slot_row, topk_weights, out);
   else
-    hipLaunchKernelGGL((combine_kernel<false, 8>), grid, dim3(kBlock), 0, stream, d, nchunks,
-                       capacity, expert_out, tok_slot_row, topk_weights, out);
+    launch_kernel(true, combine_kernel<false, 8>, grid, dim3(kBlock), 0u, stream, d, nchunks,
+                  capacity, expert_out, tok_slot_row, topk_weights, out);
   return hipGetLastError();
 }
 
@@ -1757,8 +1851,8 @@ hipError_t launch_dispatch_ranked(const Dims &d, bool fp8, const uint16_t *x,
   return hipGetLastError();
 }
 
-hipError_t launch_expand(const Dims &d, bool fp8, int64_t ranked_capacity, const void *ne_x,
-                         const float *ne_scales, const int32_t *ne_topk_idx,
+hipError_t launch_expand(const Dims &d, bool fp8, bool zero_padding, int64_t ranked_capacity,
+                         const void *ne_x, const float *ne_scales, const int32_t *ne_topk_idx,
                          const float *ne_topk_weights, const int32_t *ne_src,
                          const int32_t *rank_token_offsets, const int32_t *expert_offsets,
                          const char *ws, int64_t capacity, void *recv_x, float *recv_scales,
@@ -1781,9 +1875,10 @@ hipError_t launch_expand(const Dims &d, bool fp8, int64_t ranked_capacity, const
   }
   if (d.A > 1) {
     hipLaunchKernelGGL(pad_fill_kernel, dim3(d.E, kPadSplit), dim3(kBlock), 0, stream, d, fp8,
-                       expert_offsets, reinterpret_cast<const int32_t *>(ws + w.cnt), capacity,
-                       recv_x, recv_scales, ne_topk_weights != nullptr ? recv_weights : nullptr,
-                       row_src);
+                       zero_padding, reinterpret_cast<const int32_t *>(ws), expert_offsets,
+                       reinterpret_cast<const int32_t *>(ws + w.cnt), capacity, recv_x,
+                       recv_scales, ne_topk_weights != nullptr ? recv_weights : nullptr, row_src,
+                       status);
     return hipGetLastError();
   }
   return hipSuccess;

@@ -13,6 +13,8 @@ namespace ep {
 // Defined with the other entry points: records the message ep_last_error()
 // returns on this thread and returns st.
 ep_status_t set_error(ep_status_t st, const char *message);
+// Defined with the launchers.
+void time_next_kernel(hipEvent_t start, hipEvent_t stop);
 }  // namespace ep
 
 namespace {
@@ -129,5 +131,10 @@ extern "C" ep_status_t ep_hbm_probe(int32_t kind, int32_t nontemporal, int32_t w
   }
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return ep::set_error(EP_ERR_HIP, hipGetErrorString(err));
+  return EP_OK;
+}
+
+extern "C" ep_status_t ep_time_next_kernel(hipEvent_t start, hipEvent_t stop) {
+  ep::time_next_kernel(start, stop);
   return EP_OK;
 }

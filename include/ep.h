@@ -40,9 +40,10 @@
  *     reduction": fail at the contract boundary, not after a silent
  *     reinterpretation).  Problems only the GPU can see (a bad route, too
  *     few receive rows, a workspace that does not belong to this
- *     configuration) are OR-ed as bits into the caller's device status word
- *     and surface through ep_read_status.  HIP launch failures return
- *     EP_ERR_HIP.  ep_last_error() describes the last failure of the
+ *     configuration, an inf or NaN among the hidden values or the gates of
+ *     valid selections) are OR-ed as bits into the caller's device status
+ *     word and surface through ep_read_status.  HIP launch failures return
+ *     EP_ERR_HIP.  ep_last_error_string() describes the last failure of the
  *     calling thread.
  */
 #ifndef EP_H
@@ -63,13 +64,15 @@ typedef enum ep_status {
   EP_ERR_INVALID_ROUTE = 2, /* expert id outside [-1, E) or repeated in a token */
   EP_ERR_CAPACITY = 3,      /* receive buffer has fewer rows than the layout needs */
   EP_ERR_WORKSPACE = 4,     /* workspace not written by a layout of this config */
-  EP_ERR_HIP = 5            /* a HIP runtime call failed */
+  EP_ERR_HIP = 5,           /* a HIP runtime call failed */
+  EP_ERR_NONFINITE = 6      /* a hidden value or a valid selection's gate is inf or NaN */
 } ep_status_t;
 
 /* Bits the kernels OR into the device status word. */
 #define EP_STATUS_BIT_ROUTE 0x1
 #define EP_STATUS_BIT_CAPACITY 0x2
 #define EP_STATUS_BIT_WORKSPACE 0x4
+#define EP_STATUS_BIT_NONFINITE 0x8
 
 typedef enum ep_dtype {
   EP_DTYPE_BF16 = 0,     /* rows are bf16, copied bit for bit */
@@ -128,17 +131,26 @@ typedef struct ep_ranked_handle {
 /* Static description of a status code (never NULL). */
 const char *ep_status_string(ep_status_t status);
 
-/* Message for the last failing call on this thread ("" if none). */
+/* Message for the last failing call on this thread ("" if none).  The
+ * message says which check failed, so that a rejected call is diagnosed at
+ * the boundary ("Deep Dive - DeepEP", "Combine: reverse routing plus
+ * reduction").  ep_last_error is the same function under a shorter name. */
+const char *ep_last_error_string(void);
 const char *ep_last_error(void);
 
 /* Host only.  Bytes of device workspace that ep_get_dispatch_layout fills
- * and ep_dispatch reads for this configuration. */
+ * and ep_dispatch reads for this configuration: a planning number the caller
+ * allocates once and reuses, as a buffer size hint is ("Deep Dive - DeepEP",
+ * "V2's single interface: ElasticBuffer": reusing a buffer avoids
+ * allocation; size it for the worst case rather than growing it). */
 ep_status_t ep_layout_workspace_bytes(const ep_config_t *cfg, size_t *bytes_host);
 
 /*
- * Prepares a workspace for its first layout: clears its header (the marker
- * that a layout completed and the counter the layout's workgroups use to
- * elect the one that finishes the prefix sums).  Call once per allocation
+ * Prepares a workspace for its first layout (the one-time set-up of a
+ * reusable buffer, "Deep Dive - DeepEP", "V2's single interface:
+ * ElasticBuffer"): clears its header (the marker that a layout completed
+ * and the counter the layout's workgroups use to elect the one that
+ * finishes the prefix sums).  Call once per allocation
  * (a zero-filled allocation needs no call); every layout leaves the header
  * ready for the next one.  Enqueued on `stream` as a small kernel (no
  * memset), so it may be captured in a graph.  workspace must be 256-byte
@@ -147,7 +159,11 @@ ep_status_t ep_layout_workspace_bytes(const ep_config_t *cfg, size_t *bytes_host
 ep_status_t ep_workspace_init(void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Host only.  Receive rows that always suffice without reading counts back:
- * T*k + E*(A-1) (every slot valid, every expert segment padded). */
+ * T*k + E*(A-1) (every slot valid, every expert segment padded).  This is
+ * the worst-case envelope a caller sizes its receive buffers by ("Deep Dive
+ * - DeepEP", "V2's single interface: ElasticBuffer"); a caller that skips
+ * the CPU-synchronised count must size by it and read only the valid
+ * ranges ("Current boundary: V2.5 changes the integration contract"). */
 ep_status_t ep_recv_capacity_rows(const ep_config_t *cfg, int64_t *rows_host);
 
 /*
@@ -203,30 +219,42 @@ ep_status_t ep_get_dispatch_layout(const ep_config_t *cfg, const int32_t *topk_i
  *                 code = E4M3(x / scale) rounded to nearest even, with scale 0
  *                 and zero codes for an all-zero block ("Deep Dive - DeepEP",
  *                 "Precision: FP8 on the wire, BF16 for the reduction").
- *   x             [T, H] bf16 hidden states (finite)
+ *   x             [T, H] bf16 hidden states.  An inf or NaN sets
+ *                 EP_STATUS_BIT_NONFINITE ("Deep Dive - DeepEP", "A runnable
+ *                 routing ledger": a row that is not finite is rejected); the
+ *                 rows of every other token are still exact, and the FP8
+ *                 codes and scale of a block holding it are meaningless.
  *   topk_idx      [T, k] int32, the same array given to the layout
- *   topk_weights  [T, k] fp32 gates or NULL
+ *   topk_weights  [T, k] fp32 gates or NULL; an inf or NaN gate of a valid
+ *                 selection sets EP_STATUS_BIT_NONFINITE (the ledger rejects
+ *                 it too); unused selections' gates are never read
  *   expert_offsets[E + 1] from ep_get_dispatch_layout
  *   workspace     the workspace that layout filled for this route
  *   capacity      rows of recv_x / recv_scales / recv_weights / row_src; a
  *                 selection whose row would be >= capacity is dropped and
  *                 EP_STATUS_BIT_CAPACITY is set (ep_recv_capacity_rows() or
  *                 the synchronised row count always suffices)
+ *   zero_padding  non-zero: alignment padding rows get zero payload and zero
+ *                 scales (do_zero_padding, "Deep Dive - DeepEP", "Dispatch:
+ *                 layout, move, and epilogue": clearing the gaps is the
+ *                 caller's choice); zero: their payload and scales are left
+ *                 as they were.  Either way padding rows get row_src -1 and
+ *                 gate 0, so they never enter a combined row.
  *   recv_weights  [capacity] fp32 out or NULL: the gate of each row
  *   tok_slot_row  [T, k] int32 out: row of (t, j), -1 if unused
  *   row_src       [capacity] int32 out: t*k + j of each row, -1 for padding
  *   handle_host   optional: filled with the handle for ep_combine
  * Rows in [offsets[e] + count[e], offsets[e+1]) are alignment padding: zero
- * payload, zero scale, zero weight, row_src -1.  Rows at or past
- * expert_offsets[E] are not written.
+ * weight, row_src -1, and zero payload and scale when zero_padding is set.
+ * Rows at or past expert_offsets[E] are not written.
  */
 ep_status_t ep_dispatch(const ep_config_t *cfg, ep_dtype_t recv_dtype, const uint16_t *x,
                         const int32_t *topk_idx, const float *topk_weights,
                         const int32_t *expert_offsets, const void *workspace,
-                        size_t workspace_bytes, int64_t capacity, void *recv_x,
-                        float *recv_scales, float *recv_weights, int32_t *tok_slot_row,
-                        int32_t *row_src, int32_t *status, ep_handle_t *handle_host,
-                        hipStream_t stream);
+                        size_t workspace_bytes, int64_t capacity, int32_t zero_padding,
+                        void *recv_x, float *recv_scales, float *recv_weights,
+                        int32_t *tok_slot_row, int32_t *row_src, int32_t *status,
+                        ep_handle_t *handle_host, hipStream_t stream);
 
 /*
  * Layout and dispatch in one launch, for a batch of at most
@@ -248,7 +276,7 @@ ep_status_t ep_layout_dispatch(const ep_config_t *cfg, ep_dtype_t recv_dtype, co
                                int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
                                uint8_t *is_token_in_rank, int32_t *expert_offsets,
                                int32_t *rank_offsets, void *workspace, size_t workspace_bytes,
-                               int64_t capacity, void *recv_x, float *recv_scales,
+                               int64_t capacity, int32_t zero_padding, void *recv_x, float *recv_scales,
                                float *recv_weights, int32_t *tok_slot_row, int32_t *row_src,
                                int32_t *status, ep_handle_t *handle_host, hipStream_t stream);
 
@@ -269,7 +297,7 @@ ep_status_t ep_dispatch_fp8_input(const ep_config_t *cfg, const uint8_t *x_codes
                                   const float *x_scales, const int32_t *topk_idx,
                                   const float *topk_weights, const int32_t *expert_offsets,
                                   const void *workspace, size_t workspace_bytes,
-                                  int64_t capacity, uint8_t *recv_x, float *recv_scales,
+                                  int64_t capacity, int32_t zero_padding, uint8_t *recv_x, float *recv_scales,
                                   float *recv_weights, int32_t *tok_slot_row, int32_t *row_src,
                                   int32_t *status, ep_handle_t *handle_host,
                                   hipStream_t stream);
@@ -339,7 +367,11 @@ ep_status_t ep_combine_backward(const ep_handle_t *handle, const uint16_t *grad_
                                 uint16_t *grad_expert_out, float *grad_weights,
                                 hipStream_t stream);
 
-/* Host only.  Non-expanded rows that always suffice: T * min(k, R). */
+/* Host only.  Non-expanded rows that always suffice: T * min(k, R), the
+ * worst case of one row per (token, destination rank) ("Deep Dive -
+ * DeepEP", "V2's single interface: ElasticBuffer" for sizing by the
+ * envelope; "Why expert parallelism needs a communication layer" for one
+ * row per destination rank). */
 ep_status_t ep_ranked_capacity_rows(const ep_config_t *cfg, int64_t *rows_host);
 
 /*
@@ -384,14 +416,14 @@ ep_status_t ep_dispatch_ranked(const ep_config_t *cfg, ep_dtype_t recv_dtype, co
  * epilogue expands rows into the layout the expert GEMM reads).  Each
  * received row is copied to the expert row of each of its local slots;
  * the result (recv_x, recv_scales, recv_weights, row_src, padding) is
- * identical to ep_dispatch of the same route.  workspace / expert_offsets
- * are the layout's.  recv_weights may be NULL.  handle_host (optional)
- * receives the expanded handle for ep_combine.
+ * identical to ep_dispatch of the same route with the same zero_padding.
+ * workspace / expert_offsets are the layout's.  recv_weights may be NULL.
+ * handle_host (optional) receives the expanded handle for ep_combine.
  */
 ep_status_t ep_expand(const ep_ranked_handle_t *ranked, ep_dtype_t recv_dtype, const void *ne_x,
                       const float *ne_scales, const int32_t *expert_offsets,
-                      const void *workspace, size_t workspace_bytes, void *recv_x,
-                      float *recv_scales, float *recv_weights, int32_t *row_src,
+                      const void *workspace, size_t workspace_bytes, int32_t zero_padding,
+                      void *recv_x, float *recv_scales, float *recv_weights, int32_t *row_src,
                       int32_t *status, ep_handle_t *handle_host, hipStream_t stream);
 
 /*
@@ -418,7 +450,12 @@ ep_status_t ep_combine_ranked(const ep_ranked_handle_t *ranked, const uint16_t *
                               hipStream_t stream);
 
 /* Synchronises `stream`, reads the device status word and returns the
- * first error it holds (route, then capacity, then workspace) or EP_OK. */
+ * first error it holds (route, then capacity, then workspace, then
+ * non-finite input) or EP_OK.  It is the host-synchronising read of what
+ * the kernels found, as the CPU-synchronised dispatch mode is ("Deep Dive -
+ * DeepEP", "Dispatch: layout, move, and epilogue": exact host-side results
+ * need the CPU-synchronised path), and it surfaces failures at the
+ * boundary ("Combine: reverse routing plus reduction"). */
 ep_status_t ep_read_status(const int32_t *status, hipStream_t stream);
 
 #ifdef __cplusplus

@@ -5,7 +5,8 @@
  * report how close the path's kernels come to what this GPU's memory system
  * actually sustains: a plain streaming read, write or copy of a large
  * buffer, with the same 16-byte accesses the kernels use, either with
- * non-temporal (streaming) cache policy or with plain accesses.
+ * non-temporal (streaming) cache policy or with plain accesses; and the
+ * duration of one kernel of the path, timed by the kernel's own events.
  */
 #ifndef EP_PROBE_H
 #define EP_PROBE_H
@@ -40,6 +41,18 @@ enum {
  */
 ep_status_t ep_hbm_probe(int32_t kind, int32_t nontemporal, int32_t workgroups, const void *src,
                          void *dst, size_t bytes, hipStream_t stream);
+
+/*
+ * Kernel timing: the calling thread's next call of ep_get_dispatch_layout,
+ * ep_dispatch, ep_layout_dispatch, ep_dispatch_fp8_input or ep_combine that
+ * launches kernels records `start` when its first kernel begins executing
+ * and `stop` when its last kernel ends (hipExtLaunchKernelGGL's events), so
+ * that hipEventElapsedTime(start, stop) is the call's own GPU time, without
+ * the gaps that event markers enqueued around a call add.  Both events are
+ * caller-created timing events (either may be NULL).  The request is
+ * consumed by that call; NULL, NULL cancels it.  Never fails (EP_OK).
+ */
+ep_status_t ep_time_next_kernel(hipEvent_t start, hipEvent_t stop);
 
 #ifdef __cplusplus
 }

@@ -135,6 +135,18 @@ static int check_routes(int32_t T, int32_t k, int32_t E, const int32_t *idx) {
   return ORACLE_OK;
 }
 
+/* [P3] "A runnable routing ledger": the gate of a used selection must be a
+ * finite number; an unused selection's gate is never read.  (The ledger
+ * also rejects negative gates; here a gate is any finite number, since
+ * combine is linear in it and the pages' interfaces take float weights.) */
+static int check_gates(int32_t T, int32_t k, const int32_t *idx, const float *w) {
+  if (w == NULL) return ORACLE_OK;
+  for (int64_t t = 0; t < T; ++t)
+    for (int j = 0; j < k; ++j)
+      if (idx[t * k + j] >= 0 && !isfinite(w[t * k + j])) return ORACLE_BAD_ARG;
+  return ORACLE_OK;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Layout                                                                    */
 /* ------------------------------------------------------------------------ */
@@ -238,6 +250,10 @@ int oracle_dispatch(int32_t T, int32_t H, int32_t k, int32_t E, int32_t R,
   if (fp8 && (H % 128 != 0 || recv_scales == NULL)) return ORACLE_BAD_ARG;
   for (int64_t i = 0; i < (int64_t)T * H; ++i)
     if (!isfinite(oracle_bf16_to_float(x[i]))) return ORACLE_BAD_ARG;
+  rc = check_routes(T, k, E, topk_idx);
+  if (rc) return rc;
+  rc = check_gates(T, k, topk_idx, topk_weights);
+  if (rc) return rc;
 
   int32_t *cnt = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
   int32_t *off = (int32_t *)malloc(sizeof(int32_t) * (size_t)(E + 1));
@@ -298,7 +314,7 @@ int oracle_dispatch(int32_t T, int32_t H, int32_t k, int32_t E, int32_t R,
   return ORACLE_OK;
 }
 
-/* [DD] "Dispatch: layout, move, and epilogue" (pre-quantised input): the
+/* [P3] "Dispatch: layout, move, and epilogue" (pre-quantised input): the
  * same stable placement as oracle_dispatch, with the token's codes and
  * scales copied unchanged. */
 int oracle_dispatch_fp8_input(int32_t T, int32_t H, int32_t k, int32_t E, int32_t R,
@@ -309,6 +325,10 @@ int oracle_dispatch_fp8_input(int32_t T, int32_t H, int32_t k, int32_t E, int32_
   int rc = check_sizes(T, k, E, R, A);
   if (rc) return rc;
   if (H < 128 || H % 128 != 0 || capacity < 0) return ORACLE_BAD_ARG;
+  rc = check_routes(T, k, E, topk_idx);
+  if (rc) return rc;
+  rc = check_gates(T, k, topk_idx, topk_weights);
+  if (rc) return rc;
   int32_t *cnt = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
   int32_t *off = (int32_t *)malloc(sizeof(int32_t) * (size_t)(E + 1));
   int32_t *rank_cnt = (int32_t *)malloc(sizeof(int32_t) * (size_t)R);
@@ -404,6 +424,8 @@ int oracle_dispatch_ranked(int32_t T, int32_t H, int32_t k, int32_t E, int32_t R
   if (rc) return rc;
   for (int64_t i = 0; i < (int64_t)T * H; ++i)
     if (!isfinite(oracle_bf16_to_float(x[i]))) return ORACLE_BAD_ARG;
+  rc = check_gates(T, k, topk_idx, topk_weights);
+  if (rc) return rc;
   const int32_t epr = E / R;
   const int32_t nblk = H / 128;
 
@@ -580,7 +602,7 @@ int oracle_combine_ranked(int32_t T, int32_t H, int32_t k, int32_t R, int64_t ro
 /* Backward                                                                  */
 /* ------------------------------------------------------------------------ */
 
-/* [DD] "Combine: reverse routing plus reduction", backward duality: the
+/* [P3] "Combine: reverse routing plus reduction", backward duality: the
  * transpose of copying a token's row into each of its expert rows is
  * summing the gradients of those rows back into the token. */
 int oracle_dispatch_backward(int32_t T, int32_t H, int32_t k, int64_t capacity,
@@ -607,7 +629,7 @@ int oracle_dispatch_backward(int32_t T, int32_t H, int32_t k, int64_t capacity,
 /* Backward of out[t] = sum_j w[t,j] * y[p_j]: the gradient reaching expert
  * row p_j is w[t,j] * grad_out[t] (the gate applied once, as in the forward
  * pass), and the gradient of the gate is the dot product of the expert row
- * with grad_out[t] ([DD] "Combine: reverse routing plus reduction": the
+ * with grad_out[t] ([P3] "Combine: reverse routing plus reduction": the
  * autograd wrapper must still produce gate gradients). */
 int oracle_combine_backward(int32_t T, int32_t H, int32_t k, int64_t capacity,
                             int64_t rows_used, const uint16_t *grad_out,

@@ -32,7 +32,7 @@ extern "C" {
 #endif
 
 #define ORACLE_OK 0
-#define ORACLE_BAD_ARG 1      /* sizes / dtype / non-finite hidden values */
+#define ORACLE_BAD_ARG 1      /* sizes / dtype / non-finite hidden values or gates */
 #define ORACLE_BAD_ROUTE 2    /* expert id outside [-1, E) or repeated in a row */
 #define ORACLE_NO_CAPACITY 3  /* receive buffer has fewer rows than needed */
 
@@ -65,6 +65,8 @@ int oracle_layout(int32_t T, int32_t k, int32_t E, int32_t R, int32_t A,
  *   fp8 != 0: recv_x is e4m3 bytes [capacity, H]; recv_scales fp32
  *             [capacity, H/128]; requires H % 128 == 0.
  * topk_weights and recv_weights may be NULL (then no weights are copied).
+ * A hidden value, or the gate of a used selection, that is an infinity or
+ * NaN is rejected (ORACLE_BAD_ARG); unused selections' gates are not read.
  * Rows [0, expert_offsets[E]) are written; rows past it are left untouched. */
 int oracle_dispatch(int32_t T, int32_t H, int32_t k, int32_t E, int32_t R,
                     int32_t A, int32_t fp8, const uint16_t *x,
@@ -82,7 +84,7 @@ int oracle_combine(int32_t T, int32_t H, int32_t k, int64_t capacity,
                    const uint16_t *y, const int32_t *tok_slot_row,
                    const float *topk_weights, uint16_t *out, float *acc_out);
 
-/* Dispatch of rows that arrive already quantised ([DD] "Dispatch: layout,
+/* Dispatch of rows that arrive already quantised ([P3] "Dispatch: layout,
  * move, and epilogue": hidden states are BF16, or FP8 values plus scale
  * factors).  The E4M3 codes x_codes [T,H] and the fp32 scales
  * x_scales [T, H/128] are copied bit for bit to every receive row of the
@@ -94,7 +96,7 @@ int oracle_dispatch_fp8_input(int32_t T, int32_t H, int32_t k, int32_t E, int32_
                               int64_t capacity, uint8_t *recv_codes, float *recv_scales,
                               float *recv_weights, int32_t *tok_slot_row, int32_t *row_src);
 
-/* Non-expanded (rank-deduplicated) dispatch ([DD] "Why expert parallelism
+/* Non-expanded (rank-deduplicated) dispatch ([P3] "Why expert parallelism
  * needs a communication layer": a token crosses to a destination rank once
  * however many of its experts live there; "Dispatch: layout, move, and
  * epilogue": in non-expanded mode a received row is a source token with its
@@ -114,7 +116,7 @@ int oracle_dispatch_ranked(int32_t T, int32_t H, int32_t k, int32_t E, int32_t R
                            int32_t *recv_src, int32_t *tok_rank_row);
 
 /* Receiver-side expand of non-expanded rows into the expert-major layout
- * ([DD] "Dispatch: layout, move, and epilogue": the copy epilogue expands
+ * ([P3] "Dispatch: layout, move, and epilogue": the copy epilogue expands
  * rows into the receive layout the expert GEMM uses).  Uses only what the
  * receiver holds: the rows, recv_src, the local top-k slice and the rank
  * partition bounds.  Experts' segments start at aligned offsets (alignment
@@ -129,7 +131,7 @@ int oracle_expand(int32_t T, int32_t H, int32_t k, int32_t E, int32_t R, int32_t
                   int64_t capacity, void *recv_x, float *recv_scales, float *recv_weights,
                   int32_t *tok_slot_row, int32_t *row_src);
 
-/* Combine through per-rank partial sums ([DD] "Combine: reverse routing
+/* Combine through per-rank partial sums ([P3] "Combine: reverse routing
  * plus reduction": staging partial sums per rank sends fewer rows; kept in
  * fp32 here because a bf16 subtotal can lose a small term to cancellation).
  * Stage 1, per non-expanded row q of token t on rank r:
@@ -147,7 +149,7 @@ int oracle_combine_ranked(int32_t T, int32_t H, int32_t k, int32_t R, int64_t ro
                           const int32_t *tok_rank_row, float *partials, uint16_t *out,
                           float *acc_out);
 
-/* Backward of dispatch ([DD] "Combine: reverse routing plus reduction",
+/* Backward of dispatch ([P3] "Combine: reverse routing plus reduction",
  * backward duality: for the unweighted route, copying a row forward becomes
  * summing its gradients backward):
  *   grad_x[t,c] = bf16(sum over valid j, in slot order, of

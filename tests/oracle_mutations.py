@@ -57,6 +57,12 @@ MUTATIONS = [
     ("nonfinite_allowed",
      "if (!isfinite(oracle_bf16_to_float(x[i]))) return ORACLE_BAD_ARG;",
      "if (0) return ORACLE_BAD_ARG;", 0),
+    ("gates_nonfinite_allowed",
+     "if (idx[t * k + j] >= 0 && !isfinite(w[t * k + j])) return ORACLE_BAD_ARG;",
+     "if (0) return ORACLE_BAD_ARG;", 0),
+    ("gates_checked_on_unused_slots",
+     "if (idx[t * k + j] >= 0 && !isfinite(w[t * k + j])) return ORACLE_BAD_ARG;",
+     "if (!isfinite(w[t * k + j])) return ORACLE_BAD_ARG;", 0),
     # layout ("6.1 Layout Metadata", "Dispatch: layout, move, and epilogue")
     ("count_skips_expert0", "if (e >= 0) num_tokens_per_expert[e] += 1;",
      "if (e > 0) num_tokens_per_expert[e] += 1;", 0),

@@ -20,8 +20,8 @@ def test_library_exports_every_declared_function():
 
 def test_status_strings():
     L = ep.lib()
-    for code in range(6):
-        assert L.ep_status_string(code)
+    for code in range(7):
+        assert L.ep_status_string(code) != b"unknown status"
     assert L.ep_status_string(99) == b"unknown status"
 
 
@@ -50,7 +50,9 @@ def test_bad_config_rejected(bad):
     with pytest.raises(ep.EpError) as e:
         ep.ep_recv_capacity_rows(ep.ep_config_t(*bad))
     assert e.value.status == ep.EP_ERR_INVALID_ARG
-    assert ep.lib().ep_last_error()
+    assert ep.lib().ep_last_error_string()
+    # the short name is the same function
+    assert ep.lib().ep_last_error() == ep.lib().ep_last_error_string()
 
 
 def _fake(n):
@@ -62,24 +64,24 @@ def test_dispatch_rejections_happen_before_launch():
     cfg = ep.ep_config_t(16, 200, 2, 4, 2, 1)  # H % 128 != 0
     h = ep.ep_handle_t()
     st = L.ep_dispatch(ctypes.byref(cfg), ep.EP_DTYPE_FP8_E4M3, _fake(1), _fake(2), None,
-                       _fake(3), _fake(4), 1 << 20, 32, _fake(5), _fake(6), None, _fake(7),
+                       _fake(3), _fake(4), 1 << 20, 32, 1, _fake(5), _fake(6), None, _fake(7),
                        _fake(8), _fake(9), ctypes.byref(h), None)
     assert st == ep.EP_ERR_INVALID_ARG and b"128" in L.ep_last_error()
     cfg = ep.ep_config_t(16, 256, 2, 4, 2, 1)
     st = L.ep_dispatch(ctypes.byref(cfg), 7, _fake(1), _fake(2), None, _fake(3), _fake(4),
-                       1 << 20, 32, _fake(5), _fake(6), None, _fake(7), _fake(8), _fake(9),
+                       1 << 20, 32, 1, _fake(5), _fake(6), None, _fake(7), _fake(8), _fake(9),
                        None, None)
     assert st == ep.EP_ERR_INVALID_ARG  # unknown dtype
     st = L.ep_dispatch(ctypes.byref(cfg), ep.EP_DTYPE_BF16, _fake(1), _fake(2), None,
-                       _fake(3), _fake(4), 16, 32, _fake(5), None, None, _fake(7), _fake(8),
+                       _fake(3), _fake(4), 16, 32, 1, _fake(5), None, None, _fake(7), _fake(8),
                        _fake(9), None, None)
     assert st == ep.EP_ERR_INVALID_ARG and b"workspace" in L.ep_last_error()
     st = L.ep_dispatch(ctypes.byref(cfg), ep.EP_DTYPE_BF16, None, _fake(2), None,
-                       _fake(3), _fake(4), 1 << 20, 32, _fake(5), None, None, _fake(7),
+                       _fake(3), _fake(4), 1 << 20, 32, 1, _fake(5), None, None, _fake(7),
                        _fake(8), _fake(9), None, None)
     assert st == ep.EP_ERR_INVALID_ARG  # NULL x
     st = L.ep_dispatch(ctypes.byref(cfg), ep.EP_DTYPE_BF16, ctypes.c_void_p(0x100008),
-                       _fake(2), None, _fake(3), _fake(4), 1 << 20, 32, _fake(5), None, None,
+                       _fake(2), None, _fake(3), _fake(4), 1 << 20, 32, 1, _fake(5), None, None,
                        _fake(7), _fake(8), _fake(9), None, None)
     assert st == ep.EP_ERR_INVALID_ARG and b"aligned" in L.ep_last_error()
 
@@ -131,7 +133,7 @@ def test_layout_dispatch_rejects_large_batches_before_launch():
     cfg = ep.ep_config_t(257, 256, 8, 256, 8, 1)
     P = ctypes.c_void_p(256)
     st = L.ep_layout_dispatch(ctypes.byref(cfg), ep.EP_DTYPE_BF16, P, P, P, P, P, P, P, P, P,
-                              1 << 20, 257 * 8, P, P, P, P, P, P, None, None)
+                              1 << 20, 257 * 8, 1, P, P, P, P, P, P, None, None)
     assert st == ep.EP_ERR_INVALID_ARG
     assert "at most 256" in L.ep_last_error().decode()
 

@@ -187,3 +187,29 @@ def test_combine_starts_from_positive_zero():
     assert out[0, 0] == 0x0000
     out, acc = oracle.dispatch_backward(y, np.array([[0]], np.int32))
     assert out[0, 0] == 0x0000
+
+
+def test_dispatch_rejects_non_finite_gates_of_used_selections():
+    """A used selection's gate must be finite ("Deep Dive - DeepEP", "A
+    runnable routing ledger" rejects an invalid gate weight); an unused
+    selection's gate is never read, so NaN there is accepted.  Negative
+    gates are accepted (the reading: combine is linear in the gate)."""
+    import pytest
+
+    x = np.zeros((2, 128), np.uint16)
+    idx = np.array([[0, -1], [2, 3]], np.int32)
+    for bad in (np.inf, -np.inf, np.nan):
+        w = np.full((2, 2), 0.5, np.float32)
+        w[1, 1] = bad
+        for call in (lambda: oracle.dispatch(x, idx, w, 4, 2),
+                     lambda: oracle.dispatch(x, idx, w, 4, 2, fp8=True),
+                     lambda: oracle.dispatch_fp8_input(np.zeros((2, 128), np.uint8),
+                                                       np.ones((2, 1), np.float32), idx, w, 4, 2),
+                     lambda: oracle.dispatch_ranked(x, idx, w, 4, 2)):
+            with pytest.raises(oracle.OracleError) as e:
+                call()
+            assert e.value.code == oracle.BAD_ARG
+    w = np.array([[-0.5, np.nan], [0.25, 0.75]], np.float32)  # NaN only in the unused slot
+    d = oracle.dispatch(x, idx, w, 4, 2)
+    assert d["recv_weights"][d["tok_slot_row"][0, 0]] == np.float32(-0.5)
+    oracle.dispatch_ranked(x, idx, w, 4, 2)
