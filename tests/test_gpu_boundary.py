@@ -104,12 +104,13 @@ def test_nonfinite_gate_of_a_used_selection_is_reported():
     w_ok = w.copy()
     w_ok[idx < 0] = np.nan
     do = oracle.dispatch(x, idx, w_ok, E, R, capacity=T * k)
-    assert np.array_equal(_rows(b, False), do["recv_x"])
-    assert np.array_equal(b.row_src.cpu().numpy(), do["row_src"])
-    got_w = b.recv_weights.cpu().numpy()
+    M = int((idx >= 0).sum())                         # rows used (A = 1)
+    assert np.array_equal(_rows(b, False)[:M], do["recv_x"][:M])
+    assert np.array_equal(b.row_src.cpu().numpy()[:M], do["row_src"][:M])
+    got_w = b.recv_weights.cpu().numpy()[:M]
     p_bad = do["tok_slot_row"][t, j]
-    keep = np.arange(T * k) != p_bad
-    assert np.array_equal(got_w[keep], do["recv_weights"][keep]) and np.isinf(got_w[p_bad])
+    keep = np.arange(M) != p_bad
+    assert np.array_equal(got_w[keep], do["recv_weights"][:M][keep]) and np.isinf(got_w[p_bad])
     # NaN only in unused slots is not an error
     b2 = ep.EpBuffers(T, H, k, E, R, 1)
     b2.layout(dev(idx))
