@@ -89,6 +89,9 @@ def lib() -> ctypes.CDLL:
     L.ep_dispatch_backward.argtypes = [ctypes.POINTER(ep_handle_t), P, P, P]
     L.ep_dispatch_fp8_input.argtypes = [cfgp, P, P, P, P, P, P, S, i64, i32, P, P, P, P, P, P,
                                         ctypes.POINTER(ep_handle_t), P]
+    L.ep_layout_dispatch_noalloc.argtypes = [cfgp, ctypes.c_int, P, P, P, P, P, P, P, P, i64,
+                                             i32, P, P, P, P, P, P, ctypes.POINTER(ep_handle_t),
+                                             P]
     rhp = ctypes.POINTER(ep_ranked_handle_t)
     L.ep_ranked_capacity_rows.argtypes = [cfgp, ctypes.POINTER(i64)]
     L.ep_dispatch_ranked.argtypes = [cfgp, ctypes.c_int, P, P, P, P, P, S, i64, i64, P, P, P, P,
@@ -104,7 +107,7 @@ def lib() -> ctypes.CDLL:
               "ep_workspace_init",
               "ep_dispatch_backward", "ep_combine_backward", "ep_dispatch_fp8_input",
               "ep_ranked_capacity_rows", "ep_dispatch_ranked", "ep_expand", "ep_combine_ranked",
-              "ep_hbm_probe", "ep_time_next_kernel"):
+              "ep_hbm_probe", "ep_time_next_kernel", "ep_layout_dispatch_noalloc"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -276,6 +279,42 @@ def ep_layout_dispatch(cfg, recv_dtype, x, topk_idx, topk_weights, num_tokens_pe
         _ptr(row_src, torch.int32, (cap,), "row_src"),
         _ptr(status, torch.int32, (1,), "status"), ctypes.byref(handle), _stream(stream))
     _check(st, "ep_layout_dispatch")
+    return handle
+
+
+NOALLOC_SCRATCH_BYTES = 2 * 1024 * 1024
+
+
+def ep_layout_dispatch_noalloc(cfg, recv_dtype, x, topk_idx, topk_weights, num_tokens_per_rank,
+                               num_tokens_per_expert, is_token_in_rank, expert_offsets,
+                               rank_offsets, capacity, recv_x, recv_scales, recv_weights,
+                               tok_slot_row, row_src, status, stream=None,
+                               zero_padding: bool = True) -> ep_handle_t:
+    """Layout and dispatch with no workspace argument and no allocation (the
+    library's own per-GPU scratch holds the layout's workspace)."""
+    import torch
+
+    T, H, k, E, R = cfg.num_tokens, cfg.hidden, cfg.num_topk, cfg.num_experts, cfg.num_ranks
+    cap = int(capacity)
+    fp8 = int(recv_dtype) == EP_DTYPE_FP8_E4M3
+    handle = ep_handle_t()
+    st = lib().ep_layout_dispatch_noalloc(
+        ctypes.byref(cfg), int(recv_dtype), _ptr(x, torch.bfloat16, (T, H), "x"),
+        _ptr(topk_idx, torch.int32, (T, k), "topk_idx"),
+        _ptr(topk_weights, torch.float32, (T, k), "topk_weights"),
+        _ptr(num_tokens_per_rank, torch.int32, (R,), "num_tokens_per_rank"),
+        _ptr(num_tokens_per_expert, torch.int32, (E,), "num_tokens_per_expert"),
+        _ptr(is_token_in_rank, torch.uint8, (T, R), "is_token_in_rank"),
+        _ptr(expert_offsets, torch.int32, (E + 1,), "expert_offsets"),
+        _ptr(rank_offsets, torch.int32, (R + 1,), "rank_offsets"), cap,
+        1 if zero_padding else 0,
+        _ptr(recv_x, torch.uint8 if fp8 else torch.bfloat16, (cap, H), "recv_x"),
+        _ptr(recv_scales, torch.float32, (cap, H // 128), "recv_scales") if fp8 else None,
+        _ptr(recv_weights, torch.float32, (cap,), "recv_weights"),
+        _ptr(tok_slot_row, torch.int32, (T, k), "tok_slot_row"),
+        _ptr(row_src, torch.int32, (cap,), "row_src"),
+        _ptr(status, torch.int32, (1,), "status"), ctypes.byref(handle), _stream(stream))
+    _check(st, "ep_layout_dispatch_noalloc")
     return handle
 
 

@@ -7,6 +7,8 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "ep.h"
 #include "ep_internal.h"
 
@@ -498,3 +500,99 @@ ep_status_t ep_combine_ranked(const ep_ranked_handle_t *ranked, const uint16_t *
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Layout and dispatch without a caller workspace, for callers that cannot
+// allocate: the layout's workspace is the file-scope device array below,
+// one copy per GPU, reached through its address on that GPU.
+// ---------------------------------------------------------------------------
+
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[EP_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's device address on the current GPU.  Taken once per
+// GPU (with that GPU current), when its header is also cleared: the
+// layout's ticket must start at zero, and every layout leaves it at zero.
+ep_status_t scratch_on_current_device(hipStream_t stream, char **out) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return hip_fail(err, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(EP_ERR_HIP, "device %d is beyond the %d this library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *ptr = nullptr;
+    err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return hip_fail(err, "hipGetSymbolAddress(scratch)");
+    err = ep::launch_workspace_init(static_cast<char *>(ptr), stream);
+    if (err != hipSuccess) return hip_fail(err, "scratch header init launch");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = static_cast<char *>(g_scratch_ptr[dev]);
+  return EP_OK;
+}
+
+}  // namespace
+
+extern "C" ep_status_t ep_layout_dispatch_noalloc(
+    const ep_config_t *cfg, ep_dtype_t recv_dtype, const uint16_t *x, const int32_t *topk_idx,
+    const float *topk_weights, int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
+    uint8_t *is_token_in_rank, int32_t *expert_offsets, int32_t *rank_offsets, int64_t capacity,
+    int32_t zero_padding, void *recv_x, float *recv_scales, float *recv_weights,
+    int32_t *tok_slot_row, int32_t *row_src, int32_t *status, ep_handle_t *handle_host,
+    hipStream_t stream) {
+  EP_TRY(check_config(cfg));
+  bool fp8 = false;
+  EP_TRY(check_dtype(cfg, recv_dtype, &fp8));
+  EP_TRY(check_rows("capacity", capacity));
+  const size_t need =
+      ep::workspace_layout(cfg->num_tokens, cfg->num_topk, cfg->num_experts, cfg->num_ranks)
+          .total;
+  if (need > (size_t)EP_NOALLOC_SCRATCH_BYTES)
+    return fail(EP_ERR_INVALID_ARG,
+                "ep_layout_dispatch_noalloc: this configuration's layout workspace needs %zu "
+                "bytes, more than the library's %d-byte scratch",
+                need, EP_NOALLOC_SCRATCH_BYTES);
+  const bool empty = cfg->num_tokens == 0;
+  if ((!empty && (x == nullptr || topk_idx == nullptr || is_token_in_rank == nullptr ||
+                  tok_slot_row == nullptr)) ||
+      num_tokens_per_rank == nullptr || num_tokens_per_expert == nullptr ||
+      expert_offsets == nullptr || rank_offsets == nullptr || status == nullptr ||
+      (capacity > 0 && (recv_x == nullptr || row_src == nullptr)) ||
+      (fp8 && capacity > 0 && recv_scales == nullptr))
+    return fail(EP_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(x) || !aligned16(recv_x))
+    return fail(EP_ERR_INVALID_ARG, "x and recv_x must be 16-byte aligned");
+  char *ws = nullptr;
+  EP_TRY(scratch_on_current_device(stream, &ws));
+  const ep::Dims d = dims_of(cfg);
+  hipError_t err;
+  if (cfg->num_tokens <= EP_LAYOUT_DISPATCH_MAX_TOKENS) {
+    err = ep::launch_layout_dispatch(d, fp8, zero_padding != 0, x, topk_idx, topk_weights,
+                                     num_tokens_per_rank, num_tokens_per_expert,
+                                     is_token_in_rank, expert_offsets, rank_offsets, ws, capacity,
+                                     recv_x, recv_scales, recv_weights, tok_slot_row, row_src,
+                                     status, stream);
+  } else {
+    err = ep::launch_layout(d, topk_idx, num_tokens_per_rank, num_tokens_per_expert,
+                            is_token_in_rank, expert_offsets, rank_offsets, ws, status, stream);
+    if (err == hipSuccess)
+      err = ep::launch_dispatch(d, fp8, zero_padding != 0, x, topk_idx, topk_weights,
+                                expert_offsets, ws, capacity, recv_x, recv_scales, recv_weights,
+                                tok_slot_row, row_src, status, stream);
+  }
+  if (err != hipSuccess) return hip_fail(err, "layout-dispatch launch");
+  if (handle_host != nullptr) {
+    handle_host->config = *cfg;
+    handle_host->capacity = capacity;
+    handle_host->tok_slot_row = tok_slot_row;
+    handle_host->row_src = row_src;
+    handle_host->expert_offsets = expert_offsets;
+  }
+  return EP_OK;
+}

@@ -281,6 +281,38 @@ ep_status_t ep_layout_dispatch(const ep_config_t *cfg, ep_dtype_t recv_dtype, co
                                int32_t *status, ep_handle_t *handle_host, hipStream_t stream);
 
 /*
+ * Layout and dispatch with no workspace argument and no allocation, for
+ * callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, and harnesses that forbid allocation.
+ *
+ * It writes what ep_get_dispatch_layout followed by ep_dispatch (one launch,
+ * as ep_layout_dispatch, for at most EP_LAYOUT_DISPATCH_MAX_TOKENS tokens)
+ * writes to the caller's arrays, bit for bit; the arguments are those of
+ * ep_layout_dispatch without the workspace.  The layout's workspace is a
+ * library-owned device array of EP_NOALLOC_SCRATCH_BYTES, one per GPU, kept
+ * until the process ends: a configuration whose workspace
+ * (ep_layout_workspace_bytes) is larger is rejected with EP_ERR_INVALID_ARG
+ * and nothing enqueued.  The first call on a GPU takes the array's address
+ * on that GPU and enqueues a clear of its header on `stream`.  Every call on
+ * one GPU shares that array, so calls that overlap on one GPU (several
+ * streams or threads at once) race and give wrong results; the caller
+ * orders them.  The workspace is not visible to the caller, so the
+ * non-expanded calls (which read it) need ep_get_dispatch_layout instead;
+ * combine and both backward calls take this call's handle as usual.
+ */
+#define EP_NOALLOC_SCRATCH_BYTES (2 * 1024 * 1024)
+
+ep_status_t ep_layout_dispatch_noalloc(const ep_config_t *cfg, ep_dtype_t recv_dtype,
+                                       const uint16_t *x, const int32_t *topk_idx,
+                                       const float *topk_weights, int32_t *num_tokens_per_rank,
+                                       int32_t *num_tokens_per_expert, uint8_t *is_token_in_rank,
+                                       int32_t *expert_offsets, int32_t *rank_offsets,
+                                       int64_t capacity, int32_t zero_padding, void *recv_x,
+                                       float *recv_scales, float *recv_weights,
+                                       int32_t *tok_slot_row, int32_t *row_src, int32_t *status,
+                                       ep_handle_t *handle_host, hipStream_t stream);
+
+/*
  * Dispatch of rows that arrive already quantised ("Deep Dive - DeepEP",
  * "Dispatch: layout, move, and epilogue": hidden states are BF16 or FP8
  * values plus scale factors; "Precision: FP8 on the wire, BF16 for the
