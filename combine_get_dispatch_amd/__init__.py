@@ -254,7 +254,7 @@ def ep_layout_dispatch(cfg, recv_dtype, x, topk_idx, topk_weights, num_tokens_pe
                        num_tokens_per_expert, is_token_in_rank, expert_offsets, rank_offsets,
                        workspace, capacity, recv_x, recv_scales, recv_weights, tok_slot_row,
                        row_src, status, stream=None, zero_padding: bool = True) -> ep_handle_t:
-    """Layout and dispatch in one launch (at most 256 tokens)."""
+    """Layout and dispatch in one call (one launch up to 256 tokens)."""
     import torch
 
     T, H, k, E, R = cfg.num_tokens, cfg.hidden, cfg.num_topk, cfg.num_experts, cfg.num_ranks
@@ -632,8 +632,9 @@ class EpBuffers:
         return self.handle
 
     def layout_dispatch(self, x, topk_idx, topk_weights, stream=None):
-        """Layout and dispatch in one launch (at most 256 tokens); leaves the
-        same buffers, workspace and handle as layout() then dispatch()."""
+        """Layout and dispatch in one call (ep_layout_dispatch: one launch up
+        to 256 tokens); leaves the same buffers, workspace and handle as
+        layout() then dispatch()."""
         import torch
 
         la = self._layout_args
@@ -651,12 +652,9 @@ class EpBuffers:
         return self.handle
 
     def layout_and_dispatch(self, x, topk_idx, topk_weights, stream=None):
-        """Layout then dispatch: one launch when the batch fits one tile (at
-        most 256 tokens), else the two calls.  The results are the same."""
-        if self.cfg.num_tokens <= LAYOUT_DISPATCH_MAX_TOKENS:
-            return self.layout_dispatch(x, topk_idx, topk_weights, stream=stream)
-        self.layout(topk_idx, stream=stream)
-        return self.dispatch(x, topk_idx, topk_weights, stream=stream)
+        """Layout then dispatch through ep_layout_dispatch (the same results
+        as the two calls)."""
+        return self.layout_dispatch(x, topk_idx, topk_weights, stream=stream)
 
     def dispatch_fp8_input(self, x_codes, x_scales, topk_idx, topk_weights, stream=None):
         if not self.fp8:

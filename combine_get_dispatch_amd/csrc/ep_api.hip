@@ -247,9 +247,6 @@ ep_status_t ep_layout_dispatch(const ep_config_t *cfg, ep_dtype_t recv_dtype, co
                                float *recv_weights, int32_t *tok_slot_row, int32_t *row_src,
                                int32_t *status, ep_handle_t *handle_host, hipStream_t stream) {
   EP_TRY(check_config(cfg));
-  if (cfg->num_tokens > EP_LAYOUT_DISPATCH_MAX_TOKENS)
-    return fail(EP_ERR_INVALID_ARG, "ep_layout_dispatch takes at most %d tokens (got %d)",
-                EP_LAYOUT_DISPATCH_MAX_TOKENS, cfg->num_tokens);
   bool fp8 = false;
   EP_TRY(check_dtype(cfg, recv_dtype, &fp8));
   EP_TRY(check_rows("capacity", capacity));
@@ -570,22 +567,10 @@ extern "C" ep_status_t ep_layout_dispatch_noalloc(
     return fail(EP_ERR_INVALID_ARG, "x and recv_x must be 16-byte aligned");
   char *ws = nullptr;
   EP_TRY(scratch_on_current_device(stream, &ws));
-  const ep::Dims d = dims_of(cfg);
-  hipError_t err;
-  if (cfg->num_tokens <= EP_LAYOUT_DISPATCH_MAX_TOKENS) {
-    err = ep::launch_layout_dispatch(d, fp8, zero_padding != 0, x, topk_idx, topk_weights,
-                                     num_tokens_per_rank, num_tokens_per_expert,
-                                     is_token_in_rank, expert_offsets, rank_offsets, ws, capacity,
-                                     recv_x, recv_scales, recv_weights, tok_slot_row, row_src,
-                                     status, stream);
-  } else {
-    err = ep::launch_layout(d, topk_idx, num_tokens_per_rank, num_tokens_per_expert,
-                            is_token_in_rank, expert_offsets, rank_offsets, ws, status, stream);
-    if (err == hipSuccess)
-      err = ep::launch_dispatch(d, fp8, zero_padding != 0, x, topk_idx, topk_weights,
-                                expert_offsets, ws, capacity, recv_x, recv_scales, recv_weights,
-                                tok_slot_row, row_src, status, stream);
-  }
+  const hipError_t err = ep::launch_layout_dispatch(
+      dims_of(cfg), fp8, zero_padding != 0, x, topk_idx, topk_weights, num_tokens_per_rank,
+      num_tokens_per_expert, is_token_in_rank, expert_offsets, rank_offsets, ws, capacity, recv_x,
+      recv_scales, recv_weights, tok_slot_row, row_src, status, stream);
   if (err != hipSuccess) return hip_fail(err, "layout-dispatch launch");
   if (handle_host != nullptr) {
     handle_host->config = *cfg;

@@ -43,10 +43,11 @@ struct Dims {
   int32_t T, H, k, E, R, A;
 };
 
+// last: the layout is the call's last kernel (for kernel timing).
 hipError_t launch_layout(const Dims &d, const int32_t *topk_idx, int32_t *num_tokens_per_rank,
                          int32_t *num_tokens_per_expert, uint8_t *is_token_in_rank,
                          int32_t *expert_offsets, int32_t *rank_offsets, char *ws,
-                         int32_t *status, hipStream_t stream);
+                         int32_t *status, hipStream_t stream, bool last = true);
 
 hipError_t launch_workspace_init(char *ws, hipStream_t stream);
 
@@ -56,7 +57,8 @@ void time_next_kernel(hipEvent_t start, hipEvent_t stop);
 // Dynamic LDS bytes of a layout workgroup with E experts.
 size_t layout_lds_bytes(int32_t E);
 
-// Layout and dispatch in one launch (T <= kTileTokens).
+// Layout and dispatch: one launch up to kTileTokens tokens, else the layout
+// launch and the dispatch launch.
 hipError_t launch_layout_dispatch(const Dims &d, bool fp8, bool zero_padding,
                                   const uint16_t *x, const int32_t *topk_idx,
                                   const float *topk_weights,

@@ -1646,7 +1646,7 @@ WorkspaceLayout workspace_layout(int32_t T, int32_t k, int32_t E, int32_t R) {
 hipError_t launch_layout(const Dims &d, const int32_t *topk_idx, int32_t *num_tokens_per_rank,
                          int32_t *num_tokens_per_expert, uint8_t *is_token_in_rank,
                          int32_t *expert_offsets, int32_t *rank_offsets, char *ws,
-                         int32_t *status, hipStream_t stream) {
+                         int32_t *status, hipStream_t stream, bool last) {
   const WorkspaceLayout w = workspace_layout(d.T, d.k, d.E, d.R);
   const size_t lds = layout_lds_bytes(d.E);
   auto pick = [&](auto k8, auto k16, auto k32) { return d.k <= 8 ? k8 : (d.k <= 16 ? k16 : k32); };
@@ -1655,7 +1655,7 @@ hipError_t launch_layout(const Dims &d, const int32_t *topk_idx, int32_t *num_to
                                 : pick(layout_kernel<8, 1>, layout_kernel<16, 1>, layout_kernel<32, 1>);
   // An empty batch still needs one workgroup to write zero counts and offsets.
   const unsigned grid = w.ntiles > 0 ? (unsigned)w.ntiles : 1u;
-  launch_kernel(true, kernel, dim3(grid), dim3(kBlock), (uint32_t)lds, stream, topk_idx, d,
+  launch_kernel(last, kernel, dim3(grid), dim3(kBlock), (uint32_t)lds, stream, topk_idx, d,
                 w.ntiles, d.E / d.R, reinterpret_cast<int32_t *>(ws + w.tile_cnt),
                 reinterpret_cast<int32_t *>(ws + w.tile_rank_cnt),
                 reinterpret_cast<int32_t *>(ws + w.slot_rank), is_token_in_rank,
@@ -1716,6 +1716,16 @@ hipError_t launch_layout_dispatch(const Dims &d, bool fp8, bool zero_padding,
                                   int32_t *rank_offsets, char *ws, int64_t capacity, void *recv_x,
                                   float *recv_scales, float *recv_weights, int32_t *tok_slot_row,
                                   int32_t *row_src, int32_t *status, hipStream_t stream) {
+  if (d.T > kTileTokens) {
+    // Several tiles: the layout launch, then the dispatch launch.
+    hipError_t err = launch_layout(d, topk_idx, num_tokens_per_rank, num_tokens_per_expert,
+                                   is_token_in_rank, expert_offsets, rank_offsets, ws, status,
+                                   stream, false);
+    if (err != hipSuccess) return err;
+    return launch_dispatch(d, fp8, zero_padding, x, topk_idx, topk_weights, expert_offsets, ws,
+                           capacity, recv_x, recv_scales, recv_weights, tok_slot_row, row_src,
+                           status, stream);
+  }
   const WorkspaceLayout w = workspace_layout(d.T, d.k, d.E, d.R);
   const int32_t nchunks = (d.H + kChunkCols - 1) / kChunkCols;
   const int64_t items = (int64_t)d.T * nchunks;

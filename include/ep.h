@@ -14,7 +14,7 @@
  *                           once, fixed-order fp32 sum, bf16 result
  *
  * Further calls on the same data: ep_layout_dispatch (the first two in one
- * launch for batches of at most 256 tokens), ep_dispatch_fp8_input
+ * call, one launch for batches of at most 256 tokens), ep_dispatch_fp8_input
  * (pre-quantised rows), ep_dispatch_backward and ep_combine_backward, and
  * the non-expanded path ep_dispatch_ranked -> ep_expand ->
  * ep_combine_ranked.  A measurement aid is declared apart, in ep_probe.h.
@@ -83,7 +83,7 @@ typedef enum ep_dtype {
 #define EP_MAX_EXPERTS 1024
 #define EP_MAX_TOPK 32
 #define EP_MAX_RANKS 64
-#define EP_LAYOUT_DISPATCH_MAX_TOKENS 256 /* batch bound of ep_layout_dispatch */
+#define EP_LAYOUT_DISPATCH_MAX_TOKENS 256 /* ep_layout_dispatch's one-launch bound */
 
 typedef struct ep_config {
   int32_t num_tokens;       /* T >= 0 */
@@ -257,38 +257,39 @@ ep_status_t ep_dispatch(const ep_config_t *cfg, ep_dtype_t recv_dtype, const uin
                         ep_handle_t *handle_host, hipStream_t stream);
 
 /*
- * Layout and dispatch in one launch, for a batch of at most
- * EP_LAYOUT_DISPATCH_MAX_TOKENS tokens (count, prefix sum and scatter in a
- * single pass: "GPU microarchitecture: DeepEP first principles", "6.1
- * Layout Metadata"; "Deep Dive - DeepEP", "Dispatch: layout, move, and
- * epilogue").  It writes exactly what ep_get_dispatch_layout followed by
- * ep_dispatch writes, bit for bit: every layout output, the workspace (so
- * combine, the non-expanded path and backward work after it unchanged), the
- * receive rows and the handle.  It saves the small-batch path one launch
- * and a round trip through the workspace.  The arguments are those two
- * calls' arguments; there is no synchronising row count.
+ * Layout and dispatch in one call (count, prefix sum and scatter: "GPU
+ * microarchitecture: DeepEP first principles", "6.1 Layout Metadata"; "Deep
+ * Dive - DeepEP", "Dispatch: layout, move, and epilogue").  It writes
+ * exactly what ep_get_dispatch_layout followed by ep_dispatch writes, bit
+ * for bit: every layout output, the workspace (so combine, the non-expanded
+ * path and backward work after it unchanged), the receive rows and the
+ * handle.  The arguments are those two calls' arguments; there is no
+ * synchronising row count.
+ *   - At most EP_LAYOUT_DISPATCH_MAX_TOKENS tokens: one launch, which saves
+ *     the small-batch path a launch and a round trip through the workspace.
+ *   - More tokens: the two calls' launches, one after the other.
  *
- * Returns EP_ERR_INVALID_ARG (nothing enqueued) when num_tokens exceeds
- * EP_LAYOUT_DISPATCH_MAX_TOKENS or for any argument the two calls reject.
+ * Returns EP_ERR_INVALID_ARG (nothing enqueued) for any argument the two
+ * calls reject.
  */
 ep_status_t ep_layout_dispatch(const ep_config_t *cfg, ep_dtype_t recv_dtype, const uint16_t *x,
                                const int32_t *topk_idx, const float *topk_weights,
                                int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
                                uint8_t *is_token_in_rank, int32_t *expert_offsets,
                                int32_t *rank_offsets, void *workspace, size_t workspace_bytes,
-                               int64_t capacity, int32_t zero_padding, void *recv_x, float *recv_scales,
-                               float *recv_weights, int32_t *tok_slot_row, int32_t *row_src,
-                               int32_t *status, ep_handle_t *handle_host, hipStream_t stream);
+                               int64_t capacity, int32_t zero_padding, void *recv_x,
+                               float *recv_scales, float *recv_weights, int32_t *tok_slot_row,
+                               int32_t *row_src, int32_t *status, ep_handle_t *handle_host,
+                               hipStream_t stream);
 
 /*
  * Layout and dispatch with no workspace argument and no allocation, for
  * callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, and harnesses that forbid allocation.
  *
- * It writes what ep_get_dispatch_layout followed by ep_dispatch (one launch,
- * as ep_layout_dispatch, for at most EP_LAYOUT_DISPATCH_MAX_TOKENS tokens)
- * writes to the caller's arrays, bit for bit; the arguments are those of
- * ep_layout_dispatch without the workspace.  The layout's workspace is a
+ * It is ep_layout_dispatch without the workspace arguments: it writes what
+ * ep_get_dispatch_layout followed by ep_dispatch writes to the caller's
+ * arrays, bit for bit.  The layout's workspace is a
  * library-owned device array of EP_NOALLOC_SCRATCH_BYTES, one per GPU, kept
  * until the process ends: a configuration whose workspace
  * (ep_layout_workspace_bytes) is larger is rejected with EP_ERR_INVALID_ARG

@@ -126,16 +126,20 @@ def test_probe_rejects_bad_arguments_before_launch():
         assert L.ep_last_error().decode().startswith("probe")
 
 
-def test_layout_dispatch_rejects_large_batches_before_launch():
-    """ep_layout_dispatch takes one tile of tokens at most; more is an
-    argument error returned before anything is enqueued."""
+def test_layout_dispatch_rejects_bad_arguments_before_launch():
+    """ep_layout_dispatch takes any batch size; a bad argument is rejected
+    before anything is enqueued, on either side of the one-launch bound."""
     L = ep.lib()
-    cfg = ep.ep_config_t(257, 256, 8, 256, 8, 1)
     P = ctypes.c_void_p(256)
-    st = L.ep_layout_dispatch(ctypes.byref(cfg), ep.EP_DTYPE_BF16, P, P, P, P, P, P, P, P, P,
-                              1 << 20, 257 * 8, 1, P, P, P, P, P, P, None, None)
-    assert st == ep.EP_ERR_INVALID_ARG
-    assert "at most 256" in L.ep_last_error().decode()
+    for T in (256, 257, 4096):
+        cfg = ep.ep_config_t(T, 256, 8, 256, 8, 1)
+        st = L.ep_layout_dispatch(ctypes.byref(cfg), ep.EP_DTYPE_BF16, P, P, P, P, P, P, P, P, P,
+                                  16, T * 8, 1, P, P, P, P, P, P, None, None)
+        assert st == ep.EP_ERR_INVALID_ARG and "workspace" in L.ep_last_error().decode()
+        st = L.ep_layout_dispatch(ctypes.byref(cfg), ep.EP_DTYPE_BF16, ctypes.c_void_p(264), P,
+                                  P, P, P, P, P, P, P, 1 << 24, T * 8, 1, P, P, P, P, P, P,
+                                  None, None)
+        assert st == ep.EP_ERR_INVALID_ARG and "aligned" in L.ep_last_error().decode()
 
 
 def test_combine_ranked_rejects_item_overflow_before_launch():

@@ -1,5 +1,6 @@
-"""ep_layout_dispatch (layout and dispatch in one launch, at most 256
-tokens) against the two-call path and the oracle.
+"""ep_layout_dispatch (layout and dispatch in one call: one launch up to 256
+tokens, the two calls' launches above) against the two-call path and the
+oracle.
 
 The fused call must leave exactly what ep_get_dispatch_layout followed by
 ep_dispatch leaves: every layout output, every receive row, scale, gate
@@ -28,6 +29,10 @@ CASES = [
     (256, 512, 6, 48, 4, 2, True, False),    # FP8 without gates, padding
     (97, 256, 32, 64, 8, 1, False, True),    # k = 32
     (150, 128, 4, 1024, 64, 1, False, True), # E and R at their limits
+    (257, 256, 4, 32, 4, 1, False, True),    # two tiles: two launches
+    (1000, 1032, 6, 64, 8, 4, False, True),  # ragged tiles, padding, H % 16 == 8
+    (4096, 7168, 8, 256, 8, 1, True, True),  # the Prefill shape
+    (8193, 384, 6, 64, 8, 2, True, False),   # 33 tiles (four-batch scan), FP8, no gates
 ]
 
 OUTPUTS = ("num_tokens_per_rank", "num_tokens_per_expert", "is_token_in_rank",
@@ -162,8 +167,8 @@ def test_layout_dispatch_decode_workload():
 
 @pytest.mark.parametrize("T", [256, 257])
 def test_layout_and_dispatch_picks_either_path(T):
-    """EpBuffers.layout_and_dispatch fuses up to 256 tokens and falls back to
-    the two calls above; both give the oracle's rows."""
+    """EpBuffers.layout_and_dispatch runs one launch up to 256 tokens and the
+    layout and dispatch launches above; both give the oracle's rows."""
     H, k, E, R = 256, 4, 32, 4
     say(f"layout_and_dispatch T={T}")
     rng = np.random.default_rng(T)
