@@ -20,9 +20,12 @@ plain) give the rates this machine's HBM sustains, as context for the roofline.
 
 `value` and `ms_per_step` are the median over K cold steps: before each,
 an untimed read pass over 1 GiB evicts the 256 MB MALL and the L2s, so the
-step reads its inputs from HBM with clean caches.  `kernel_us` and the
-roofline time each call's kernel by its own start and stop events
-(ep_time_next_kernel) over K more cold steps.  Also reported: warm steps
+step reads its inputs from HBM with clean caches.  Each step is timed from
+its first kernel's start to its last kernel's end by the kernels' own
+events (ep_time_next_kernel), the span a kernel trace shows; the same
+steps timed by events enqueued around them (which add the markers' own
+overhead) are reported beside.  `kernel_us` and the roofline time each
+call's kernels the same way over K more cold steps.  Also reported: warm steps
 (back to back, part of x and the routes still in the MALL), and cold steps
 after a write pass (`cold_dirty`, which also pays for writing back the
 scratch's dirty lines).
@@ -189,12 +192,13 @@ KERNEL_KEYS = {"layout": "layout_kernel", "dispatch": "dispatch_kernel<true>",
 
 def phase_slices(warmup: int, steps: int) -> dict:
     """Which launches of each step kernel belong to which phase of the
-    default command, in launch order: the warm-up steps, 2K cold steps
-    (whole steps, then per-call timing), 3K warm steps (back to back, per
-    step, per call) and min(K, 30) cold steps after a write pass."""
+    default command, in launch order: the warm-up steps, 3K cold steps
+    (timed by kernel events, by markers, then per call), 3K warm steps
+    (back to back, per step, per call) and min(K, 30) cold steps after a
+    write pass."""
     W, K = warmup, steps
-    return {"warmup": (0, W), "cold": (W, W + 2 * K), "warm": (W + 2 * K, W + 5 * K),
-            "cold_dirty": (W + 5 * K, W + 5 * K + min(K, 30))}
+    return {"warmup": (0, W), "cold": (W, W + 3 * K), "warm": (W + 3 * K, W + 6 * K),
+            "cold_dirty": (W + 6 * K, W + 6 * K + min(K, 30))}
 
 
 def load_trace_cold_us(workload: str, kernel: str):
@@ -235,7 +239,7 @@ def trace_summary(run_dir: str, workload: str, cmd: str, warmup: int, steps: int
     ph = phase_slices(warmup, steps)
     total = ph["cold_dirty"][1]
     lines += ["", f"Step kernels per phase, by launch order (warm-up {warmup} steps, then "
-              f"cold {2 * steps}, warm {3 * steps}, cold after a write pass "
+              f"cold {3 * steps}, warm {3 * steps}, cold after a write pass "
               f"{ph['cold_dirty'][1] - ph['cold_dirty'][0]}; average us):", "",
               "| kernel | cold | warm | cold_dirty |", "|---|---|---|---|"]
     kv = []
@@ -800,28 +804,44 @@ def main():
         elif kind == "write":
             scratch.fill_(i)
 
-    def timed_steps(n, kind):
-        """Per-step microseconds of n steps (events around each step)."""
+    def new_pairs(n, create):
         pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                  for _ in range(n)]
+        if create:  # the events must exist on the device before a kernel records them
+            for a, c in pairs:
+                a.record(stream)
+                c.record(stream)
+            torch.cuda.synchronize()
+        return pairs
+
+    def timed_steps(n, kind, markers=False):
+        """Per-step microseconds of n steps.  By default a step is timed from
+        the start of its first kernel to the end of its last, by the
+        kernels' own events (ep_time_next_kernel); with markers (and for
+        graph replays), by events enqueued before and after the step, which
+        add the markers' own overhead."""
+        markers = markers or args.graph
+        pairs = new_pairs(n, not markers)
         for i, (a, c) in enumerate(pairs):
             evict(kind, i)
-            a.record(stream)
-            step()
-            c.record(stream)
+            if markers:
+                a.record(stream)
+                step()
+                c.record(stream)
+            else:
+                for j, fn in enumerate(fns):
+                    if j == 0:
+                        ep.ep_time_next_kernel(a, c if len(fns) == 1 else None)
+                    elif j == len(fns) - 1:
+                        ep.ep_time_next_kernel(None, c)
+                    fn()
         torch.cuda.synchronize()
         return np.array([a.elapsed_time(c) * 1e3 for a, c in pairs])
 
     def timed_kernels(n, kind):
         """Mean duration (us) of each call's kernel over n steps, timed by
         the kernel's own start and stop events (ep_time_next_kernel)."""
-        ev = {nm: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(n)] for nm in names}
-        for pairs in ev.values():  # creates the events on the device
-            for a, c in pairs:
-                a.record(stream)
-                c.record(stream)
-        torch.cuda.synchronize()
+        ev = {nm: new_pairs(n, True) for nm in names}
         for i in range(n):
             evict(kind, i)
             for nm, fn in zip(names, fns):
@@ -844,6 +864,7 @@ def main():
     ms_per_step = float(np.median(cold_us)) / 1e3
     print(f"bench: {args.steps} cold steps, median {ms_per_step * 1e3:.1f} us/step",
           file=sys.stderr, flush=True)
+    cold_marker_us = timed_steps(args.steps, "read", markers=True)
     per_us = timed_kernels(args.steps, "read")
     b.check_status()
 
@@ -860,8 +881,9 @@ def main():
     dirty_us = timed_steps(min(args.steps, 30), "write")
     b.check_status()
     del scratch
-    step_us = {"cold": dist(cold_us), "warm": dict(dist(warm_us), back_to_back_mean=round(
-        warm_mean_us, 2)), "cold_dirty": dist(dirty_us)}
+    step_us = {"cold": dist(cold_us), "cold_marker_events": dist(cold_marker_us),
+               "warm": dict(dist(warm_us), back_to_back_mean=round(warm_mean_us, 2)),
+               "cold_dirty": dist(dirty_us)}
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20
@@ -965,9 +987,12 @@ def main():
         "pct_of_peak": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
         "tokens_per_s": round(w.num_tokens / step_s, 1),
         "algorithmic_bytes_per_step": by,
-        "timing": ("value and ms_per_step: median of the K cold steps (an untimed read "
-                   "pass over 1 GiB evicts the MALL and L2s before each); kernel_us: each "
-                   "call's kernel timed by its own start/stop events over K more cold steps"),
+        "timing": ("value and ms_per_step: median of K cold steps (an untimed read pass "
+                   "over 1 GiB evicts the MALL and L2s before each), each timed from its first "
+                   "kernel's start to its last kernel's end by the kernels' own events; "
+                   "step_us.cold_marker_events times K more with events enqueued around the "
+                   "step (their overhead included); kernel_us: each call timed the same way "
+                   "over K more cold steps"),
         "kernel_us": {n: round(v, 2) for n, v in per_us.items()},
         "kernel_us_warm": {n: round(v, 2) for n, v in per_us_warm.items()},
         "kernel_roofline_frac": {n: round(by[n] / (per_us[n] / 1e6) / 1e9 / PEAK_HBM_GBPS, 4)
