@@ -511,9 +511,11 @@ def ep_time_next_kernel(start, stop):
     """The calling thread's next layout, dispatch or combine kernel records
     the two torch timing events when it starts and ends (include/ep_probe.h);
     start.elapsed_time(stop) is then that kernel's own duration.  The events
-    must already exist on the device (recorded once)."""
-    _check(lib().ep_time_next_kernel(ctypes.c_void_p(start.cuda_event),
-                                     ctypes.c_void_p(stop.cuda_event)), "ep_time_next_kernel")
+    must already exist on the device (recorded once); either may be None."""
+    def handle(ev):
+        return None if ev is None else ctypes.c_void_p(ev.cuda_event)
+
+    _check(lib().ep_time_next_kernel(handle(start), handle(stop)), "ep_time_next_kernel")
 
 
 # --------------------------------------------------------------------------
