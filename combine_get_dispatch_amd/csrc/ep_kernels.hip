@@ -247,8 +247,11 @@ __device__ __forceinline__ int32_t tile_rank(const LayoutLds &L, int E, int wave
   return __popcll(L.masks[wave * E + e] & ((1ull << lane) - 1ull)) + L.prefix[wave * E + e];
 }
 
-// Per-token outputs: the rank mask and the stable in-tile rank of each
-// selection.
+// Per-token outputs: the rank mask (one byte per rank) and the stable
+// in-tile rank of each selection.  Every LDS read is issued before the first
+// result is used, and each row is written with the widest stores its size
+// and alignment allow (one store per lane covers many slots, where one per
+// slot would make every store instruction touch a cache line per few lanes).
 template <int K>
 __device__ __forceinline__ void token_outputs(const Dims &d, int64_t t, const LayoutLds &L,
                                               const int32_t (&ex)[K], unsigned long long rmask,
@@ -256,22 +259,56 @@ __device__ __forceinline__ void token_outputs(const Dims &d, int64_t t, const La
                                               int32_t *__restrict__ slot_rank) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int R = d.R;
+  const int R = d.R, k = d.k;
+  unsigned long long m[K];
+  int32_t pre[K], rank[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const int32_t e = ex[j] >= 0 ? ex[j] : 0;
+    m[j] = L.masks[wave * d.E + e];
+    pre[j] = L.prefix[wave * d.E + e];
+  }
+#pragma unroll
+  for (int j = 0; j < K; ++j)
+    rank[j] = ex[j] >= 0 ? __popcll(m[j] & ((1ull << lane) - 1ull)) + pre[j] : -1;
+
+  // Four mask bits b0..b3 to the bytes b0, b1, b2, b3 of a word: the
+  // multiplier's shifted copies (0, 7, 14, 21) do not overlap.
+  auto bytes4 = [](unsigned long long bits) {
+    return ((uint32_t)bits & 0xFu) * 0x204081u & 0x01010101u;
+  };
   uint8_t *dst = is_token_in_rank + t * R;
-  if ((R & 3) == 0) {
-    for (int r = 0; r < R; r += 4) {
-      const uint32_t b = (uint32_t)(rmask >> r);
-      *reinterpret_cast<uint32_t *>(dst + r) =
-          (b & 1u) | ((b >> 1) & 1u) << 8 | ((b >> 2) & 1u) << 16 | ((b >> 3) & 1u) << 24;
-    }
+  const uintptr_t base = reinterpret_cast<uintptr_t>(is_token_in_rank);
+  if ((R & 15) == 0 && (base & 15) == 0) {
+    for (int r = 0; r < R; r += 16)
+      *reinterpret_cast<uint4 *>(dst + r) =
+          make_uint4(bytes4(rmask >> r), bytes4(rmask >> (r + 4)), bytes4(rmask >> (r + 8)),
+                     bytes4(rmask >> (r + 12)));
+  } else if ((R & 7) == 0 && (base & 7) == 0) {
+    for (int r = 0; r < R; r += 8)
+      *reinterpret_cast<uint2 *>(dst + r) = make_uint2(bytes4(rmask >> r), bytes4(rmask >> (r + 4)));
+  } else if ((R & 3) == 0) {
+    for (int r = 0; r < R; r += 4) *reinterpret_cast<uint32_t *>(dst + r) = bytes4(rmask >> r);
   } else {
     for (int r = 0; r < R; ++r) dst[r] = (uint8_t)((rmask >> r) & 1ull);
   }
+
+  // The workspace row t * k is 16-byte aligned when k % 4 == 0, 8-byte
+  // aligned when k is even.
+  int32_t *row = slot_rank + t * k;
+  if ((k & 3) == 0) {
 #pragma unroll
-  for (int j = 0; j < K; ++j) {
-    const int32_t e = ex[j];
-    const int32_t rank = e >= 0 ? tile_rank(L, d.E, wave, lane, e) : -1;
-    if (j < d.k) slot_rank[t * d.k + j] = rank;
+    for (int j = 0; j + 3 < K; j += 4)
+      if (j < k)
+        *reinterpret_cast<int4 *>(row + j) = make_int4(rank[j], rank[j + 1], rank[j + 2], rank[j + 3]);
+  } else if ((k & 1) == 0) {
+#pragma unroll
+    for (int j = 0; j + 1 < K; j += 2)
+      if (j < k) *reinterpret_cast<int2 *>(row + j) = make_int2(rank[j], rank[j + 1]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+      if (j < k) row[j] = rank[j];
   }
 }
 
@@ -384,6 +421,57 @@ __device__ __forceinline__ void scan_counts(const Dims &d, int experts_per_rank,
   if (tid <= R) rank_offsets[tid] = L.counts[tid * experts_per_rank];
 }
 
+// Scan phase for at most 256 experts (one per thread): thread tid holds
+// expert tid's count in the batch in cnt and, for tid < R, rank tid's token
+// count in rank_sum.  One barrier (the four waves' totals), then every
+// store.  Rank r's row range starts at the aligned offset of its first
+// expert, e = r * (E / R), and the thread that owns that expert writes it.
+__device__ __forceinline__ void scan_small(const Dims &d, int experts_per_rank,
+                                           const LayoutLds &L, int32_t cnt, int32_t rank_sum,
+                                           int32_t *__restrict__ cnt_ws,
+                                           int32_t *__restrict__ num_tokens_per_expert,
+                                           int32_t *__restrict__ num_tokens_per_rank,
+                                           int32_t *__restrict__ rank_tok_off,
+                                           int32_t *__restrict__ expert_offsets,
+                                           int32_t *__restrict__ rank_offsets) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int E = d.E, R = d.R;
+  const int32_t size = tid < E ? (d.A == 1 ? cnt : (cnt + d.A - 1) / d.A * d.A) : 0;
+  const int32_t incl = wave_inclusive_sum(size);
+  if (lane == kWave - 1) L.wave_total[wave] = incl;
+  int32_t rank_start = 0, rank_total = 0;
+  if (wave == 0) {
+    const int32_t v = lane < R ? rank_sum : 0;
+    rank_total = wave_inclusive_sum(v);
+    rank_start = rank_total - v;
+  }
+  __syncthreads();
+  int32_t base = incl - size, total = 0;
+#pragma unroll
+  for (int w = 0; w < kWavesPerBlock; ++w) {
+    const int32_t wt = L.wave_total[w];
+    base += w < wave ? wt : 0;
+    total += wt;
+  }
+  if (tid < E) {
+    cnt_ws[tid] = cnt;
+    num_tokens_per_expert[tid] = cnt;
+    expert_offsets[tid] = base;
+    if (tid % experts_per_rank == 0) rank_offsets[tid / experts_per_rank] = base;
+  }
+  if (tid == 0) {
+    expert_offsets[E] = total;
+    rank_offsets[R] = total;
+  }
+  if (tid < R) {
+    num_tokens_per_rank[tid] = rank_sum;
+    rank_tok_off[tid] = rank_start;
+  }
+  if (tid == R - 1) rank_tok_off[R] = rank_total;
+}
+
 // Marks the workspace as written by a layout of this configuration.
 __device__ __forceinline__ void write_header(int32_t *__restrict__ header, const Dims &d,
                                              int32_t ntiles) {
@@ -429,16 +517,6 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
   if (has_tile) {
     load_ids<K>(d, t, live, topk_idx, ex);
     count_tile<K>(d, tile, experts_per_rank, L, ex, rmask, rank_ballot_ws, status);
-    // With several tiles the tile's counts are published for the scan.
-    // Every wave releases its own stores at device scope before the
-    // barrier, so the scanning workgroup's acquire sees them without
-    // relying on the barrier to carry one wave's stores into another
-    // wave's release.
-    if (many) {
-      for (int e = tid; e < E; e += kBlock) tile_cnt[(int64_t)tile * E + e] = L.counts[e];
-      for (int r = tid; r < R; r += kBlock) tile_rank_cnt[(int64_t)tile * R + r] = L.rank_cnt[r];
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    }
   } else {
     // An empty batch: one workgroup writes zero counts and offsets.
     for (int e = tid; e < E; e += kBlock) L.counts[e] = 0;
@@ -446,22 +524,39 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
   }
   __syncthreads();
 
-  // Ticket: the workgroup that draws the last one scans.  Each wave has
-  // released its published counts (above); thread 0's release-acquire
-  // increment then orders the workgroup's arrival after them, and the
-  // scanner's acquire makes every tile's counts visible to it.
+  // With several tiles the first wave publishes the tile's counts for the
+  // scan and draws a ticket; the workgroup that draws the last one scans.
+  // The publishing wave issues a device-scope release fence after all of
+  // its count stores and before its (relaxed) ticket increment; the thread
+  // that draws the last ticket issues a device-scope acquire fence after
+  // its increment, before the barrier that tells the rest of its
+  // workgroup.  The increments form one modification order, so each
+  // publisher's release fence synchronises with that acquire fence, and
+  // every tile's counts happen before the scan.  One wave stores all of a
+  // tile's counts, so the release covers stores of its own instruction
+  // stream only, and it is issued once per workgroup.
   if (many) {
-    if (tid == 0)
-      is_last = __hip_atomic_fetch_add(&header[kHeaderTicket], 1, __ATOMIC_ACQ_REL,
-                                       __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1;
+    if (tid < kWave) {
+      for (int e = tid; e < E; e += kWave) tile_cnt[(int64_t)tile * E + e] = L.counts[e];
+      for (int r = tid; r < R; r += kWave) tile_rank_cnt[(int64_t)tile * R + r] = L.rank_cnt[r];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      if (tid == 0) {
+        const bool last = __hip_atomic_fetch_add(&header[kHeaderTicket], 1, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT) ==
+                          (int)gridDim.x - 1;
+        if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        is_last = last;
+      }
+    }
     __syncthreads();
   }
   const bool scans = !many || is_last;
 
   // The scanning workgroup's first kPre batches of tile counts (expert tid,
   // tiles 0..15 in c0, 16..31 in c1, 32..47 in c2, 48..63 in c3) are loaded
-  // here together, so that their latency overlaps the acquire and (with
-  // more batches) the per-token outputs below.
+  // here together.  Each wave issues its own acquire fence before its loads,
+  // so that none of them can be served from a cached copy older than the
+  // scanner's acquire.
   constexpr int kBatch = 16;
   int32_t c0[kBatch], rc0[kBatch], c1[kBatch], rc1[kBatch], c2[kBatch], rc2[kBatch],
       c3[kBatch], rc3[kBatch];
@@ -493,14 +588,16 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
     }
   }
 
-  // Up to two batches of tiles with one expert per thread (Prefill: 16
-  // tiles, Skewed: 32, each of at most 256 experts): the scanner's totals
-  // come from the counts already in registers, and it issues every store
-  // (tile bases, its per-token outputs, the scan's outputs) only after its
-  // scan, so that the scan does not start behind a wait for any of them (see
-  // scan_counts).  With more batches the read-back itself stores between
-  // batches, and the scanner's per-token outputs are better overlapped with
-  // its first loads.
+  // Up to kPre batches of tiles with one expert per thread (at most 256
+  // experts): the scanner's totals come from the counts already in
+  // registers, and it issues every store (tile bases, its per-token
+  // outputs, the scan's outputs) only after its scan, so that the scan does
+  // not start behind a wait for any of them (loads and stores share one
+  // counter on this chip).  With more batches the read-back itself stores
+  // between batches, and the scanner's per-token outputs go out before it.
+  // The other workgroups write their per-token outputs after the ticket:
+  // stores issued before the publishing wave's release would be written
+  // back by it too, and delay the ticket.
   const bool one_batch = many && ntiles <= kPre * kBatch && E <= kBlock;
   if (!scans || !one_batch) {
     if (live) token_outputs<K>(d, t, L, ex, rmask, is_token_in_rank, slot_rank);
@@ -512,7 +609,7 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
   // e = r is its first expert).  Tiles go in batches whose loads are all
   // issued before any store.  A single workgroup already holds its counts
   // and its tile's bases are zero.
-  int32_t rank_sum = 0;
+  int32_t rank_sum = 0, batch_cnt = 0;
   if (one_batch) {
     if (tid < E) {
       int32_t run = 0;
@@ -529,7 +626,7 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
           rank_sum += rc2[b] + rc3[b];
         }
       }
-      L.counts[tid] = run;
+      batch_cnt = run;
     }
   } else if (many) {
     for (int e = tid; e < E; e += kBlock) {
@@ -561,18 +658,20 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
         }
       }
       L.counts[e] = run;
+      if (e == tid) batch_cnt = run;
     }
   } else {
     if (ntiles > 0)
       for (int e = tid; e < E; e += kBlock) tile_cnt[e] = 0;
+    if (tid < E) batch_cnt = L.counts[tid];
     if (tid < R) {
       rank_sum = L.rank_cnt[tid];
       if (ntiles > 0) tile_rank_cnt[tid] = 0;
     }
   }
-  if (one_batch)
-    scan_counts<true>(d, experts_per_rank, L, rank_sum, true, cnt_ws, num_tokens_per_expert,
-                      num_tokens_per_rank, rank_tok_off, expert_offsets, rank_offsets);
+  if (E <= kBlock)
+    scan_small(d, experts_per_rank, L, batch_cnt, rank_sum, cnt_ws, num_tokens_per_expert,
+               num_tokens_per_rank, rank_tok_off, expert_offsets, rank_offsets);
   else
     scan_counts<false>(d, experts_per_rank, L, rank_sum, true, cnt_ws, num_tokens_per_expert,
                        num_tokens_per_rank, rank_tok_off, expert_offsets, rank_offsets);
