@@ -25,11 +25,42 @@ constexpr int32_t kWorkspaceMagic = 0x45504C59;  // "EPLY"
 constexpr int kHeaderInts = 16;
 constexpr int kHeaderTicket = 8;
 
+// A tile row of the workspace: the tile's count per expert, padded with
+// zeros to a multiple of 4, then its token count per rank, padded likewise,
+// so that every 16-byte quad of the row holds expert columns only or rank
+// columns only.  After the layout's scan the same rows hold the tile bases
+// (the counts of the earlier tiles).
+__host__ __device__ constexpr int32_t tile_row_experts(int32_t E) { return (E + 3) & ~3; }
+__host__ __device__ constexpr int32_t tile_row_ints(int32_t E, int32_t R) {
+  return ((E + 3) & ~3) + ((R + 3) & ~3);
+}
+
+// How the scanning workgroup of a layout splits the tile rows: the tiles
+// are cut into S slices of `per` consecutive tiles, and thread (q, s) =
+// (tid % C4, tid / C4) owns column quad q of the tiles of slice s.  S is
+// as small as slices of at most 8 tiles allow (every slice costs the
+// column totals one more LDS read), and at most what the threads cover.
+// With more quads than threads (E + R above 1024) there is one slice and a
+// thread owns quads tid and tid + 256.
+struct TileGrid {
+  int32_t C4, S, per;
+};
+
+__host__ __device__ inline TileGrid tile_grid(int32_t E, int32_t R, int32_t ntiles) {
+  TileGrid g;
+  g.C4 = tile_row_ints(E, R) / 4;
+  g.S = g.C4 <= kBlock ? kBlock / g.C4 : 1;
+  const int32_t want = ntiles > 0 ? (ntiles + 7) / 8 : 1;
+  if (g.S > want) g.S = want;
+  g.per = (ntiles + g.S - 1) / g.S;
+  return g;
+}
+
 // Byte offsets of the workspace sections for one configuration.
 struct WorkspaceLayout {
   int32_t ntiles;
-  size_t tile_cnt;       // int32 [ntiles, E]: tile histogram, then tile base
-  size_t tile_rank_cnt;  // int32 [ntiles, R]: tokens per rank per tile, then tile base
+  size_t tile_cnt;       // int32 [ntiles, tile_row_ints(E, R)]: tile rows (above)
+  size_t tile_rank_cnt;  // the rank columns of the tile rows (same rows, past the experts)
   size_t cnt;            // int32 [E]: unaligned count per expert
   size_t slot_rank;      // int32 [T, k]: rank of (t, j) inside its tile's run of e
   size_t rank_ballot;    // u64 [ntiles, 4 waves, R]: which lanes' tokens have an expert on r

@@ -287,7 +287,7 @@ __device__ __forceinline__ void token_outputs(const Dims &d, int64_t t, const La
   } else if ((R & 7) == 0 && (base & 7) == 0) {
     for (int r = 0; r < R; r += 8)
       *reinterpret_cast<uint2 *>(dst + r) = make_uint2(bytes4(rmask >> r), bytes4(rmask >> (r + 4)));
-  } else if ((R & 3) == 0) {
+  } else if ((R & 3) == 0 && (base & 3) == 0) {
     for (int r = 0; r < R; r += 4) *reinterpret_cast<uint32_t *>(dst + r) = bytes4(rmask >> r);
   } else {
     for (int r = 0; r < R; ++r) dst[r] = (uint8_t)((rmask >> r) & 1ull);
@@ -472,6 +472,83 @@ __device__ __forceinline__ void scan_small(const Dims &d, int experts_per_rank,
   if (tid == R - 1) rank_tok_off[R] = rank_total;
 }
 
+// Scan phase of a multi-tile layout with at most 256 experts, by the first
+// wave alone once st holds the S slices' column totals (rows of C ints, the
+// tile-row layout): lane l takes experts 4l..4l+3 (one column quad, so no
+// barrier is needed) and, for l < R, rank l.  Writes what scan_small writes.
+__device__ __forceinline__ void scan_quads(const Dims &d, int experts_per_rank,
+                                           const int32_t *__restrict__ st, int S, int C,
+                                           int32_t *__restrict__ cnt_ws,
+                                           int32_t *__restrict__ num_tokens_per_expert,
+                                           int32_t *__restrict__ num_tokens_per_rank,
+                                           int32_t *__restrict__ rank_tok_off,
+                                           int32_t *__restrict__ expert_offsets,
+                                           int32_t *__restrict__ rank_offsets) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int E = d.E, R = d.R, Ep = tile_row_experts(E);
+  int32_t cnt[4] = {0, 0, 0, 0};
+  if (4 * lane < Ep) {
+    for (int ss = 0; ss < S; ++ss) {
+      const int4 c4 = *reinterpret_cast<const int4 *>(st + ss * C + 4 * lane);
+      cnt[0] += c4.x;
+      cnt[1] += c4.y;
+      cnt[2] += c4.z;
+      cnt[3] += c4.w;
+    }
+  }
+  int32_t size[4], quad = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    size[i] = d.A == 1 ? cnt[i] : (cnt[i] + d.A - 1) / d.A * d.A;
+    quad += size[i];
+  }
+  const int32_t incl = wave_inclusive_sum(quad);
+  const int32_t total = __builtin_amdgcn_readlane(incl, kWave - 1);
+  // e / experts_per_rank as in count_tile (exact for e < 1024).
+  const uint32_t rank_magic = ((1u << 21) + (uint32_t)experts_per_rank - 1u) /
+                              (uint32_t)experts_per_rank;
+  int32_t off[4];
+  off[0] = incl - quad;
+#pragma unroll
+  for (int i = 1; i < 4; ++i) off[i] = off[i - 1] + size[i - 1];
+  // A lane's four experts go out as one 16-byte store per array where the
+  // array allows it (the workspace always does), so that each store
+  // instruction covers contiguous memory.
+  const int e0 = 4 * lane;
+  auto aligned = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  const bool whole = e0 + 4 <= E;
+  if (whole) *reinterpret_cast<int4 *>(cnt_ws + e0) = make_int4(cnt[0], cnt[1], cnt[2], cnt[3]);
+  if (whole && aligned(num_tokens_per_expert))
+    *reinterpret_cast<int4 *>(num_tokens_per_expert + e0) =
+        make_int4(cnt[0], cnt[1], cnt[2], cnt[3]);
+  if (whole && aligned(expert_offsets))
+    *reinterpret_cast<int4 *>(expert_offsets + e0) = make_int4(off[0], off[1], off[2], off[3]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = e0 + i;
+    if (e < E) {
+      if (!whole) cnt_ws[e] = cnt[i];
+      if (!whole || !aligned(num_tokens_per_expert)) num_tokens_per_expert[e] = cnt[i];
+      if (!whole || !aligned(expert_offsets)) expert_offsets[e] = off[i];
+      const int r = (int)(((uint32_t)e * rank_magic) >> 21);
+      if (r * experts_per_rank == e) rank_offsets[r] = off[i];
+    }
+  }
+  if (lane == 0) {
+    expert_offsets[E] = total;
+    rank_offsets[R] = total;
+  }
+  int32_t rank_sum = 0;
+  if (lane < R)
+    for (int ss = 0; ss < S; ++ss) rank_sum += st[ss * C + Ep + lane];
+  const int32_t rincl = wave_inclusive_sum(rank_sum);
+  if (lane < R) {
+    num_tokens_per_rank[lane] = rank_sum;
+    rank_tok_off[lane] = rincl - rank_sum;
+  }
+  if (lane == R - 1) rank_tok_off[R] = rincl;
+}
+
 // Marks the workspace as written by a layout of this configuration.
 __device__ __forceinline__ void write_header(int32_t *__restrict__ header, const Dims &d,
                                              int32_t ntiles) {
@@ -484,24 +561,96 @@ __device__ __forceinline__ void write_header(int32_t *__restrict__ header, const
   header[0] = kWorkspaceMagic;
 }
 
+// Word 3 of a raw buffer resource on this chip family (32-bit data format,
+// no swizzle): loads past num_records return zero.
+constexpr int32_t kBufferWord3 = 0x00020000;
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int4 add4(int4 a, int4 b) {
+  return make_int4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+
+// Zero tile bases: the row of a batch's only tile.
+__device__ __forceinline__ void zero_tile_row(const Dims &d, int32_t *__restrict__ rows) {
+  const int C4 = tile_row_ints(d.E, d.R) / 4;
+  for (int q = threadIdx.x; q < C4; q += kBlock)
+    reinterpret_cast<int4 *>(rows)[q] = make_int4(0, 0, 0, 0);
+}
+
+// Quad q of this tile's row, from its counts in LDS (zeros in the padding).
+// Both LDS arrays are 16-byte aligned, so a whole quad is one LDS read.
+__device__ __forceinline__ int4 tile_row_quad(const Dims &d, const LayoutLds &L, int q) {
+  const int Ep = tile_row_experts(d.E);
+  const bool expert = 4 * q < Ep;
+  const int32_t *src = expert ? L.counts : L.rank_cnt;
+  const int c = expert ? 4 * q : 4 * q - Ep;
+  const int n = expert ? d.E : d.R;
+  if (c + 4 <= n) return *reinterpret_cast<const int4 *>(src + c);
+  return make_int4(c < n ? src[c] : 0, c + 1 < n ? src[c + 1] : 0, c + 2 < n ? src[c + 2] : 0,
+                   c + 3 < n ? src[c + 3] : 0);
+}
+
+// Quad q of tile row tt, or zero when tt is not below te.  The load itself
+// is unconditional (from a row clamped into [0, te - 1], row 0 if te <= 0),
+// so that a run of these issues every load before the first result is
+// used: a load in a branch of its own gets its result copied, and so
+// waited for, inside that branch.
+__device__ __forceinline__ int4 row_quad_or_zero(const int4 *__restrict__ rows, int C4, int q,
+                                                 int tt, int te) {
+  const int4 v = rows[(int64_t)max(0, min(tt, te - 1)) * C4 + q];
+  return tt < te ? v : make_int4(0, 0, 0, 0);
+}
+
+// Sum of quad q over tiles [tb, te), eight rows in flight at a time.
+__device__ __forceinline__ int4 sum_quad(const int4 *__restrict__ rows, int C4, int q, int tb,
+                                         int te) {
+  int4 acc = make_int4(0, 0, 0, 0);
+  for (int t0 = tb; t0 < te; t0 += 8) {
+    int4 c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = row_quad_or_zero(rows, C4, q, t0 + i, te);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = add4(acc, c[i]);
+  }
+  return acc;
+}
+
+// Quad q of tiles [tb, te) replaced in place by its running sum from run
+// (the exclusive prefix over the tiles), eight rows at a time: every load
+// of a batch is issued before its stores.
+__device__ __forceinline__ void quad_bases(int4 *__restrict__ rows, int C4, int q, int tb, int te,
+                                           int4 run) {
+  for (int t0 = tb; t0 < te; t0 += 8) {
+    int4 c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = row_quad_or_zero(rows, C4, q, t0 + i, te);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (t0 + i < te) rows[(int64_t)(t0 + i) * C4 + q] = run;
+      run = add4(run, c[i]);
+    }
+  }
+}
+
 // K is a compile-time bound on k (k <= K) so that a token's expert ids stay
-// in registers between the marking pass and the ranking pass.  kPre (1 or
-// 2) is the number of 16-tile batches of counts the scanning workgroup
-// prefetches into registers: 2 serves up to 32 tiles without a second
-// round trip, and costs registers and time that 16 tiles do not need.
-template <int K, int kPre>
+// in registers between the marking pass and the ranking pass.  kRegs selects
+// the scanner's read-back: 0 for the per-expert columns (at most 16 tiles of
+// at most 256 experts), otherwise the number of tile-row quads a scanning
+// thread holds in registers (the tiles of its slice; a slice longer than
+// that is read twice).
+template <int K, int kRegs>
 __global__ __launch_bounds__(kBlock) void layout_kernel(
     const int32_t *__restrict__ topk_idx, Dims d, int32_t ntiles, int32_t experts_per_rank,
-    int32_t *__restrict__ tile_cnt, int32_t *__restrict__ tile_rank_cnt,
-    int32_t *__restrict__ slot_rank, uint8_t *__restrict__ is_token_in_rank,
-    int32_t *__restrict__ cnt_ws, int32_t *__restrict__ num_tokens_per_expert,
-    int32_t *__restrict__ num_tokens_per_rank, int32_t *__restrict__ expert_offsets,
-    int32_t *__restrict__ rank_offsets, int32_t *__restrict__ header,
-    unsigned long long *__restrict__ rank_ballot_ws, int32_t *__restrict__ rank_tok_off,
-    int32_t *__restrict__ status) {
-  extern __shared__ unsigned long long dyn_lds[];
-  __shared__ int32_t rank_cnt[EP_MAX_RANKS];
+    int32_t *__restrict__ tile_rows, int32_t *__restrict__ slot_rank,
+    uint8_t *__restrict__ is_token_in_rank, int32_t *__restrict__ cnt_ws,
+    int32_t *__restrict__ num_tokens_per_expert, int32_t *__restrict__ num_tokens_per_rank,
+    int32_t *__restrict__ expert_offsets, int32_t *__restrict__ rank_offsets,
+    int32_t *__restrict__ header, unsigned long long *__restrict__ rank_ballot_ws,
+    int32_t *__restrict__ rank_tok_off, int32_t *__restrict__ status) {
+  extern __shared__ __align__(16) unsigned long long dyn_lds[];
+  __shared__ __align__(16) int32_t rank_cnt[EP_MAX_RANKS];
   __shared__ int32_t wave_total[kWavesPerBlock];
+  __shared__ int4 slice_total[kBlock + EP_MAX_RANKS / 4];
   __shared__ int is_last;
   const LayoutLds L = layout_lds(dyn_lds, d.E, rank_cnt, wave_total);
   const int tid = threadIdx.x;
@@ -513,6 +662,8 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
   const bool live = has_tile && t < d.T;
   unsigned long long rmask = 0ull;
   int32_t ex[K];
+  int4 *rows4 = reinterpret_cast<int4 *>(tile_rows);
+  const TileGrid g = tile_grid(E, R, ntiles);
 
   if (has_tile) {
     load_ids<K>(d, t, live, topk_idx, ex);
@@ -524,21 +675,21 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
   }
   __syncthreads();
 
-  // With several tiles the first wave publishes the tile's counts for the
-  // scan and draws a ticket; the workgroup that draws the last one scans.
-  // The publishing wave issues a device-scope release fence after all of
-  // its count stores and before its (relaxed) ticket increment; the thread
-  // that draws the last ticket issues a device-scope acquire fence after
-  // its increment, before the barrier that tells the rest of its
+  // With several tiles the first wave publishes the tile's row of counts
+  // for the scan and draws a ticket; the workgroup that draws the last one
+  // scans.  The publishing wave issues a device-scope release fence after
+  // all of its row stores and before its (relaxed) ticket increment; the
+  // thread that draws the last ticket issues a device-scope acquire fence
+  // after its increment, before the barrier that tells the rest of its
   // workgroup.  The increments form one modification order, so each
   // publisher's release fence synchronises with that acquire fence, and
-  // every tile's counts happen before the scan.  One wave stores all of a
-  // tile's counts, so the release covers stores of its own instruction
-  // stream only, and it is issued once per workgroup.
+  // every tile's counts happen before the scan.  One wave stores the whole
+  // row, so the release covers stores of its own instruction stream only,
+  // and it is issued once per workgroup.
   if (many) {
     if (tid < kWave) {
-      for (int e = tid; e < E; e += kWave) tile_cnt[(int64_t)tile * E + e] = L.counts[e];
-      for (int r = tid; r < R; r += kWave) tile_rank_cnt[(int64_t)tile * R + r] = L.rank_cnt[r];
+      for (int q = tid; q < g.C4; q += kWave)
+        rows4[(int64_t)tile * g.C4 + q] = tile_row_quad(d, L, q);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       if (tid == 0) {
         const bool last = __hip_atomic_fetch_add(&header[kHeaderTicket], 1, __ATOMIC_RELAXED,
@@ -552,141 +703,163 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
   }
   const bool scans = !many || is_last;
 
-  // The scanning workgroup's first kPre batches of tile counts (expert tid,
-  // tiles 0..15 in c0, 16..31 in c1, 32..47 in c2, 48..63 in c3) are loaded
-  // here together.  Each wave issues its own acquire fence before its loads,
-  // so that none of them can be served from a cached copy older than the
+  // The scanner reads the tile rows back in one of two ways.  Up to
+  // kColumnTiles tiles of at most 256 experts (the kRegs = 0 kernel),
+  // thread e holds its expert's
+  // column (and thread r < R its rank's) in registers, one word per tile:
+  // the totals need no exchange between threads.  Otherwise it reads them
+  // by column quads, 16 bytes per load: thread (q, s) takes quad q of the
+  // tiles of slice s (see TileGrid), and holds them in registers when the
+  // slice fits.  Each wave issues its own acquire fence before its loads, so
+  // that none of them can be served from a cached copy older than the
   // scanner's acquire.
-  constexpr int kBatch = 16;
-  int32_t c0[kBatch], rc0[kBatch], c1[kBatch], rc1[kBatch], c2[kBatch], rc2[kBatch],
-      c3[kBatch], rc3[kBatch];
+  constexpr int kColumnTiles = 16;
+  const int Ep = tile_row_experts(E), C = 4 * g.C4;
+  constexpr bool kColumns = kRegs == 0;
+  const bool by_column = kColumns && many;
+  int32_t col[kColumnTiles], rcol[kColumnTiles];
 #pragma unroll
-  for (int b = 0; b < kBatch; ++b)
-    c0[b] = rc0[b] = c1[b] = rc1[b] = c2[b] = rc2[b] = c3[b] = rc3[b] = 0;
+  for (int b = 0; b < kColumnTiles; ++b) col[b] = rcol[b] = 0;
+  const bool wide = g.C4 > kBlock;
+  const int q0 = wide ? tid : tid % g.C4;
+  const int s = wide ? 0 : tid / g.C4;
+  const bool owner = s < g.S;
+  const int tb = s * g.per;
+  const int te = min(ntiles, tb + g.per);
+  const bool in_regs = !kColumns && !wide && g.per <= kRegs;
+  constexpr int kQuads = kColumns ? 1 : kRegs;
+  int4 v[kQuads];
+#pragma unroll
+  for (int i = 0; i < kQuads; ++i) v[i] = make_int4(0, 0, 0, 0);
   if (many && scans) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    if (tid < E) {
+    if (by_column) {
+      if (tid < E) {
 #pragma unroll
-      for (int b = 0; b < kBatch; ++b) {
-        if (b < ntiles) {
-          c0[b] = tile_cnt[(int64_t)b * E + tid];
-          if (tid < R) rc0[b] = tile_rank_cnt[(int64_t)b * R + tid];
+        for (int b = 0; b < kColumnTiles; ++b) {
+          if (b < ntiles) {
+            col[b] = tile_rows[(int64_t)b * C + tid];
+            if (tid < R) rcol[b] = tile_rows[(int64_t)b * C + Ep + tid];
+          }
         }
-        if (kPre > 1 && kBatch + b < ntiles) {
-          c1[b] = tile_cnt[(int64_t)(kBatch + b) * E + tid];
-          if (tid < R) rc1[b] = tile_rank_cnt[(int64_t)(kBatch + b) * R + tid];
-        }
-        if (kPre > 2 && 2 * kBatch + b < ntiles) {
-          c2[b] = tile_cnt[(int64_t)(2 * kBatch + b) * E + tid];
-          if (tid < R) rc2[b] = tile_rank_cnt[(int64_t)(2 * kBatch + b) * R + tid];
-        }
-        if (kPre > 2 && 3 * kBatch + b < ntiles) {
-          c3[b] = tile_cnt[(int64_t)(3 * kBatch + b) * E + tid];
-          if (tid < R) rc3[b] = tile_rank_cnt[(int64_t)(3 * kBatch + b) * R + tid];
-        }
+      }
+    } else if (in_regs) {
+      // Buffer loads, whose hardware range check returns zeros for an
+      // offset at or past the end: a row outside the thread's slice is
+      // given that offset, so every load is issued unconditionally and none
+      // waits inside a branch of its own.  Here ntiles <= 24 * 256, so the
+      // rows' bytes fit the 32-bit range.
+      const uint32_t nbytes = (uint32_t)ntiles * (uint32_t)g.C4 * 16u;
+      const __amdgpu_buffer_rsrc_t rsrc =
+          __builtin_amdgcn_make_buffer_rsrc(tile_rows, (short)0, (int)nbytes, kBufferWord3);
+#pragma unroll
+      for (int i = 0; i < kQuads; ++i) {
+        const int tt = tb + i;
+        const uint32_t off =
+            owner && tt < te ? ((uint32_t)tt * (uint32_t)g.C4 + (uint32_t)q0) * 16u : nbytes;
+        const i32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)off, 0, 0);
+        v[i] = make_int4(w.x, w.y, w.z, w.w);
       }
     }
   }
 
-  // Up to kPre batches of tiles with one expert per thread (at most 256
-  // experts): the scanner's totals come from the counts already in
-  // registers, and it issues every store (tile bases, its per-token
-  // outputs, the scan's outputs) only after its scan, so that the scan does
-  // not start behind a wait for any of them (loads and stores share one
-  // counter on this chip).  With more batches the read-back itself stores
-  // between batches, and the scanner's per-token outputs go out before it.
   // The other workgroups write their per-token outputs after the ticket:
   // stores issued before the publishing wave's release would be written
   // back by it too, and delay the ticket.
-  const bool one_batch = many && ntiles <= kPre * kBatch && E <= kBlock;
-  if (!scans || !one_batch) {
+  if (!scans) {
     if (live) token_outputs<K>(d, t, L, ex, rmask, is_token_in_rank, slot_rank);
+    return;
   }
-  if (!scans) return;
 
-  // Per expert: tile histograms -> exclusive tile bases (in place) and the
-  // batch total; thread r < R also sums rank r's tile counts (R <= E, so
-  // e = r is its first expert).  Tiles go in batches whose loads are all
-  // issued before any store.  A single workgroup already holds its counts
-  // and its tile's bases are zero.
+  // Column totals: each owner sums its quads over its slice, the slice
+  // totals meet in LDS, and thread e < E (r < R) adds up column e (rank
+  // column r) over the slices.  A single workgroup already holds its counts.
   int32_t rank_sum = 0, batch_cnt = 0;
-  if (one_batch) {
-    if (tid < E) {
-      int32_t run = 0;
+  int4 base = make_int4(0, 0, 0, 0);
+  if (by_column) {
 #pragma unroll
-      for (int b = 0; b < kBatch; ++b) {
-        run += c0[b];
-        rank_sum += rc0[b];
-        if (kPre > 1) {
-          run += c1[b];
-          rank_sum += rc1[b];
-        }
-        if (kPre > 2) {
-          run += c2[b] + c3[b];
-          rank_sum += rc2[b] + rc3[b];
-        }
-      }
-      batch_cnt = run;
+    for (int b = 0; b < kColumnTiles; ++b) {
+      batch_cnt += col[b];
+      rank_sum += rcol[b];
     }
-  } else if (many) {
-    for (int e = tid; e < E; e += kBlock) {
-      int32_t run = 0;
-      for (int t0 = 0; t0 < ntiles; t0 += kBatch) {
-        int32_t c[kBatch], rc[kBatch];
-        if (e == tid && t0 < kPre * kBatch) {
-#pragma unroll
-          for (int b = 0; b < kBatch; ++b) {
-            c[b] = t0 == 0 ? c0[b] : t0 == kBatch ? c1[b] : t0 == 2 * kBatch ? c2[b] : c3[b];
-            rc[b] = t0 == 0 ? rc0[b] : t0 == kBatch ? rc1[b] : t0 == 2 * kBatch ? rc2[b] : rc3[b];
-          }
-        } else {
-#pragma unroll
-          for (int b = 0; b < kBatch; ++b) {
-            const bool in = t0 + b < ntiles;
-            c[b] = in ? tile_cnt[(int64_t)(t0 + b) * E + e] : 0;
-            rc[b] = (in && e < R) ? tile_rank_cnt[(int64_t)(t0 + b) * R + e] : 0;
-          }
-        }
-#pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
-          if (t0 + b < ntiles) {
-            tile_cnt[(int64_t)(t0 + b) * E + e] = run;
-            if (e < R) tile_rank_cnt[(int64_t)(t0 + b) * R + e] = rank_sum;
-          }
-          run += c[b];
-          rank_sum += rc[b];
-        }
-      }
-      L.counts[e] = run;
-      if (e == tid) batch_cnt = run;
-    }
-  } else {
-    if (ntiles > 0)
-      for (int e = tid; e < E; e += kBlock) tile_cnt[e] = 0;
-    if (tid < E) batch_cnt = L.counts[tid];
-    if (tid < R) {
-      rank_sum = L.rank_cnt[tid];
-      if (ntiles > 0) tile_rank_cnt[tid] = 0;
-    }
-  }
-  if (E <= kBlock)
     scan_small(d, experts_per_rank, L, batch_cnt, rank_sum, cnt_ws, num_tokens_per_expert,
                num_tokens_per_rank, rank_tok_off, expert_offsets, rank_offsets);
-  else
-    scan_counts<false>(d, experts_per_rank, L, rank_sum, true, cnt_ws, num_tokens_per_expert,
-                       num_tokens_per_rank, rank_tok_off, expert_offsets, rank_offsets);
-  if (one_batch && live) token_outputs<K>(d, t, L, ex, rmask, is_token_in_rank, slot_rank);
-  if (one_batch && tid < E) {
-    int32_t run = 0, rank_run = 0;
+  } else if (!kColumns && many) {
+    if (owner) {
+      int4 tot = make_int4(0, 0, 0, 0);
+      if (in_regs) {
 #pragma unroll
-    for (int b = 0; b < kPre * kBatch; ++b) {
-      if (b < ntiles) {
-        tile_cnt[(int64_t)b * E + tid] = run;
-        if (tid < R) tile_rank_cnt[(int64_t)b * R + tid] = rank_run;
+        for (int i = 0; i < kQuads; ++i) tot = add4(tot, v[i]);
+      } else {
+        tot = sum_quad(rows4, g.C4, q0, tb, te);
+        if (wide && q0 + kBlock < g.C4)
+          slice_total[q0 + kBlock] = sum_quad(rows4, g.C4, q0 + kBlock, tb, te);
       }
-      const int q = b / kBatch, i = b % kBatch;
-      run += q == 0 ? c0[i] : q == 1 ? c1[i] : q == 2 ? c2[i] : c3[i];
-      rank_run += q == 0 ? rc0[i] : q == 1 ? rc1[i] : q == 2 ? rc2[i] : rc3[i];
+      slice_total[s * g.C4 + q0] = tot;
+    }
+    __syncthreads();
+    if (owner)
+      for (int ss = 0; ss < s; ++ss) base = add4(base, slice_total[ss * g.C4 + q0]);
+    const int32_t *st = reinterpret_cast<const int32_t *>(slice_total);
+    if (E <= kBlock) {
+      if (tid < kWave)
+        scan_quads(d, experts_per_rank, st, g.S, C, cnt_ws, num_tokens_per_expert,
+                   num_tokens_per_rank, rank_tok_off, expert_offsets, rank_offsets);
+    } else {
+      for (int e = tid; e < E; e += kBlock) {
+        int32_t sum = 0;
+        for (int ss = 0; ss < g.S; ++ss) sum += st[ss * C + e];
+        L.counts[e] = sum;
+      }
+      if (tid < R)
+        for (int ss = 0; ss < g.S; ++ss) rank_sum += st[ss * C + Ep + tid];
+      scan_counts<false>(d, experts_per_rank, L, rank_sum, true, cnt_ws, num_tokens_per_expert,
+                         num_tokens_per_rank, rank_tok_off, expert_offsets, rank_offsets);
+    }
+  } else {
+    if (ntiles > 0) zero_tile_row(d, tile_rows);
+    if (tid < E) batch_cnt = L.counts[tid];
+    if (tid < R) rank_sum = L.rank_cnt[tid];
+    if (E <= kBlock)
+      scan_small(d, experts_per_rank, L, batch_cnt, rank_sum, cnt_ws, num_tokens_per_expert,
+                 num_tokens_per_rank, rank_tok_off, expert_offsets, rank_offsets);
+    else
+      scan_counts<false>(d, experts_per_rank, L, rank_sum, true, cnt_ws, num_tokens_per_expert,
+                         num_tokens_per_rank, rank_tok_off, expert_offsets, rank_offsets);
+  }
+
+  // Every store of the scanner comes after its scan (loads and stores share
+  // one wait counter on this chip, so an earlier store could hold up the
+  // scan's loads): its own per-token outputs, then the tile bases, written
+  // over the counts as each quad's running sum over the tiles from its
+  // slice's base.
+  if (live) token_outputs<K>(d, t, L, ex, rmask, is_token_in_rank, slot_rank);
+  if (by_column) {
+    if (tid < E) {
+      int32_t run = 0, rank_run = 0;
+#pragma unroll
+      for (int b = 0; b < kColumnTiles; ++b) {
+        if (b < ntiles) {
+          tile_rows[(int64_t)b * C + tid] = run;
+          if (tid < R) tile_rows[(int64_t)b * C + Ep + tid] = rank_run;
+        }
+        run += col[b];
+        rank_run += rcol[b];
+      }
+    }
+  } else if (!kColumns && many && owner) {
+    if (in_regs) {
+      int4 run = base;
+#pragma unroll
+      for (int i = 0; i < kQuads; ++i)
+        if (tb + i < te) {
+          rows4[(int64_t)(tb + i) * g.C4 + q0] = run;
+          run = add4(run, v[i]);
+        }
+    } else {
+      quad_bases(rows4, g.C4, q0, tb, te, base);
+      if (wide && q0 + kBlock < g.C4)
+        quad_bases(rows4, g.C4, q0 + kBlock, tb, te, make_int4(0, 0, 0, 0));
     }
   }
   if (tid == 0) {
@@ -735,7 +908,7 @@ __device__ __forceinline__ int32_t selection_row(const Dims &d, int64_t t, int l
       const int32_t rank = slot_rank[s];
       if (rank >= 0) {
         const int64_t r = (int64_t)expert_offsets[e] +
-                          tile_base[(t / kTileTokens) * d.E + e] + rank;
+                          tile_base[(t / kTileTokens) * tile_row_ints(d.E, d.R) + e] + rank;
         if (r >= 0 && r < capacity)
           row = (int32_t)r;
         else
@@ -928,8 +1101,8 @@ template <int K, bool kFp8>
 __global__ __launch_bounds__(kBlock) void layout_dispatch_kernel(
     const int32_t *__restrict__ topk_idx, Dims d, int32_t ntiles, int32_t experts_per_rank,
     int32_t nchunks, const uint16_t *__restrict__ x, const float *__restrict__ topk_weights,
-    int32_t *__restrict__ tile_cnt, int32_t *__restrict__ tile_rank_cnt,
-    int32_t *__restrict__ slot_rank, uint8_t *__restrict__ is_token_in_rank,
+    int32_t *__restrict__ tile_cnt, int32_t *__restrict__ slot_rank,
+    uint8_t *__restrict__ is_token_in_rank,
     int32_t *__restrict__ cnt_ws, int32_t *__restrict__ num_tokens_per_expert,
     int32_t *__restrict__ num_tokens_per_rank, int32_t *__restrict__ expert_offsets,
     int32_t *__restrict__ rank_offsets, int32_t *__restrict__ header,
@@ -937,8 +1110,8 @@ __global__ __launch_bounds__(kBlock) void layout_dispatch_kernel(
     int64_t capacity, void *__restrict__ recv_x, float *__restrict__ recv_scales,
     float *__restrict__ recv_weights, int32_t *__restrict__ tok_slot_row,
     int32_t *__restrict__ row_src, int32_t *__restrict__ status) {
-  extern __shared__ unsigned long long dyn_lds[];
-  __shared__ int32_t rank_cnt[EP_MAX_RANKS];
+  extern __shared__ __align__(16) unsigned long long dyn_lds[];
+  __shared__ __align__(16) int32_t rank_cnt[EP_MAX_RANKS];
   __shared__ int32_t wave_total[kWavesPerBlock];
   const LayoutLds L = layout_lds(dyn_lds, d.E, rank_cnt, wave_total);
   const int tid = threadIdx.x;
@@ -986,10 +1159,7 @@ __global__ __launch_bounds__(kBlock) void layout_dispatch_kernel(
                     rank_offsets);
   if (lead) {
     // One tile: its bases are zero.
-    if (ntiles > 0) {
-      for (int e = tid; e < d.E; e += kBlock) tile_cnt[e] = 0;
-      if (tid < d.R) tile_rank_cnt[tid] = 0;
-    }
+    if (ntiles > 0) zero_tile_row(d, tile_cnt);
     if (tid == 0) write_header(header, d, ntiles);
   }
   if (!has_item) return;
@@ -1271,7 +1441,8 @@ __device__ __forceinline__ int32_t rank_row(const Dims &d, int64_t t, int lane,
     if ((mine >> tl) & 1ull) {
       int32_t pos = __popcll(mine & ((1ull << tl) - 1ull));
       for (int ww = 0; ww < w; ++ww) pos += __popcll(b[(int64_t)ww * d.R]);
-      const int64_t r = (int64_t)rank_tok_off[lane] + tile_rank_base[tile * d.R + lane] + pos;
+      const int64_t r = (int64_t)rank_tok_off[lane] +
+                        tile_rank_base[tile * tile_row_ints(d.E, d.R) + lane] + pos;
       if (r < ranked_capacity)
         row = (int32_t)r;
       else
@@ -1425,7 +1596,8 @@ __global__ __launch_bounds__(kBlock) void expand_kernel(
       const int32_t rank = slot_rank[t * d.k + lane];
       const int64_t p = rank < 0 ? -1
                                  : (int64_t)expert_offsets[e] +
-                                       tile_base[(t / kTileTokens) * d.E + e] + rank;
+                                       tile_base[(t / kTileTokens) * tile_row_ints(d.E, d.R) +
+                                                 e] + rank;
       if (p >= 0 && p < capacity) {
         row = (int32_t)p;
         if (batch == 0) {
@@ -1727,9 +1899,8 @@ WorkspaceLayout workspace_layout(int32_t T, int32_t k, int32_t E, int32_t R) {
   w.ntiles = (T + kTileTokens - 1) / kTileTokens;
   size_t off = align256(sizeof(int32_t) * kHeaderInts);
   w.tile_cnt = off;
-  off += align256(sizeof(int32_t) * (size_t)w.ntiles * E);
-  w.tile_rank_cnt = off;
-  off += align256(sizeof(int32_t) * (size_t)w.ntiles * R);
+  w.tile_rank_cnt = off + sizeof(int32_t) * (size_t)tile_row_experts(E);
+  off += align256(sizeof(int32_t) * (size_t)w.ntiles * tile_row_ints(E, R));
   w.cnt = off;
   off += align256(sizeof(int32_t) * (size_t)E);
   w.slot_rank = off;
@@ -1749,14 +1920,20 @@ hipError_t launch_layout(const Dims &d, const int32_t *topk_idx, int32_t *num_to
   const WorkspaceLayout w = workspace_layout(d.T, d.k, d.E, d.R);
   const size_t lds = layout_lds_bytes(d.E);
   auto pick = [&](auto k8, auto k16, auto k32) { return d.k <= 8 ? k8 : (d.k <= 16 ? k16 : k32); };
-  auto kernel = w.ntiles > 32   ? pick(layout_kernel<8, 4>, layout_kernel<16, 4>, layout_kernel<32, 4>)
-                : w.ntiles > 16 ? pick(layout_kernel<8, 2>, layout_kernel<16, 2>, layout_kernel<32, 2>)
-                                : pick(layout_kernel<8, 1>, layout_kernel<16, 1>, layout_kernel<32, 1>);
+  // Up to 16 tiles of at most 256 experts: the per-expert column read-back.
+  // Otherwise slices of up to 8 tiles per scanning thread take the smaller
+  // quad kernel, up to 24 the one that holds 24 quads, and longer slices are
+  // read twice.
+  const TileGrid g = tile_grid(d.E, d.R, w.ntiles);
+  auto kernel = w.ntiles <= 16 && d.E <= kBlock
+                    ? pick(layout_kernel<8, 0>, layout_kernel<16, 0>, layout_kernel<32, 0>)
+                : g.C4 <= kBlock && g.per > 8 && g.per <= 24
+                    ? pick(layout_kernel<8, 24>, layout_kernel<16, 24>, layout_kernel<32, 24>)
+                    : pick(layout_kernel<8, 8>, layout_kernel<16, 8>, layout_kernel<32, 8>);
   // An empty batch still needs one workgroup to write zero counts and offsets.
   const unsigned grid = w.ntiles > 0 ? (unsigned)w.ntiles : 1u;
   launch_kernel(last, kernel, dim3(grid), dim3(kBlock), (uint32_t)lds, stream, topk_idx, d,
                 w.ntiles, d.E / d.R, reinterpret_cast<int32_t *>(ws + w.tile_cnt),
-                reinterpret_cast<int32_t *>(ws + w.tile_rank_cnt),
                 reinterpret_cast<int32_t *>(ws + w.slot_rank), is_token_in_rank,
                 reinterpret_cast<int32_t *>(ws + w.cnt), num_tokens_per_expert,
                 num_tokens_per_rank, expert_offsets, rank_offsets, reinterpret_cast<int32_t *>(ws),
@@ -1838,7 +2015,6 @@ hipError_t launch_layout_dispatch(const Dims &d, bool fp8, bool zero_padding,
   launch_kernel(d.A == 1, kernel, dim3(grid), dim3(kBlock), (uint32_t)layout_lds_bytes(d.E),
                 stream, topk_idx, d, w.ntiles, d.E / d.R, nchunks, x, topk_weights,
                 reinterpret_cast<int32_t *>(ws + w.tile_cnt),
-                reinterpret_cast<int32_t *>(ws + w.tile_rank_cnt),
                 reinterpret_cast<int32_t *>(ws + w.slot_rank), is_token_in_rank,
                 reinterpret_cast<int32_t *>(ws + w.cnt), num_tokens_per_expert,
                 num_tokens_per_rank, expert_offsets, rank_offsets, reinterpret_cast<int32_t *>(ws),

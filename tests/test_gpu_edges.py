@@ -304,15 +304,21 @@ def test_workspace_reused_across_layouts():
 
 @pytest.mark.parametrize("T,E,k", [(255, 16, 3), (256, 16, 3), (257, 16, 3), (1, 256, 8),
                                    (2049, 256, 8), (1537, 512, 8), (1000, 1024, 4),
-                                   (4096, 64, 4), (4097, 256, 8), (8192, 256, 8),
-                                   (8193, 64, 6), (9000, 128, 12),
-                                   (16384, 64, 20), (16385, 32, 2), (70001, 32, 2)])
+                                   (5000, 1024, 4), (4096, 64, 4), (4096, 256, 8),
+                                   (4097, 256, 8), (6145, 256, 8), (8192, 256, 8),
+                                   (8193, 64, 6), (9000, 128, 12), (16384, 256, 8),
+                                   (16385, 256, 8), (18433, 256, 8), (16384, 64, 20),
+                                   (16385, 32, 2), (70001, 32, 2), (3000, 6, 2), (5000, 6, 2),
+                                   (5000, 250, 5)])
 def test_layout_tile_boundaries(T, E, k):
     """Layout counts 256-token tiles in separate workgroups (one workgroup
     skips the ticket); ranks must carry across tile boundaries.  The
-    scanning workgroup reads tile counts back in batches of 16 tiles, the
-    first two together and held in registers (up to 32 tiles it stores
-    nothing before its scan): one batch, two, more, and their edges, with k
+    scanning workgroup reads the tile rows back per expert column up to 16
+    tiles of at most 256 experts, else by column quads in slices of tiles
+    held in registers (up to 8 or 24 per thread) or read twice (longer
+    slices, or more than 1024 columns).  The cases sit on each side of
+    those limits (16/17 tiles, 24/25 tiles per slice, 64/65/73 tiles), take
+    expert and rank counts that are not multiples of 4 (padded rows), and k
     in each of the kernel's register bounds (8, 16, 32)."""
     rng = np.random.default_rng(T + E)
     R = 8 if E % 8 == 0 else 1
@@ -326,6 +332,35 @@ def test_layout_tile_boundaries(T, E, k):
     assert np.array_equal(dg["tok_slot_row"], do["tok_slot_row"])
     used = int(lo["expert_offsets"][-1])
     assert np.array_equal(dg["row_src"][:used], do["row_src"][:used])
+
+
+@pytest.mark.parametrize("T,E,k", [(4096, 256, 8), (6000, 256, 8), (20000, 64, 6)])
+def test_layout_outputs_at_unaligned_addresses(T, E, k):
+    """The layout writes a token's rank mask, and the scan its per-expert
+    counts and offsets, with 8- or 16-byte stores where the caller's arrays
+    are aligned for them.  Arrays that start one element (one byte for the
+    mask) past an aligned address must get the same values, by the narrow
+    stores."""
+    rng = np.random.default_rng(T + E + 5)
+    R = 8
+    idx = W.random_routes(rng, T, E, k, mask_prob=0.05)
+    lo = oracle.layout(idx, E, R, 1)
+    cfg = ep.ep_config_t(T, 8, k, E, R, 1)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    ntpr = torch.full((R + 1,), -3, **i32)[1:]
+    ntpe = torch.full((E + 1,), -3, **i32)[1:]
+    eoff = torch.full((E + 2,), -3, **i32)[1:]
+    roff = torch.full((R + 2,), -3, **i32)[1:]
+    itir = torch.full((T * R + 1,), 7, dtype=torch.uint8, device="cuda")[1:].view(T, R)
+    ws = torch.empty(ep.ep_layout_workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, **i32)
+    ep.ep_workspace_init(ws)
+    say(f"unaligned layout outputs T={T} E={E} k={k}")
+    ep.ep_get_dispatch_layout(cfg, dev(idx), ntpr, ntpe, itir, eoff, roff, ws, status, sync=True)
+    for key, got in (("num_tokens_per_rank", ntpr), ("num_tokens_per_expert", ntpe),
+                     ("expert_offsets", eoff), ("rank_offsets", roff),
+                     ("is_token_in_rank", itir)):
+        assert np.array_equal(got.cpu().numpy(), lo[key]), key
 
 
 def test_cached_route_replay():
