@@ -286,7 +286,8 @@ __device__ __forceinline__ void token_outputs(const Dims &d, int64_t t, const La
                      bytes4(rmask >> (r + 12)));
   } else if ((R & 7) == 0 && (base & 7) == 0) {
     for (int r = 0; r < R; r += 8)
-      *reinterpret_cast<uint2 *>(dst + r) = make_uint2(bytes4(rmask >> r), bytes4(rmask >> (r + 4)));
+      *reinterpret_cast<uint2 *>(dst + r) =
+          make_uint2(bytes4(rmask >> r), bytes4(rmask >> (r + 4)));
   } else if ((R & 3) == 0 && (base & 3) == 0) {
     for (int r = 0; r < R; r += 4) *reinterpret_cast<uint32_t *>(dst + r) = bytes4(rmask >> r);
   } else {
@@ -300,7 +301,8 @@ __device__ __forceinline__ void token_outputs(const Dims &d, int64_t t, const La
 #pragma unroll
     for (int j = 0; j + 3 < K; j += 4)
       if (j < k)
-        *reinterpret_cast<int4 *>(row + j) = make_int4(rank[j], rank[j + 1], rank[j + 2], rank[j + 3]);
+        *reinterpret_cast<int4 *>(row + j) =
+            make_int4(rank[j], rank[j + 1], rank[j + 2], rank[j + 3]);
   } else if ((k & 1) == 0) {
 #pragma unroll
     for (int j = 0; j + 1 < K; j += 2)
@@ -424,11 +426,14 @@ __device__ __forceinline__ void scan_counts(const Dims &d, int experts_per_rank,
 // Scan phase for at most 256 experts (one per thread): thread tid holds
 // expert tid's count in the batch in cnt and, for tid < R, rank tid's token
 // count in rank_sum.  One barrier (the four waves' totals), then every
-// store.  Rank r's row range starts at the aligned offset of its first
-// expert, e = r * (E / R), and the thread that owns that expert writes it.
+// store (none unless write).  Rank r's row range starts at the aligned
+// offset of its first expert, e = r * (E / R), and the thread that owns that
+// expert writes it.  With kKeep the aligned offsets are also left in
+// L.counts[0..E), visible to the whole workgroup on return.
+template <bool kKeep = false>
 __device__ __forceinline__ void scan_small(const Dims &d, int experts_per_rank,
                                            const LayoutLds &L, int32_t cnt, int32_t rank_sum,
-                                           int32_t *__restrict__ cnt_ws,
+                                           bool write, int32_t *__restrict__ cnt_ws,
                                            int32_t *__restrict__ num_tokens_per_expert,
                                            int32_t *__restrict__ num_tokens_per_rank,
                                            int32_t *__restrict__ rank_tok_off,
@@ -455,6 +460,11 @@ __device__ __forceinline__ void scan_small(const Dims &d, int experts_per_rank,
     base += w < wave ? wt : 0;
     total += wt;
   }
+  if (kKeep) {
+    if (tid < E) L.counts[tid] = base;
+    __syncthreads();
+  }
+  if (!write) return;
   if (tid < E) {
     cnt_ws[tid] = cnt;
     num_tokens_per_expert[tid] = cnt;
@@ -782,8 +792,9 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
       batch_cnt += col[b];
       rank_sum += rcol[b];
     }
-    scan_small(d, experts_per_rank, L, batch_cnt, rank_sum, cnt_ws, num_tokens_per_expert,
-               num_tokens_per_rank, rank_tok_off, expert_offsets, rank_offsets);
+    scan_small(d, experts_per_rank, L, batch_cnt, rank_sum, true, cnt_ws,
+               num_tokens_per_expert, num_tokens_per_rank, rank_tok_off, expert_offsets,
+               rank_offsets);
   } else if (!kColumns && many) {
     if (owner) {
       int4 tot = make_int4(0, 0, 0, 0);
@@ -821,8 +832,9 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
     if (tid < E) batch_cnt = L.counts[tid];
     if (tid < R) rank_sum = L.rank_cnt[tid];
     if (E <= kBlock)
-      scan_small(d, experts_per_rank, L, batch_cnt, rank_sum, cnt_ws, num_tokens_per_expert,
-                 num_tokens_per_rank, rank_tok_off, expert_offsets, rank_offsets);
+      scan_small(d, experts_per_rank, L, batch_cnt, rank_sum, true, cnt_ws,
+                 num_tokens_per_expert, num_tokens_per_rank, rank_tok_off, expert_offsets,
+                 rank_offsets);
     else
       scan_counts<false>(d, experts_per_rank, L, rank_sum, true, cnt_ws, num_tokens_per_expert,
                          num_tokens_per_rank, rank_tok_off, expert_offsets, rank_offsets);
@@ -1154,9 +1166,14 @@ __global__ __launch_bounds__(kBlock) void layout_dispatch_kernel(
                 lead && ntiles > 0 ? rank_ballot_ws : nullptr, lead ? status : nullptr);
   __syncthreads();
   if (lead && live) token_outputs<K>(d, t, L, ex, rmask, is_token_in_rank, slot_rank);
-  scan_counts<true>(d, experts_per_rank, L, tid < d.R ? L.rank_cnt[tid] : 0, lead, cnt_ws,
-                    num_tokens_per_expert, num_tokens_per_rank, rank_tok_off, expert_offsets,
-                    rank_offsets);
+  if (d.E <= kBlock)
+    scan_small<true>(d, experts_per_rank, L, tid < d.E ? L.counts[tid] : 0,
+                     tid < d.R ? L.rank_cnt[tid] : 0, lead, cnt_ws, num_tokens_per_expert,
+                     num_tokens_per_rank, rank_tok_off, expert_offsets, rank_offsets);
+  else
+    scan_counts<true>(d, experts_per_rank, L, tid < d.R ? L.rank_cnt[tid] : 0, lead, cnt_ws,
+                      num_tokens_per_expert, num_tokens_per_rank, rank_tok_off, expert_offsets,
+                      rank_offsets);
   if (lead) {
     // One tile: its bases are zero.
     if (ntiles > 0) zero_tile_row(d, tile_cnt);
