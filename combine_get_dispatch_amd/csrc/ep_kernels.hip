@@ -482,83 +482,6 @@ __device__ __forceinline__ void scan_small(const Dims &d, int experts_per_rank,
   if (tid == R - 1) rank_tok_off[R] = rank_total;
 }
 
-// Scan phase of a multi-tile layout with at most 256 experts, by the first
-// wave alone once st holds the S slices' column totals (rows of C ints, the
-// tile-row layout): lane l takes experts 4l..4l+3 (one column quad, so no
-// barrier is needed) and, for l < R, rank l.  Writes what scan_small writes.
-__device__ __forceinline__ void scan_quads(const Dims &d, int experts_per_rank,
-                                           const int32_t *__restrict__ st, int S, int C,
-                                           int32_t *__restrict__ cnt_ws,
-                                           int32_t *__restrict__ num_tokens_per_expert,
-                                           int32_t *__restrict__ num_tokens_per_rank,
-                                           int32_t *__restrict__ rank_tok_off,
-                                           int32_t *__restrict__ expert_offsets,
-                                           int32_t *__restrict__ rank_offsets) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int E = d.E, R = d.R, Ep = tile_row_experts(E);
-  int32_t cnt[4] = {0, 0, 0, 0};
-  if (4 * lane < Ep) {
-    for (int ss = 0; ss < S; ++ss) {
-      const int4 c4 = *reinterpret_cast<const int4 *>(st + ss * C + 4 * lane);
-      cnt[0] += c4.x;
-      cnt[1] += c4.y;
-      cnt[2] += c4.z;
-      cnt[3] += c4.w;
-    }
-  }
-  int32_t size[4], quad = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    size[i] = d.A == 1 ? cnt[i] : (cnt[i] + d.A - 1) / d.A * d.A;
-    quad += size[i];
-  }
-  const int32_t incl = wave_inclusive_sum(quad);
-  const int32_t total = __builtin_amdgcn_readlane(incl, kWave - 1);
-  // e / experts_per_rank as in count_tile (exact for e < 1024).
-  const uint32_t rank_magic = ((1u << 21) + (uint32_t)experts_per_rank - 1u) /
-                              (uint32_t)experts_per_rank;
-  int32_t off[4];
-  off[0] = incl - quad;
-#pragma unroll
-  for (int i = 1; i < 4; ++i) off[i] = off[i - 1] + size[i - 1];
-  // A lane's four experts go out as one 16-byte store per array where the
-  // array allows it (the workspace always does), so that each store
-  // instruction covers contiguous memory.
-  const int e0 = 4 * lane;
-  auto aligned = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
-  const bool whole = e0 + 4 <= E;
-  if (whole) *reinterpret_cast<int4 *>(cnt_ws + e0) = make_int4(cnt[0], cnt[1], cnt[2], cnt[3]);
-  if (whole && aligned(num_tokens_per_expert))
-    *reinterpret_cast<int4 *>(num_tokens_per_expert + e0) =
-        make_int4(cnt[0], cnt[1], cnt[2], cnt[3]);
-  if (whole && aligned(expert_offsets))
-    *reinterpret_cast<int4 *>(expert_offsets + e0) = make_int4(off[0], off[1], off[2], off[3]);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = e0 + i;
-    if (e < E) {
-      if (!whole) cnt_ws[e] = cnt[i];
-      if (!whole || !aligned(num_tokens_per_expert)) num_tokens_per_expert[e] = cnt[i];
-      if (!whole || !aligned(expert_offsets)) expert_offsets[e] = off[i];
-      const int r = (int)(((uint32_t)e * rank_magic) >> 21);
-      if (r * experts_per_rank == e) rank_offsets[r] = off[i];
-    }
-  }
-  if (lane == 0) {
-    expert_offsets[E] = total;
-    rank_offsets[R] = total;
-  }
-  int32_t rank_sum = 0;
-  if (lane < R)
-    for (int ss = 0; ss < S; ++ss) rank_sum += st[ss * C + Ep + lane];
-  const int32_t rincl = wave_inclusive_sum(rank_sum);
-  if (lane < R) {
-    num_tokens_per_rank[lane] = rank_sum;
-    rank_tok_off[lane] = rincl - rank_sum;
-  }
-  if (lane == R - 1) rank_tok_off[R] = rincl;
-}
-
 // Marks the workspace as written by a layout of this configuration.
 __device__ __forceinline__ void write_header(int32_t *__restrict__ header, const Dims &d,
                                              int32_t ntiles) {
@@ -813,9 +736,13 @@ __global__ __launch_bounds__(kBlock) void layout_kernel(
       for (int ss = 0; ss < s; ++ss) base = add4(base, slice_total[ss * g.C4 + q0]);
     const int32_t *st = reinterpret_cast<const int32_t *>(slice_total);
     if (E <= kBlock) {
-      if (tid < kWave)
-        scan_quads(d, experts_per_rank, st, g.S, C, cnt_ws, num_tokens_per_expert,
-                   num_tokens_per_rank, rank_tok_off, expert_offsets, rank_offsets);
+      if (tid < E)
+        for (int ss = 0; ss < g.S; ++ss) batch_cnt += st[ss * C + tid];
+      if (tid < R)
+        for (int ss = 0; ss < g.S; ++ss) rank_sum += st[ss * C + Ep + tid];
+      scan_small(d, experts_per_rank, L, batch_cnt, rank_sum, true, cnt_ws,
+                 num_tokens_per_expert, num_tokens_per_rank, rank_tok_off, expert_offsets,
+                 rank_offsets);
     } else {
       for (int e = tid; e < E; e += kBlock) {
         int32_t sum = 0;
