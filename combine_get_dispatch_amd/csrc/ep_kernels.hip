@@ -1421,42 +1421,60 @@ __global__ __launch_bounds__(kBlock) void dispatch_ranked_kernel(
   const int64_t t = item / nchunks;
   const int chunk = item - (int)t * nchunks;
   // The payload's loads go first: they overlap the reads that give the
-  // token's rank rows.  FP8 encoding waits until those are issued.
+  // token's rank rows.  FP8 encoding waits until those are issued.  The
+  // first chunk's wave also loads the token's ids, gates and in-tile ranks
+  // here, so that they arrive with the rank rows: its metadata then takes
+  // one more round trip (the expanded rows' segment starts), not three.
   const int64_t H = d.H;
   const int col = chunk * kChunkCols + lane * 16;
   const bool in = col < H;
   Payload16 p = load_payload(x, t, H, col, in);
+  int32_t ej = -1, srank = -1;
+  float gj = 0.0f;
+  if (chunk == 0 && lane < d.k) {
+    ej = topk_idx[t * d.k + lane];
+    srank = slot_rank[t * d.k + lane];
+    if (topk_weights != nullptr) gj = topk_weights[t * d.k + lane];
+  }
   if (!workspace_ok(header, d)) return;
   const int32_t row = rank_row(d, t, lane, rank_ballot, rank_tok_off, tile_rank_base,
                                ranked_capacity, status);
   if (chunk == 0) {
     const int epr = d.E / d.R;
+    // The expanded handle (rows the receiver's expand will fill), as
+    // selection_row gives them: segment start + earlier tiles + in-tile rank.
+    int32_t srow = -1;
+    if (lane < d.k && ej >= 0 && ej < d.E && srank >= 0) {
+      const int64_t r = (int64_t)expert_offsets[ej] +
+                        tile_base[(t / kTileTokens) * tile_row_ints(d.E, d.R) + ej] + srank;
+      if (r >= 0 && r < capacity)
+        srow = (int32_t)r;
+      else
+        flag(status, EP_STATUS_BIT_CAPACITY);
+    }
     if (lane < d.R) {
       tok_rank_row[t * d.R + lane] = row;
       if (row >= 0) ne_src[row] = (int32_t)t;
     }
     // The token's top-k slice for each of its ranks: pairs (r, j) over
-    // lanes.  Every lane runs every round so the shuffle's source lane is
+    // lanes.  Every lane runs every round so the shuffles' source lanes are
     // always active.
     for (int base = 0; base < d.R * d.k; base += kWave) {
       const int pr = base + lane;
       const int r = min(pr / d.k, d.R - 1);
       const int j = pr - (pr / d.k) * d.k;
       const int32_t rr = __shfl(row, r);
+      const int32_t e = __shfl(ej, j);
+      const float g = __shfl(gj, j);
       if (pr >= d.R * d.k || rr < 0) continue;
-      const int32_t e = topk_idx[t * d.k + j];
       const bool local = e >= 0 && e < d.E && e / epr == r;
       ne_topk_idx[(int64_t)rr * d.k + j] = local ? e - r * epr : -1;
       // each valid slot is local to exactly one rank, so its gate is
       // checked once
-      const float gate = (local && topk_weights != nullptr) ? topk_weights[t * d.k + j] : 0.0f;
+      const float gate = (local && topk_weights != nullptr) ? g : 0.0f;
       if (!__builtin_isfinite(gate)) flag(status, EP_STATUS_BIT_NONFINITE);
       if (ne_topk_weights != nullptr) ne_topk_weights[(int64_t)rr * d.k + j] = gate;
     }
-    // The expanded handle (rows the receiver's expand will fill).
-    const int32_t srow = selection_row(d, t, lane, false, topk_idx, topk_weights, expert_offsets,
-                                       tile_base, slot_rank, capacity, nullptr, nullptr, nullptr,
-                                       status);
     if (lane < d.k) tok_slot_row[t * d.k + lane] = srow;
   }
 
