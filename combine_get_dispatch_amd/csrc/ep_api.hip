@@ -113,7 +113,7 @@ const char *ep_status_string(ep_status_t status) {
     case EP_ERR_INVALID_ARG: return "invalid argument";
     case EP_ERR_INVALID_ROUTE: return "invalid route (expert id out of range or repeated)";
     case EP_ERR_CAPACITY: return "receive buffer too small";
-    case EP_ERR_WORKSPACE: return "workspace not written by a layout of this configuration";
+    case EP_ERR_WORKSPACE: return "workspace not written by a layout of this configuration and route";
     case EP_ERR_HIP: return "HIP runtime error";
     case EP_ERR_NONFINITE: return "a hidden value or a valid selection's gate is inf or NaN";
   }
@@ -165,7 +165,7 @@ ep_status_t ep_read_status(const int32_t *status, hipStream_t stream) {
   if (host & EP_STATUS_BIT_CAPACITY)
     return fail(EP_ERR_CAPACITY, "a selection did not fit in the receive rows");
   if (host & EP_STATUS_BIT_WORKSPACE)
-    return fail(EP_ERR_WORKSPACE, "dispatch workspace does not match its configuration");
+    return fail(EP_ERR_WORKSPACE, "dispatch workspace does not match its configuration or route");
   if (host & EP_STATUS_BIT_NONFINITE)
     return fail(EP_ERR_NONFINITE,
                 "a hidden value or the gate of a valid selection is an infinity or NaN");

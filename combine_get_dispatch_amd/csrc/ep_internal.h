@@ -56,13 +56,20 @@ __host__ __device__ inline TileGrid tile_grid(int32_t E, int32_t R, int32_t ntil
   return g;
 }
 
+// A selection's word in the workspace's slot table: its expert id in the
+// high half and its stable rank inside its tile (below 256) in the low half,
+// or -1 for a selection the layout did not count.  The expert lets every
+// later reader check that it was given the layout's own route.
+constexpr int kSlotExpertShift = 16;
+constexpr int32_t kSlotRankMask = 0xFFFF;
+
 // Byte offsets of the workspace sections for one configuration.
 struct WorkspaceLayout {
   int32_t ntiles;
   size_t tile_cnt;       // int32 [ntiles, tile_row_ints(E, R)]: tile rows (above)
   size_t tile_rank_cnt;  // the rank columns of the tile rows (same rows, past the experts)
   size_t cnt;            // int32 [E]: unaligned count per expert
-  size_t slot_rank;      // int32 [T, k]: rank of (t, j) inside its tile's run of e
+  size_t slot_rank;      // int32 [T, k]: (e, rank of (t, j) inside its tile's run of e)
   size_t rank_ballot;    // u64 [ntiles, 4 waves, R]: which lanes' tokens have an expert on r
   size_t rank_tok_off;   // int32 [R + 1]: starts of the ranks' token partitions
   size_t total;

@@ -247,8 +247,8 @@ __device__ __forceinline__ int32_t tile_rank(const LayoutLds &L, int E, int wave
   return __popcll(L.masks[wave * E + e] & ((1ull << lane) - 1ull)) + L.prefix[wave * E + e];
 }
 
-// Per-token outputs: the rank mask (one byte per rank) and the stable
-// in-tile rank of each selection.  Every LDS read is issued before the first
+// Per-token outputs: the rank mask (one byte per rank) and each selection's
+// slot word (its expert and its stable in-tile rank, kSlotExpertShift).  Every LDS read is issued before the first
 // result is used, and each row is written with the widest stores its size
 // and alignment allow (one store per lane covers many slots, where one per
 // slot would make every store instruction touch a cache line per few lanes).
@@ -270,7 +270,9 @@ __device__ __forceinline__ void token_outputs(const Dims &d, int64_t t, const La
   }
 #pragma unroll
   for (int j = 0; j < K; ++j)
-    rank[j] = ex[j] >= 0 ? __popcll(m[j] & ((1ull << lane) - 1ull)) + pre[j] : -1;
+    rank[j] = ex[j] >= 0 ? ex[j] << kSlotExpertShift |
+                               (__popcll(m[j] & ((1ull << lane) - 1ull)) + pre[j])
+                         : -1;
 
   // Four mask bits b0..b3 to the bytes b0, b1, b2, b3 of a word: the
   // multiplier's shifted copies (0, 7, 14, 21) do not overlap.
@@ -820,7 +822,10 @@ __global__ void workspace_init_kernel(int32_t *__restrict__ header) {
 // Receive row of selection (t, lane) for lanes below k, -1 otherwise.  The
 // row is the expert's segment start, plus the selections of e in earlier
 // tiles, plus the rank inside this tile: the stable counting-sort position.
-// Wave-uniform t.  The first chunk's wave also writes the handle.
+// The layout's slot word must name the same expert (or both must leave the
+// slot out): otherwise the route is not the layout's, the workspace bit is
+// set and the selection gets no row.  Wave-uniform t.  The first chunk's
+// wave also writes the handle.
 __device__ __forceinline__ int32_t selection_row(const Dims &d, int64_t t, int lane,
                                                  bool write_handle,
                                                  const int32_t *__restrict__ topk_idx,
@@ -835,24 +840,26 @@ __device__ __forceinline__ int32_t selection_row(const Dims &d, int64_t t, int l
   int32_t row = -1;
   if (lane < d.k) {
     const int64_t s = t * d.k + lane;
+    // The id, the slot word and the gate are loaded together (the gate
+    // before the handle's stores, so that no wait for those stores is
+    // needed before it is written).  A valid selection's gate must be
+    // finite ("Deep Dive - DeepEP", "A runnable routing ledger").
     const int32_t e = topk_idx[s];
-    // Loaded before the handle's stores, so that no wait for those stores
-    // is needed before the gate is written.  A valid selection's gate must
-    // be finite ("Deep Dive - DeepEP", "A runnable routing ledger").
+    const int32_t w = slot_rank[s];
     const bool gates = write_handle && topk_weights != nullptr;
     const float gate = gates ? topk_weights[s] : 0.0f;
-    if (gates && e >= 0 && e < d.E && !__builtin_isfinite(gate))
-      flag(status, EP_STATUS_BIT_NONFINITE);
-    if (e >= 0 && e < d.E) {
-      const int32_t rank = slot_rank[s];
-      if (rank >= 0) {
-        const int64_t r = (int64_t)expert_offsets[e] +
-                          tile_base[(t / kTileTokens) * tile_row_ints(d.E, d.R) + e] + rank;
-        if (r >= 0 && r < capacity)
-          row = (int32_t)r;
-        else
-          flag(status, EP_STATUS_BIT_CAPACITY);
-      }
+    const bool valid = e >= 0 && e < d.E;
+    if (gates && valid && !__builtin_isfinite(gate)) flag(status, EP_STATUS_BIT_NONFINITE);
+    if (valid != (w >= 0) || (valid && (w >> kSlotExpertShift) != e)) {
+      flag(status, EP_STATUS_BIT_WORKSPACE);
+    } else if (valid) {
+      const int64_t r = (int64_t)expert_offsets[e] +
+                        tile_base[(t / kTileTokens) * tile_row_ints(d.E, d.R) + e] +
+                        (w & kSlotRankMask);
+      if (r >= 0 && r < capacity)
+        row = (int32_t)r;
+      else
+        flag(status, EP_STATUS_BIT_CAPACITY);
     }
     if (write_handle) {
       tok_slot_row[s] = row;
@@ -1442,15 +1449,22 @@ __global__ __launch_bounds__(kBlock) void dispatch_ranked_kernel(
   if (chunk == 0) {
     const int epr = d.E / d.R;
     // The expanded handle (rows the receiver's expand will fill), as
-    // selection_row gives them: segment start + earlier tiles + in-tile rank.
+    // selection_row gives them: segment start + earlier tiles + in-tile rank,
+    // with the same check of the layout's slot word.
     int32_t srow = -1;
-    if (lane < d.k && ej >= 0 && ej < d.E && srank >= 0) {
-      const int64_t r = (int64_t)expert_offsets[ej] +
-                        tile_base[(t / kTileTokens) * tile_row_ints(d.E, d.R) + ej] + srank;
-      if (r >= 0 && r < capacity)
-        srow = (int32_t)r;
-      else
-        flag(status, EP_STATUS_BIT_CAPACITY);
+    if (lane < d.k) {
+      const bool valid = ej >= 0 && ej < d.E;
+      if (valid != (srank >= 0) || (valid && (srank >> kSlotExpertShift) != ej)) {
+        flag(status, EP_STATUS_BIT_WORKSPACE);
+      } else if (valid) {
+        const int64_t r = (int64_t)expert_offsets[ej] +
+                          tile_base[(t / kTileTokens) * tile_row_ints(d.E, d.R) + ej] +
+                          (srank & kSlotRankMask);
+        if (r >= 0 && r < capacity)
+          srow = (int32_t)r;
+        else
+          flag(status, EP_STATUS_BIT_CAPACITY);
+      }
     }
     if (lane < d.R) {
       tok_rank_row[t * d.R + lane] = row;
@@ -1555,11 +1569,13 @@ __global__ __launch_bounds__(kBlock) void expand_kernel(
     const int32_t le = ne_topk_idx[q * d.k + lane];
     if (le >= 0 && le < epr) {
       const int e = r * epr + le;
-      const int32_t rank = slot_rank[t * d.k + lane];
-      const int64_t p = rank < 0 ? -1
-                                 : (int64_t)expert_offsets[e] +
-                                       tile_base[(t / kTileTokens) * tile_row_ints(d.E, d.R) +
-                                                 e] + rank;
+      const int32_t w = slot_rank[t * d.k + lane];
+      const bool same = w >= 0 && (w >> kSlotExpertShift) == e;
+      if (!same && batch == 0) flag(status, EP_STATUS_BIT_WORKSPACE);
+      const int64_t p = !same ? -1
+                              : (int64_t)expert_offsets[e] +
+                                    tile_base[(t / kTileTokens) * tile_row_ints(d.E, d.R) + e] +
+                                    (w & kSlotRankMask);
       if (p >= 0 && p < capacity) {
         row = (int32_t)p;
         if (batch == 0) {
@@ -1567,7 +1583,7 @@ __global__ __launch_bounds__(kBlock) void expand_kernel(
           if (recv_weights != nullptr && ne_topk_weights != nullptr)
             recv_weights[p] = ne_topk_weights[q * d.k + lane];
         }
-      } else if (batch == 0) {
+      } else if (same && batch == 0) {
         flag(status, EP_STATUS_BIT_CAPACITY);
       }
     }

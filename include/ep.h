@@ -40,7 +40,7 @@
  *     reduction": fail at the contract boundary, not after a silent
  *     reinterpretation).  Problems only the GPU can see (a bad route, too
  *     few receive rows, a workspace that does not belong to this
- *     configuration, an inf or NaN among the hidden values or the gates of
+ *     configuration and route, an inf or NaN among the hidden values or the gates of
  *     valid selections) are OR-ed as bits into the caller's device status
  *     word and surface through ep_read_status.  HIP launch failures return
  *     EP_ERR_HIP.  ep_last_error_string() describes the last failure of the
@@ -63,7 +63,8 @@ typedef enum ep_status {
   EP_ERR_INVALID_ARG = 1,   /* sizes, pointers, dtype, alignment (synchronous) */
   EP_ERR_INVALID_ROUTE = 2, /* expert id outside [-1, E) or repeated in a token */
   EP_ERR_CAPACITY = 3,      /* receive buffer has fewer rows than the layout needs */
-  EP_ERR_WORKSPACE = 4,     /* workspace not written by a layout of this config */
+  EP_ERR_WORKSPACE = 4,     /* workspace not written by a layout of this config
+                               and this route */
   EP_ERR_HIP = 5,           /* a HIP runtime call failed */
   EP_ERR_NONFINITE = 6      /* a hidden value or a valid selection's gate is inf or NaN */
 } ep_status_t;
@@ -229,7 +230,10 @@ ep_status_t ep_get_dispatch_layout(const ep_config_t *cfg, const int32_t *topk_i
  *                 selection sets EP_STATUS_BIT_NONFINITE (the ledger rejects
  *                 it too); unused selections' gates are never read
  *   expert_offsets[E + 1] from ep_get_dispatch_layout
- *   workspace     the workspace that layout filled for this route
+ *   workspace     the workspace that layout filled for this route.  The
+ *                 layout records each selection's expert, so a route that
+ *                 differs from the layout's is seen per selection: such a
+ *                 selection gets no row and EP_STATUS_BIT_WORKSPACE is set
  *   capacity      rows of recv_x / recv_scales / recv_weights / row_src; a
  *                 selection whose row would be >= capacity is dropped and
  *                 EP_STATUS_BIT_CAPACITY is set (ep_recv_capacity_rows() or

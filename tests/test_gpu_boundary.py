@@ -296,3 +296,53 @@ def test_padding_fill_with_garbage_counts_stays_in_bounds(fp8):
     b.dispatch(dev_bf16(x), dev(idx), dev(w))
     _status_of(b)
     _guards_intact(big, bigs, bsrc, fp8)
+
+
+# --------------------------------------------------------------------------
+# a dispatch given another route than its layout's
+# --------------------------------------------------------------------------
+
+def _other_route(idx, E):
+    """idx with token 5's first slot moved to an expert it does not hold and
+    token 9's second slot masked: the same configuration, another route."""
+    other = idx.copy()
+    held = set(int(e) for e in idx[5])
+    other[5, 0] = next(e for e in range(E) if e not in held)
+    other[9, 1] = -1
+    return other
+
+
+@pytest.mark.parametrize("path", ["dispatch_bf16", "dispatch_fp8", "fp8_input", "ranked"])
+def test_dispatch_with_another_route_is_reported(path):
+    """The layout records each selection's expert in the workspace; a
+    dispatch given a different route with the same sizes sets the workspace
+    status bit, gives the two changed selections no row, and places every
+    other selection where the layout's route puts it."""
+    T, H, k, E, R = 300, 256, 4, 16, 4
+    rng = np.random.default_rng(55)
+    idx = W.random_routes(rng, T, E, k)
+    x = W.normal_bf16(rng, (T, H))
+    w = rng.random((T, k)).astype(np.float32)
+    other = _other_route(idx, E)
+    fp8 = path in ("dispatch_fp8", "fp8_input")
+    b = ep.EpBuffers(T, H, k, E, R, 1, fp8=fp8)
+    b.status.zero_()
+    b.layout(dev(idx))
+    say(f"another route through {path}")
+    if path == "ranked":
+        b.dispatch_ranked(dev_bf16(x), dev(other), dev(w))
+    elif path == "fp8_input":
+        codes = rng.integers(0, 256, (T, H), dtype=np.uint8)
+        scales = rng.random((T, H // 128)).astype(np.float32)
+        b.dispatch_fp8_input(dev(codes), dev(scales), dev(other), dev(w))
+    else:
+        b.dispatch(dev_bf16(x), dev(other), dev(w))
+    assert _status_of(b) == ep.EP_ERR_WORKSPACE
+    if path == "ranked":
+        return
+    do = oracle.dispatch(x, idx, w, E, R, capacity=T * k)
+    tsr = b.tok_slot_row.cpu().numpy()
+    changed = np.zeros((T, k), bool)
+    changed[5, 0] = changed[9, 1] = True
+    assert np.all(tsr[changed] == -1)
+    assert np.array_equal(tsr[~changed], do["tok_slot_row"][~changed])
