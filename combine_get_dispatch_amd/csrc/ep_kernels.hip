@@ -102,10 +102,15 @@ __device__ __forceinline__ int32_t wave_inclusive_sum(int32_t v) {
 }
 
 // Workspace header check shared by the dispatch kernels: the workspace must
-// have been written by a layout of exactly this configuration.
-__device__ __forceinline__ bool workspace_ok(const int32_t *hdr, const Dims &d) {
-  return hdr[0] == kWorkspaceMagic && hdr[1] == d.T && hdr[2] == d.k && hdr[3] == d.E &&
-         hdr[4] == d.R && hdr[5] == d.A;
+// have been written by a layout of exactly this configuration.  The six
+// words come in two wide loads and are compared without short-circuit, so
+// that the check costs one round trip instead of one per word.
+__device__ __forceinline__ bool workspace_ok(const int32_t *__restrict__ hdr, const Dims &d) {
+  const int4 a = *reinterpret_cast<const int4 *>(hdr);
+  const int2 b = *reinterpret_cast<const int2 *>(hdr + 4);
+  const int ok = (a.x == kWorkspaceMagic) & (a.y == d.T) & (a.z == d.k) & (a.w == d.E) &
+                 (b.x == d.R) & (b.y == d.A);
+  return ok != 0;
 }
 
 }  // namespace
@@ -501,6 +506,15 @@ __device__ __forceinline__ void write_header(int32_t *__restrict__ header, const
 constexpr int32_t kBufferWord3 = 0x00020000;
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 
+// Raw buffer resource over n bytes from p.  A load at an offset at or past n
+// returns zeros (the hardware's range check) without touching memory, so a
+// lane with nothing to load is given offset n and the load is still issued:
+// it has no branch of its own, and the waits after it can count it.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void *p, uint32_t n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)n,
+                                           kBufferWord3);
+}
+
 __device__ __forceinline__ int4 add4(int4 a, int4 b) {
   return make_int4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
 }
@@ -819,13 +833,118 @@ __global__ void workspace_init_kernel(int32_t *__restrict__ header) {
 // "Deep Dive - DeepEP", "Dispatch: layout, move, and epilogue")
 // ---------------------------------------------------------------------------
 
+// A selection's inputs to its receive row, for lanes below k: its expert id,
+// the layout's slot word and (for the handle) its gate, loaded together by
+// buffer loads over the token's k entries (zeros on the other lanes, and for
+// the gate when it is not wanted).
+struct SlotIn {
+  int32_t e, w;
+  float gate;
+};
+
+__device__ __forceinline__ SlotIn load_slot(const Dims &d, int64_t t, int lane, bool want_gate,
+                                            const int32_t *__restrict__ topk_idx,
+                                            const float *__restrict__ topk_weights,
+                                            const int32_t *__restrict__ slot_rank) {
+  const uint32_t n = (uint32_t)d.k * 4u;
+  const uint32_t off = lane < d.k ? (uint32_t)lane * 4u : n;
+  const int64_t s0 = t * d.k;
+  const bool g = want_gate && topk_weights != nullptr;
+  const void *gp = g ? static_cast<const void *>(topk_weights + s0)
+                     : static_cast<const void *>(topk_idx + s0);
+  SlotIn in;
+  in.e = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(buffer_over(topk_idx + s0, n), (int)off,
+                                                       0, 0);
+  in.w = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(buffer_over(slot_rank + s0, n), (int)off,
+                                                       0, 0);
+  in.gate = __builtin_bit_cast(
+      float, __builtin_amdgcn_raw_buffer_load_b32(buffer_over(gp, g ? n : 0u), (int)off, 0, 0));
+  return in;
+}
+
+// Segment start plus tile base of expert e for token t, read from the
+// layout's arrays in global memory.
+struct GlobalBases {
+  const int32_t *__restrict__ offsets;
+  const int32_t *__restrict__ rows;
+  int32_t C;
+  __device__ __forceinline__ int64_t operator()(int32_t e, int64_t t) const {
+    return (int64_t)offsets[e] + rows[(t / kTileTokens) * C + e];
+  }
+};
+
+// The checks on a selection's inputs, as values of the whole wave (not
+// branches, so that the loads of `in` are not moved into a branch, where
+// their wait would also wait for every load issued before them).  act: a
+// lane below k of a workspace that passed its header check (ok).  The
+// layout's slot word must name the same expert (or both must leave the slot
+// out): otherwise the route is not the layout's (mismatch).  use: a valid
+// selection with a matching slot word, which gets a row.  A valid
+// selection's gate must be finite ("Deep Dive - DeepEP", "A runnable
+// routing ledger").
+struct SlotCheck {
+  bool act, use, mismatch, nonfinite;
+};
+
+__device__ __forceinline__ SlotCheck check_slot(const Dims &d, int lane, const SlotIn &in, bool ok,
+                                                bool gates) {
+  SlotCheck c;
+  c.act = ok && lane < d.k;
+  const bool valid = c.act && in.e >= 0 && in.e < d.E;
+  const bool slotted = c.act && in.w >= 0;
+  c.mismatch = valid != slotted || (valid && (in.w >> kSlotExpertShift) != in.e);
+  c.use = valid && !c.mismatch;
+  c.nonfinite = gates && valid && !__builtin_isfinite(in.gate);
+  return c;
+}
+
+// The handle of selection (t, lane): its row, and for a row the source
+// selection and (with gates) the gate.
+__device__ __forceinline__ void write_handle_entry(const Dims &d, int64_t t, int lane,
+                                                   int32_t row, float gate, bool gates,
+                                                   float *__restrict__ recv_weights,
+                                                   int32_t *__restrict__ tok_slot_row,
+                                                   int32_t *__restrict__ row_src) {
+  const int64_t s = t * d.k + lane;
+  tok_slot_row[s] = row;
+  if (row >= 0) {
+    row_src[row] = (int32_t)s;
+    if (gates && recv_weights != nullptr) recv_weights[row] = gate;
+  }
+}
+
 // Receive row of selection (t, lane) for lanes below k, -1 otherwise.  The
 // row is the expert's segment start, plus the selections of e in earlier
 // tiles, plus the rank inside this tile: the stable counting-sort position.
-// The layout's slot word must name the same expert (or both must leave the
-// slot out): otherwise the route is not the layout's, the workspace bit is
-// set and the selection gets no row.  Wave-uniform t.  The first chunk's
-// wave also writes the handle.
+// A selection that check_slot rejects gets no row and sets its status bit.
+// Wave-uniform t.  With write_handle (the first chunk's wave) it also
+// writes the handle.
+template <typename Bases>
+__device__ __forceinline__ int32_t slot_row(const Dims &d, int64_t t, int lane, const SlotIn &in,
+                                            bool ok, bool write_handle, const Bases &bases,
+                                            int64_t capacity, float *__restrict__ recv_weights,
+                                            int32_t *__restrict__ tok_slot_row,
+                                            int32_t *__restrict__ row_src,
+                                            int32_t *__restrict__ status, bool gates) {
+  const SlotCheck c = check_slot(d, lane, in, ok, gates);
+  int32_t row = -1;
+  if (c.use) {
+    const int64_t r = bases(in.e, t) + (in.w & kSlotRankMask);
+    if (r >= 0 && r < capacity)
+      row = (int32_t)r;
+    else
+      flag(status, EP_STATUS_BIT_CAPACITY);
+  }
+  if (c.mismatch) flag(status, EP_STATUS_BIT_WORKSPACE);
+  if (c.nonfinite) flag(status, EP_STATUS_BIT_NONFINITE);
+  if (write_handle && c.act)
+    write_handle_entry(d, t, lane, row, in.gate, gates, recv_weights, tok_slot_row, row_src);
+  return row;
+}
+
+// slot_row over the layout's arrays in global memory, its inputs loaded
+// here.  The gate is loaded with the id (before the handle's stores, so
+// that no wait for those stores is needed before it is written).
 __device__ __forceinline__ int32_t selection_row(const Dims &d, int64_t t, int lane,
                                                  bool write_handle,
                                                  const int32_t *__restrict__ topk_idx,
@@ -837,39 +956,11 @@ __device__ __forceinline__ int32_t selection_row(const Dims &d, int64_t t, int l
                                                  int32_t *__restrict__ tok_slot_row,
                                                  int32_t *__restrict__ row_src,
                                                  int32_t *__restrict__ status) {
-  int32_t row = -1;
-  if (lane < d.k) {
-    const int64_t s = t * d.k + lane;
-    // The id, the slot word and the gate are loaded together (the gate
-    // before the handle's stores, so that no wait for those stores is
-    // needed before it is written).  A valid selection's gate must be
-    // finite ("Deep Dive - DeepEP", "A runnable routing ledger").
-    const int32_t e = topk_idx[s];
-    const int32_t w = slot_rank[s];
-    const bool gates = write_handle && topk_weights != nullptr;
-    const float gate = gates ? topk_weights[s] : 0.0f;
-    const bool valid = e >= 0 && e < d.E;
-    if (gates && valid && !__builtin_isfinite(gate)) flag(status, EP_STATUS_BIT_NONFINITE);
-    if (valid != (w >= 0) || (valid && (w >> kSlotExpertShift) != e)) {
-      flag(status, EP_STATUS_BIT_WORKSPACE);
-    } else if (valid) {
-      const int64_t r = (int64_t)expert_offsets[e] +
-                        tile_base[(t / kTileTokens) * tile_row_ints(d.E, d.R) + e] +
-                        (w & kSlotRankMask);
-      if (r >= 0 && r < capacity)
-        row = (int32_t)r;
-      else
-        flag(status, EP_STATUS_BIT_CAPACITY);
-    }
-    if (write_handle) {
-      tok_slot_row[s] = row;
-      if (row >= 0) {
-        row_src[row] = (int32_t)s;
-        if (gates && recv_weights != nullptr) recv_weights[row] = gate;
-      }
-    }
-  }
-  return row;
+  const bool gates = write_handle && topk_weights != nullptr;
+  const SlotIn in = load_slot(d, t, lane, gates, topk_idx, topk_weights, slot_rank);
+  const GlobalBases bases{expert_offsets, tile_base, tile_row_ints(d.E, d.R)};
+  return slot_row(d, t, lane, in, true, write_handle, bases, capacity, recv_weights, tok_slot_row,
+                  row_src, status, gates);
 }
 
 // Largest magnitude of the 16 bf16 values of v0 and v1, as bf16 bits with
@@ -955,6 +1046,9 @@ __device__ __forceinline__ int slice_col(int chunk, int lane, int u) {
 template <bool kFp8>
 __device__ __forceinline__ XSlice load_x_slice(const uint16_t *__restrict__ x, int64_t t,
                                                int64_t H, int chunk, int lane) {
+  // Buffer loads over the token's row: a part past its end reads zeros.
+  const uint32_t n = (uint32_t)H * 2u;
+  const __amdgpu_buffer_rsrc_t rsrc = buffer_over(x + t * H, n);
   XSlice xs;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -962,36 +1056,57 @@ __device__ __forceinline__ XSlice load_x_slice(const uint16_t *__restrict__ x, i
     // all out; bf16 guards each 8-column part.
     const int col = slice_col<kFp8>(chunk, lane, u);
     const bool in = kFp8 ? slice_col<kFp8>(chunk, lane, 0) < H : col < H;
-    xs.v[u] = in ? *reinterpret_cast<const uint4 *>(x + t * H + col) : make_uint4(0, 0, 0, 0);
+    const uint32_t off = in ? (uint32_t)col * 2u : n;
+    const i32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)off, 0, 0);
+    xs.v[u] = make_uint4((uint32_t)w.x, (uint32_t)w.y, (uint32_t)w.z, (uint32_t)w.w);
   }
   return xs;
 }
 
-// Stores the slice to each of the token's receive rows (lane j holds the
-// row of slot j, -1 for none): bf16 bits, or E4M3 codes plus one scale per
-// 128-value block.  One 16-byte non-temporal store per lane per row part.
+// The slice as stored: E4M3 codes in v[0] plus the block's scale, or the
+// bf16 bits as loaded.  finite is false when one of its hidden values is an
+// infinity or NaN.
+struct XOut {
+  uint4 v[2];
+  float scale;
+  bool finite;
+};
+
 template <bool kFp8>
-__device__ __forceinline__ void store_x_slice(const XSlice &xs, int32_t row, int k, int64_t H,
-                                              int chunk, int lane, void *__restrict__ recv_x,
-                                              float *__restrict__ recv_scales,
-                                              int32_t *__restrict__ status) {
+__device__ __forceinline__ XOut encode_slice(const XSlice &xs) {
+  XOut o;
+  if (kFp8) {
+    o.v[0] = quantize16(xs.v[0], xs.v[1], o.scale, o.finite);
+    o.v[1] = o.v[0];
+  } else {
+    // lanes past the row's end hold zeros, which are finite
+    o.v[0] = xs.v[0];
+    o.v[1] = xs.v[1];
+    o.scale = 0.0f;
+    o.finite = absmax_bits16(xs.v[0], xs.v[1]) < kBf16Inf;
+  }
+  return o;
+}
+
+// Stores the encoded slice to each of the token's receive rows (lane j
+// holds the row of slot j, -1 for none): bf16 bits, or E4M3 codes plus one
+// scale per 128-value block.  One 16-byte non-temporal store per lane per
+// row part.
+template <bool kFp8>
+__device__ __forceinline__ void store_slice(const XOut &o, int32_t row, int k, int64_t H,
+                                            int chunk, int lane, void *__restrict__ recv_x,
+                                            float *__restrict__ recv_scales) {
   if (kFp8) {
     const int col = slice_col<true>(chunk, lane, 0);
     const bool in = col < H;
-    float scale;
-    bool finite;
-    const uint4 q = quantize16(xs.v[0], xs.v[1], scale, finite);
-    report_nonfinite(!finite, lane, status);
     const int64_t nblk = H / 128;
     for (int j = 0; j < k; ++j) {
       const int32_t r = lane_value(row, j);
       if (r < 0 || !in) continue;
-      store_stream(static_cast<uint8_t *>(recv_x) + (int64_t)r * H + col, q);
-      if ((lane & 7) == 0) recv_scales[(int64_t)r * nblk + col / 128] = scale;
+      store_stream(static_cast<uint8_t *>(recv_x) + (int64_t)r * H + col, o.v[0]);
+      if ((lane & 7) == 0) recv_scales[(int64_t)r * nblk + col / 128] = o.scale;
     }
   } else {
-    // lanes past the row's end hold zeros, which are finite
-    report_nonfinite(absmax_bits16(xs.v[0], xs.v[1]) >= kBf16Inf, lane, status);
     for (int j = 0; j < k; ++j) {
       const int32_t r = lane_value(row, j);
       if (r < 0) continue;
@@ -999,14 +1114,36 @@ __device__ __forceinline__ void store_x_slice(const XSlice &xs, int32_t row, int
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int col = slice_col<false>(chunk, lane, u);
-        if (col < H) store_stream(dst + col, xs.v[u]);
+        if (col < H) store_stream(dst + col, o.v[u]);
       }
     }
   }
 }
 
+// Encodes and stores the slice, reporting a non-finite hidden value.
+template <bool kFp8>
+__device__ __forceinline__ void store_x_slice(const XSlice &xs, int32_t row, int k, int64_t H,
+                                              int chunk, int lane, void *__restrict__ recv_x,
+                                              float *__restrict__ recv_scales,
+                                              int32_t *__restrict__ status) {
+  const XOut o = encode_slice<kFp8>(xs);
+  report_nonfinite(!o.finite, lane, status);
+  store_slice<kFp8>(o, row, k, H, chunk, lane, recv_x, recv_scales);
+}
+
 // One wave per (token, 1024-column chunk): the selection rows, then the x
 // slice to each of them (bf16 bit copy, or fused FP8 quantisation).
+//
+// Every load is issued before the first wait, in one straight line: the
+// selection's id, slot word and gate first, then the x slice, then (once the
+// ids are in) the segment start and tile base, by buffer loads whose lanes
+// without a row read zeros.  Loads return in issue order, so the wait for
+// the ids does not include x, the second link of the row chain overlaps the
+// x loads, and the FP8 encoding overlaps that link.  The status bits are
+// raised after the stores.  The loads before the header check stay in
+// bounds whatever the header says (the host has checked that the workspace
+// holds this configuration's arrays), and a failed check gives every
+// selection no row.
 template <bool kFp8>
 __global__ __launch_bounds__(kBlock) void dispatch_kernel(
     Dims d, int32_t nchunks, const uint16_t *__restrict__ x, const int32_t *__restrict__ topk_idx,
@@ -1021,17 +1158,30 @@ __global__ __launch_bounds__(kBlock) void dispatch_kernel(
   if (item >= d.T * nchunks) return;
   const int64_t t = item / nchunks;
   const int chunk = item - (int)t * nchunks;
-  // The x slice depends on nothing else, so its loads go first and overlap
-  // the chain of workspace reads that gives the rows.
+  const bool gates = chunk == 0 && topk_weights != nullptr;
+  const SlotIn in = load_slot(d, t, lane, gates, topk_idx, topk_weights, slot_rank);
   const XSlice xs = load_x_slice<kFp8>(x, t, d.H, chunk, lane);
-  if (!workspace_ok(header, d)) {
-    if (lane == 0) flag(status, EP_STATUS_BIT_WORKSPACE);
-    return;
-  }
-  const int32_t row = selection_row(d, t, lane, chunk == 0, topk_idx, topk_weights,
-                                    expert_offsets, tile_base, slot_rank, capacity,
-                                    recv_weights, tok_slot_row, row_src, status);
-  store_x_slice<kFp8>(xs, row, d.k, d.H, chunk, lane, recv_x, recv_scales, status);
+  const bool ok = workspace_ok(header, d);
+  const SlotCheck c = check_slot(d, lane, in, ok, gates);
+  const uint32_t nb = (uint32_t)d.E * 4u;
+  const uint32_t eo = c.use ? (uint32_t)in.e * 4u : nb;
+  const int32_t *trow = tile_base + (t / kTileTokens) * tile_row_ints(d.E, d.R);
+  const int32_t start =
+      (int32_t)__builtin_amdgcn_raw_buffer_load_b32(buffer_over(expert_offsets, nb), (int)eo, 0, 0);
+  const int32_t base =
+      (int32_t)__builtin_amdgcn_raw_buffer_load_b32(buffer_over(trow, nb), (int)eo, 0, 0);
+  const XOut o = encode_slice<kFp8>(xs);
+  const int64_t r = (int64_t)start + base + (in.w & kSlotRankMask);
+  const bool fits = r >= 0 && r < capacity;
+  const int32_t row = c.use && fits ? (int32_t)r : -1;
+  store_slice<kFp8>(o, row, d.k, d.H, chunk, lane, recv_x, recv_scales);
+  if (chunk == 0 && c.act)
+    write_handle_entry(d, t, lane, row, in.gate, gates, recv_weights, tok_slot_row, row_src);
+  if (!ok && lane == 0) flag(status, EP_STATUS_BIT_WORKSPACE);
+  if (c.use && !fits) flag(status, EP_STATUS_BIT_CAPACITY);
+  if (c.mismatch) flag(status, EP_STATUS_BIT_WORKSPACE);
+  if (c.nonfinite) flag(status, EP_STATUS_BIT_NONFINITE);
+  report_nonfinite(ok && !o.finite, lane, status);
 }
 
 // Layout and dispatch in one launch, for a batch of at most one tile (256
