@@ -862,17 +862,6 @@ __device__ __forceinline__ SlotIn load_slot(const Dims &d, int64_t t, int lane, 
   return in;
 }
 
-// Segment start plus tile base of expert e for token t, read from the
-// layout's arrays in global memory.
-struct GlobalBases {
-  const int32_t *__restrict__ offsets;
-  const int32_t *__restrict__ rows;
-  int32_t C;
-  __device__ __forceinline__ int64_t operator()(int32_t e, int64_t t) const {
-    return (int64_t)offsets[e] + rows[(t / kTileTokens) * C + e];
-  }
-};
-
 // The checks on a selection's inputs, as values of the whole wave (not
 // branches, so that the loads of `in` are not moved into a branch, where
 // their wait would also wait for every load issued before them).  act: a
@@ -913,54 +902,42 @@ __device__ __forceinline__ void write_handle_entry(const Dims &d, int64_t t, int
   }
 }
 
-// Receive row of selection (t, lane) for lanes below k, -1 otherwise.  The
-// row is the expert's segment start, plus the selections of e in earlier
-// tiles, plus the rank inside this tile: the stable counting-sort position.
-// A selection that check_slot rejects gets no row and sets its status bit.
-// Wave-uniform t.  With write_handle (the first chunk's wave) it also
-// writes the handle.
-template <typename Bases>
-__device__ __forceinline__ int32_t slot_row(const Dims &d, int64_t t, int lane, const SlotIn &in,
-                                            bool ok, bool write_handle, const Bases &bases,
-                                            int64_t capacity, float *__restrict__ recv_weights,
-                                            int32_t *__restrict__ tok_slot_row,
-                                            int32_t *__restrict__ row_src,
-                                            int32_t *__restrict__ status, bool gates) {
-  const SlotCheck c = check_slot(d, lane, in, ok, gates);
-  int32_t row = -1;
-  if (c.use) {
-    const int64_t r = bases(in.e, t) + (in.w & kSlotRankMask);
-    if (r >= 0 && r < capacity)
-      row = (int32_t)r;
-    else
-      flag(status, EP_STATUS_BIT_CAPACITY);
-  }
-  if (c.mismatch) flag(status, EP_STATUS_BIT_WORKSPACE);
-  if (c.nonfinite) flag(status, EP_STATUS_BIT_NONFINITE);
-  if (write_handle && c.act)
-    write_handle_entry(d, t, lane, row, in.gate, gates, recv_weights, tok_slot_row, row_src);
-  return row;
+// A selection's receive row is the expert's segment start, plus the
+// selections of e in earlier tiles (the tile base), plus its rank inside
+// the tile: the stable counting-sort position.  The first two come by
+// buffer loads, issued whatever the lane (zeros, and no memory access, for
+// a selection check_slot did not accept), so that they have no branch of
+// their own; the caller adds them up as late as it can.
+struct RowBase {
+  int32_t start, base;
+};
+
+__device__ __forceinline__ RowBase load_row_base(const Dims &d, int64_t t, int32_t e, bool use,
+                                                 const int32_t *__restrict__ expert_offsets,
+                                                 const int32_t *__restrict__ tile_base) {
+  const uint32_t nb = (uint32_t)d.E * 4u;
+  const int eo = (int)(use ? (uint32_t)e * 4u : nb);
+  const int32_t *trow = tile_base + (t / kTileTokens) * tile_row_ints(d.E, d.R);
+  RowBase b;
+  b.start = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(buffer_over(expert_offsets, nb), eo, 0, 0);
+  b.base = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(buffer_over(trow, nb), eo, 0, 0);
+  return b;
 }
 
-// slot_row over the layout's arrays in global memory, its inputs loaded
-// here.  The gate is loaded with the id (before the handle's stores, so
-// that no wait for those stores is needed before it is written).
-__device__ __forceinline__ int32_t selection_row(const Dims &d, int64_t t, int lane,
-                                                 bool write_handle,
-                                                 const int32_t *__restrict__ topk_idx,
-                                                 const float *__restrict__ topk_weights,
-                                                 const int32_t *__restrict__ expert_offsets,
-                                                 const int32_t *__restrict__ tile_base,
-                                                 const int32_t *__restrict__ slot_rank,
-                                                 int64_t capacity, float *__restrict__ recv_weights,
-                                                 int32_t *__restrict__ tok_slot_row,
-                                                 int32_t *__restrict__ row_src,
-                                                 int32_t *__restrict__ status) {
-  const bool gates = write_handle && topk_weights != nullptr;
-  const SlotIn in = load_slot(d, t, lane, gates, topk_idx, topk_weights, slot_rank);
-  const GlobalBases bases{expert_offsets, tile_base, tile_row_ints(d.E, d.R)};
-  return slot_row(d, t, lane, in, true, write_handle, bases, capacity, recv_weights, tok_slot_row,
-                  row_src, status, gates);
+// The row from its base and the slot word's in-tile rank: -1 for a
+// selection not accepted or past the capacity (fits false).
+__device__ __forceinline__ int32_t row_from_base(const RowBase &b, int32_t w, bool use,
+                                                 int64_t capacity, bool &fits) {
+  const int64_t r = (int64_t)b.start + b.base + (w & kSlotRankMask);
+  fits = r >= 0 && r < capacity;
+  return use && fits ? (int32_t)r : -1;
+}
+
+// A selection's status bits, raised after its stores.
+__device__ __forceinline__ void report_slot(const SlotCheck &c, bool fits, int32_t *status) {
+  if (c.use && !fits) flag(status, EP_STATUS_BIT_CAPACITY);
+  if (c.mismatch) flag(status, EP_STATUS_BIT_WORKSPACE);
+  if (c.nonfinite) flag(status, EP_STATUS_BIT_NONFINITE);
 }
 
 // Largest magnitude of the 16 bf16 values of v0 and v1, as bf16 bits with
@@ -1163,24 +1140,15 @@ __global__ __launch_bounds__(kBlock) void dispatch_kernel(
   const XSlice xs = load_x_slice<kFp8>(x, t, d.H, chunk, lane);
   const bool ok = workspace_ok(header, d);
   const SlotCheck c = check_slot(d, lane, in, ok, gates);
-  const uint32_t nb = (uint32_t)d.E * 4u;
-  const uint32_t eo = c.use ? (uint32_t)in.e * 4u : nb;
-  const int32_t *trow = tile_base + (t / kTileTokens) * tile_row_ints(d.E, d.R);
-  const int32_t start =
-      (int32_t)__builtin_amdgcn_raw_buffer_load_b32(buffer_over(expert_offsets, nb), (int)eo, 0, 0);
-  const int32_t base =
-      (int32_t)__builtin_amdgcn_raw_buffer_load_b32(buffer_over(trow, nb), (int)eo, 0, 0);
+  const RowBase b = load_row_base(d, t, in.e, c.use, expert_offsets, tile_base);
   const XOut o = encode_slice<kFp8>(xs);
-  const int64_t r = (int64_t)start + base + (in.w & kSlotRankMask);
-  const bool fits = r >= 0 && r < capacity;
-  const int32_t row = c.use && fits ? (int32_t)r : -1;
+  bool fits;
+  const int32_t row = row_from_base(b, in.w, c.use, capacity, fits);
   store_slice<kFp8>(o, row, d.k, d.H, chunk, lane, recv_x, recv_scales);
   if (chunk == 0 && c.act)
     write_handle_entry(d, t, lane, row, in.gate, gates, recv_weights, tok_slot_row, row_src);
   if (!ok && lane == 0) flag(status, EP_STATUS_BIT_WORKSPACE);
-  if (c.use && !fits) flag(status, EP_STATUS_BIT_CAPACITY);
-  if (c.mismatch) flag(status, EP_STATUS_BIT_WORKSPACE);
-  if (c.nonfinite) flag(status, EP_STATUS_BIT_NONFINITE);
+  report_slot(c, fits, status);
   report_nonfinite(ok && !o.finite, lane, status);
 }
 
@@ -1266,7 +1234,7 @@ __global__ __launch_bounds__(kBlock) void layout_dispatch_kernel(
   if (!has_item) return;
 
   // Receive rows of the token's selections: segment start plus the stable
-  // rank inside the batch, as selection_row gives them.
+  // rank inside the batch, as the dispatch kernels give them.
   int32_t row = -1;
   if (lane < d.k) {
     if (eid >= 0 && eid < d.E) {
@@ -1309,30 +1277,49 @@ __global__ __launch_bounds__(kBlock) void dispatch_fp8_input_kernel(
   if (item >= d.T * nchunks) return;
   const int64_t t = item / nchunks;
   const int chunk = item - (int)t * nchunks;
-  // The codes and scale first: they overlap the workspace reads.
+  // The loads in one straight line: the codes and the block scale (buffer
+  // loads: zeros past the row's end, and the scale only on a block's first
+  // lane), the ids and slot words, then the segment start and tile base.
+  // (Codes first measured a little faster here than ids first; with no
+  // encoding to overlap, the second link has nothing to hide behind.)  The
+  // codes are used only in the store loop, and the compiler would otherwise
+  // place their loads there, after the row chain: their pointers are made
+  // opaque (so that the loads cannot be taken for reads of constant memory,
+  // which may be placed anywhere), and an empty asm statement that clobbers
+  // memory and takes the ids and slot words follows the loads, so that what
+  // is computed from the ids stays after them.
+  asm volatile("" : "+s"(x_codes), "+s"(x_scales));
+  const bool gates = chunk == 0 && topk_weights != nullptr;
   const int64_t H = d.H;
   const int64_t nblk = H / 128;
   const int col = chunk * kChunkCols + lane * 16;
-  const bool in = col < H;
-  uint4 q = make_uint4(0, 0, 0, 0);
-  float scale = 0.0f;
-  if (in) {
-    q = *reinterpret_cast<const uint4 *>(x_codes + t * H + col);
-    if ((lane & 7) == 0) scale = x_scales[t * nblk + col / 128];
-  }
-  if (!workspace_ok(header, d)) {
-    if (lane == 0) flag(status, EP_STATUS_BIT_WORKSPACE);
-    return;
-  }
-  const int32_t row = selection_row(d, t, lane, chunk == 0, topk_idx, topk_weights,
-                                    expert_offsets, tile_base, slot_rank, capacity,
-                                    recv_weights, tok_slot_row, row_src, status);
+  const bool live = col < H;
+  const uint32_t nq = (uint32_t)H;
+  const uint32_t ns = (uint32_t)nblk * 4u;
+  const i32x4_t qw = __builtin_amdgcn_raw_buffer_load_b128(buffer_over(x_codes + t * H, nq),
+                                                           (int)(live ? (uint32_t)col : nq), 0, 0);
+  const float scale = __builtin_bit_cast(
+      float, __builtin_amdgcn_raw_buffer_load_b32(
+                 buffer_over(x_scales + t * nblk, ns),
+                 (int)(live && (lane & 7) == 0 ? (uint32_t)(col / 128) * 4u : ns), 0, 0));
+  SlotIn in = load_slot(d, t, lane, gates, topk_idx, topk_weights, slot_rank);
+  const bool ok = workspace_ok(header, d);
+  asm volatile("" : "+v"(in.e), "+v"(in.w)::"memory");
+  const SlotCheck c = check_slot(d, lane, in, ok, gates);
+  const RowBase b = load_row_base(d, t, in.e, c.use, expert_offsets, tile_base);
+  const uint4 q = make_uint4((uint32_t)qw.x, (uint32_t)qw.y, (uint32_t)qw.z, (uint32_t)qw.w);
+  bool fits;
+  const int32_t row = row_from_base(b, in.w, c.use, capacity, fits);
   for (int j = 0; j < d.k; ++j) {
     const int32_t r = lane_value(row, j);
-    if (r < 0 || !in) continue;
+    if (r < 0 || !live) continue;
     store_stream(recv_x + (int64_t)r * H + col, q);
     if ((lane & 7) == 0) recv_scales[(int64_t)r * nblk + col / 128] = scale;
   }
+  if (chunk == 0 && c.act)
+    write_handle_entry(d, t, lane, row, in.gate, gates, recv_weights, tok_slot_row, row_src);
+  if (!ok && lane == 0) flag(status, EP_STATUS_BIT_WORKSPACE);
+  report_slot(c, fits, status);
 }
 
 // Alignment padding rows of expert e: no source, zero gate and, with
@@ -1598,9 +1585,9 @@ __global__ __launch_bounds__(kBlock) void dispatch_ranked_kernel(
                                ranked_capacity, status);
   if (chunk == 0) {
     const int epr = d.E / d.R;
-    // The expanded handle (rows the receiver's expand will fill), as
-    // selection_row gives them: segment start + earlier tiles + in-tile rank,
-    // with the same check of the layout's slot word.
+    // The expanded handle (rows the receiver's expand will fill), as the
+    // dispatch kernels give them: segment start + earlier tiles + in-tile
+    // rank, with the same check of the layout's slot word.
     int32_t srow = -1;
     if (lane < d.k) {
       const bool valid = ej >= 0 && ej < d.E;
@@ -1652,9 +1639,14 @@ __global__ __launch_bounds__(kBlock) void dispatch_ranked_kernel(
 
 // Receiver-side expand: non-expanded row q (rank r, token t) goes to the
 // expert-major row of each of its local slots.  One wave per (received row,
-// batch of kExpandBatch 1024-column chunks): the batch's payload loads are
-// issued before the row's metadata chain, so they overlap it; the first
-// batch's wave also writes the rows' sources and gates.
+// batch of kExpandBatch 1024-column chunks); the first batch's wave also
+// writes the rows' sources and gates.  The loads take three round trips:
+// the row count and the workspace header (a row past the count has nothing
+// to load); then the batch's payload with everything that depends on q
+// alone (the partition starts that give r, the source token, the local ids
+// and gates); then everything that depends on t and the expert (the slot
+// words, segment starts and tile bases).  Buffer loads give lanes with
+// nothing to load zeros, so no load has a branch of its own.
 constexpr int kExpandBatch = 4;
 
 template <bool kFp8>
@@ -1674,84 +1666,109 @@ __global__ __launch_bounds__(kBlock) void expand_kernel(
   const int batch = (int)(item - q * nbatches);
   if (q >= ranked_capacity) return;
   const int64_t rows = rank_token_offsets[d.R];
-  if (q >= rows) return;
-  if (!workspace_ok(header, d)) {
-    if (lane == 0) flag(status, EP_STATUS_BIT_WORKSPACE);
+  const bool ok = workspace_ok(header, d);
+  if (q >= rows || !ok) {
+    if (q < rows && lane == 0) flag(status, EP_STATUS_BIT_WORKSPACE);
     return;
   }
   const int64_t H = d.H;
+  asm volatile("" : "+s"(ne_x), "+s"(ne_scales));
 
-  // The batch's payload only depends on q: load it before the metadata
-  // chain.
+  // The row's rank: how many partition starts 1..R are at or below q.
+  const uint32_t nro = (uint32_t)(d.R + 1) * 4u;
+  int32_t start_l = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(
+      buffer_over(rank_token_offsets, nro),
+      (int)(lane >= 1 && lane <= d.R ? (uint32_t)lane * 4u : nro), 0, 0);
+  int64_t t = ne_src[q];
+  const uint32_t nk = (uint32_t)d.k * 4u;
+  const int koff = (int)(lane < d.k ? (uint32_t)lane * 4u : nk);
+  int32_t le = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(
+      buffer_over(ne_topk_idx + q * d.k, nk), koff, 0, 0);
+  const bool gates = batch == 0 && recv_weights != nullptr && ne_topk_weights != nullptr;
+  const float gate = __builtin_bit_cast(
+      float, __builtin_amdgcn_raw_buffer_load_b32(
+                 buffer_over(gates ? static_cast<const void *>(ne_topk_weights + q * d.k)
+                                   : static_cast<const void *>(ne_topk_idx + q * d.k),
+                             gates ? nk : 0u),
+                 koff, 0, 0));
+
+  // Then the batch's payload.  It is used only in the store loop, and the
+  // compiler would otherwise place its loads there, after the chain below.
+  // Its pointers are made opaque (so that the loads cannot be taken for
+  // reads of constant memory, which may be placed anywhere), and an empty
+  // asm statement that clobbers memory and takes the values loaded above
+  // follows them: the payload's loads stay before the wait for those
+  // values, and what is computed from them stays after it.
   Payload16 pl[kExpandBatch];
-  auto load_batch = [&](int c0) {
+  const int c0 = batch * kExpandBatch;
+  if (kFp8) {
+    const uint32_t nq = (uint32_t)H;
+    const uint32_t ns = (uint32_t)(H / 128) * 4u;
+    const __amdgpu_buffer_rsrc_t codes =
+        buffer_over(static_cast<const uint8_t *>(ne_x) + q * H, nq);
+    const __amdgpu_buffer_rsrc_t scales = buffer_over(ne_scales + q * (H / 128), ns);
 #pragma unroll
     for (int b = 0; b < kExpandBatch; ++b) {
       const int col = (c0 + b) * kChunkCols + lane * 16;
-      pl[b].lo = make_uint4(0, 0, 0, 0);
+      const bool live = c0 + b < nchunks && col < H;
+      const i32x4_t w =
+          __builtin_amdgcn_raw_buffer_load_b128(codes, (int)(live ? (uint32_t)col : nq), 0, 0);
+      pl[b].lo = make_uint4((uint32_t)w.x, (uint32_t)w.y, (uint32_t)w.z, (uint32_t)w.w);
       pl[b].hi = pl[b].lo;
-      pl[b].scale = 0.0f;
-      if (c0 + b < nchunks && col < H) {
-        if (kFp8) {
-          pl[b].lo = *reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(ne_x) + q * H + col);
-          if ((lane & 7) == 0) pl[b].scale = ne_scales[q * (H / 128) + col / 128];
-        } else {
-          const uint16_t *src = static_cast<const uint16_t *>(ne_x) + q * H + col;
-          pl[b].lo = *reinterpret_cast<const uint4 *>(src);
-          if (col + 8 < H) pl[b].hi = *reinterpret_cast<const uint4 *>(src + 8);
-        }
-      }
+      pl[b].scale = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(
+                     scales, (int)(live && (lane & 7) == 0 ? (uint32_t)(col / 128) * 4u : ns),
+                     0, 0));
     }
-  };
-  load_batch(batch * kExpandBatch);
-
-  // The row's rank: how many partition starts 1..R are at or below q.
-  const bool le_q = lane >= 1 && lane <= d.R && rank_token_offsets[lane] <= q;
-  const int r = uniform((int)__popcll(__ballot(le_q)));
-  const int64_t t = uniform(ne_src[q]);
-  if (r >= d.R || t < 0 || t >= d.T) {
-    if (lane == 0) flag(status, EP_STATUS_BIT_ROUTE);
-    return;
-  }
-  const int epr = d.E / d.R;
-  int32_t row = -1;
-  if (lane < d.k) {
-    const int32_t le = ne_topk_idx[q * d.k + lane];
-    if (le >= 0 && le < epr) {
-      const int e = r * epr + le;
-      const int32_t w = slot_rank[t * d.k + lane];
-      const bool same = w >= 0 && (w >> kSlotExpertShift) == e;
-      if (!same && batch == 0) flag(status, EP_STATUS_BIT_WORKSPACE);
-      const int64_t p = !same ? -1
-                              : (int64_t)expert_offsets[e] +
-                                    tile_base[(t / kTileTokens) * tile_row_ints(d.E, d.R) + e] +
-                                    (w & kSlotRankMask);
-      if (p >= 0 && p < capacity) {
-        row = (int32_t)p;
-        if (batch == 0) {
-          row_src[p] = (int32_t)(t * d.k + lane);
-          if (recv_weights != nullptr && ne_topk_weights != nullptr)
-            recv_weights[p] = ne_topk_weights[q * d.k + lane];
-        }
-      } else if (same && batch == 0) {
-        flag(status, EP_STATUS_BIT_CAPACITY);
-      }
-    }
-  }
-
-  {
-    const int c0 = batch * kExpandBatch;
-    for (int j = 0; j < d.k; ++j) {
-      const int32_t rr = lane_value(row, j);
-      if (rr < 0) continue;
+  } else {
+    // With H % 16 == 8 the last lane's upper half lies past the row's end
+    // and reads zeros.
+    const uint32_t nx = (uint32_t)H * 2u;
+    const __amdgpu_buffer_rsrc_t src = buffer_over(static_cast<const uint16_t *>(ne_x) + q * H, nx);
 #pragma unroll
-      for (int b = 0; b < kExpandBatch; ++b) {
-        const int col = (c0 + b) * kChunkCols + lane * 16;
-        if (c0 + b < nchunks && col < H)
-          store_payload<kFp8>(recv_x, recv_scales, rr, H, col, lane, pl[b]);
-      }
+    for (int b = 0; b < kExpandBatch; ++b) {
+      const int col = (c0 + b) * kChunkCols + lane * 16;
+      const bool live = c0 + b < nchunks && col < H;
+      const uint32_t off = live ? (uint32_t)col * 2u : nx;
+      const i32x4_t lo = __builtin_amdgcn_raw_buffer_load_b128(src, (int)off, 0, 0);
+      const i32x4_t hi = __builtin_amdgcn_raw_buffer_load_b128(src, (int)(live ? off + 16u : nx), 0, 0);
+      pl[b].lo = make_uint4((uint32_t)lo.x, (uint32_t)lo.y, (uint32_t)lo.z, (uint32_t)lo.w);
+      pl[b].hi = make_uint4((uint32_t)hi.x, (uint32_t)hi.y, (uint32_t)hi.z, (uint32_t)hi.w);
+      pl[b].scale = 0.0f;
     }
   }
+  asm volatile("" : "+v"(start_l), "+v"(le), "+s"(t)::"memory");
+
+  const int r = uniform((int)__popcll(__ballot(lane >= 1 && lane <= d.R && start_l <= q)));
+  const bool route_ok = r < d.R && t >= 0 && t < d.T;
+  const int epr = d.E / d.R;
+  const bool local = route_ok && lane < d.k && le >= 0 && le < epr;
+  const int32_t e = r * epr + le;
+  const int64_t ts = route_ok ? t : 0;  // the loads' token, in range
+  const int32_t w = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(
+      buffer_over(slot_rank + ts * d.k, nk), (int)(local ? (uint32_t)lane * 4u : nk), 0, 0);
+  const RowBase base = load_row_base(d, ts, e, local, expert_offsets, tile_base);
+  const bool same = local && w >= 0 && (w >> kSlotExpertShift) == e;
+  bool fits;
+  const int32_t row = row_from_base(base, w, same, capacity, fits);
+
+  for (int j = 0; j < d.k; ++j) {
+    const int32_t rr = lane_value(row, j);
+    if (rr < 0) continue;
+#pragma unroll
+    for (int b = 0; b < kExpandBatch; ++b) {
+      const int col = (c0 + b) * kChunkCols + lane * 16;
+      if (c0 + b < nchunks && col < H)
+        store_payload<kFp8>(recv_x, recv_scales, rr, H, col, lane, pl[b]);
+    }
+  }
+  if (batch == 0 && row >= 0) {
+    row_src[row] = (int32_t)(t * d.k + lane);
+    if (gates) recv_weights[row] = gate;
+  }
+  if (!route_ok && lane == 0) flag(status, EP_STATUS_BIT_ROUTE);
+  if (batch == 0 && local && !same) flag(status, EP_STATUS_BIT_WORKSPACE);
+  if (batch == 0 && same && !fits) flag(status, EP_STATUS_BIT_CAPACITY);
 }
 
 // Ranked combine, stage 1: per non-expanded row, the fp32 sum of its local
