@@ -13,6 +13,8 @@ constexpr int kTileTokens = 256;
 constexpr int kWave = 64;
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
+// Waves MI355X holds at once: 256 compute units x 4 SIMDs x 8 waves.
+constexpr int64_t kChipWaves = 256 * 4 * 8;
 
 // Columns one dispatch wave moves per work item: 64 lanes x 16 values.
 constexpr int kChunkCols = 1024;

@@ -504,6 +504,8 @@ __device__ __forceinline__ void write_header(int32_t *__restrict__ header, const
 // Word 3 of a raw buffer resource on this chip family (32-bit data format,
 // no swizzle): loads past num_records return zero.
 constexpr int32_t kBufferWord3 = 0x00020000;
+// Cache-policy operand of a buffer load: the non-temporal (streaming) hint.
+constexpr int kBufferNt = 2;
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 
 // Raw buffer resource over n bytes from p.  A load at an offset at or past n
@@ -1372,8 +1374,17 @@ __global__ __launch_bounds__(kBlock) void pad_fill_kernel(
 // - DeepEP", "Combine: reverse routing plus reduction")
 // ---------------------------------------------------------------------------
 
-// Rows are gathered in batches of KB slots so that KB x U 16-byte loads per
-// lane are in flight before the FMAs, which then run in slot order.
+// Rows are gathered in batches of KB slots: the batch's KB 16-byte loads per
+// lane are all issued before its FMAs, which then run in slot order.  They
+// are buffer loads over each slot's row (an empty buffer for a slot with no
+// row, a lane past the row's end given an offset past it), issued whatever
+// the slot and the lane and all consumed by the FMAs, with a select keeping
+// the sum of a slot with no row as it was; so the compiler's waits count
+// them exactly.  KB = 8 serves grids the chip holds at once (a decode-sized
+// batch, latency-bound: every row of the token in flight together).  KB = 1
+// serves larger grids: the chip is then full of waves anyway, and one row
+// load in flight per wave measured faster than several (more rows' pages
+// open at once in the memory queues).
 template <bool kWeighted, int KB>
 __global__ __launch_bounds__(kBlock) void combine_kernel(
     Dims d, int32_t nchunks, int64_t capacity, const uint16_t *__restrict__ y,
@@ -1385,71 +1396,60 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(
   const int64_t t = item / nchunks;
   const int chunk = item - (int)t * nchunks;
 
-  int32_t row = -1;
-  float gate = 0.0f;
-  if (lane < d.k) {
-    const int32_t r = tok_slot_row[t * d.k + lane];
-    if (r >= 0 && r < capacity) {
-      row = r;
-      if (kWeighted) gate = topk_weights[t * d.k + lane];
-    }
-  }
+  // The token's rows and gates, loaded together (lanes below k).
+  const uint32_t nk = (uint32_t)d.k * 4u;
+  const int koff = (int)(lane < d.k ? (uint32_t)lane * 4u : nk);
+  const int32_t r = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(
+      buffer_over(tok_slot_row + t * d.k, nk), koff, 0, 0);
+  const float gate =
+      kWeighted ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                buffer_over(topk_weights + t * d.k, nk), koff,
+                                                0, 0))
+                : 1.0f;
+  const int32_t row = lane < d.k && r >= 0 && r < capacity ? r : -1;
 
-  constexpr int U = kCombineCols / (kWave * 8);
   const int64_t H = d.H;
-  int col[U];
-  float acc[U][8];
+  const int col = chunk * kCombineCols + lane * 8;
+  const uint32_t nrow = (uint32_t)H * 2u;
+  const int off = (int)(col < H ? (uint32_t)col * 2u : nrow);
+  float acc[8];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    col[u] = chunk * kCombineCols + u * (kWave * 8) + lane * 8;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[u][i] = 0.0f;
-  }
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
 
   for (int jb = 0; jb < d.k; jb += KB) {
-    uint4 v[KB][U];
-    int32_t r[KB];
+    i32x4_t v[KB];
+    int32_t rj[KB];
 #pragma unroll
     for (int jj = 0; jj < KB; ++jj) {
-      r[jj] = (jb + jj < d.k) ? lane_value(row, jb + jj) : -1;
-      if (r[jj] >= 0) {
-        const uint16_t *src = y + (int64_t)r[jj] * H;
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-          if (col[u] < H) v[jj][u] = load_stream(src + col[u]);
-      }
+      rj[jj] = jb + jj < d.k ? lane_value(row, jb + jj) : -1;
+      const uint16_t *src = y + (int64_t)(rj[jj] >= 0 ? rj[jj] : 0) * H;
+      v[jj] = __builtin_amdgcn_raw_buffer_load_b128(buffer_over(src, rj[jj] >= 0 ? nrow : 0u),
+                                                    off, 0, kBufferNt);
     }
 #pragma unroll
     for (int jj = 0; jj < KB; ++jj) {
-      if (r[jj] < 0) continue;
-      const float g = kWeighted ? lane_value_f(gate, jb + jj) : 1.0f;
+      const bool use = rj[jj] >= 0;
+      const float g = kWeighted ? lane_value_f(gate, (jb + jj) & (kWave - 1)) : 1.0f;
+      const uint32_t w4[4] = {(uint32_t)v[jj].x, (uint32_t)v[jj].y, (uint32_t)v[jj].z,
+                              (uint32_t)v[jj].w};
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const uint32_t w4[4] = {v[jj][u].x, v[jj][u].y, v[jj][u].z, v[jj][u].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (kWeighted) {
-            acc[u][2 * i] = __builtin_fmaf(g, bf16_lo(w4[i]), acc[u][2 * i]);
-            acc[u][2 * i + 1] = __builtin_fmaf(g, bf16_hi(w4[i]), acc[u][2 * i + 1]);
-          } else {
-            acc[u][2 * i] = acc[u][2 * i] + bf16_lo(w4[i]);
-            acc[u][2 * i + 1] = acc[u][2 * i + 1] + bf16_hi(w4[i]);
-          }
-        }
+      for (int i = 0; i < 4; ++i) {
+        const float lo = bf16_lo(w4[i]), hi = bf16_hi(w4[i]);
+        const float a0 = kWeighted ? __builtin_fmaf(g, lo, acc[2 * i]) : acc[2 * i] + lo;
+        const float a1 = kWeighted ? __builtin_fmaf(g, hi, acc[2 * i + 1]) : acc[2 * i + 1] + hi;
+        acc[2 * i] = use ? a0 : acc[2 * i];
+        acc[2 * i + 1] = use ? a1 : acc[2 * i + 1];
       }
     }
   }
 
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    if (col[u] < H) {
-      uint4 o;
-      o.x = pack_bf16(acc[u][0], acc[u][1]);
-      o.y = pack_bf16(acc[u][2], acc[u][3]);
-      o.z = pack_bf16(acc[u][4], acc[u][5]);
-      o.w = pack_bf16(acc[u][6], acc[u][7]);
-      store_stream(out + t * H + col[u], o);
-    }
+  if (col < H) {
+    uint4 o;
+    o.x = pack_bf16(acc[0], acc[1]);
+    o.y = pack_bf16(acc[2], acc[3]);
+    o.z = pack_bf16(acc[4], acc[5]);
+    o.w = pack_bf16(acc[6], acc[7]);
+    store_stream(out + t * H + col, o);
   }
 }
 
@@ -2218,12 +2218,14 @@ hipError_t launch_combine(const Dims &d, int64_t capacity, const uint16_t *exper
   const int32_t nchunks = (d.H + kCombineCols - 1) / kCombineCols;
   const int64_t items = (int64_t)d.T * nchunks;
   const dim3 grid((unsigned)((items + kWavesPerBlock - 1) / kWavesPerBlock));
-  if (topk_weights != nullptr)
-    launch_kernel(true, combine_kernel<true, 8>, grid, dim3(kBlock), 0u, stream, d, nchunks,
-                  capacity, expert_out, tok_slot_row, topk_weights, out);
-  else
-    launch_kernel(true, combine_kernel<false, 8>, grid, dim3(kBlock), 0u, stream, d, nchunks,
-                  capacity, expert_out, tok_slot_row, topk_weights, out);
+  // One wave per item: up to kChipWaves items the chip holds them all at
+  // once, and the wide batches serve the latency-bound launch.
+  const bool wide = items <= kChipWaves;
+  auto kernel = topk_weights != nullptr
+                    ? (wide ? combine_kernel<true, 8> : combine_kernel<true, 1>)
+                    : (wide ? combine_kernel<false, 8> : combine_kernel<false, 1>);
+  launch_kernel(true, kernel, grid, dim3(kBlock), 0u, stream, d, nchunks, capacity, expert_out,
+                tok_slot_row, topk_weights, out);
   return hipGetLastError();
 }
 
