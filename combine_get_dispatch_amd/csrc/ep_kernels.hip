@@ -1374,17 +1374,63 @@ __global__ __launch_bounds__(kBlock) void pad_fill_kernel(
 // - DeepEP", "Combine: reverse routing plus reduction")
 // ---------------------------------------------------------------------------
 
-// Rows are gathered in batches of KB slots: the batch's KB 16-byte loads per
-// lane are all issued before its FMAs, which then run in slot order.  They
-// are buffer loads over each slot's row (an empty buffer for a slot with no
-// row, a lane past the row's end given an offset past it), issued whatever
-// the slot and the lane and all consumed by the FMAs, with a select keeping
-// the sum of a slot with no row as it was; so the compiler's waits count
-// them exactly.  KB = 8 serves grids the chip holds at once (a decode-sized
-// batch, latency-bound: every row of the token in flight together).  KB = 1
-// serves larger grids: the chip is then full of waves anyway, and one row
-// load in flight per wave measured faster than several (more rows' pages
-// open at once in the memory queues).
+// The fixed-order gather-reduce of one token's (or one non-expanded row's)
+// slots over its 8 columns at col: acc = sum over slots j in order of
+// g_j * y[row_j] (an FMA each from +0), or of y[row_j] unweighted, over the
+// slots with a row only.  Lane j below k holds slot j's row (-1 for none)
+// and gate.  The slots with a row are taken in slot order, KB at a time:
+// the batch's KB 16-byte loads per lane are all issued before its FMAs.
+// They are buffer loads over each slot's row (an empty buffer for a batch
+// entry past the last slot, a lane past the row's end given an offset past
+// it), issued whatever the entry and the lane and all consumed by the FMAs,
+// with a select keeping the sum as it was for an entry with no slot; so the
+// compiler's waits count them exactly (plain loads under a branch per slot
+// had it wait for each gather before issuing the next).  KB = 8 serves
+// grids the chip holds at once (a decode-sized batch, latency-bound: every
+// row of the token in flight together).  KB = 1 serves larger grids: the
+// chip is then full of waves anyway, and one row load in flight per wave
+// measured faster than several (more rows' pages open at once in the
+// memory queues).
+template <bool kWeighted, int KB>
+__device__ __forceinline__ void gather_rows(const uint16_t *__restrict__ y, int64_t H,
+                                            int32_t row, float gate, int col, float acc[8]) {
+  const uint32_t nrow = (uint32_t)H * 2u;
+  const int off = (int)(col < H ? (uint32_t)col * 2u : nrow);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+  unsigned long long left = __ballot(row >= 0);
+  while (left != 0ull) {
+    i32x4_t v[KB];
+    int32_t rj[KB];
+    int sj[KB];
+#pragma unroll
+    for (int jj = 0; jj < KB; ++jj) {
+      sj[jj] = left != 0ull ? (int)__builtin_ctzll(left) : -1;
+      left &= left - 1ull;
+      rj[jj] = sj[jj] >= 0 ? lane_value(row, sj[jj]) : -1;
+      const uint16_t *src = y + (int64_t)(rj[jj] >= 0 ? rj[jj] : 0) * H;
+      v[jj] = __builtin_amdgcn_raw_buffer_load_b128(buffer_over(src, rj[jj] >= 0 ? nrow : 0u),
+                                                    off, 0, kBufferNt);
+    }
+#pragma unroll
+    for (int jj = 0; jj < KB; ++jj) {
+      const bool use = rj[jj] >= 0;
+      const float g = kWeighted ? lane_value_f(gate, sj[jj] & (kWave - 1)) : 1.0f;
+      const uint32_t w4[4] = {(uint32_t)v[jj].x, (uint32_t)v[jj].y, (uint32_t)v[jj].z,
+                              (uint32_t)v[jj].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float lo = bf16_lo(w4[i]), hi = bf16_hi(w4[i]);
+        const float a0 = kWeighted ? __builtin_fmaf(g, lo, acc[2 * i]) : acc[2 * i] + lo;
+        const float a1 = kWeighted ? __builtin_fmaf(g, hi, acc[2 * i + 1]) : acc[2 * i + 1] + hi;
+        acc[2 * i] = use ? a0 : acc[2 * i];
+        acc[2 * i + 1] = use ? a1 : acc[2 * i + 1];
+      }
+    }
+  }
+}
+
+// One wave per (token, 512-column chunk).
 template <bool kWeighted, int KB>
 __global__ __launch_bounds__(kBlock) void combine_kernel(
     Dims d, int32_t nchunks, int64_t capacity, const uint16_t *__restrict__ y,
@@ -1410,39 +1456,8 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(
 
   const int64_t H = d.H;
   const int col = chunk * kCombineCols + lane * 8;
-  const uint32_t nrow = (uint32_t)H * 2u;
-  const int off = (int)(col < H ? (uint32_t)col * 2u : nrow);
   float acc[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-
-  for (int jb = 0; jb < d.k; jb += KB) {
-    i32x4_t v[KB];
-    int32_t rj[KB];
-#pragma unroll
-    for (int jj = 0; jj < KB; ++jj) {
-      rj[jj] = jb + jj < d.k ? lane_value(row, jb + jj) : -1;
-      const uint16_t *src = y + (int64_t)(rj[jj] >= 0 ? rj[jj] : 0) * H;
-      v[jj] = __builtin_amdgcn_raw_buffer_load_b128(buffer_over(src, rj[jj] >= 0 ? nrow : 0u),
-                                                    off, 0, kBufferNt);
-    }
-#pragma unroll
-    for (int jj = 0; jj < KB; ++jj) {
-      const bool use = rj[jj] >= 0;
-      const float g = kWeighted ? lane_value_f(gate, (jb + jj) & (kWave - 1)) : 1.0f;
-      const uint32_t w4[4] = {(uint32_t)v[jj].x, (uint32_t)v[jj].y, (uint32_t)v[jj].z,
-                              (uint32_t)v[jj].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float lo = bf16_lo(w4[i]), hi = bf16_hi(w4[i]);
-        const float a0 = kWeighted ? __builtin_fmaf(g, lo, acc[2 * i]) : acc[2 * i] + lo;
-        const float a1 = kWeighted ? __builtin_fmaf(g, hi, acc[2 * i + 1]) : acc[2 * i + 1] + hi;
-        acc[2 * i] = use ? a0 : acc[2 * i];
-        acc[2 * i + 1] = use ? a1 : acc[2 * i + 1];
-      }
-    }
-  }
-
+  gather_rows<kWeighted, KB>(y, H, row, gate, col, acc);
   if (col < H) {
     uint4 o;
     o.x = pack_bf16(acc[0], acc[1]);
@@ -1773,7 +1788,7 @@ __global__ __launch_bounds__(kBlock) void expand_kernel(
 
 // Ranked combine, stage 1: per non-expanded row, the fp32 sum of its local
 // slots' (weighted) expert rows in slot order.
-template <bool kWeighted>
+template <bool kWeighted, int KB>
 __global__ __launch_bounds__(kBlock) void combine_ranked_partial_kernel(
     Dims d, int32_t nchunks, int64_t capacity, int64_t ranked_capacity,
     const uint16_t *__restrict__ y, const int32_t *__restrict__ tok_slot_row,
@@ -1784,49 +1799,38 @@ __global__ __launch_bounds__(kBlock) void combine_ranked_partial_kernel(
   const int item = uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
   const int64_t q = item / nchunks;
   const int chunk = item - (int)q * nchunks;
+  if (q >= ranked_capacity) return;
+  // The row count first: the grid covers the capacity, and the rows past the
+  // count (a third to a half of them) should cost no more than that.  Then
+  // the row's source token, local ids and gates in one round trip, the
+  // expanded rows of the local slots in a second (buffer loads: zeros for
+  // lanes with nothing to load), then the gathers.  The empty asm statement
+  // taking the ids and gates keeps their loads before the source check,
+  // which the compiler would otherwise move first.
   const int64_t rows = rank_token_offsets[d.R];
-  if (q >= rows || q >= ranked_capacity) return;
-  const int64_t t = uniform(ne_src[q]);
-  if (t < 0 || t >= d.T) return;
-  int32_t row = -1;
-  float gate = 0.0f;
-  if (lane < d.k && ne_topk_idx[q * d.k + lane] >= 0) {
-    const int32_t p = tok_slot_row[t * d.k + lane];
-    if (p >= 0 && p < capacity) {
-      row = p;
-      if (kWeighted) gate = ne_topk_weights[q * d.k + lane];
-    }
-  }
+  if (q >= rows) return;
+  const int64_t t = ne_src[q];
+  const uint32_t nk = (uint32_t)d.k * 4u;
+  const int koff = (int)(lane < d.k ? (uint32_t)lane * 4u : nk);
+  int32_t le = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(
+      buffer_over(ne_topk_idx + q * d.k, nk), koff, 0, 0);
+  float gate =
+      kWeighted ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                buffer_over(ne_topk_weights + q * d.k, nk), koff,
+                                                0, 0))
+                : 1.0f;
+  asm volatile("" : "+v"(le), "+v"(gate));
+  const bool live = t >= 0 && t < d.T;
+  const bool local = live && lane < d.k && le >= 0;
+  const int32_t p = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(
+      buffer_over(tok_slot_row + (live ? t : 0) * d.k, nk),
+      (int)(local ? (uint32_t)lane * 4u : nk), 0, 0);
+  const int32_t row = local && p >= 0 && p < capacity ? p : -1;
+  if (!live) return;
   const int64_t H = d.H;
   const int col = chunk * kCombineCols + lane * 8;
   float acc[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-  for (int jb = 0; jb < d.k; jb += 8) {
-    uint4 v[8];
-    int32_t r[8];
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      r[jj] = (jb + jj < d.k) ? lane_value(row, jb + jj) : -1;
-      if (r[jj] >= 0 && col < H) v[jj] = load_stream(y + (int64_t)r[jj] * H + col);
-    }
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      if (r[jj] < 0) continue;
-      const float g = kWeighted ? lane_value_f(gate, jb + jj) : 1.0f;
-      const uint32_t w4[4] = {v[jj].x, v[jj].y, v[jj].z, v[jj].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (kWeighted) {
-          acc[2 * i] = __builtin_fmaf(g, bf16_lo(w4[i]), acc[2 * i]);
-          acc[2 * i + 1] = __builtin_fmaf(g, bf16_hi(w4[i]), acc[2 * i + 1]);
-        } else {
-          acc[2 * i] = acc[2 * i] + bf16_lo(w4[i]);
-          acc[2 * i + 1] = acc[2 * i + 1] + bf16_hi(w4[i]);
-        }
-      }
-    }
-  }
+  gather_rows<kWeighted, KB>(y, H, row, gate, col, acc);
   if (col < H) {
     // Plain (not streaming) stores: the partials are read again by stage 2
     // right away.  Measured over a whole non-expanded step, they save more
@@ -2326,14 +2330,16 @@ hipError_t launch_combine_ranked(const Dims &d, int64_t capacity, int64_t ranked
   if (ranked_capacity > 0) {
     const int64_t items = ranked_capacity * nchunks;
     const dim3 grid((unsigned)((items + kWavesPerBlock - 1) / kWavesPerBlock));
-    if (ne_topk_weights != nullptr)
-      hipLaunchKernelGGL(combine_ranked_partial_kernel<true>, grid, dim3(kBlock), 0, stream, d,
-                         nchunks, capacity, ranked_capacity, y, tok_slot_row, ne_topk_idx,
-                         ne_topk_weights, ne_src, rank_token_offsets, partials);
-    else
-      hipLaunchKernelGGL(combine_ranked_partial_kernel<false>, grid, dim3(kBlock), 0, stream, d,
-                         nchunks, capacity, ranked_capacity, y, tok_slot_row, ne_topk_idx,
-                         ne_topk_weights, ne_src, rank_token_offsets, partials);
+    // The gathers' batch width as in launch_combine.
+    const bool wide = items <= kChipWaves;
+    auto kernel = ne_topk_weights != nullptr
+                      ? (wide ? combine_ranked_partial_kernel<true, 8>
+                              : combine_ranked_partial_kernel<true, 1>)
+                      : (wide ? combine_ranked_partial_kernel<false, 8>
+                              : combine_ranked_partial_kernel<false, 1>);
+    hipLaunchKernelGGL(kernel, grid, dim3(kBlock), 0, stream, d, nchunks, capacity,
+                       ranked_capacity, y, tok_slot_row, ne_topk_idx, ne_topk_weights, ne_src,
+                       rank_token_offsets, partials);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
