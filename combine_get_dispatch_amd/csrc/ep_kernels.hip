@@ -1024,10 +1024,12 @@ __device__ __forceinline__ int slice_col(int chunk, int lane, int u) {
 
 template <bool kFp8>
 __device__ __forceinline__ XSlice load_x_slice(const uint16_t *__restrict__ x, int64_t t,
-                                               int64_t H, int chunk, int lane) {
-  // Buffer loads over the token's row: a part past its end reads zeros.
-  const uint32_t n = (uint32_t)H * 2u;
-  const __amdgpu_buffer_rsrc_t rsrc = buffer_over(x + t * H, n);
+                                               int64_t H, int chunk, int lane,
+                                               bool live = true) {
+  // Buffer loads over the token's row: a part past its end reads zeros, and
+  // so does every part when live is false (an empty buffer).
+  const uint32_t n = live ? (uint32_t)H * 2u : 0u;
+  const __amdgpu_buffer_rsrc_t rsrc = buffer_over(x + (live ? t : 0) * H, n);
   XSlice xs;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -1193,22 +1195,29 @@ __global__ __launch_bounds__(kBlock) void layout_dispatch_kernel(
   const bool has_item = !lead && item < (int64_t)d.T * nchunks;
   const int64_t ti = has_item ? item / nchunks : 0;
   const int chunk = has_item ? (int)(item - ti * nchunks) : 0;
-  // The count waits on the batch's ids, so they are loaded first.
+  // The count waits on the batch's ids, so they are loaded first; then the
+  // x slice, the item token's ids and (for the handle) its gate, by buffer
+  // loads issued whatever the wave (an empty buffer when it has no item), so
+  // that the count's wait for the ids counts the later loads and leaves
+  // them in flight (loads return in issue order; in a branch they made the
+  // compiler wait for all of them).  The gate is loaded here too: a
+  // load issued after the handle's stores would make the wave wait for those
+  // stores before its row stores.
   int32_t ex[K];
   load_ids<K>(d, t, live, topk_idx, ex);
-  XSlice xs;
-  xs.v[0] = xs.v[1] = make_uint4(0, 0, 0, 0);
-  // The gate is loaded here too: a load issued after the handle's stores
-  // would make the wave wait for those stores before its row stores.
-  int32_t eid = -1;
-  float gate = 0.0f;
-  if (has_item) {
-    xs = load_x_slice<kFp8>(x, ti, d.H, chunk, lane);
-    if (lane < d.k) {
-      eid = topk_idx[ti * d.k + lane];
-      if (chunk == 0 && topk_weights != nullptr) gate = topk_weights[ti * d.k + lane];
-    }
-  }
+  const XSlice xs = load_x_slice<kFp8>(x, ti, d.H, chunk, lane, has_item);
+  const uint32_t nki = has_item ? (uint32_t)d.k * 4u : 0u;
+  const int koff = (int)(lane < d.k ? (uint32_t)lane * 4u : nki);
+  const int32_t eid_l = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(
+      buffer_over(topk_idx + ti * d.k, nki), koff, 0, 0);
+  const bool gates = has_item && chunk == 0 && topk_weights != nullptr;
+  const float gate = __builtin_bit_cast(
+      float, __builtin_amdgcn_raw_buffer_load_b32(
+                 buffer_over(gates ? static_cast<const void *>(topk_weights + ti * d.k)
+                                   : static_cast<const void *>(topk_idx),
+                             gates ? nki : 0u),
+                 koff, 0, 0));
+  const int32_t eid = has_item && lane < d.k ? eid_l : -1;
 
   // Every workgroup counts, also for an empty batch (no live token: zero
   // counts, and no ballots, for which the workspace then has no room).  A
