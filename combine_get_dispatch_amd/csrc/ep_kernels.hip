@@ -1394,12 +1394,13 @@ __global__ __launch_bounds__(kBlock) void pad_fill_kernel(
 // it), issued whatever the entry and the lane and all consumed by the FMAs,
 // with a select keeping the sum as it was for an entry with no slot; so the
 // compiler's waits count them exactly (plain loads under a branch per slot
-// had it wait for each gather before issuing the next).  KB = 8 serves
-// grids the chip holds at once (a decode-sized batch, latency-bound: every
-// row of the token in flight together).  KB = 1 serves larger grids: the
-// chip is then full of waves anyway, and one row load in flight per wave
-// measured faster than several (more rows' pages open at once in the
-// memory queues).
+// had it wait for each gather before issuing the next).  combine_kernel
+// takes KB = 1 while the chip is full of waves: one row load in flight per
+// wave then measured faster than several (more rows' pages open at once in
+// the memory queues).  Its last kChipWaves work items take KB = 8 (every
+// row of the token in flight together): they run while the chip empties,
+// where a wave's latency is the launch's tail, and a grid the chip holds
+// at once (a decode-sized batch) is all tail.
 template <bool kWeighted, int KB>
 __device__ __forceinline__ void gather_rows(const uint16_t *__restrict__ y, int64_t H,
                                             int32_t row, float gate, int col, float acc[8]) {
@@ -1440,7 +1441,7 @@ __device__ __forceinline__ void gather_rows(const uint16_t *__restrict__ y, int6
 }
 
 // One wave per (token, 512-column chunk).
-template <bool kWeighted, int KB>
+template <bool kWeighted>
 __global__ __launch_bounds__(kBlock) void combine_kernel(
     Dims d, int32_t nchunks, int64_t capacity, const uint16_t *__restrict__ y,
     const int32_t *__restrict__ tok_slot_row, const float *__restrict__ topk_weights,
@@ -1466,7 +1467,10 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(
   const int64_t H = d.H;
   const int col = chunk * kCombineCols + lane * 8;
   float acc[8];
-  gather_rows<kWeighted, KB>(y, H, row, gate, col, acc);
+  if (item >= d.T * nchunks - kChipWaves)
+    gather_rows<kWeighted, 8>(y, H, row, gate, col, acc);
+  else
+    gather_rows<kWeighted, 1>(y, H, row, gate, col, acc);
   if (col < H) {
     uint4 o;
     o.x = pack_bf16(acc[0], acc[1]);
@@ -2231,12 +2235,7 @@ hipError_t launch_combine(const Dims &d, int64_t capacity, const uint16_t *exper
   const int32_t nchunks = (d.H + kCombineCols - 1) / kCombineCols;
   const int64_t items = (int64_t)d.T * nchunks;
   const dim3 grid((unsigned)((items + kWavesPerBlock - 1) / kWavesPerBlock));
-  // One wave per item: up to kChipWaves items the chip holds them all at
-  // once, and the wide batches serve the latency-bound launch.
-  const bool wide = items <= kChipWaves;
-  auto kernel = topk_weights != nullptr
-                    ? (wide ? combine_kernel<true, 8> : combine_kernel<true, 1>)
-                    : (wide ? combine_kernel<false, 8> : combine_kernel<false, 1>);
+  auto kernel = topk_weights != nullptr ? combine_kernel<true> : combine_kernel<false>;
   launch_kernel(true, kernel, grid, dim3(kBlock), 0u, stream, d, nchunks, capacity, expert_out,
                 tok_slot_row, topk_weights, out);
   return hipGetLastError();
@@ -2339,7 +2338,11 @@ hipError_t launch_combine_ranked(const Dims &d, int64_t capacity, int64_t ranked
   if (ranked_capacity > 0) {
     const int64_t items = ranked_capacity * nchunks;
     const dim3 grid((unsigned)((items + kWavesPerBlock - 1) / kWavesPerBlock));
-    // The gathers' batch width as in launch_combine.
+    // KB = 8 only for a grid the chip holds at once: a non-expanded row has
+    // few local slots (1.5 to 2 of 8 in the workloads), so a wide batch is
+    // mostly empty entries, and as the tail of a large grid (as combine_kernel
+    // takes it) it measured slower (Large 1083 -> 1093 us).  One kernel
+    // holding both widths also measured slower than either alone.
     const bool wide = items <= kChipWaves;
     auto kernel = ne_topk_weights != nullptr
                       ? (wide ? combine_ranked_partial_kernel<true, 8>
