@@ -161,6 +161,26 @@ def test_wide_rows(H, fp8):
                           oracle.combine(y, do["tok_slot_row"], w)[0])
 
 
+@pytest.mark.parametrize("T,H,mask", [(8191, 512, 0.0), (8193, 512, 0.05), (4097, 1024, 0.3),
+                                      (16385, 512, 0.0), (5000, 8, 0.05)])
+def test_combine_both_gather_widths(T, H, mask):
+    """Combine gathers a token's rows one at a time, except in the launch's
+    last 8192 work items (one wave per token and 512-column chunk), which
+    gather all of them at once; a grid of at most 8192 items is all tail.
+    Grids just below, at and above that size, with masked slots, weighted
+    and unweighted, bit for bit against the oracle."""
+    k, E, R = 8, 64, 8
+    rng = np.random.default_rng(T * 7 + H)
+    idx = W.random_routes(rng, T, E, k, mask_prob=mask)
+    x = W.normal_bf16(rng, (T, H))
+    w = rng.random((T, k)).astype(np.float32)
+    cap = T * k
+    tsr = oracle.dispatch(x, idx, w, E, R, 1, fp8=False, capacity=cap)["tok_slot_row"]
+    y = W.normal_bf16(rng, (cap, H))
+    for weights in (w, None):
+        assert np.array_equal(GPU.combine(y, tsr, weights), oracle.combine(y, tsr, weights)[0])
+
+
 def _raw_run(T, H, k, E, R, idx, capacity=None, x=None):
     b = ep.EpBuffers(T, H, k, E, R, 1, capacity=capacity)
     b.status.zero_()
