@@ -70,6 +70,8 @@ def test_ranked_workloads(name):
     (300, 24, 3, 16, 4, 1, False), (257, 136, 2, 80, 40, 1, False), (100, 128, 4, 128, 64, 2, True),
     (1000, 1032, 8, 64, 8, 4, False), (513, 384, 6, 24, 3, 8, True), (1, 256, 2, 4, 2, 1, True),
     (700, 2056, 5, 40, 5, 1, False), (64, 128, 8, 8, 8, 1, False),
+    # Rows wider than one expand wave's batch of 8 column chunks (H > 8192).
+    (40, 9216, 4, 16, 4, 1, True), (33, 8200, 3, 12, 3, 2, False), (17, 16512, 8, 8, 2, 1, True),
 ])
 def test_ranked_random_small(case):
     T, H, k, E, R, A, fp8 = case
