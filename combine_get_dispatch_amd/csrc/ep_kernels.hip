@@ -1858,7 +1858,48 @@ __global__ __launch_bounds__(kBlock) void combine_ranked_partial_kernel(
 }
 
 // Ranked combine, stage 2: per token, the fp32 sum of its ranks' partials in
-// rank order, rounded once to bf16.
+// rank order, rounded once to bf16.  Lane r below R holds the token's row on
+// rank r (-1 for none); the ranks with a row are taken in rank order, KB at
+// a time, with the loads of gather_rows: buffer loads (two 16-byte parts per
+// lane of a row's 8 fp32 columns) issued whatever the entry, all consumed
+// through a select, so the waits count them exactly.
+template <int KB>
+__device__ __forceinline__ void sum_partials(const float *__restrict__ partials, int64_t H,
+                                             int32_t q, int col, float acc[8]) {
+  const uint32_t nrow = (uint32_t)H * 4u;
+  const uint32_t off = col < H ? (uint32_t)col * 4u : nrow;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+  unsigned long long left = __ballot(q >= 0);
+  while (left != 0ull) {
+    i32x4_t a[KB], b[KB];
+    int32_t qj[KB];
+#pragma unroll
+    for (int jj = 0; jj < KB; ++jj) {
+      const int s = left != 0ull ? (int)__builtin_ctzll(left) : -1;
+      left &= left - 1ull;
+      qj[jj] = s >= 0 ? lane_value(q, s) : -1;
+      const __amdgpu_buffer_rsrc_t rsrc =
+          buffer_over(partials + (int64_t)(qj[jj] >= 0 ? qj[jj] : 0) * H, qj[jj] >= 0 ? nrow : 0u);
+      a[jj] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)off, 0, kBufferNt);
+      b[jj] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)(off + 16u), 0, kBufferNt);
+    }
+#pragma unroll
+    for (int jj = 0; jj < KB; ++jj) {
+      const bool use = qj[jj] >= 0;
+      const float v[8] = {__int_as_float(a[jj].x), __int_as_float(a[jj].y),
+                          __int_as_float(a[jj].z), __int_as_float(a[jj].w),
+                          __int_as_float(b[jj].x), __int_as_float(b[jj].y),
+                          __int_as_float(b[jj].z), __int_as_float(b[jj].w)};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = use ? acc[i] + v[i] : acc[i];
+    }
+  }
+}
+
+// One wave per (token, 512-column chunk); the launch's last kChipWaves work
+// items take every rank's row at once, the others one at a time, as in
+// combine_kernel.
 __global__ __launch_bounds__(kBlock) void combine_ranked_sum_kernel(
     Dims d, int32_t nchunks, int64_t ranked_capacity, const float *__restrict__ partials,
     const int32_t *__restrict__ tok_rank_row, uint16_t *__restrict__ out) {
@@ -1867,43 +1908,18 @@ __global__ __launch_bounds__(kBlock) void combine_ranked_sum_kernel(
   if (item >= d.T * nchunks) return;
   const int64_t t = item / nchunks;
   const int chunk = item - (int)t * nchunks;
-  int32_t q = -1;
-  if (lane < d.R) {
-    const int32_t v = tok_rank_row[t * d.R + lane];
-    if (v >= 0 && v < ranked_capacity) q = v;
-  }
+  const uint32_t nr = (uint32_t)d.R * 4u;
+  const int32_t v = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(
+      buffer_over(tok_rank_row + t * d.R, nr), (int)(lane < d.R ? (uint32_t)lane * 4u : nr), 0,
+      0);
+  const int32_t q = lane < d.R && v >= 0 && v < ranked_capacity ? v : -1;
   const int64_t H = d.H;
   const int col = chunk * kCombineCols + lane * 8;
   float acc[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-  // Ranks in batches of 8: the batch's loads are all issued before the
-  // first add, and the adds run in rank order.
-  for (int rb = 0; rb < d.R; rb += 8) {
-    int32_t qq[8];
-    uint4 a[8], b[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      qq[i] = rb + i < d.R ? lane_value(q, rb + i) : -1;
-      if (qq[i] >= 0 && col < H) {
-        const float *src = partials + (int64_t)qq[i] * H + col;
-        a[i] = load_stream(src);
-        b[i] = load_stream(src + 4);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (qq[i] < 0 || col >= H) continue;
-      acc[0] += __uint_as_float(a[i].x);
-      acc[1] += __uint_as_float(a[i].y);
-      acc[2] += __uint_as_float(a[i].z);
-      acc[3] += __uint_as_float(a[i].w);
-      acc[4] += __uint_as_float(b[i].x);
-      acc[5] += __uint_as_float(b[i].y);
-      acc[6] += __uint_as_float(b[i].z);
-      acc[7] += __uint_as_float(b[i].w);
-    }
-  }
+  if (item >= d.T * nchunks - kChipWaves)
+    sum_partials<8>(partials, H, q, col, acc);
+  else
+    sum_partials<1>(partials, H, q, col, acc);
   if (col < H) {
     uint4 o;
     o.x = pack_bf16(acc[0], acc[1]);
