@@ -133,13 +133,52 @@ def _code_only(text: str) -> str:
     return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
 
 
+_IDENT = re.compile(r"\b[A-Za-z_]\w*\b")
+_ATTRIBUTE = re.compile(r"\b(?:__\w+__|alignas)\s*\((?:[^()]|\([^()]*\))*\)")
+_ONE_FUNCTION = re.compile(
+    r"(?:template\s*<[^{};]*>\s*)?[^{};()]*?\b(\w+)\s*\([^{};]*\)\s*(?:const\s*)?\{\}")
+_ONE_STRUCT = re.compile(r"(?:template\s*<[^{};]*>\s*)?struct\s+(\w+)[^{};]*\{\};")
+
+
+def _outside_braces(code: str) -> str:
+    """The code with the inside of every top-level brace pair dropped."""
+    out, depth = [], 0
+    for ch in code:
+        if ch == "{":
+            if depth == 0:
+                out.append(ch)
+            depth += 1
+        elif ch == "}":
+            depth -= 1
+            if depth == 0:
+                out.append(ch)
+        elif depth == 0:
+            out.append(ch)
+    return "".join(out)
+
+
+def _sole_definition(piece: str):
+    """The name of the one function or struct a helper piece defines, or None
+    when the piece holds anything besides (constants, typedefs, variables,
+    preprocessor lines, a namespace, a second definition)."""
+    top = _ATTRIBUTE.sub("", _outside_braces(_code_only(piece))).strip()
+    for pattern in (_ONE_FUNCTION, _ONE_STRUCT):
+        m = pattern.fullmatch(top)
+        if m:
+            return m.group(1)
+    return None
+
+
 def kernel_source_hash(kernel: str = None, src: str = None, extra: bytes = None) -> str:
-    """Hash of what a kernel's measured behaviour depends on: every helper
-    piece of the kernel source (anything that is neither a kernel nor a
-    launcher), the kernel's own function and launcher, the internal header
-    and the compiler flags, all without comments.  With kernel=None, the
-    whole sources.  Editing another kernel, or a comment, leaves a kernel's
-    hash unchanged."""
+    """Hash of what a kernel's measured behaviour depends on: the kernel's
+    own function and launcher, the helper pieces of the kernel source
+    (anything that is neither a kernel nor a launcher) that they use, the
+    internal header and the compiler flags, all without comments.  A helper
+    piece that defines one function or struct is used when its name appears
+    in a piece already taken, followed to a fixed point; every other helper
+    piece is always taken.  With kernel=None, the whole sources.  Editing
+    another kernel, a helper only other kernels use, or a comment leaves a
+    kernel's hash unchanged."""
     h = hashlib.sha256()
     if src is None:
         with open(KERNEL_SOURCES[0]) as f:
@@ -157,9 +196,27 @@ def kernel_source_hash(kernel: str = None, src: str = None, extra: bytes = None)
         h.update(_code_only(src).encode())
         return h.hexdigest()[:16]
     kname, lname = KERNEL_FUNCS[kernel]
-    for piece in split_functions(src):
+    pieces = split_functions(src)
+    taken = [False] * len(pieces)
+    used = set()
+    helpers = []
+    for i, piece in enumerate(pieces):
         kind, name = _piece_name(piece)
-        if kind == "helper" or name in (kname, lname):
+        if name in (kname, lname):
+            taken[i] = True
+            used |= set(_IDENT.findall(_code_only(piece)))
+        elif kind == "helper":
+            helpers.append((i, _sole_definition(piece)))
+    grew = True
+    while grew:
+        grew = False
+        for i, name in helpers:
+            if not taken[i] and (name is None or name in used):
+                taken[i] = True
+                used |= set(_IDENT.findall(_code_only(pieces[i])))
+                grew = True
+    for piece, take in zip(pieces, taken):
+        if take:
             h.update(_code_only(piece).encode())
     return h.hexdigest()[:16]
 

@@ -43,6 +43,75 @@ def test_hash_follows_kernel_launcher_and_helpers():
     assert _h(SRC, "dispatch") != _h(SRC.replace("p[0] = 2;", "p[0] = 3;"), "dispatch")
 
 
+SRC_USES = """// helpers
+__device__ int inner(int v) { return v * 3;
+}
+__device__ int outer(int v) { return inner(v) + 1;
+}
+struct Pair {
+  int a, b;
+};
+__device__ int other_only(int v) { return v - 1;
+}
+constexpr int kUnused = 4;
+__device__ int next_to_a_constant(int v) { return v;
+}
+template <bool kWeighted, int KB>
+__global__ __launch_bounds__(kBlock) void combine_kernel(int *p) {
+  Pair q{1, 2};
+  p[0] = outer(q.a);
+}
+template <bool kFp8>
+__global__ __launch_bounds__(kBlock) void dispatch_kernel(int *p) {
+  p[0] = other_only(2);
+}
+hipError_t launch_combine(int *p) {
+  return hipSuccess;
+}
+"""
+
+
+def test_hash_follows_only_the_helpers_the_kernel_uses():
+    base = _h(SRC_USES)
+    # used directly, through another helper, or as a type
+    assert base != _h(SRC_USES.replace("inner(v) + 1", "inner(v) + 2"))
+    assert base != _h(SRC_USES.replace("v * 3", "v * 4"))
+    assert base != _h(SRC_USES.replace("int a, b;", "int a, b, c;"))
+    # used by another kernel only
+    assert base == _h(SRC_USES.replace("v - 1", "v - 2"))
+    assert _h(SRC_USES, "dispatch") != _h(SRC_USES.replace("v - 1", "v - 2"), "dispatch")
+    # a piece holding more than one definition is always taken
+    assert base != _h(SRC_USES.replace("kUnused = 4", "kUnused = 5"))
+
+
+def test_measured_kernels_take_their_helpers_from_the_real_source():
+    with open(bench.KERNEL_SOURCES[0]) as f:
+        src = f.read()
+    names = {bench._sole_definition(p) for p in bench.split_functions(src)
+             if bench._piece_name(p)[0] == "helper"}
+    # helpers of each measured kernel are recognised as single definitions
+    for helper in ("gather_rows", "quantize16", "load_x_slice", "count_tile", "scan_counts",
+                   "launch_kernel"):
+        assert helper in names
+
+    def edited(helper, kernel):
+        pieces = bench.split_functions(src)
+        for i, p in enumerate(pieces):
+            if bench._piece_name(p)[0] == "helper" and bench._sole_definition(p) == helper:
+                body = p.rstrip()
+                pieces[i] = body[:-1] + "  (void)0;\n}\n"
+        return bench.kernel_source_hash(kernel, src="".join(pieces), extra=b"")
+
+    def plain(kernel):
+        return bench.kernel_source_hash(kernel, src=src, extra=b"")
+
+    assert edited("gather_rows", "combine") != plain("combine")
+    assert edited("quantize16", "dispatch") != plain("dispatch")
+    assert edited("count_tile", "layout") != plain("layout")
+    assert edited("quantize16", "combine") == plain("combine")
+    assert edited("gather_rows", "layout") == plain("layout")
+
+
 def test_every_measured_kernel_is_found_in_the_source():
     with open(bench.KERNEL_SOURCES[0]) as f:
         src = f.read()
