@@ -16,9 +16,10 @@
 //                         x chunk once with 16-byte loads, optionally
 //                         quantises it to E4M3 in registers, and stores it to
 //                         each of the token's receive rows.
-//   combine_kernel        one wave per (token, 512-column chunk): k gathered
-//                         16-byte loads per lane, fp32 FMAs in slot order,
-//                         one bf16 rounding, one 16-byte store.
+//   combine_kernel        one one-wave workgroup per (token, 512-column
+//                         chunk): k gathered 16-byte loads per lane, fp32
+//                         FMAs in slot order, one bf16 rounding, one
+//                         16-byte store.
 //   layout_dispatch_kernel  layout and dispatch in one launch for at most
 //                         256 tokens: every workgroup recounts the batch in
 //                         LDS; workgroup 0 writes the layout outputs and the
