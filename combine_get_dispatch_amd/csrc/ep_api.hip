@@ -28,6 +28,14 @@ ep_status_t hip_fail(hipError_t err, const char *what) {
   return fail(EP_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
 }
 
+// Work items one launch holds.  The item kernels run one 64-lane wave per
+// work item (a token or non-expanded row and a 512-column chunk at most), in
+// workgroups of at most four waves, and a launch holds fewer than 2^32 work
+// items of one lane each: ceil(items / 4) * 256 <= 2^32 - 1.
+constexpr int64_t kMaxLaunchItems = (int64_t{1} << 26) - 4;
+// Tokens combine backward holds: one 256-lane workgroup per token.
+constexpr int64_t kMaxBackwardTokens = (int64_t{1} << 24) - 1;
+
 ep_status_t check_config(const ep_config_t *c) {
   if (c == nullptr) return fail(EP_ERR_INVALID_ARG, "config is NULL");
   if (c->num_tokens < 0) return fail(EP_ERR_INVALID_ARG, "num_tokens %d < 0", c->num_tokens);
@@ -51,8 +59,11 @@ ep_status_t check_config(const ep_config_t *c) {
     return fail(EP_ERR_INVALID_ARG, "T*k + E*(A-1) = %lld does not fit int32 row indices",
                 (long long)rows);
   const int64_t chunks = (c->hidden + ep::kCombineCols - 1) / ep::kCombineCols;
-  if ((int64_t)c->num_tokens * chunks >= INT32_MAX)
-    return fail(EP_ERR_INVALID_ARG, "num_tokens x hidden too large");
+  if ((int64_t)c->num_tokens * chunks > kMaxLaunchItems)
+    return fail(EP_ERR_INVALID_ARG,
+                "num_tokens x hidden too large: %lld (token, 512-column) items, at most %lld "
+                "fit one launch",
+                (long long)((int64_t)c->num_tokens * chunks), (long long)kMaxLaunchItems);
   return EP_OK;
 }
 
@@ -77,6 +88,17 @@ ep_status_t check_dtype(const ep_config_t *c, ep_dtype_t recv_dtype, bool *fp8) 
 ep_status_t check_rows(const char *what, int64_t rows) {
   if (rows < 0 || rows >= INT32_MAX)
     return fail(EP_ERR_INVALID_ARG, "%s %lld outside [0, 2^31 - 1)", what, (long long)rows);
+  return EP_OK;
+}
+
+// Non-expanded rows whose (row, 512-column chunk) items fit one launch.
+ep_status_t check_ranked_items(int64_t ranked_capacity, int32_t hidden) {
+  const int64_t chunks = (hidden + ep::kCombineCols - 1) / ep::kCombineCols;
+  if (ranked_capacity * chunks > kMaxLaunchItems)
+    return fail(EP_ERR_INVALID_ARG,
+                "ranked_capacity %lld x hidden %d too large: at most %lld (row, 512-column) "
+                "items fit one launch",
+                (long long)ranked_capacity, hidden, (long long)kMaxLaunchItems);
   return EP_OK;
 }
 
@@ -355,6 +377,11 @@ ep_status_t ep_combine_backward(const ep_handle_t *handle, const uint16_t *grad_
   if (handle == nullptr) return fail(EP_ERR_INVALID_ARG, "handle is NULL");
   EP_TRY(check_config(&handle->config));
   EP_TRY(check_rows("handle capacity", handle->capacity));
+  if (handle->config.num_tokens > kMaxBackwardTokens)
+    return fail(EP_ERR_INVALID_ARG,
+                "num_tokens %d too large for combine backward (one workgroup per token, at "
+                "most %lld)",
+                handle->config.num_tokens, (long long)kMaxBackwardTokens);
   const bool empty = handle->config.num_tokens == 0;
   if ((!empty && (handle->tok_slot_row == nullptr || grad_out == nullptr)) ||
       (handle->capacity > 0 && grad_expert_out == nullptr) ||
@@ -395,6 +422,7 @@ ep_status_t ep_dispatch_ranked(const ep_config_t *cfg, ep_dtype_t recv_dtype, co
   EP_TRY(check_dtype(cfg, recv_dtype, &fp8));
   EP_TRY(check_rows("capacity", capacity));
   EP_TRY(check_rows("ranked_capacity", ranked_capacity));
+  EP_TRY(check_ranked_items(ranked_capacity, cfg->hidden));
   const bool empty = cfg->num_tokens == 0;
   if ((!empty && (x == nullptr || topk_idx == nullptr || tok_rank_row == nullptr ||
                   tok_slot_row == nullptr)) ||
@@ -431,6 +459,7 @@ static ep_status_t check_ranked(const ep_ranked_handle_t *h) {
   EP_TRY(check_config(&h->config));
   EP_TRY(check_rows("handle capacity", h->capacity));
   EP_TRY(check_rows("handle ranked_capacity", h->ranked_capacity));
+  EP_TRY(check_ranked_items(h->ranked_capacity, h->config.hidden));
   if (h->rank_token_offsets == nullptr ||
       (h->config.num_tokens > 0 && (h->tok_rank_row == nullptr || h->tok_slot_row == nullptr)) ||
       (h->ranked_capacity > 0 && (h->ne_topk_idx == nullptr || h->ne_src == nullptr)))
@@ -475,11 +504,6 @@ ep_status_t ep_combine_ranked(const ep_ranked_handle_t *ranked, const uint16_t *
                               int32_t weighted, float *partials, uint16_t *out,
                               hipStream_t stream) {
   EP_TRY(check_ranked(ranked));
-  // stage 1 numbers its (row, 512-column chunk) items with int32
-  const int64_t chunks = (ranked->config.hidden + ep::kCombineCols - 1) / ep::kCombineCols;
-  if (ranked->ranked_capacity * chunks >= INT32_MAX)
-    return fail(EP_ERR_INVALID_ARG, "ranked_capacity %lld x hidden %d too large",
-                (long long)ranked->ranked_capacity, ranked->config.hidden);
   if (weighted && ranked->ranked_capacity > 0 && ranked->ne_topk_weights == nullptr)
     return fail(EP_ERR_INVALID_ARG, "weighted combine needs ne_topk_weights in the handle");
   if ((ranked->config.num_tokens > 0 && out == nullptr) ||

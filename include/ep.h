@@ -89,7 +89,9 @@ typedef enum ep_dtype {
 typedef struct ep_config {
   int32_t num_tokens;       /* T >= 0 */
   int32_t hidden;           /* H >= 8, H % 8 == 0 (H % 128 == 0 for FP8);
-                               T * ceil(H / 512) < 2^31 */
+                               T * ceil(H / 512) <= 2^26 - 4: one 64-lane
+                               wave per (token, 512-column chunk), and a
+                               launch holds fewer than 2^32 lanes */
   int32_t num_topk;         /* 1 <= k <= min(E, EP_MAX_TOPK) */
   int32_t num_experts;      /* 1 <= E <= EP_MAX_EXPERTS */
   int32_t num_ranks;        /* 1 <= R <= EP_MAX_RANKS, E % R == 0 */
@@ -120,7 +122,8 @@ typedef struct ep_handle {
 typedef struct ep_ranked_handle {
   ep_config_t config;
   int64_t capacity;                  /* expanded rows (expert-major buffers) */
-  int64_t ranked_capacity;           /* non-expanded rows */
+  int64_t ranked_capacity;           /* non-expanded rows;
+                                        ranked_capacity * ceil(H / 512) <= 2^26 - 4 */
   const int32_t *rank_token_offsets; /* [R + 1]: rank r's rows are [off[r], off[r+1]) */
   const int32_t *tok_rank_row;       /* [T, R]: non-expanded row of (t, r), -1 if none */
   const int32_t *tok_slot_row;       /* [T, k]: expanded row of (t, j), -1 if unused */
@@ -398,6 +401,7 @@ ep_status_t ep_dispatch_backward(const ep_handle_t *handle, const uint16_t *grad
  *                    for grad_weights)
  *   grad_expert_out  [capacity, H] bf16 out
  *   grad_weights     [T, k] fp32 out, or NULL to skip the gate gradient
+ * Rejects (EP_ERR_INVALID_ARG) T >= 2^24: one 256-lane workgroup per token.
  */
 ep_status_t ep_combine_backward(const ep_handle_t *handle, const uint16_t *grad_out,
                                 const float *topk_weights, const uint16_t *expert_out,
@@ -428,7 +432,8 @@ ep_status_t ep_ranked_capacity_rows(const ep_config_t *cfg, int64_t *rows_host);
  *
  *   workspace / expert_offsets  from ep_get_dispatch_layout of this route
  *   capacity         rows of the expanded buffers (for tok_slot_row)
- *   ranked_capacity  rows of ne_x / ne_scales / ne_topk_* / ne_src
+ *   ranked_capacity  rows of ne_x / ne_scales / ne_topk_* / ne_src;
+ *                    ranked_capacity * ceil(H / 512) <= 2^26 - 4
  *   ne_x             [ranked_capacity, H] bf16 or uint8 (E4M3) out
  *   ne_scales        [ranked_capacity, H/128] fp32 out (FP8 only)
  *   ne_topk_idx      [ranked_capacity, k] int32 out
@@ -480,7 +485,8 @@ ep_status_t ep_expand(const ep_ranked_handle_t *ranked, ep_dtype_t recv_dtype, c
  *   expert_out  [capacity, H] bf16
  *   partials    [ranked_capacity, H] fp32 scratch/out
  *   out         [T, H] bf16 out
- * Also rejects (EP_ERR_INVALID_ARG) ranked_capacity * ceil(H / 512) >= 2^31.
+ * Rejects (EP_ERR_INVALID_ARG), as every call taking a ranked handle does,
+ * ranked_capacity * ceil(H / 512) > 2^26 - 4.
  */
 ep_status_t ep_combine_ranked(const ep_ranked_handle_t *ranked, const uint16_t *expert_out,
                               int32_t weighted, float *partials, uint16_t *out,

@@ -143,20 +143,38 @@ def test_layout_dispatch_rejects_bad_arguments_before_launch():
 
 
 def test_combine_ranked_rejects_item_overflow_before_launch():
-    """The ranked combine numbers its (row, 512-column chunk) items with
-    int32; a handle whose rows x chunks would overflow that is rejected
-    before anything is enqueued (2^24 tokens, top-32 over 32 ranks, hidden
-    7168: 2^29 rows x 14 chunks)."""
+    """The ranked combine runs one 64-lane wave per (row, 512-column chunk)
+    item, and one launch holds fewer than 2^32 lanes; a handle with more
+    items than that is rejected before anything is enqueued (2^22 tokens,
+    top-8 over 8 ranks, hidden 7168: a valid config, but 2^25 rows x 14
+    chunks)."""
     L = ep.lib()
     h = ep.ep_ranked_handle_t()
-    h.config = ep.ep_config_t(1 << 24, 7168, 32, 32, 32, 1)
-    h.capacity = (1 << 24) * 32
-    h.ranked_capacity = (1 << 24) * 32
+    h.config = ep.ep_config_t(1 << 22, 7168, 8, 32, 8, 1)
+    h.capacity = (1 << 22) * 8
+    h.ranked_capacity = (1 << 22) * 8
     for i, name in enumerate(("rank_token_offsets", "tok_rank_row", "tok_slot_row",
                               "ne_topk_idx", "ne_topk_weights", "ne_src")):
         setattr(h, name, 0x100000 * (i + 1))
     P = ctypes.c_void_p(256)
     st = L.ep_combine_ranked(ctypes.byref(h), P, 1, P, P, None)
+    assert st == ep.EP_ERR_INVALID_ARG
+    assert "too large" in L.ep_last_error().decode()
+    h.ranked_capacity = ((1 << 26) - 4) // 14 + 1
+    assert L.ep_combine_ranked(ctypes.byref(h), P, 1, P, P, None) == ep.EP_ERR_INVALID_ARG
+    assert "too large" in L.ep_last_error().decode()
+
+
+def test_combine_backward_rejects_too_many_tokens_before_launch():
+    """Combine backward runs one 256-lane workgroup per token, so at most
+    2^24 - 1 tokens fit one launch (hidden 8 keeps the config itself valid)."""
+    L = ep.lib()
+    h = ep.ep_handle_t()
+    h.config = ep.ep_config_t(1 << 24, 8, 1, 1, 1, 1)
+    h.capacity = 1 << 24
+    h.tok_slot_row = 256
+    P = ctypes.c_void_p(256)
+    st = L.ep_combine_backward(ctypes.byref(h), P, None, P, P, None, None)
     assert st == ep.EP_ERR_INVALID_ARG
     assert "too large" in L.ep_last_error().decode()
 
@@ -193,7 +211,7 @@ def _config_is_valid(T, H, k, E, R, A):
     return (T >= 0 and H >= 8 and H % 8 == 0 and 1 <= E <= 1024 and 1 <= k <= min(E, 32)
             and 1 <= R <= 64 and E % R == 0 and A >= 1
             and T * k + E * (A - 1) < int32_max
-            and T * -(-H // 512) < int32_max)
+            and T * -(-H // 512) <= 2**26 - 4)
 
 
 @st.composite
@@ -207,7 +225,7 @@ def _configs(draw):
     A = draw(st.sampled_from([1, 2, 4, 128]))
     T = draw(st.one_of(st.integers(0, 5000), st.sampled_from([
         (2**31 - 1 - E * (A - 1)) // k, (2**31 - 1 - E * (A - 1)) // k + 1,
-        (2**31 - 1) // -(-H // 512), (2**31 - 1) // -(-H // 512) + 1])))
+        (2**26 - 4) // -(-H // 512), (2**26 - 4) // -(-H // 512) + 1])))
     f = [T, H, k, E, R, A]
     edits = {0: [-1, 2**31 - 1], 1: [0, 4, H + 4, 12], 2: [0, E + 1, 33], 3: [0, 1025, E + 1],
              4: [0, 65, 3, E + 1], 5: [0, -1, 2**30]}
