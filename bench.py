@@ -30,7 +30,7 @@ call's kernels the same way over K more cold steps.  Also reported: warm steps
 after a write pass (`cold_dirty`, which also pays for writing back the
 scratch's dirty lines).
 
-Prints one JSON line.  --gpus above 1 exits: this build runs on one GPU.
+Prints one JSON line.  --gpus above 1 exits: the library runs on one GPU per process.
 """
 from __future__ import annotations
 
@@ -745,7 +745,7 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the library runs on one GPU per process; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
