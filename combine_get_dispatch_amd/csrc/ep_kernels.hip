@@ -1673,13 +1673,14 @@ __global__ __launch_bounds__(kBlock) void dispatch_ranked_kernel(
 // Receiver-side expand: non-expanded row q (rank r, token t) goes to the
 // expert-major row of each of its local slots.  One wave per (received row,
 // batch of kExpandBatch 1024-column chunks: the whole row up to H = 8192);
-// the first batch's wave also writes the rows' sources and gates.  The loads take three round trips:
-// the row count and the workspace header (a row past the count has nothing
-// to load); then the batch's payload with everything that depends on q
-// alone (the partition starts that give r, the source token, the local ids
-// and gates); then everything that depends on t and the expert (the slot
-// words, segment starts and tile bases).  Buffer loads give lanes with
-// nothing to load zeros, so no load has a branch of its own.
+// the first batch's wave also writes the rows' sources and gates.  The
+// loads take three round trips: the row count and the workspace header (a
+// row past the count has nothing to load); then the batch's payload with
+// everything that depends on q alone (the partition starts that give r, the
+// source token, the local ids and gates); then everything that depends on t
+// and the expert (the slot words, segment starts and tile bases).  Buffer
+// loads give lanes with nothing to load zeros, so no load has a branch of
+// its own.
 constexpr int kExpandBatch = 8;
 
 template <bool kFp8>
