@@ -272,27 +272,47 @@ def load_trace_cold_us(workload: str, kernel: str):
     return float(v) if v is not None else None
 
 
+def _trace_rows(run_dir: str, name: str) -> list:
+    import csv
+
+    with open(os.path.join(run_dir, "trace", name)) as f:
+        return list(csv.DictReader(f))
+
+
+def _launch_table(run_dir: str, title: str, cmd: str) -> list:
+    """Markdown lines: the command, then every kernel's statistics over all
+    launches of a rocprofv3 --kernel-trace --stats run (run_dir/trace)."""
+    lines = ["# Kernel durations, " + title, "", "Command:", "", "    " + cmd, "",
+             "All launches:", "",
+             "| kernel | calls | average (us) | min (us) | max (us) |", "|---|---|---|---|---|"]
+    for r in _trace_rows(run_dir, "ep_kernel_stats.csv"):
+        lines.append(f"| {short_kernel_name(r['Name'])} | {r['Calls']} | "
+                     f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} |")
+    return lines
+
+
+def ranked_trace_summary(run_dir: str, workload: str, cmd: str) -> None:
+    """Summarise a kernel trace of `bench.py --ranked` into
+    profiles/ranked_<workload>_kernel_trace.md: every kernel's statistics
+    over all launches.  That mode runs its steps back to back (warm), so the
+    averages hold no per-phase split."""
+    lines = _launch_table(run_dir, f"non-expanded path, {workload} workload", cmd)
+    with open(os.path.join(ROOT, "profiles", f"ranked_{workload}_kernel_trace.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"ranked trace summary written for {workload}")
+
+
 def trace_summary(run_dir: str, workload: str, cmd: str, warmup: int, steps: int) -> None:
     """Summarise a rocprofv3 --kernel-trace --stats run of the default
     command (run_dir/trace) into profiles/<workload>_kernel_trace.md: every
     kernel's statistics over all launches, and the step kernels' averages
     per phase (cold, warm, cold_dirty), taken from the launch order."""
-    import csv
     import statistics
 
-    def rows(name):
-        with open(os.path.join(run_dir, "trace", name)) as f:
-            return list(csv.DictReader(f))
-
-    stats = {r["Name"]: r for r in rows("ep_kernel_stats.csv")}
-    launches = sorted(rows("ep_kernel_trace.csv"), key=lambda r: int(r["Dispatch_Id"]))
-    lines = ["# Kernel durations, " + workload + " workload", "", "Command:", "",
-             "    " + cmd, "", "All launches:", "",
-             "| kernel | calls | average (us) | min (us) | max (us) |", "|---|---|---|---|---|"]
-    for name, r in stats.items():
-        lines.append(f"| {short_kernel_name(name)} | {r['Calls']} | "
-                     f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
-                     f"{float(r['MaxNs']) / 1e3:.2f} |")
+    launches = sorted(_trace_rows(run_dir, "ep_kernel_trace.csv"),
+                      key=lambda r: int(r["Dispatch_Id"]))
+    lines = _launch_table(run_dir, workload + " workload", cmd)
     ph = phase_slices(warmup, steps)
     total = ph["cold_dirty"][1]
     lines += ["", f"Step kernels per phase, by launch order (warm-up {warmup} steps, then "
@@ -728,6 +748,13 @@ def main():
                          "(--warmup and --steps as in the traced command)")
     args = ap.parse_args()
 
+    if args.trace_summary and args.ranked:
+        ranked_trace_summary(
+            args.trace_summary, args.workload,
+            "rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace -o ep -- "
+            "python3 bench.py --ranked --no-cpu-baseline"
+            + ("" if args.workload == "prefill" else f" --workload {args.workload}"))
+        return
     if args.pmc_summary or args.trace_summary:
         base = (f"python3 bench.py --workload {args.workload} --steps 3 --warmup 1 "
                 f"--no-cpu-baseline --copy-probe-mib 256")
