@@ -292,15 +292,15 @@ def _launch_table(run_dir: str, title: str, cmd: str) -> list:
     return lines
 
 
-def ranked_trace_summary(run_dir: str, workload: str, cmd: str) -> None:
-    """Summarise a kernel trace of `bench.py --ranked` into
-    profiles/ranked_<workload>_kernel_trace.md: every kernel's statistics
-    over all launches.  That mode runs its steps back to back (warm), so the
-    averages hold no per-phase split."""
-    lines = _launch_table(run_dir, f"non-expanded path, {workload} workload", cmd)
-    with open(os.path.join(ROOT, "profiles", f"ranked_{workload}_kernel_trace.md"), "w") as f:
+def mode_trace_summary(run_dir: str, mode: str, title: str, workload: str, cmd: str) -> None:
+    """Summarise a kernel trace of one of the bench's other modes (`--ranked`,
+    `--direction backward`) into profiles/<mode>_<workload>_kernel_trace.md:
+    every kernel's statistics over all launches.  Those modes run their steps
+    back to back (warm), so the averages hold no per-phase split."""
+    lines = _launch_table(run_dir, f"{title}, {workload} workload", cmd)
+    with open(os.path.join(ROOT, "profiles", f"{mode}_{workload}_kernel_trace.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
-    print(f"ranked trace summary written for {workload}")
+    print(f"{mode} trace summary written for {workload}")
 
 
 def trace_summary(run_dir: str, workload: str, cmd: str, warmup: int, steps: int) -> None:
@@ -748,11 +748,13 @@ def main():
                          "(--warmup and --steps as in the traced command)")
     args = ap.parse_args()
 
-    if args.trace_summary and args.ranked:
-        ranked_trace_summary(
-            args.trace_summary, args.workload,
+    if args.trace_summary and (args.ranked or args.direction == "backward"):
+        mode, title, flag = (("ranked", "non-expanded path", "--ranked") if args.ranked else
+                             ("backward", "backward pair", "--direction backward"))
+        mode_trace_summary(
+            args.trace_summary, mode, title, args.workload,
             "rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace -o ep -- "
-            "python3 bench.py --ranked --no-cpu-baseline"
+            f"python3 bench.py {flag} --no-cpu-baseline"
             + ("" if args.workload == "prefill" else f" --workload {args.workload}"))
         return
     if args.pmc_summary or args.trace_summary:
