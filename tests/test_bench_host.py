@@ -213,3 +213,23 @@ def test_logical_network_bytes_counts_token_rank_rows():
     assert got["remote_rows"] == 2
     w8 = types.SimpleNamespace(num_tokens=4, hidden=256, num_ranks=2, fp8=True)
     assert bench.logical_network_bytes(w8, b)["dispatch_bytes"] == 6 * (256 + 8)
+
+
+def test_mode_trace_summary_lists_every_kernel(tmp_path, monkeypatch):
+    """The summary of a --ranked or backward trace keeps each kernel's calls
+    and its average, minimum and maximum duration, in microseconds."""
+    run = tmp_path / "run" / "trace"
+    run.mkdir(parents=True)
+    (run / "ep_kernel_stats.csv").write_text(
+        '"Name","Calls","TotalDurationNs","AverageNs","Percentage","MinNs","MaxNs","StdDev"\n'
+        '"void ep::expand_kernel<true>(ep::Dims, int)",3,300000,100000,50.0,90000,110000,1.0\n'
+        '"__amd_rocclr_copyBuffer",2,5000,2500,1.0,2000,3000,1.0\n')
+    root = tmp_path / "root"
+    (root / "profiles").mkdir(parents=True)
+    monkeypatch.setattr(bench, "ROOT", str(root))
+    bench.mode_trace_summary(str(tmp_path / "run"), "ranked", "non-expanded path", "prefill",
+                             "rocprofv3 ... -- python3 bench.py --ranked")
+    text = (root / "profiles" / "ranked_prefill_kernel_trace.md").read_text()
+    assert "python3 bench.py --ranked" in text
+    assert "| ep::expand_kernel<true> | 3 | 100.00 | 90.00 | 110.00 |" in text
+    assert "| __amd_rocclr_copyBuffer | 2 | 2.50 | 2.00 | 3.00 |" in text
